@@ -1,0 +1,175 @@
+"""MI355X (gfx950) Kimi Delta Attention forward: chunked prefill and in-place decode.
+
+Thin Python binding over the C ABI in ``include/kda.h`` (``libkda.so``).  It only
+marshals arguments: checks dtypes, devices and contiguity, allocates outputs with
+torch, and passes device pointers plus the current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback, and a missing
+library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    """A non-zero status from the KDA C ABI."""
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkda.so (built in-tree by ``gated_delta_rule_39_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"KDA HIP library not built: {LIB_PATH} is missing; run "
+            "`python -m gated_delta_rule_39_amd.build` (or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    L.kda_abi_version.restype = ctypes.c_int
+    L.kda_abi_version.argtypes = []
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_status_string.argtypes = [ctypes.c_int]
+    L.kda_prefill.restype = ctypes.c_int
+    L.kda_prefill.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32,
+                              f32, vp, vp, vp, vp, sz, vp]
+    L.kda_prefill_workspace_bytes.restype = sz
+    L.kda_prefill_workspace_bytes.argtypes = [ctypes.c_int, i32, i64, i32, i32, i32]
+    L.kda_prefill_plan.restype = ctypes.c_int
+    L.kda_prefill_plan.argtypes = [ctypes.c_int, i32, i32, i32, i32,
+                                   ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.kda_decode_step.restype = ctypes.c_int
+    L.kda_decode_step.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                  f32, vp]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise KDAError(lib().kda_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (HIP) tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def prefill_plan(dtype: torch.dtype, N: int, H: int, d_k: int, d_v: int) -> Tuple[int, int]:
+    """(v_tiles, workgroups) the prefill launch uses for these sizes."""
+    nv, wg = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().kda_prefill_plan(_DTYPE_CODE[dtype], N, H, d_k, d_v, ctypes.byref(nv),
+                                  ctypes.byref(wg)))
+    return nv.value, wg.value
+
+
+def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None,
+            output_final_state=True, out=None, final_state=None):
+    """Chunked KDA forward over packed sequences.
+
+    q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (all fp32 or all bf16); g (log alpha):
+    [B, T, H, d_k] fp32; beta: [B, T, H] fp32; cu_seqlens: int32 [N+1] device tensor
+    (B must be 1) or None (N = B); initial_state: [N, H, d_v, d_k] fp32 or None.
+    ``final_state`` may be passed (and may be ``initial_state`` itself) to write the
+    state in place.  Returns (o [B, T, H, d_v], final_state or None).
+    """
+    dev = q.device
+    _need(q, "q", device=dev)
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"q/k/v must be float32 or bfloat16, got {dt}")
+    for t, nm in ((k, "k"), (v, "v")):
+        _need(t, nm, dtype=dt, device=dev)
+    _need(g, "g", dtype=torch.float32, device=dev)
+    _need(beta, "beta", dtype=torch.float32, device=dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, d_v) \
+            or beta.shape != (B, T, H):
+        raise ValueError("inconsistent q/k/v/g/beta shapes")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=dev)
+        N = cu_seqlens.numel() - 1
+        if B != 1:
+            raise ValueError("packed sequences (cu_seqlens) need B == 1")
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", dtype=torch.float32, device=dev)
+        if initial_state.shape != (N, H, d_v, d_k):
+            raise ValueError("initial_state must be [N, H, d_v, d_k]")
+    if scale is None:
+        scale = d_k ** -0.5
+    o = out if out is not None else torch.empty((B, T, H, d_v), dtype=dt, device=dev)
+    _need(o, "out", dtype=dt, device=dev)
+    fs = final_state
+    if fs is None and output_final_state:
+        fs = torch.empty((N, H, d_v, d_k), dtype=torch.float32, device=dev)
+    if fs is not None:
+        _need(fs, "final_state", dtype=torch.float32, device=dev)
+        if fs.shape != (N, H, d_v, d_k):
+            raise ValueError("final_state must be [N, H, d_v, d_k]")
+    _check(lib().kda_prefill(_DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(cu_seqlens), N, B, T, H, d_k, d_v, float(scale),
+                             _ptr(initial_state), _ptr(fs), _ptr(o), None, 0, _stream(dev)))
+    return o, fs
+
+
+def decode_step(q, k, v, g, beta, state, *, scale=None, out=None):
+    """One decode token per (sequence, head); ``state`` [N, H, d_v, d_k] fp32 is
+    updated in place.  q, k: [N, H, d_k]; v: [N, H, d_v]; g: [N, H, d_k] fp32;
+    beta: [N, H] fp32.  Returns o [N, H, d_v]."""
+    dev = q.device
+    _need(q, "q", device=dev)
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"q/k/v must be float32 or bfloat16, got {dt}")
+    for t, nm in ((k, "k"), (v, "v")):
+        _need(t, nm, dtype=dt, device=dev)
+    _need(g, "g", dtype=torch.float32, device=dev)
+    _need(beta, "beta", dtype=torch.float32, device=dev)
+    _need(state, "state", dtype=torch.float32, device=dev)
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (N, H, d_v) \
+            or beta.shape != (N, H) or state.shape != (N, H, d_v, d_k):
+        raise ValueError("inconsistent decode shapes")
+    if scale is None:
+        scale = d_k ** -0.5
+    o = out if out is not None else torch.empty((N, H, d_v), dtype=dt, device=dev)
+    _need(o, "out", dtype=dt, device=dev)
+    _check(lib().kda_decode_step(_DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(state), _ptr(o), N, H, d_k, d_v, float(scale), _stream(dev)))
+    return o

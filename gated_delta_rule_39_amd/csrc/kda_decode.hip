@@ -1,0 +1,108 @@
+// One-token KDA decode step on gfx950: the state is streamed through once and
+// updated in place.
+//
+// Per (sequence, head) the state S (d_v rows x d_k columns, fp32, d_k contiguous)
+// is read once and written once.  For each row i (value index):
+//   decayed_i = s_i * alpha            (alpha = exp(g) per key channel)
+//   p_i       = decayed_i . k          (prediction for the key)
+//   r_i       = decayed_i . (scale q)  (read of the decayed state)
+//   e_i       = beta (v_i - p_i)
+//   s_i      <- decayed_i + e_i k
+//   o_i       = r_i + e_i (k . scale q)
+// which is the step-by-step page's decay / predict / error / correct / read cycle
+// ("Kimi Delta Attention: The Linear Attention Behind Kimi K2 and Qwen3",
+// "How Kimi Delta Attention works step by step") for one token, with the read of
+// the corrected state expanded as (decayed + e k^T) scale q.  The deep-dive page
+// ("Systems and implementation tradeoffs" -> "Decoding", "Kernel design") asks for
+// exactly this: one state update plus one query-state product per token, fused,
+// with the state updated in place and no intermediate tensors.
+//
+// HBM-bound: 8 bytes of state traffic per element against ~4 flops.  Launch: one
+// 256-thread workgroup per (sequence, head); each row of d_k floats is covered by
+// d_k/4 lanes holding one float4 each, so every wave load is a contiguous,
+// fully coalesced 1 KiB; all of a thread's state rows are loaded before any is
+// reduced, so each workgroup keeps its whole 64 KiB tile in flight.
+
+#include "kda_device.h"
+
+namespace kda {
+
+template <typename Tin, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
+    Tin* __restrict__ o, float scale) {
+  constexpr int LPR = DK / 4;      // lanes covering one state row
+  constexpr int RPP = 256 / LPR;   // rows per pass of the workgroup
+  constexpr int NP = DV / RPP;     // passes (rows per thread)
+  static_assert(NP * RPP == DV, "d_v must be a multiple of the rows per pass");
+
+  const int unit = blockIdx.x;     // sequence * H + head
+  const int tid = threadIdx.x;
+  const int c4 = tid % LPR;        // this thread's 4 key channels: 4*c4 .. 4*c4+3
+  const int r0 = tid / LPR;        // first row; rows r0 + RPP*i
+
+  const int64_t kbase = static_cast<int64_t>(unit) * DK + 4 * c4;
+  const int64_t vbase = static_cast<int64_t>(unit) * DV;
+  float* S = state + static_cast<int64_t>(unit) * DV * DK + 4 * c4;
+
+  // Issue every state load first: the whole tile is in flight at once.
+  f32x4 s[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i)
+    s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (r0 + RPP * i) * DK));
+
+  const f32x4 kk = load4(k + kbase);
+  f32x4 qq = load4(q + kbase);
+  qq *= scale;
+  const f32x4 gg = load4(g + kbase);
+  const f32x4 a = f32x4{exp_hw(gg[0]), exp_hw(gg[1]), exp_hw(gg[2]), exp_hw(gg[3])};
+  const float b = beta[unit];
+  float vv[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) vv[i] = to_f32(v[vbase + r0 + RPP * i]);
+
+  const float kq = group_sum<LPR>(dot4(kk, qq));
+
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const f32x4 d = s[i] * a;
+    const float p = group_sum<LPR>(dot4(d, kk));
+    const float r = group_sum<LPR>(dot4(d, qq));
+    const float e = b * (vv[i] - p);
+    const f32x4 sn = d + e * kk;
+    __builtin_nontemporal_store(sn, reinterpret_cast<f32x4*>(S + (r0 + RPP * i) * DK));
+    if (c4 == 0) o[vbase + r0 + RPP * i] = from_f32<Tin>(r + e * kq);
+  }
+}
+
+template <typename Tin, int DK, int DV>
+static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, float* state, void* o, int32_t units,
+                                  float scale, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<Tin, DK, DV>), dim3(units), dim3(256), 0, stream,
+                     static_cast<const Tin*>(q), static_cast<const Tin*>(k),
+                     static_cast<const Tin*>(v), g, beta, state, static_cast<Tin*>(o), scale);
+  return hipGetLastError();
+}
+
+template <typename Tin>
+static hipError_t launch_decode_d(int dk, int dv, const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta, float* state, void* o,
+                                  int32_t units, float scale, hipStream_t stream) {
+  if (dk == 64 && dv == 64) return launch_decode_t<Tin, 64, 64>(q, k, v, g, beta, state, o, units, scale, stream);
+  if (dk == 64 && dv == 128) return launch_decode_t<Tin, 64, 128>(q, k, v, g, beta, state, o, units, scale, stream);
+  if (dk == 128 && dv == 64) return launch_decode_t<Tin, 128, 64>(q, k, v, g, beta, state, o, units, scale, stream);
+  return launch_decode_t<Tin, 128, 128>(q, k, v, g, beta, state, o, units, scale, stream);
+}
+
+// Called by the C ABI after validation: dtype 0 = fp32, 1 = bf16; dk, dv in {64, 128}.
+hipError_t launch_decode(int dtype, int dk, int dv, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, float* state, void* o,
+                         int32_t units, float scale, hipStream_t stream) {
+  if (dtype == 1)
+    return launch_decode_d<bf16>(dk, dv, q, k, v, g, beta, state, o, units, scale, stream);
+  return launch_decode_d<float>(dk, dv, q, k, v, g, beta, state, o, units, scale, stream);
+}
+
+}  // namespace kda

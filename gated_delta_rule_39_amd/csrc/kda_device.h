@@ -1,0 +1,49 @@
+// Device-side helpers shared by the gfx950 KDA kernels (decode and prefill).
+// gfx950 only: 64-wide wavefronts, MFMA 16x16 tiles, hardware bf16 conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// e^x through the hardware base-2 exponential (v_exp_f32).
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// round-to-nearest-even through the gfx950 conversion instruction
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// Four consecutive elements of an fp32 or bf16 array, widened to fp32.
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load4(const bf16* p) {
+  bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+               static_cast<float>(v[3])};
+}
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
+  return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64); every lane
+// of the group receives the total.
+template <int width>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = width / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, width);
+  return x;
+}
+
+}  // namespace kda

@@ -1,0 +1,129 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * The operation (per independent unit = one sequence, one head): a state S with
+ * d_v rows and d_k columns maps keys to values.  For each token t, with
+ * alpha_t = exp(g_t) per key channel:
+ *   decay    S~  = S_{t-1} Diag(alpha_t)          (column j scaled by alpha_t[j])
+ *   predict  p   = S~ k_t
+ *   error    e   = beta_t (v_t - p)
+ *   correct  S_t = S~ + e k_t^T
+ *   read     o_t = S_t (scale q_t)
+ * Source: "Kimi Delta Attention: The Linear Attention Behind Kimi K2 and Qwen3"
+ * (elsolitario.org), section "How Kimi Delta Attention works step by step"
+ * (listing and flowchart); scale defaults to d_k^{-1/2} there.  Chunked prefill
+ * and in-place one-token decode follow "Kimi Delta Attention Technical Deep Dive"
+ * (mohalkarushikesh.github.io), "Systems and implementation tradeoffs"
+ * ("Training", "Decoding", "Kernel design": one state layout for both paths).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP device memory of the current
+ *    device), row-major and contiguous in the layouts stated.  The caller owns
+ *    every buffer; the library allocates nothing and keeps no state except a
+ *    per-device cached compute-unit count.
+ *  - Calls enqueue work on `stream` and return at once; nothing synchronises with
+ *    the host.  A device fault surfaces at the caller's next synchronisation.
+ *  - Every argument is validated before any HIP call.  Status codes are below;
+ *    nothing throws across the ABI.
+ *  - Unchecked device-side preconditions: keys L2-normalised; g <= 0 with the
+ *    per-64-token-chunk sum of |g| below about 80 per channel; beta in [0, 2];
+ *    cu_seqlens non-decreasing with cu[0] = 0 and cu[N] = B*T.  Outside these the
+ *    numerics are defined but not guaranteed; NaN propagates.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+/* dtype of q, k, v and o.  g, beta and all states are always fp32. */
+enum { KDA_F32 = 0, KDA_BF16 = 1 };
+
+enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                          */
+  KDA_ERR_BAD_SHAPE = 2,    /* negative or inconsistent sizes                      */
+  KDA_ERR_UNSUPPORTED = 3,  /* d_k or d_v not in {64, 128}                         */
+  KDA_ERR_BAD_DTYPE = 4,    /* dtype not KDA_F32 / KDA_BF16                         */
+  KDA_ERR_HIP = 5           /* kernel launch failed (hipGetLastError)              */
+};
+
+/* Returns KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* kda_status_string(int status);
+
+/*
+ * kda_prefill -- chunked (64-token chunks) forward over N sequences.
+ *
+ * Layout: token rows are packed as [B, T, H, d]: element (row r, head h,
+ * channel j) is at ((r * H + h) * d + j).
+ *   q, k : [B, T, H, d_k]  dtype      v, o : [B, T, H, d_v]  dtype
+ *   g    : [B, T, H, d_k]  fp32 (log alpha)
+ *   beta : [B, T, H]       fp32
+ *   cu_seqlens : [N + 1] int32 on the device, or NULL.  With NULL, N must equal B
+ *     and sequence n is batch row n (rows n*T .. n*T+T-1).  Otherwise B must be 1
+ *     and sequence n is rows cu[n] .. cu[n+1]-1 of the T packed rows; empty
+ *     sequences are allowed.
+ *   initial_state : [N, H, d_v, d_k] fp32, or NULL for zeros.
+ *   final_state   : [N, H, d_v, d_k] fp32, or NULL (not written).  It may alias
+ *     initial_state exactly (each state tile is read before it is written).
+ *   o : written for every token row that belongs to a sequence.
+ * N = 0 or T = 0 is a no-op returning KDA_OK (nothing launched).
+ * scale: query scale (the pages use d_k^{-1/2}).
+ * workspace / workspace_bytes: reserved, pass NULL / 0 (the fused kernel keeps
+ * every intermediate on chip).
+ */
+int kda_prefill(int dtype,
+                const void* q, const void* k, const void* v,
+                const float* g, const float* beta,
+                const int32_t* cu_seqlens,
+                int32_t N, int32_t B, int64_t T, int32_t H, int32_t d_k, int32_t d_v,
+                float scale,
+                const float* initial_state, float* final_state,
+                void* o,
+                void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* Device workspace kda_prefill needs for these sizes (0 for this library). */
+size_t kda_prefill_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_t H,
+                                   int32_t d_k, int32_t d_v);
+
+/*
+ * Launch geometry kda_prefill would use on the current device: the number of
+ * d_v tiles each (sequence, head) is split into (rows of S never mix, so the
+ * tiles run independently) and the resulting workgroup count.  Either output
+ * pointer may be NULL.  Host-only apart from a cached device-attribute query.
+ */
+int kda_prefill_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                     int32_t* v_tiles, int32_t* workgroups);
+
+/*
+ * kda_decode_step -- one token per (sequence, head); the state is advanced IN
+ * PLACE ("Decoding": one state update and one query-state product per token,
+ * cost independent of the context length).
+ *   q, k : [N, H, d_k] dtype     v, o : [N, H, d_v] dtype
+ *   g    : [N, H, d_k] fp32      beta : [N, H] fp32
+ *   state: [N, H, d_v, d_k] fp32, read and overwritten.
+ * N = 0 is a no-op returning KDA_OK.
+ */
+int kda_decode_step(int dtype,
+                    const void* q, const void* k, const void* v,
+                    const float* g, const float* beta,
+                    float* state, void* o,
+                    int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                    float scale, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,88 @@
+"""C ABI: the library loads, exports every declared symbol, and validates arguments
+before any HIP call (so these run without a GPU and launch nothing)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_39_amd as kda
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "kda.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kda.LIB_PATH),
+                                reason="libkda.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"kda_prefill", "kda_decode_step", "kda_abi_version", "kda_status_string",
+            "kda_prefill_workspace_bytes", "kda_prefill_plan"} <= set(names)
+    L = kda.lib()
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in kda.h but not exported"
+
+
+def test_version_and_status_strings():
+    L = kda.lib()
+    assert L.kda_abi_version() == 1
+    for code in range(6):
+        s = L.kda_status_string(code).decode()
+        assert s.startswith("KDA")
+    assert "unknown" in L.kda_status_string(99).decode()
+    assert L.kda_prefill_workspace_bytes(1, 8, 1 << 20, 16, 128, 128) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def prefill_status(dtype=1, N=1, B=1, T=64, H=2, dk=64, dv=64, cu=None, q=FAKE, o=FAKE,
+                   state=None):
+    L = kda.lib()
+    return L.kda_prefill(dtype, q, FAKE, FAKE, FAKE, FAKE, cu, N, B, T, H, dk, dv, 0.125,
+                         state, state, o, None, 0, None)
+
+
+def test_prefill_validation_codes():
+    assert prefill_status(dtype=7) == 4                 # bad dtype
+    assert prefill_status(dk=96) == 3                   # unsupported head dim
+    assert prefill_status(dv=256) == 3
+    assert prefill_status(N=-1) == 2                    # bad shape
+    assert prefill_status(T=-5) == 2
+    assert prefill_status(H=0) == 2
+    assert prefill_status(N=2, B=1) == 2                # N != B without cu_seqlens
+    assert prefill_status(cu=FAKE, N=2, B=2) == 2       # packed needs B == 1
+    assert prefill_status(q=None) == 1                  # NULL input
+    assert prefill_status(o=None) == 1
+    assert prefill_status(N=0, B=0) == 0                # nothing to do: no launch
+    assert prefill_status(T=0) == 0                     # empty and no final state
+
+
+def test_decode_validation_codes():
+    L = kda.lib()
+
+    def st(dtype=1, N=4, H=2, dk=128, dv=128, state=FAKE):
+        return L.kda_decode_step(dtype, FAKE, FAKE, FAKE, FAKE, FAKE, state, FAKE, N, H, dk, dv,
+                                 0.1, None)
+
+    assert st(dtype=3) == 4
+    assert st(dk=32) == 3
+    assert st(N=-1) == 2
+    assert st(H=0) == 2
+    assert st(state=None) == 1
+    assert st(N=0) == 0
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError, match="device"):
+        kda.prefill(x, x, x, x, torch.zeros(1, 4, 1))
