@@ -52,6 +52,9 @@ def lib() -> ctypes.CDLL:
     L.kda_prefill_plan.restype = ctypes.c_int
     L.kda_prefill_plan.argtypes = [ctypes.c_int, i32, i32, i32, i32,
                                    ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.kda_prefill_coop_plan.restype = ctypes.c_int
+    L.kda_prefill_coop_plan.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.POINTER(i32),
+                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                   f32, vp]
@@ -93,15 +96,49 @@ def prefill_plan(dtype: torch.dtype, N: int, H: int, d_k: int, d_v: int) -> Tupl
     return nv.value, wg.value
 
 
+def prefill_coop_plan(dtype: torch.dtype, N: int, H: int, d_k: int, d_v: int):
+    """(consumers, producers, ring_slots) of the producer/consumer prefill, or zeros."""
+    a, b, c = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().kda_prefill_coop_plan(_DTYPE_CODE[dtype], N, H, d_k, d_v, ctypes.byref(a),
+                                       ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def workspace_bytes(dtype: torch.dtype, N: int, T_total: int, H: int, d_k: int, d_v: int) -> int:
+    """Workspace size that selects the producer/consumer prefill (0: not applicable)."""
+    return int(lib().kda_prefill_workspace_bytes(_DTYPE_CODE[dtype], N, T_total, H, d_k, d_v))
+
+
+_workspaces = {}
+
+
+def _auto_workspace(device, nbytes: int):
+    """A workspace of at least ``nbytes`` cached per (device, stream): calls that share
+    it are ordered on that stream."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def workspace_aborted(ws: torch.Tensor) -> bool:
+    """True if the last producer/consumer call on ``ws`` stopped early (synchronises)."""
+    return int(ws[:4].view(torch.int32).item()) != 0
+
+
 def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None,
-            output_final_state=True, out=None, final_state=None):
+            output_final_state=True, out=None, final_state=None, workspace="auto"):
     """Chunked KDA forward over packed sequences.
 
     q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (all fp32 or all bf16); g (log alpha):
     [B, T, H, d_k] fp32; beta: [B, T, H] fp32; cu_seqlens: int32 [N+1] device tensor
     (B must be 1) or None (N = B); initial_state: [N, H, d_v, d_k] fp32 or None.
     ``final_state`` may be passed (and may be ``initial_state`` itself) to write the
-    state in place.  Returns (o [B, T, H, d_v], final_state or None).
+    state in place.  ``workspace``: "auto" (a cached device buffer when the
+    producer/consumer kernel applies), None (fused kernel), or a uint8 device tensor.
+    Returns (o [B, T, H, d_v], final_state or None).
     """
     dev = q.device
     _need(q, "q", device=dev)
@@ -141,9 +178,19 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None
         _need(fs, "final_state", dtype=torch.float32, device=dev)
         if fs.shape != (N, H, d_v, d_k):
             raise ValueError("final_state must be [N, H, d_v, d_k]")
+    ws = None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+        nb = workspace_bytes(dt, N, B * T, H, d_k, d_v)
+        ws = _auto_workspace(dev, nb) if nb > 0 else None
+    elif workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, device=dev)
+        ws = workspace
     _check(lib().kda_prefill(_DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(cu_seqlens), N, B, T, H, d_k, d_v, float(scale),
-                             _ptr(initial_state), _ptr(fs), _ptr(o), None, 0, _stream(dev)))
+                             _ptr(initial_state), _ptr(fs), _ptr(o), _ptr(ws),
+                             0 if ws is None else ws.numel(), _stream(dev)))
     return o, fs
 
 

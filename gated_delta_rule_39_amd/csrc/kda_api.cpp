@@ -8,17 +8,7 @@
 #include <cstdlib>
 #include <hip/hip_runtime_api.h>
 
-namespace kda {
-hipError_t launch_decode(int dtype, int dk, int dv, const void* q, const void* k, const void* v,
-                         const float* g, const float* beta, float* state, void* o,
-                         int32_t units, float scale, hipStream_t stream);
-hipError_t launch_prefill(int dtype, int dk, int bv, const void* q, const void* k,
-                          const void* v, const float* g, const float* beta, const int32_t* cu,
-                          int64_t T, int32_t H, int32_t DV, int32_t NV, int32_t units,
-                          int32_t xcd_remap, float scale, const float* s0, float* s1, void* o,
-                          hipStream_t stream);
-int prefill_max_bv(int dtype, int dk);
-}  // namespace kda
+#include "kda_launch.h"
 
 namespace {
 
@@ -55,6 +45,40 @@ int choose_bv(int dtype, int32_t units, int32_t dk, int32_t dv, int cus) {
   return bv;
 }
 
+int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  return e ? std::atoi(e) : dflt;
+}
+
+// Producer/consumer geometry: W = CUs / units workgroups per unit (all resident at
+// once, one per CU), split into NC consumers (value tiles of d_v / NC rows, NC a
+// power of two, tiles of at least 16 rows) and NP = W - NC producers.  Needs bf16
+// inputs and W >= 2.  KDA_PREFILL_COOP=0 disables it; KDA_COOP_NC / KDA_COOP_NP /
+// KDA_COOP_R override the split and the ring depth (tuning only).
+struct CoopPlan {
+  int NC = 0, NP = 0, R = 0;
+  bool ok() const { return NC > 0; }
+};
+CoopPlan coop_plan(int dtype, int64_t units, int32_t d_v, int cus) {
+  CoopPlan p;
+  if (dtype != KDA_BF16 || units <= 0 || env_int("KDA_PREFILL_COOP", 1) == 0) return p;
+  int W = static_cast<int>(cus / units);
+  if (W > 16) W = 16;
+  if (W < 2) return p;
+  int nc = 1;
+  while (nc * 2 <= W / 2 && d_v / (nc * 2) >= 16) nc *= 2;
+  int np = W - nc;
+  const int enc = env_int("KDA_COOP_NC", 0), enp = env_int("KDA_COOP_NP", 0);
+  if (enc > 0 && (enc & (enc - 1)) == 0 && d_v / enc >= 16 && d_v % enc == 0) nc = enc;
+  if (enp > 0) np = enp;
+  if (static_cast<int64_t>(units) * (nc + np) > cus) return p;
+  p.NC = nc;
+  p.NP = np;
+  p.R = env_int("KDA_COOP_R", 8);
+  if (p.R < 2) p.R = 2;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -73,7 +97,30 @@ const char* kda_status_string(int status) {
   }
 }
 
-size_t kda_prefill_workspace_bytes(int, int32_t, int64_t, int32_t, int32_t, int32_t) { return 0; }
+size_t kda_prefill_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_t H, int32_t d_k,
+                                   int32_t d_v) {
+  (void)T_total;
+  if (N <= 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
+  const int64_t units = static_cast<int64_t>(N) * H;
+  if (units > (1 << 24)) return 0;
+  const CoopPlan p = coop_plan(dtype, units, d_v, cu_count());
+  if (!p.ok()) return 0;
+  return kda::prefill_coop_workspace_bytes(d_k, static_cast<int>(units), p.R);
+}
+
+int kda_prefill_coop_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                          int32_t* consumers, int32_t* producers, int32_t* ring_slots) {
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (N < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
+  if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
+  const int64_t units = static_cast<int64_t>(N) * H;
+  if (units > (1 << 24)) return KDA_ERR_BAD_SHAPE;
+  const CoopPlan p = coop_plan(dtype, units, d_v, cu_count());
+  if (consumers) *consumers = p.NC;
+  if (producers) *producers = p.NP;
+  if (ring_slots) *ring_slots = p.R;
+  return KDA_OK;
+}
 
 int kda_prefill_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
                      int32_t* v_tiles, int32_t* workgroups) {
@@ -93,8 +140,6 @@ int kda_prefill(int dtype, const void* q, const void* k, const void* v, const fl
                 int32_t H, int32_t d_k, int32_t d_v, float scale, const float* initial_state,
                 float* final_state, void* o, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
   if (N < 0 || B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
   if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
@@ -107,12 +152,37 @@ int kda_prefill(int dtype, const void* q, const void* k, const void* v, const fl
   if (static_cast<int64_t>(B) * T > 0 && (!q || !k || !v || !g || !beta || !o))
     return KDA_ERR_NULL_ARG;
   if (static_cast<int64_t>(B) * T == 0 && !final_state) return KDA_OK;
-  const int bv = choose_bv(dtype, static_cast<int32_t>(units), d_k, d_v, cu_count());
-  const int32_t nv = d_v / bv;
-  const int32_t xcd_remap = (units % 8 == 0) ? 1 : 0;
-  hipError_t err = kda::launch_prefill(dtype, d_k, bv, q, k, v, g, beta, cu_seqlens, T, H, d_v,
-                                       nv, static_cast<int32_t>(units), xcd_remap, scale,
-                                       initial_state, final_state, o, stream);
+  kda::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu_seqlens = cu_seqlens;
+  a.initial_state = initial_state;
+  a.final_state = final_state;
+  a.o = o;
+  a.T = T;
+  a.H = H;
+  a.DV = d_v;
+  a.units = static_cast<int32_t>(units);
+  a.xcd_remap = (units % 8 == 0) ? 1 : 0;
+  a.scale = scale;
+  const int cus = cu_count();
+  const CoopPlan p = coop_plan(dtype, units, d_v, cus);
+  if (p.ok() && workspace != nullptr &&
+      workspace_bytes >= kda::prefill_coop_workspace_bytes(d_k, static_cast<int>(units), p.R)) {
+    a.workspace = static_cast<unsigned char*>(workspace);
+    a.NC = p.NC;
+    a.NP = p.NP;
+    a.R = p.R;
+    if (kda::launch_prefill_coop(d_k, a, stream) == hipSuccess) return KDA_OK;
+    (void)hipGetLastError();   // not launchable as one resident grid: use the fused kernel
+  }
+  const int bv = choose_bv(dtype, static_cast<int32_t>(units), d_k, d_v, cus);
+  a.NV = d_v / bv;
+  a.workspace = nullptr;
+  hipError_t err = kda::launch_prefill(dtype, d_k, bv, a, stream);
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -24,6 +24,7 @@
 // reduced, so each workgroup keeps its whole 64 KiB tile in flight.
 
 #include "kda_device.h"
+#include "kda_launch.h"
 
 namespace kda {
 

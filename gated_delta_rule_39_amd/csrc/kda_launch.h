@@ -1,0 +1,41 @@
+// Host-side launch interface between the C ABI (kda_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Arguments of both prefill kernels (validated by the C ABI).
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const int32_t* cu_seqlens;
+  const float* initial_state;
+  float* final_state;
+  void* o;
+  unsigned char* workspace;   // producer/consumer kernel only
+  int64_t T;
+  int32_t H, DV, units;
+  int32_t NV;                 // fused kernel: value tiles per unit
+  int32_t NC, NP, R;          // producer/consumer kernel: consumers, producers, ring slots
+  int32_t xcd_remap;          // units % 8 == 0: keep a unit's workgroups on one XCD
+  float scale;
+};
+
+// dtype: 0 = fp32, 1 = bf16; dk, dv in {64, 128}.
+hipError_t launch_decode(int dtype, int dk, int dv, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, float* state, void* o,
+                         int32_t units, float scale, hipStream_t stream);
+// Fused prefill: bv in {16, 32, 64}, bv <= prefill_max_bv(dtype, dk), a.NV = DV / bv.
+hipError_t launch_prefill(int dtype, int dk, int bv, const PrefillArgs& a, hipStream_t stream);
+int prefill_max_bv(int dtype, int dk);
+// Producer/consumer prefill (bf16): a.workspace holds prefill_coop_workspace_bytes bytes.
+hipError_t launch_prefill_coop(int dk, const PrefillArgs& a, hipStream_t stream);
+size_t prefill_coop_workspace_bytes(int dk, int units, int R);
+
+}  // namespace kda

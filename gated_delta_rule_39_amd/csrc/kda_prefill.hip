@@ -1,343 +1,128 @@
-// Chunked KDA prefill on gfx950 (chunk = 64 tokens), fused into one kernel.
+// Chunked KDA prefill on gfx950 (chunk = 64 tokens).
 //
 // Method: the per-token recurrence of "Kimi Delta Attention: The Linear Attention
 // Behind Kimi K2 and Qwen3" (elsolitario.org, "How Kimi Delta Attention works step
-// by step"), evaluated a chunk at a time; the state at the end of a chunk seeds
-// the next ("Kimi Delta Attention Technical Deep Dive", "Systems and
-// implementation tradeoffs" -> "Training").  Per chunk of n <= 64 rows, starting
-// from the state S (d_v x d_k), with alpha_r = e^{g_r}:
+// by step"), evaluated a chunk at a time; the state at the end of a chunk seeds the
+// next ("Kimi Delta Attention Technical Deep Dive", "Systems and implementation
+// tradeoffs" -> "Training").  The chunk algebra and the chunk-local tiles are
+// described in kda_chunk.h; this file holds the two kernels built on them.
 //
-//   e^{G_r} = alpha_1 ... alpha_r         (inclusive prefix product per key channel)
-//   Kg_r = k_r e^{G_r}      Ki_r = k_r e^{-G_r}      Qg_r = scale q_r e^{G_r}
-//   A    = strictly-lower(diag(beta) Kg Ki^T)
-//   X    = (I + A)^{-1}                              (unit lower triangular)
-//   E    = X diag(beta) (V - Kg S^T)                 (row r = token error e_r)
-//   O    = Qg S^T + lower-incl(Qg Ki^T) E
-//   S'   = (S + E^T Ki) Diag(e^{G_n})
+// Rows of the state S (the d_v index) never mix, so each (sequence, head) -- a
+// "unit" -- is split into value tiles of BV rows that run as independent workgroups.
+// The state tile is fp32 and lives in MFMA accumulators for the whole sequence,
+// held transposed (S^T: rows = key channel) so that S^T <- (S^T + Ki^T E) Diag(e^{G_n})
+// lands in the registers that hold it; after each chunk a snapshot (bf16 on the bf16
+// path) goes to LDS as the next chunk's operand.
 //
-// This is exact (up to rounding) for any chunk size; it follows from unrolling the
-// recurrence inside the chunk.  Rows of S (the d_v index) never mix, so each
-// (sequence, head) is split into d_v tiles of BV rows that run as independent
-// workgroups; the d_v-independent chunk work is recomputed by each tile.
+// prefill_kernel (fused): one workgroup per (unit, value tile) computes the chunk
+//   tiles itself (ChunkProducer) and then the state step from LDS.  Every value tile
+//   of a unit recomputes the same chunk tiles.  Used for fp32 inputs, and whenever
+//   the producer/consumer kernel does not apply.
 //
-// Per chunk, 256 threads (4 waves), one workgroup per (seq, head, v-tile):
-//  1. factors: the chunk's g, k, q (loaded one chunk ahead, branch-free) give
-//     alpha = e^g with one hardware exp per element; e^{G_r} and e^{G_n - G_r}
-//     are prefix / suffix products (so e^{-G_r} = e^{G_n - G_r} / e^{G_n} costs
-//     one reciprocal per channel).  Kg, Qg, Ki and Ki^T go to LDS as MFMA operands.
-//  2. A and M = lower(Qg Ki^T): 20 16x16 output blocks, 5 independent MFMA chains
-//     per wave.
-//  3. X = (I + A)^{-1} in fp32, blocked 4 x 16: one wave inverts the four diagonal
-//     blocks by right-looking substitution (lane = block column) and forms the two
-//     sub-diagonal blocks; the 32x32 off-diagonal super-block follows in two
-//     fp32-MFMA steps (6 dependent 16x16 products in all).
-//  4. the state step: P = Kg S^T and Qs = Qg S^T; R' = diag(beta)(V - P);
-//     E = X R'; O = Qs + M E (stored); S^T <- (S^T + Ki^T E) Diag(e^{G_n}).
-//
-// The fp32 state tile lives in MFMA accumulators for the whole sequence, held
-// transposed (S^T: rows = key channel) so the update lands in the registers that
-// hold it; after each chunk a snapshot (bf16 on the bf16 path) goes to LDS as the
-// next chunk's operand.  bf16 inputs use v_mfma_f32_16x16x32_bf16 with fp32
-// accumulation; fp32 inputs use v_mfma_f32_16x16x4_f32 throughout, so the fp32
-// path never rounds to bf16.  The inverse is always built in fp32.
-//
-// Operand convention: an MFMA A operand is an M x K row-major LDS array, a B
-// operand is stored N x K row-major (K contiguous), so both are read with the same
-// fragment load.  A 16x16 accumulator holds D[4*(l/16)+i][l%16] in lane l.
+// prefill_coop_kernel (producer/consumer, bf16): per unit, NP producer workgroups
+//   compute each chunk's tiles once (producer p takes chunks p, p+NP, ...) and
+//   publish them into a ring of R slots in the caller's workspace, in MFMA fragment
+//   order; NC consumer workgroups (value tiles) load the fragments straight into
+//   registers, one chunk ahead, and run only the state step.  Hand-off: slots are
+//   written and read with device-scope (sc1) accesses; a producer waits until all
+//   its slot stores are acknowledged, then sets ready[slot] = chunk + 1 (a
+//   device-scope atomic); consumers poll it, read the slot, and after using a chunk
+//   add 1 to done[slot]; a producer reuses a slot only once all NC consumers are
+//   done with its previous chunk.
+//   Every wait is bounded: a wait that runs out, or sees the workspace's abort
+//   word set, sets that word and the whole grid leaves its loops, so a broken
+//   hand-off cannot hang the device (the results of such a call are invalid and the
+//   abort word stays nonzero).  The grid (units x (NC + NP) <= compute units, one
+//   workgroup per CU) is launched cooperatively, which guarantees that all its
+//   workgroups are resident at once.  The workgroups of a unit are numbered so that
+//   they run on one XCD (ids are dealt round-robin to the 8 XCDs) and the ring slots
+//   they share stay in that XCD's L2.
 
-#include "kda_device.h"
+#include "kda_chunk.h"
+#include "kda_launch.h"
 
 namespace kda {
 
-constexpr int kChunk = 64;
-constexpr int kThreads = 256;
 
-// MFMA flavour per input dtype.
-template <typename Tin> struct Mfma;
-template <> struct Mfma<bf16> {
-  using TC = bf16;                  // operand type in LDS
-  using frag = bf16x8;
-  using raw4 = bf16x4;              // four input elements as loaded
-  static constexpr int KSTEP = 32;  // K per instruction
-  static constexpr int KPL = 8;     // K elements per lane
-  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ void unit_bounds(const PrefillArgs& a, int unit, int& n_seq, int& h,
+                                            int64_t& bos, int64_t& eos) {
+  n_seq = unit / a.H;
+  h = unit % a.H;
+  if (a.cu_seqlens) {
+    bos = a.cu_seqlens[n_seq];
+    eos = a.cu_seqlens[n_seq + 1];
+  } else {
+    bos = static_cast<int64_t>(n_seq) * a.T;
+    eos = bos + a.T;
   }
+}
+
+// Workgroup id -> (unit, role index) with W workgroups per unit.  With xcd_remap the
+// W workgroups of a unit get ids congruent modulo 8 (the same XCD).
+__device__ __forceinline__ void unit_role(int x, int W, int units, int xcd_remap, int& unit,
+                                          int& role) {
+  if (xcd_remap) {
+    const int xcd = x & 7, y = x >> 3;
+    unit = xcd * (units >> 3) + y / W;
+    role = y % W;
+  } else {
+    unit = x / W;
+    role = x % W;
+  }
+}
+
+// S^T accumulator tiles of a value tile: wave w owns key blocks
+// [w * KPW, (w + 1) * KPW) for every 16-row value block, KPW = DK / 64.
+template <int DK, int BV>
+struct StateTiles {
+  static constexpr int NVB = BV / 16;
+  static constexpr int KPW = DK / 64;
+  static constexpr int NST = KPW * NVB;
+  static __device__ __forceinline__ int kb(int wave, int s) { return wave * KPW + s / NVB; }
+  static __device__ __forceinline__ int vb(int s) { return s % NVB; }
 };
-template <> struct Mfma<float> {
-  using TC = float;
-  using frag = float;
-  using raw4 = f32x4;
-  static constexpr int KSTEP = 4;
-  static constexpr int KPL = 1;
-  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-  }
-};
 
-__device__ __forceinline__ f32x4 widen(f32x4 x) { return x; }
-__device__ __forceinline__ f32x4 widen(bf16x4 x) {
-  return f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
-               static_cast<float>(x[3])};
-}
-
-// Store four consecutive operand elements (fp32 rows are padded by one float, so
-// they are written element by element; bf16 rows stay 8-byte aligned).
-__device__ __forceinline__ void store4(float* p, f32x4 x) {
-  p[0] = x[0];
-  p[1] = x[1];
-  p[2] = x[2];
-  p[3] = x[3];
-}
-__device__ __forceinline__ void store4(bf16* p, f32x4 x) {
-  *reinterpret_cast<bf16x4*>(p) = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]),
-                                         static_cast<bf16>(x[2]), static_cast<bf16>(x[3])};
-}
-
-// Fragment of a row-major M x K (or N x K) LDS array: lane l reads row row0 + l%16,
-// K elements k0 + KPL*(l/16) .. +KPL.
-template <typename M>
-__device__ __forceinline__ typename M::frag frag_rows(const typename M::TC* base, int ld, int row0,
-                                                      int k0, int lane) {
-  return *reinterpret_cast<const typename M::frag*>(base + (row0 + (lane & 15)) * ld + k0 +
-                                                    M::KPL * (lane >> 4));
-}
-
-// Fragment of an operand stored K x N (N contiguous): lane l needs column col0 + l%16,
-// K element k0 + l/16.  Only for single-element lanes (fp32).
-template <typename M>
-__device__ __forceinline__ typename M::frag frag_cols(const typename M::TC* base, int ld, int k0,
-                                                      int col0, int lane) {
-  static_assert(M::KPL == 1, "strided fragment only for single-element lanes");
-  return base[(k0 + (lane >> 4)) * ld + col0 + (lane & 15)];
-}
-
-// acc += A16 * B16 for 16x16 fp32 blocks (A row-major with stride lda, B row-major
-// K x N with stride ldb), on the fp32 MFMA.
-__device__ __forceinline__ f32x4 mm16(f32x4 acc, const float* A, int lda, const float* B, int ldb,
-                                      int lane) {
-#pragma unroll
-  for (int kk = 0; kk < 16; kk += 4)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(lane & 15) * lda + kk + (lane >> 4)],
-                                               B[(kk + (lane >> 4)) * ldb + (lane & 15)], acc, 0,
-                                               0, 0);
-  return acc;
-}
-
-// Make this wave's LDS writes visible to its own later LDS reads by other lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Workgroup barrier for LDS traffic only.  The workgroup's waves exchange data
-// through LDS alone, so the barrier waits for this wave's LDS operations
-// (lgkmcnt(0)) and leaves global loads in flight: a full __syncthreads() fence
-// would also drain the next chunk's prefetched loads.  The signal fences keep the
-// compiler from moving memory operations across it.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// The 10 lower-triangular 16x16 blocks of a 64x64 product, in two row-block pairs
-// (RA, RB) = (0, 3) or (1, 2): five blocks per wave, as five independent MFMA chains.
-template <typename M, int DK, int LDK, int RA, int RB>
-__device__ __forceinline__ void lower_blocks(f32x4 (&acc)[5], const typename M::TC* lhs,
-                                             const typename M::TC* rhs, int lane) {
-#pragma unroll
-  for (int i = 0; i < 5; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < DK; kk += M::KSTEP) {
-    const auto a0 = frag_rows<M>(lhs, LDK, 16 * RA, kk, lane);
-    const auto a1 = frag_rows<M>(lhs, LDK, 16 * RB, kk, lane);
-    typename M::frag bk[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) bk[cb] = frag_rows<M>(rhs, LDK, 16 * cb, kk, lane);
-#pragma unroll
-    for (int cb = 0; cb <= RA; ++cb) acc[cb] = M::mma(a0, bk[cb], acc[cb]);
-#pragma unroll
-    for (int cb = 0; cb <= RB; ++cb) acc[RA + 1 + cb] = M::mma(a1, bk[cb], acc[RA + 1 + cb]);
-  }
-}
-
-// Epilogue of lower_blocks: A (fp32, strictly lower, row r scaled by beta_r) when
-// IS_A, else M (operand type, lower including the diagonal).
-template <bool IS_A, typename TC, int LDF, int LDC, int RA, int RB>
-__device__ __forceinline__ void store_lower_blocks(const f32x4 (&acc)[5], f32x4 bta, f32x4 btb,
-                                                   float* sA, TC* sM, int lane) {
+// Load the initial state tile (or zeros) into accumulators and its snapshot into LDS.
+template <int DK, int BV, int LDK, typename TC, int NST>
+__device__ __forceinline__ void load_state(f32x4 (&sacc)[NST], const float* s0, int64_t st_base,
+                                           int v0, TC* sS, int wave, int lane) {
+  using ST = StateTiles<DK, BV>;
+  static_assert(NST == ST::NST, "state tile count");
   const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
-  for (int s = 0; s < 5; ++s) {
-    const int rb = s <= RA ? RA : RB;
-    const int cb = s <= RA ? s : s - RA - 1;
-    const f32x4 bt = s <= RA ? bta : btb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rb + 4 * lq + i, c = 16 * cb + lr;
-      if constexpr (IS_A)
-        sA[r * LDF + c] = c < r ? acc[s][i] * bt[i] : 0.f;
-      else
-        sM[r * LDC + c] = from_f32<TC>(c <= r ? acc[s][i] : 0.f);
-    }
+  for (int s = 0; s < ST::NST; ++s) {
+    const int kb = ST::kb(wave, s), vb = ST::vb(s);
+    const int vrow = v0 + 16 * vb + lr, kcol = 16 * kb + 4 * lq;
+    sacc[s] = s0 ? *reinterpret_cast<const f32x4*>(s0 + st_base + int64_t(vrow) * DK + kcol)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    store4(sS + (16 * vb + lr) * LDK + kcol, sacc[s]);
   }
 }
 
-// Byte layout of the workgroup's LDS.
-template <typename Tin, int DK, int BV>
-struct Smem {
-  using TC = typename Mfma<Tin>::TC;
-  static constexpr bool kBf16 = sizeof(TC) == 2;
-  static constexpr int PADC = kBf16 ? 8 : 1;        // 16 B row pad for bf16, 1 float for fp32
-  static constexpr int LDK = DK + PADC;             // [64][DK] tiles and the [BV][DK] snapshot
-  static constexpr int LDC = kChunk + PADC;         // [*][64] operand tiles
-  static constexpr int LDF = kChunk + 4;            // fp32 [64][64] (A, inverse), 16 B rows
-  static constexpr int LDX = kBf16 ? LDF : LDC;     // fp32 path: the inverse is the operand
-  static constexpr bool kKiT = kBf16;               // bf16 keeps Ki^T (16 B fragments)
-  static constexpr int CG = DK / 4, RG = kThreads / CG, RPG = kChunk / RG;
-
-  static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
-  static constexpr size_t tileK = size_t(kChunk) * LDK * sizeof(TC);
-  static constexpr size_t tileC = size_t(kChunk) * LDC * sizeof(TC);
-  static constexpr size_t tileF = size_t(kChunk) * LDF * 4;
-  static constexpr size_t oKg = 0;
-  static constexpr size_t oQg = al(oKg + tileK);
-  static constexpr size_t oKi = al(oQg + tileK);
-  static constexpr size_t oKiT = al(oKi + tileK);
-  static constexpr size_t oTm = al(oKiT + (kKiT ? size_t(DK) * LDC * sizeof(TC) : 0));
-  static constexpr size_t oM = al(oTm + tileC);
-  static constexpr size_t oA = al(oM + tileC);
-  static constexpr size_t oX = al(oA + tileF);
-  static constexpr size_t oS = al(oX + (kBf16 ? tileF : 0));
-  static constexpr size_t scrTot = size_t(RG) * DK * 4;
-  static constexpr size_t scrY = size_t(4) * 16 * 17 * 4;
-  static constexpr size_t oScr = al(oS + size_t(BV) * LDK * sizeof(TC));
-  static constexpr size_t oBeta = al(oScr + (scrTot > scrY ? scrTot : scrY));
-  static constexpr size_t oEgn = al(oBeta + kChunk * 4);
-  static constexpr size_t kBytes = al(oEgn + DK * 4);
-  // R'^T and E^T ([BV][64]) reuse the A (and fp32 inverse) region, dead by then.
-  static constexpr size_t oRT = oA;
-  static constexpr size_t oET = al(oRT + size_t(BV) * LDC * sizeof(TC));
-  static_assert(oET + size_t(BV) * LDC * sizeof(TC) <= oS, "R^T/E^T overflow their region");
-  static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
-};
-
-template <typename Tin, int DK, int BV>
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
-    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta,
-    const int32_t* __restrict__ cu_seqlens, int64_t T, int32_t H, int32_t DV, int32_t NV,
-    int32_t units, int32_t xcd_remap, float scale, const float* initial_state,
-    float* final_state, Tin* __restrict__ o) {
-  using M = Mfma<Tin>;
-  using TC = typename M::TC;
-  using raw4 = typename M::raw4;
-  using L = Smem<Tin, DK, BV>;
-  constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF, LDX = L::LDX;
-  constexpr int CG = L::CG, RG = L::RG, RPG = L::RPG;
-  constexpr int NVB = BV / 16;                 // 16-wide value blocks in the tile
-  constexpr int NST = (DK / 16) * NVB / 4;     // S^T accumulator tiles per wave
-  static_assert(NST >= 1, "tile too small");
-
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
-  TC* sKg = reinterpret_cast<TC*>(smem + L::oKg);
-  TC* sQg = reinterpret_cast<TC*>(smem + L::oQg);
-  TC* sKi = reinterpret_cast<TC*>(smem + L::oKi);
-  TC* sKiT = reinterpret_cast<TC*>(smem + L::oKiT);
-  TC* sTm = reinterpret_cast<TC*>(smem + L::oTm);
-  TC* sM = reinterpret_cast<TC*>(smem + L::oM);
-  float* sA = reinterpret_cast<float*>(smem + L::oA);
-  float* sX = L::kBf16 ? reinterpret_cast<float*>(smem + L::oX) : reinterpret_cast<float*>(smem + L::oTm);
-  TC* sS = reinterpret_cast<TC*>(smem + L::oS);
-  float* sScr = reinterpret_cast<float*>(smem + L::oScr);
-  float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
-  float* sEgn = reinterpret_cast<float*>(smem + L::oEgn);
-  TC* sRT = reinterpret_cast<TC*>(smem + L::oRT);
-  TC* sET = reinterpret_cast<TC*>(smem + L::oET);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int lr = lane & 15;          // accumulator column / fragment row
-  const int lq = lane >> 4;          // accumulator row quad
-
-  // ---- work decomposition: workgroup -> (sequence, head, v-tile) ------------------
-  int unit, vt;
-  {
-    const int x = blockIdx.x;
-    if (xcd_remap) {
-      // consecutive workgroup ids go round-robin to the 8 XCDs; keep the NV tiles of
-      // one (seq, head) on one XCD so its q/k/g chunk reads hit that XCD's L2.
-      const int xcd = x & 7, y = x >> 3;
-      unit = xcd * (units >> 3) + y / NV;
-      vt = y % NV;
-    } else {
-      unit = x / NV;
-      vt = x % NV;
-    }
-  }
-  const int n_seq = unit / H, h = unit % H;
-  int64_t bos, eos;
-  if (cu_seqlens) {
-    bos = cu_seqlens[n_seq];
-    eos = cu_seqlens[n_seq + 1];
-  } else {
-    bos = static_cast<int64_t>(n_seq) * T;
-    eos = bos + T;
-  }
-  const int v0 = vt * BV;
-  const int cg = tid % CG, rg = tid / CG, j0 = 4 * cg;
-
-  // ---- zero the operand tiles whose upper blocks are never written ---------------
-  for (int i = tid; i < kChunk * LDC; i += kThreads) {
-    sTm[i] = from_f32<TC>(0.f);
-    sM[i] = from_f32<TC>(0.f);
-  }
-
-  // ---- initial state -> S^T accumulators ------------------------------------------
-  // tile index t = kb * NVB + vb is owned by wave t % 4 (slot t / 4).
-  f32x4 sacc[NST];
-  const int64_t st_base = (static_cast<int64_t>(n_seq) * H + h) * DV * DK;
+template <int DK, int BV, int NST>
+__device__ __forceinline__ void store_state(const f32x4 (&sacc)[NST], float* s1, int64_t st_base,
+                                            int v0, int wave, int lane) {
+  using ST = StateTiles<DK, BV>;
+  static_assert(NST == ST::NST, "state tile count");
+  const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
-  for (int s = 0; s < NST; ++s) {
-    const int t = wave + 4 * s, kb = t / NVB, vb = t % NVB;
+  for (int s = 0; s < ST::NST; ++s) {
+    const int kb = ST::kb(wave, s), vb = ST::vb(s);
     const int vrow = v0 + 16 * vb + lr, kcol = 16 * kb + 4 * lq;
-    if (initial_state)
-      sacc[s] = *reinterpret_cast<const f32x4*>(initial_state + st_base + int64_t(vrow) * DK + kcol);
-    else
-      sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    store4(sS + (16 * vb + lr) * LDK + kcol, sacc[s]);
+    *reinterpret_cast<f32x4*>(s1 + st_base + int64_t(vrow) * DK + kcol) = sacc[s];
   }
+}
 
-  // ---- chunk inputs, loaded one chunk ahead into the registers that consumed the
-  //      previous chunk (rows past the end re-read the last valid row and are masked
-  //      at use, so every load is unconditional).  Addresses are a wave-uniform
-  //      chunk base plus 32-bit per-lane offsets.
-  const uint32_t rowK = static_cast<uint32_t>(H) * DK;       // elements between token rows
-  const uint32_t rowV = static_cast<uint32_t>(H) * DV;
-  f32x4 gr[RPG];
-  raw4 kr[RPG], qr[RPG];
-  uint32_t vr[NVB][4];                // raw value bits (bf16 in the low half, or fp32)
-  float br = 0.f;
-  auto load_factors = [&](int64_t c0, int n) {
-    const int64_t base = (c0 * H + h) * DK;
-    const float* gb = g + base;
-    const Tin* kb = k + base;
-    const Tin* qb = q + base;
-#pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      const uint32_t off = static_cast<uint32_t>(min(rg * RPG + i, n - 1)) * rowK + j0;
-      gr[i] = *reinterpret_cast<const f32x4*>(gb + off);
-      kr[i] = *reinterpret_cast<const raw4*>(kb + off);
-      qr[i] = *reinterpret_cast<const raw4*>(qb + off);
-    }
-    br = beta[(c0 + min(lane, n - 1)) * H + h];
-  };
-  auto load_values = [&](int64_t c0, int n) {
+// The value tile of one chunk in accumulator layout (row block = wave), loaded ahead
+// as raw bits: bf16 in the low half of a 32-bit register, or fp32.
+template <typename Tin, int NVB>
+struct ValueRegs {
+  uint32_t r[NVB][4];
+  __device__ __forceinline__ void load(const Tin* v, int64_t c0, int n, int32_t H, int h,
+                                       int32_t DV, int v0, int wave, int lane) {
     const Tin* vb0 = v + (c0 * H + h) * DV + v0;
+    const uint32_t rowV = static_cast<uint32_t>(H) * DV;
+    const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
@@ -345,18 +130,73 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
         const uint32_t off =
             static_cast<uint32_t>(min(16 * wave + 4 * lq + i, n - 1)) * rowV + 16 * vb + lr;
         if constexpr (sizeof(Tin) == 2)
-          vr[vb][i] = *reinterpret_cast<const unsigned short*>(vb0 + off);
+          r[vb][i] = *reinterpret_cast<const unsigned short*>(vb0 + off);
         else
-          vr[vb][i] = *reinterpret_cast<const uint32_t*>(vb0 + off);
+          r[vb][i] = *reinterpret_cast<const uint32_t*>(vb0 + off);
       }
-  };
-  auto value_f32 = [&](uint32_t bits) {
-    return sizeof(Tin) == 2 ? __uint_as_float(bits << 16) : __uint_as_float(bits);
-  };
+  }
+  __device__ __forceinline__ float f32(int vb, int i) const {
+    return sizeof(Tin) == 2 ? __uint_as_float(r[vb][i] << 16) : __uint_as_float(r[vb][i]);
+  }
+};
+
+// ====================================================================================
+// Fused kernel
+// ====================================================================================
+
+template <typename Tin, int DK, int BV>
+struct FusedLayout {
+  using CL = ChunkLayout<Tin, DK>;
+  using TC = typename CL::TC;
+  static constexpr size_t oS = CL::kBytes;                           // [BV][LDK] snapshot
+  static constexpr size_t kBytes = CL::al(oS + size_t(BV) * CL::LDK * sizeof(TC));
+  // R'^T and E^T ([BV][64]) reuse the A (and inverse) region, dead by then.
+  static constexpr size_t oRT = CL::oA;
+  static constexpr size_t oET = CL::al(oRT + size_t(BV) * CL::LDC * sizeof(TC));
+  static_assert(oET + size_t(BV) * CL::LDC * sizeof(TC) <= CL::oScr, "R^T/E^T overflow");
+  static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <typename Tin, int DK, int BV>
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
+  using CP = ChunkProducer<Tin, DK>;
+  using M = typename CP::M;
+  using TC = typename CP::TC;
+  using FL = FusedLayout<Tin, DK, BV>;
+  using ST = StateTiles<DK, BV>;
+  constexpr int LDK = CP::LDK, LDC = CP::LDC;
+  constexpr int NVB = BV / 16;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[FL::kBytes];
+  TC* sS = reinterpret_cast<TC*>(smem + FL::oS);
+  TC* sRT = reinterpret_cast<TC*>(smem + FL::oRT);
+  TC* sET = reinterpret_cast<TC*>(smem + FL::oET);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int lr = lane & 15, lq = lane >> 4;
+
+  int unit, vt, n_seq, h;
+  int64_t bos, eos;
+  unit_role(blockIdx.x, a.NV, a.units, a.xcd_remap, unit, vt);
+  unit_bounds(a, unit, n_seq, h, bos, eos);
+  const int v0 = vt * BV;
+  const Tin* v = static_cast<const Tin*>(a.v);
+  Tin* o = static_cast<Tin*>(a.o);
+
+  CP cp;
+  cp.init(smem, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, a.H, h,
+          a.scale, tid, wave);
+  f32x4 sacc[ST::NST];
+  const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * a.DV * DK;
+  load_state<DK, BV, LDK>(sacc, a.initial_state, st_base, v0, sS, wave, lane);
+
+  ValueRegs<Tin, NVB> vr;
   if (bos < eos) {
     const int n0 = static_cast<int>(min(eos - bos, static_cast<int64_t>(kChunk)));
-    load_factors(bos, n0);
-    load_values(bos, n0);
+    cp.load(bos, n0);
+    vr.load(v, bos, n0, a.H, h, a.DV, v0, wave, lane);
   }
 
   for (int64_t c0 = bos; c0 < eos; c0 += kChunk) {
@@ -365,183 +205,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     const bool has_next = c1 < eos;
     const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
 
-    // ---- 1. factor tiles ---------------------------------------------------------
-    {
-      // alpha = e^g in place (1 for rows past the end); per-thread product of its rows
-      f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-      for (int i = 0; i < RPG; ++i) {
-        const f32x4 gg = gr[i];
-        gr[i] = rg * RPG + i < n ? f32x4{exp_hw(gg[0]), exp_hw(gg[1]), exp_hw(gg[2]), exp_hw(gg[3])}
-                                 : f32x4{1.f, 1.f, 1.f, 1.f};
-        tot *= gr[i];
-      }
-      store4(sScr + rg * DK + j0, tot);
-      if (tid < kChunk) sBeta[tid] = tid < n ? br : 0.f;
-      lds_barrier();
-      // products of the other row groups' totals: before (cp) and after (cs) this one
-      f32x4 tots[RG];
-#pragma unroll
-      for (int r2 = 0; r2 < RG; ++r2) tots[r2] = *reinterpret_cast<const f32x4*>(sScr + r2 * DK + j0);
-      f32x4 cp = f32x4{1.f, 1.f, 1.f, 1.f}, cs = f32x4{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-      for (int r2 = 0; r2 < RG; ++r2) {
-        if (r2 < rg) cp *= tots[r2];
-        if (r2 > rg) cs *= tots[r2];
-      }
-      const f32x4 egn = cp * tot * cs;                            // e^{G_n}
-      // forward pass: e^{G_r} = cp * alpha_{first} ... alpha_r  ->  Kg, Qg
-      f32x4 run = cp;
-#pragma unroll
-      for (int i = 0; i < RPG; ++i) {
-        const bool ok = rg * RPG + i < n;
-        run *= gr[i];
-        const f32x4 k4 = ok ? widen(kr[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 q4 = ok ? widen(qr[i]) * scale : f32x4{0.f, 0.f, 0.f, 0.f};
-        store4(sKg + (rg * RPG + i) * LDK + j0, k4 * run);
-        store4(sQg + (rg * RPG + i) * LDK + j0, q4 * run);
-      }
-      // backward pass: e^{-G_r} = (alpha_{r+1} ... alpha_n) / e^{G_n}  ->  Ki, Ki^T
-      run = cs * f32x4{__builtin_amdgcn_rcpf(egn[0]), __builtin_amdgcn_rcpf(egn[1]),
-                       __builtin_amdgcn_rcpf(egn[2]), __builtin_amdgcn_rcpf(egn[3])};
-      TC kit[4][RPG];
-#pragma unroll
-      for (int i = RPG - 1; i >= 0; --i) {
-        const bool ok = rg * RPG + i < n;
-        const f32x4 k4 = ok ? widen(kr[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 ki = k4 * run;
-        store4(sKi + (rg * RPG + i) * LDK + j0, ki);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kit[c][i] = from_f32<TC>(ki[c]);
-        run *= gr[i];
-      }
-      if constexpr (L::kKiT) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          TC* dst = sKiT + (j0 + c) * LDC + rg * RPG;
-          if constexpr (RPG == 8)
-            *reinterpret_cast<bf16x8*>(dst) = bf16x8{kit[c][0], kit[c][1], kit[c][2], kit[c][3],
-                                                     kit[c][4], kit[c][5], kit[c][6], kit[c][7]};
-          else
-            *reinterpret_cast<bf16x4*>(dst) = bf16x4{kit[c][0], kit[c][1], kit[c][2], kit[c][3]};
-        }
-      }
-      if (rg == 0) store4(sEgn + j0, egn);
-      // the registers are free: prefetch the next chunk's g, k, q, beta
-      if (has_next) load_factors(c1, n1);
-    }
-    lds_barrier();
+    cp.factors(n, has_next, c1, n1);
+    cp.products();
+    cp.inverse();
 
-    // ---- 2. A = strict-lower(diag(beta) Kg Ki^T), M = lower(Qg Ki^T) --------------
-    //      waves 0, 1: A row blocks (0, 3) and (1, 2); waves 2, 3: the same for M
-    {
-      f32x4 acc[5];
-      const f32x4 bta = *reinterpret_cast<const f32x4*>(sBeta + 16 * ((wave & 1) ? 1 : 0) + 4 * lq);
-      const f32x4 btb = *reinterpret_cast<const f32x4*>(sBeta + 16 * ((wave & 1) ? 2 : 3) + 4 * lq);
-      if (wave == 0) {
-        lower_blocks<M, DK, LDK, 0, 3>(acc, sKg, sKi, lane);
-        store_lower_blocks<true, TC, LDF, LDC, 0, 3>(acc, bta, btb, sA, sM, lane);
-      } else if (wave == 1) {
-        lower_blocks<M, DK, LDK, 1, 2>(acc, sKg, sKi, lane);
-        store_lower_blocks<true, TC, LDF, LDC, 1, 2>(acc, bta, btb, sA, sM, lane);
-      } else if (wave == 2) {
-        lower_blocks<M, DK, LDK, 0, 3>(acc, sQg, sKi, lane);
-        store_lower_blocks<false, TC, LDF, LDC, 0, 3>(acc, bta, btb, sA, sM, lane);
-      } else {
-        lower_blocks<M, DK, LDK, 1, 2>(acc, sQg, sKi, lane);
-        store_lower_blocks<false, TC, LDF, LDC, 1, 2>(acc, bta, btb, sA, sM, lane);
-      }
-    }
-    lds_barrier();
-
-    // ---- 3. X = (I + A)^{-1} ---------------------------------------------------------
-    float* sY = sScr;   // four 16x17 fp32 scratch blocks
-    if (wave == 0) {
-      // 3a: diagonal blocks, lane = (block b, column c): x = column c of X_bb, row by
-      //     row (left-looking), each A row read as four 16-byte loads
-      {
-        const int b = lane >> 4, c = lane & 15;
-        const float* Ab = sA + (16 * b) * LDF + 16 * b;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float acc = (r == c) ? 1.f : 0.f;
-#pragma unroll
-          for (int j4 = 0; j4 < r; j4 += 4) {
-            const f32x4 a4 = *reinterpret_cast<const f32x4*>(Ab + r * LDF + j4);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (j4 + u < r) acc -= a4[u] * x[j4 + u];
-          }
-          x[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sX[(16 * b + r) * LDX + 16 * b + c] = x[r];
-          if constexpr (L::kBf16) sTm[(16 * b + r) * LDC + 16 * b + c] = from_f32<TC>(x[r]);
-        }
-      }
-      wave_lds_sync();
-      // 3b: X_10 = -X_11 A_10 X_00 and X_32 = -X_33 A_32 X_22
-      {
-        const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 y0 = mm16(z, sA + 16 * LDF, LDF, sX, LDX, lane);
-        const f32x4 y1 = mm16(z, sA + 48 * LDF + 32, LDF, sX + 32 * LDX + 32, LDX, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sY[(4 * lq + i) * 17 + lr] = y0[i];
-          sY[16 * 17 + (4 * lq + i) * 17 + lr] = y1[i];
-        }
-        wave_lds_sync();
-        const f32x4 x10 = mm16(z, sX + 16 * LDX + 16, LDX, sY, 17, lane);
-        const f32x4 x32 = mm16(z, sX + 48 * LDX + 48, LDX, sY + 16 * 17, 17, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * lq + i;
-          sX[(16 + r) * LDX + lr] = -x10[i];
-          sX[(48 + r) * LDX + 32 + lr] = -x32[i];
-          if constexpr (L::kBf16) {
-            sTm[(16 + r) * LDC + lr] = from_f32<TC>(-x10[i]);
-            sTm[(48 + r) * LDC + 32 + lr] = from_f32<TC>(-x32[i]);
-          }
-        }
-      }
-    }
-    lds_barrier();
-    // 3c: the 32x32 block below the diagonal: X_lo = -X_B11 (A_lo X_B00)
-    //     wave w computes Y_w = (A_lo X_B00) block (w/2, w%2)
-    {
-      const int bi = 2 + (wave >> 1), bj = wave & 1;          // block of A_lo X_B00
-      f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
-      // sum over k-blocks bj..1 of A[bi][kb] X[kb][bj]
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        if (kb >= bj) y = mm16(y, sA + (16 * bi) * LDF + 16 * kb, LDF,
-                               sX + (16 * kb) * LDX + 16 * bj, LDX, lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sY[wave * 16 * 17 + (4 * lq + i) * 17 + lr] = y[i];
-    }
-    lds_barrier();
-    {
-      // wave w: X[2 + w/2][w%2] = -(sum_{kb=2}^{2+w/2} X[2+w/2][kb] Y[kb-2][w%2])
-      const int bi = 2 + (wave >> 1), bj = wave & 1;
-      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 2; kb < 4; ++kb)
-        if (kb <= bi) x = mm16(x, sX + (16 * bi) * LDX + 16 * kb, LDX,
-                               sY + ((kb - 2) * 2 + bj) * 16 * 17, 17, lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * bi + 4 * lq + i, c = 16 * bj + lr;
-        if constexpr (L::kBf16)
-          sTm[r * LDC + c] = from_f32<TC>(-x[i]);
-        else
-          sX[r * LDX + c] = -x[i];
-      }
-    }
-    lds_barrier();
-
-    // ---- 4a. P = Kg S^T, Qs = Qg S^T; R' = diag(beta)(V - P) -> R'^T ----------------
+    // ---- P = Kg S^T, Qs = Qg S^T; R' = diag(beta)(V - P) -> R'^T ---------------------
     f32x4 accQ[NVB];
     {
       f32x4 accP[NVB];
@@ -549,8 +217,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
       for (int vb = 0; vb < NVB; ++vb) accP[vb] = accQ[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < DK; kk += M::KSTEP) {
-        const auto aK = frag_rows<M>(sKg, LDK, 16 * wave, kk, lane);
-        const auto aQ = frag_rows<M>(sQg, LDK, 16 * wave, kk, lane);
+        const auto aK = frag_rows<M>(cp.sKg, LDK, 16 * wave, kk, lane);
+        const auto aQ = frag_rows<M>(cp.sQg, LDK, 16 * wave, kk, lane);
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb) {
           const auto bS = frag_rows<M>(sS, LDK, 16 * vb, kk, lane);
@@ -558,65 +226,65 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
           accQ[vb] = M::mma(aQ, bS, accQ[vb]);
         }
       }
-      const f32x4 bt = *reinterpret_cast<const f32x4*>(sBeta + 16 * wave + 4 * lq);
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(cp.sBeta + 16 * wave + 4 * lq);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         f32x4 rv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool ok = 16 * wave + 4 * lq + i < n;
-          rv[i] = ok ? bt[i] * (value_f32(vr[vb][i]) - accP[vb][i]) : 0.f;
+          rv[i] = ok ? bt[i] * (vr.f32(vb, i) - accP[vb][i]) : 0.f;
         }
         store4(sRT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, rv);
       }
-      // the value registers are free: prefetch the next chunk's tile
-      if (has_next) load_values(c1, n1);
+      // the value registers are free: load the next chunk's tile
+      if (has_next) vr.load(v, c1, n1, a.H, h, a.DV, v0, wave, lane);
     }
     lds_barrier();
 
-    // ---- 4b. E = X R' -> E^T ---------------------------------------------------------
+    // ---- E = X R' -> E^T ---------------------------------------------------------------
     {
       const int kend = 16 * (wave + 1);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int kk = 0; kk < kend; kk += M::KSTEP)
-          acc = M::mma(frag_rows<M>(sTm, LDC, 16 * wave, kk, lane),
+          acc = M::mma(frag_rows<M>(cp.sTm, LDC, 16 * wave, kk, lane),
                        frag_rows<M>(sRT, LDC, 16 * vb, kk, lane), acc);
         store4(sET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, acc);
       }
     }
     lds_barrier();
 
-    // ---- 4c. O = Qs + M E (store); S^T = (S^T + Ki^T E) Diag(e^{G_n}) -----------------
+    // ---- O = Qs + M E (store); S^T = (S^T + Ki^T E) Diag(e^{G_n}) -----------------------
     {
       const int kend = 16 * (wave + 1);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         f32x4 acc = accQ[vb];
         for (int kk = 0; kk < kend; kk += M::KSTEP)
-          acc = M::mma(frag_rows<M>(sM, LDC, 16 * wave, kk, lane),
+          acc = M::mma(frag_rows<M>(cp.sM, LDC, 16 * wave, kk, lane),
                        frag_rows<M>(sET, LDC, 16 * vb, kk, lane), acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * wave + 4 * lq + i;
-          if (r < n) o[((c0 + r) * H + h) * DV + v0 + 16 * vb + lr] = from_f32<Tin>(acc[i]);
+          if (r < n) o[((c0 + r) * a.H + h) * a.DV + v0 + 16 * vb + lr] = from_f32<Tin>(acc[i]);
         }
       }
 #pragma unroll
-      for (int s = 0; s < NST; ++s) {
-        const int t = wave + 4 * s, kb = t / NVB, vb = t % NVB;
+      for (int s = 0; s < ST::NST; ++s) {
+        const int kb = ST::kb(wave, s), vb = ST::vb(s);
         f32x4 acc = sacc[s];
 #pragma unroll
         for (int kk = 0; kk < kChunk; kk += M::KSTEP) {
-          typename M::frag a;
-          if constexpr (L::kKiT)
-            a = frag_rows<M>(sKiT, LDC, 16 * kb, kk, lane);
+          typename M::frag af;
+          if constexpr (CP::L::kKiT)
+            af = frag_rows<M>(cp.sKiT, LDC, 16 * kb, kk, lane);
           else
-            a = frag_cols<M>(sKi, LDK, kk, 16 * kb, lane);
-          acc = M::mma(a, frag_rows<M>(sET, LDC, 16 * vb, kk, lane), acc);
+            af = frag_cols<M>(cp.sKi, LDK, kk, 16 * kb, lane);
+          acc = M::mma(af, frag_rows<M>(sET, LDC, 16 * vb, kk, lane), acc);
         }
-        const f32x4 e = *reinterpret_cast<const f32x4*>(sEgn + 16 * kb + 4 * lq);
+        const f32x4 e = *reinterpret_cast<const f32x4*>(cp.sEgn + 16 * kb + 4 * lq);
         acc *= e;
         store4(sS + (16 * vb + lr) * LDK + 16 * kb + 4 * lq, acc);
         sacc[s] = acc;
@@ -625,75 +293,435 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     lds_barrier();
   }
 
-  // ---- final state ------------------------------------------------------------------
-  if (final_state) {
-#pragma unroll
-    for (int s = 0; s < NST; ++s) {
-      const int t = wave + 4 * s, kb = t / NVB, vb = t % NVB;
-      const int vrow = v0 + 16 * vb + lr, kcol = 16 * kb + 4 * lq;
-      *reinterpret_cast<f32x4*>(final_state + st_base + int64_t(vrow) * DK + kcol) = sacc[s];
+  if (a.final_state) store_state<DK, BV>(sacc, a.final_state, st_base, v0, wave, lane);
+}
+
+// ====================================================================================
+// Producer / consumer kernel (bf16)
+// ====================================================================================
+
+// One ring slot: the chunk's operands in MFMA fragment order.  A fragment block is
+// the 16 bytes each of the 64 lanes loads for one 16x32 operand step (1 KiB), so a
+// consumer wave reads every block as one contiguous 1 KiB load.
+template <int DK>
+struct SlotLayout {
+  static constexpr int kKs = DK / 32;                 // k steps of Kg / Qg
+  static constexpr int nKg = 4 * kKs;                 // (row block, k step)
+  static constexpr int nKiT = (DK / 16) * 2;          // (key block, token step)
+  static constexpr int nTm = 8;                       // (row block, token step)
+  static constexpr size_t kFrag = 1024;
+  static constexpr size_t oKg = 0;
+  static constexpr size_t oQg = oKg + nKg * kFrag;
+  static constexpr size_t oKiT = oQg + nKg * kFrag;
+  static constexpr size_t oTm = oKiT + nKiT * kFrag;
+  static constexpr size_t oM = oTm + nTm * kFrag;
+  static constexpr size_t oBeta = oM + nTm * kFrag;   // 64 fp32
+  static constexpr size_t oEgn = oBeta + 64 * 4;      // DK fp32
+  static constexpr size_t kBytes = (oEgn + DK * 4 + 255) & ~size_t(255);
+  static constexpr int nBlocks = 2 * nKg + nKiT + 2 * nTm;
+};
+
+// Workspace: [0, 256) header (word 0: abort), then per-unit flags ready[R], done[R]
+// (int32), then the ring slots.
+constexpr size_t kWsHeader = 256;
+__host__ __device__ inline size_t coop_flags_bytes(int units, int R) {
+  return (size_t(units) * 2 * R * 4 + 255) & ~size_t(255);
+}
+template <int DK>
+__host__ __device__ inline size_t coop_workspace_bytes(int units, int R) {
+  return kWsHeader + coop_flags_bytes(units, R) + size_t(units) * R * SlotLayout<DK>::kBytes;
+}
+
+constexpr uint32_t kSpinLimit = 1u << 22;   // ~ a second of s_sleep polling
+
+// Ring slots are written and read with device-scope (sc1) buffer accesses: a store
+// is acknowledged only once it is visible device-wide and a load reads the
+// device-coherent copy, so the hand-off needs no cache write-back or invalidate.
+constexpr int kDeviceScope = 16;             // cache-policy bit SC1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(unsigned char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void ring_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16x8 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ void ring_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ bf16x8 ring_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope);
+  return __builtin_bit_cast(bf16x8, x);
+}
+__device__ __forceinline__ f32x4 ring_load16f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope);
+  return __builtin_bit_cast(f32x4, x);
+}
+
+// Wait (one lane) until *p >= target.  False if the wait ran out or the grid aborted;
+// a wait that runs out raises the abort word.
+__device__ __forceinline__ bool wait_at_least(const int* p, int target, int* abort_word) {
+  for (uint32_t it = 0;; ++it) {
+    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return true;
+    if ((it & 15) == 15 &&
+        __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+      return false;
+    if (it >= kSpinLimit) {
+      __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
     }
+    __builtin_amdgcn_s_sleep(2);
   }
 }
 
-template <typename Tin, int DK, int BV>
-static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const float* g,
-                                   const float* beta, const int32_t* cu, int64_t T, int32_t H,
-                                   int32_t DV, int32_t NV, int32_t units, int32_t xcd_remap,
-                                   float scale, const float* s0, float* s1, void* o,
-                                   hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<Tin, DK, BV>), dim3(units * NV), dim3(kThreads), 0, stream,
-                     static_cast<const Tin*>(q), static_cast<const Tin*>(k),
-                     static_cast<const Tin*>(v), g, beta, cu, T, H, DV, NV, units, xcd_remap,
-                     scale, s0, s1, static_cast<Tin*>(o));
-  return hipGetLastError();
+template <int DK, int BV>
+struct ConsumerLayout {
+  static constexpr int LDK = DK + 8, LDC = kChunk + 8;
+  static constexpr size_t oS = 0;                                         // [BV][LDK] bf16
+  static constexpr size_t oRT = (oS + size_t(BV) * LDK * 2 + 15) & ~size_t(15);   // [BV][LDC]
+  static constexpr size_t oET = (oRT + size_t(BV) * LDC * 2 + 15) & ~size_t(15);
+  static constexpr size_t oFlag = (oET + size_t(BV) * LDC * 2 + 15) & ~size_t(15);
+  static constexpr size_t kBytes = oFlag + 16;
+};
+
+// A consumer's operand fragments for one chunk (wave w: row block w; key blocks of
+// its state tiles).
+template <int DK>
+struct ChunkFrags {
+  using SL = SlotLayout<DK>;
+  static constexpr int KPW = DK / 64;
+  bf16x8 kg[SL::kKs], qg[SL::kKs], tm[2], mm[2], kit[KPW][2];
+  f32x4 bt;          // beta of rows 16w + 4*lq .. +3
+  f32x4 egn[KPW];    // e^{G_n} of key channels 16*kb + 4*lq .. +3
+  // slot: byte offset of the slot in the unit's ring
+  __device__ __forceinline__ void load_kq(__amdgpu_buffer_rsrc_t r, uint32_t slot, int wave,
+                                          int lane) {
+#pragma unroll
+    for (int s = 0; s < SL::kKs; ++s) {
+      kg[s] = ring_load16(r, slot + SL::oKg + (wave * SL::kKs + s) * SL::kFrag + 16 * lane);
+      qg[s] = ring_load16(r, slot + SL::oQg + (wave * SL::kKs + s) * SL::kFrag + 16 * lane);
+    }
+    bt = ring_load16f(r, slot + SL::oBeta + (16 * wave + 4 * (lane >> 4)) * 4);
+  }
+  __device__ __forceinline__ void load_tm(__amdgpu_buffer_rsrc_t r, uint32_t slot, int wave,
+                                          int lane) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      tm[t] = ring_load16(r, slot + SL::oTm + (wave * 2 + t) * SL::kFrag + 16 * lane);
+  }
+  __device__ __forceinline__ void load_rest(__amdgpu_buffer_rsrc_t r, uint32_t slot, int wave,
+                                            int lane) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      mm[t] = ring_load16(r, slot + SL::oM + (wave * 2 + t) * SL::kFrag + 16 * lane);
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int kb = wave * KPW + j;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        kit[j][t] = ring_load16(r, slot + SL::oKiT + (kb * 2 + t) * SL::kFrag + 16 * lane);
+      egn[j] = ring_load16f(r, slot + SL::oEgn + (16 * kb + 4 * (lane >> 4)) * 4);
+    }
+  }
+};
+
+template <int DK, int BV>
+struct CoopLayout {
+  static constexpr size_t a = ChunkLayout<bf16, DK>::kBytes;
+  static constexpr size_t b = ConsumerLayout<DK, BV>::kBytes;
+  static constexpr size_t kBytes = a > b ? a : b;
+  static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <int DK, int BV>
+__global__ __launch_bounds__(kThreads, 1) void prefill_coop_kernel(PrefillArgs a) {
+  using CP = ChunkProducer<bf16, DK>;
+  using M = Mfma<bf16>;
+  using SL = SlotLayout<DK>;
+  using CL = ConsumerLayout<DK, BV>;
+  using ST = StateTiles<DK, BV>;
+  constexpr int NVB = BV / 16;
+  constexpr int LDK = CL::LDK, LDC = CL::LDC;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[CoopLayout<DK, BV>::kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+
+  const int W = a.NC + a.NP;
+  int unit, role, n_seq, h;
+  int64_t bos, eos;
+  unit_role(blockIdx.x, W, a.units, a.xcd_remap, unit, role);
+  unit_bounds(a, unit, n_seq, h, bos, eos);
+  const int nch = static_cast<int>((eos - bos + kChunk - 1) / kChunk);
+
+  int* abort_word = reinterpret_cast<int*>(a.workspace);
+  int* ready = reinterpret_cast<int*>(a.workspace + kWsHeader) + size_t(unit) * 2 * a.R;
+  int* done = ready + a.R;
+  unsigned char* ring = a.workspace + kWsHeader + coop_flags_bytes(a.units, a.R) +
+                        size_t(unit) * a.R * SL::kBytes;
+  int* sFlag = reinterpret_cast<int*>(smem + CL::oFlag);   // consumer: wait result
+  const __amdgpu_buffer_rsrc_t rr = ring_rsrc(ring, static_cast<uint32_t>(a.R * SL::kBytes));
+
+  if (role >= a.NC) {
+    // ================================ producer ==================================
+    const int p = role - a.NC;
+    CP cp;
+    cp.init(smem, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), a.g, a.beta,
+            a.H, h, a.scale, tid, wave);
+    if (p < nch) {
+      const int64_t c0 = bos + int64_t(p) * kChunk;
+      cp.load(c0, static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk))));
+    }
+    int* pFlag = reinterpret_cast<int*>(smem + ChunkLayout<bf16, DK>::oScr);
+    for (int c = p; c < nch; c += a.NP) {
+      const int64_t c0 = bos + int64_t(c) * kChunk;
+      const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
+      const int cn = c + a.NP;
+      const bool has_next = cn < nch;
+      const int64_t c1 = bos + int64_t(cn) * kChunk;
+      const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
+      cp.factors(n, has_next, c1, n1);
+      cp.products();
+      cp.inverse();
+      // the slot must have been read by every consumer of its previous chunk
+      const int s = c % a.R;
+      if (tid == 0) pFlag[0] = wait_at_least(done + s, a.NC * (c / a.R), abort_word) ? 1 : 0;
+      lds_barrier();
+      const bool ok = pFlag[0] != 0;
+      lds_barrier();
+      if (!ok) break;
+      const uint32_t slot = static_cast<uint32_t>(s) * SL::kBytes;
+      // fragment blocks: waves take blocks w, w+4, ...
+      for (int b = wave; b < SL::nBlocks; b += 4) {
+        bf16x8 f;
+        uint32_t off;
+        if (b < SL::nKg) {
+          f = frag_rows<M>(cp.sKg, CP::LDK, 16 * (b / SL::kKs), 32 * (b % SL::kKs), lane);
+          off = SL::oKg + b * SL::kFrag;
+        } else if (b < 2 * SL::nKg) {
+          const int i = b - SL::nKg;
+          f = frag_rows<M>(cp.sQg, CP::LDK, 16 * (i / SL::kKs), 32 * (i % SL::kKs), lane);
+          off = SL::oQg + i * SL::kFrag;
+        } else if (b < 2 * SL::nKg + SL::nKiT) {
+          const int i = b - 2 * SL::nKg;
+          f = frag_rows<M>(cp.sKiT, CP::LDC, 16 * (i / 2), 32 * (i % 2), lane);
+          off = SL::oKiT + i * SL::kFrag;
+        } else if (b < 2 * SL::nKg + SL::nKiT + SL::nTm) {
+          const int i = b - 2 * SL::nKg - SL::nKiT;
+          f = frag_rows<M>(cp.sTm, CP::LDC, 16 * (i / 2), 32 * (i % 2), lane);
+          off = SL::oTm + i * SL::kFrag;
+        } else {
+          const int i = b - 2 * SL::nKg - SL::nKiT - SL::nTm;
+          f = frag_rows<M>(cp.sM, CP::LDC, 16 * (i / 2), 32 * (i % 2), lane);
+          off = SL::oM + i * SL::kFrag;
+        }
+        ring_store16(rr, slot + off + 16 * lane, f);
+      }
+      if (tid < kChunk) ring_store4(rr, slot + SL::oBeta + 4 * tid, cp.sBeta[tid]);
+      if (tid < DK) ring_store4(rr, slot + SL::oEgn + 4 * tid, cp.sEgn[tid]);
+      // every store of the workgroup acknowledged (device-visible), then publish
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();
+      if (tid == 0) __hip_atomic_store(ready + s, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+
+  // ================================== consumer =====================================
+  const int vt = role;
+  const int v0 = vt * BV;
+  bf16* sS = reinterpret_cast<bf16*>(smem + CL::oS);
+  bf16* sRT = reinterpret_cast<bf16*>(smem + CL::oRT);
+  bf16* sET = reinterpret_cast<bf16*>(smem + CL::oET);
+  const bf16* v = static_cast<const bf16*>(a.v);
+  bf16* o = static_cast<bf16*>(a.o);
+
+  f32x4 sacc[ST::NST];
+  const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * a.DV * DK;
+  load_state<DK, BV, LDK>(sacc, a.initial_state, st_base, v0, sS, wave, lane);
+
+  ChunkFrags<DK> fr;
+  ValueRegs<bf16, NVB> vr;
+  bool ok = true;
+  if (nch > 0) {
+    if (tid == 0) sFlag[0] = wait_at_least(ready, 1, abort_word) ? 1 : 0;
+    lds_barrier();
+    ok = sFlag[0] != 0;
+    if (ok) {
+      fr.load_kq(rr, 0, wave, lane);
+      fr.load_tm(rr, 0, wave, lane);
+      fr.load_rest(rr, 0, wave, lane);
+      vr.load(v, bos, static_cast<int>(min(eos - bos, static_cast<int64_t>(kChunk))), a.H, h,
+              a.DV, v0, wave, lane);
+    }
+  }
+
+  for (int c = 0; ok && c < nch; ++c) {
+    const int64_t c0 = bos + int64_t(c) * kChunk;
+    const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
+    const bool has_next = c + 1 < nch;
+    const int64_t c1 = c0 + kChunk;
+    const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
+    const uint32_t nslot = static_cast<uint32_t>((c + 1) % a.R) * SL::kBytes;
+    // wait for the next chunk's slot while this chunk computes
+    if (tid == 0 && has_next)
+      sFlag[1] = wait_at_least(ready + (c + 1) % a.R, c + 2, abort_word) ? 1 : 0;
+
+    // ---- P = Kg S^T, Qs = Qg S^T; R' = diag(beta)(V - P) -> R'^T ---------------------
+    f32x4 accQ[NVB];
+    {
+      f32x4 accP[NVB];
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) accP[vb] = accQ[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < SL::kKs; ++ks) {
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+          const auto bS = frag_rows<M>(sS, LDK, 16 * vb, 32 * ks, lane);
+          accP[vb] = M::mma(fr.kg[ks], bS, accP[vb]);
+          accQ[vb] = M::mma(fr.qg[ks], bS, accQ[vb]);
+        }
+      }
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        f32x4 rv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool okr = 16 * wave + 4 * lq + i < n;
+          rv[i] = okr ? fr.bt[i] * (vr.f32(vb, i) - accP[vb][i]) : 0.f;
+        }
+        store4(sRT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, rv);
+      }
+    }
+    lds_barrier();
+    const bool nok = has_next ? sFlag[1] != 0 : true;
+    if (has_next && nok) {
+      fr.load_kq(rr, nslot, wave, lane);
+      vr.load(v, c1, n1, a.H, h, a.DV, v0, wave, lane);
+    }
+
+    // ---- E = X R' -> E^T ---------------------------------------------------------------
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc = M::mma(fr.tm[0], frag_rows<M>(sRT, LDC, 16 * vb, 0, lane), acc);
+      if (wave >= 2) acc = M::mma(fr.tm[1], frag_rows<M>(sRT, LDC, 16 * vb, 32, lane), acc);
+      store4(sET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, acc);
+    }
+    lds_barrier();
+    if (has_next && nok) fr.load_tm(rr, nslot, wave, lane);
+
+    // ---- O = Qs + M E (store); S^T = (S^T + Ki^T E) Diag(e^{G_n}) -----------------------
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      f32x4 acc = accQ[vb];
+      acc = M::mma(fr.mm[0], frag_rows<M>(sET, LDC, 16 * vb, 0, lane), acc);
+      if (wave >= 2) acc = M::mma(fr.mm[1], frag_rows<M>(sET, LDC, 16 * vb, 32, lane), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * lq + i;
+        if (r < n) o[((c0 + r) * a.H + h) * a.DV + v0 + 16 * vb + lr] = from_f32<bf16>(acc[i]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < ST::NST; ++s) {
+      const int j = s / NVB, vb = ST::vb(s);
+      const int kb = ST::kb(wave, s);
+      f32x4 acc = sacc[s];
+      acc = M::mma(fr.kit[j][0], frag_rows<M>(sET, LDC, 16 * vb, 0, lane), acc);
+      acc = M::mma(fr.kit[j][1], frag_rows<M>(sET, LDC, 16 * vb, 32, lane), acc);
+      acc *= fr.egn[j];
+      store4(sS + (16 * vb + lr) * LDK + 16 * kb + 4 * lq, acc);
+      sacc[s] = acc;
+    }
+    if (has_next && nok) fr.load_rest(rr, nslot, wave, lane);
+    lds_barrier();
+    // this chunk's fragments were all used: free its slot
+    if (tid == 0) __hip_atomic_fetch_add(done + c % a.R, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ok = nok;
+  }
+
+  if (ok && a.final_state) store_state<DK, BV>(sacc, a.final_state, st_base, v0, wave, lane);
 }
 
-// Largest value-tile height each dtype / d_k instantiation supports (LDS budget:
-// fp32 operands are twice the size of bf16 ones).
+// Zero the abort word and the hand-off flags before a producer/consumer launch.
+__global__ void coop_reset_kernel(int* words, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    words[i] = 0;
+}
+
+// ====================================================================================
+// Launch
+// ====================================================================================
+
+// Largest value-tile height each dtype / d_k instantiation of the fused kernel
+// supports (LDS budget: fp32 operands are twice the size of bf16 ones).
 constexpr int max_bv(bool fp32, int dk) { return fp32 ? (dk == 128 ? 16 : 32) : 64; }
 int prefill_max_bv(int dtype, int dk) { return max_bv(dtype == 0, dk); }
 
 template <typename Tin, int DK>
-static hipError_t launch_prefill_dk(int bv, const void* q, const void* k, const void* v,
-                                    const float* g, const float* beta, const int32_t* cu,
-                                    int64_t T, int32_t H, int32_t DV, int32_t NV, int32_t units,
-                                    int32_t xcd_remap, float scale, const float* s0, float* s1,
-                                    void* o, hipStream_t stream) {
+static hipError_t launch_fused_dk(int bv, const PrefillArgs& a, hipStream_t stream) {
   constexpr int kMax = max_bv(sizeof(Tin) == 4, DK);
+  const dim3 grid(a.units * a.NV), block(kThreads);
   if constexpr (kMax >= 64) {
-    if (bv == 64)
-      return launch_prefill_t<Tin, DK, 64>(q, k, v, g, beta, cu, T, H, DV, NV, units, xcd_remap,
-                                           scale, s0, s1, o, stream);
+    if (bv == 64) {
+      hipLaunchKernelGGL((prefill_kernel<Tin, DK, 64>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
   }
   if constexpr (kMax >= 32) {
-    if (bv == 32)
-      return launch_prefill_t<Tin, DK, 32>(q, k, v, g, beta, cu, T, H, DV, NV, units, xcd_remap,
-                                           scale, s0, s1, o, stream);
+    if (bv == 32) {
+      hipLaunchKernelGGL((prefill_kernel<Tin, DK, 32>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
   }
-  return launch_prefill_t<Tin, DK, 16>(q, k, v, g, beta, cu, T, H, DV, NV, units, xcd_remap,
-                                       scale, s0, s1, o, stream);
+  hipLaunchKernelGGL((prefill_kernel<Tin, DK, 16>), grid, block, 0, stream, a);
+  return hipGetLastError();
 }
 
-// Called by the C ABI after validation.  bv in {16, 32, 64} with bv <= prefill_max_bv,
-// NV = DV / bv.
-hipError_t launch_prefill(int dtype, int dk, int bv, const void* q, const void* k,
-                          const void* v, const float* g, const float* beta, const int32_t* cu,
-                          int64_t T, int32_t H, int32_t DV, int32_t NV, int32_t units,
-                          int32_t xcd_remap, float scale, const float* s0, float* s1, void* o,
-                          hipStream_t stream) {
-  if (dtype == 1) {
-    if (dk == 64)
-      return launch_prefill_dk<bf16, 64>(bv, q, k, v, g, beta, cu, T, H, DV, NV, units, xcd_remap,
-                                         scale, s0, s1, o, stream);
-    return launch_prefill_dk<bf16, 128>(bv, q, k, v, g, beta, cu, T, H, DV, NV, units, xcd_remap,
-                                        scale, s0, s1, o, stream);
+// Fused kernel.  bv in {16, 32, 64}, bv <= prefill_max_bv; a.NV = DV / bv.
+hipError_t launch_prefill(int dtype, int dk, int bv, const PrefillArgs& a, hipStream_t stream) {
+  if (dtype == 1)
+    return dk == 64 ? launch_fused_dk<bf16, 64>(bv, a, stream)
+                    : launch_fused_dk<bf16, 128>(bv, a, stream);
+  return dk == 64 ? launch_fused_dk<float, 64>(bv, a, stream)
+                  : launch_fused_dk<float, 128>(bv, a, stream);
+}
+
+size_t prefill_coop_workspace_bytes(int dk, int units, int R) {
+  return dk == 64 ? coop_workspace_bytes<64>(units, R) : coop_workspace_bytes<128>(units, R);
+}
+
+template <int DK, int BV>
+static hipError_t launch_coop_t(const PrefillArgs& a, hipStream_t stream) {
+  const int nwords = static_cast<int>((kWsHeader + coop_flags_bytes(a.units, a.R)) / 4);
+  hipLaunchKernelGGL(coop_reset_kernel, dim3((nwords + 255) / 256), dim3(256), 0, stream,
+                     reinterpret_cast<int*>(a.workspace), nwords);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PrefillArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&prefill_coop_kernel<DK, BV>),
+                                    dim3(a.units * (a.NC + a.NP)), dim3(kThreads), params, 0,
+                                    stream);
+}
+
+// Producer/consumer kernel (bf16).  a.NC consumers of a.DV / a.NC rows, a.NP producers,
+// a.R ring slots per unit; a.workspace holds prefill_coop_workspace_bytes bytes.
+hipError_t launch_prefill_coop(int dk, const PrefillArgs& a, hipStream_t stream) {
+  const int bv = a.DV / a.NC;
+  if (dk == 64) {
+    if (bv == 64) return launch_coop_t<64, 64>(a, stream);
+    if (bv == 32) return launch_coop_t<64, 32>(a, stream);
+    return launch_coop_t<64, 16>(a, stream);
   }
-  if (dk == 64)
-    return launch_prefill_dk<float, 64>(bv, q, k, v, g, beta, cu, T, H, DV, NV, units, xcd_remap,
-                                        scale, s0, s1, o, stream);
-  return launch_prefill_dk<float, 128>(bv, q, k, v, g, beta, cu, T, H, DV, NV, units, xcd_remap,
-                                       scale, s0, s1, o, stream);
+  if (bv == 128) return launch_coop_t<128, 128>(a, stream);
+  if (bv == 64) return launch_coop_t<128, 64>(a, stream);
+  if (bv == 32) return launch_coop_t<128, 32>(a, stream);
+  return launch_coop_t<128, 16>(a, stream);
 }
 
 }  // namespace kda

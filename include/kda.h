@@ -79,8 +79,17 @@ const char* kda_status_string(int status);
  *   o : written for every token row that belongs to a sequence.
  * N = 0 or T = 0 is a no-op returning KDA_OK (nothing launched).
  * scale: query scale (the pages use d_k^{-1/2}).
- * workspace / workspace_bytes: reserved, pass NULL / 0 (the fused kernel keeps
- * every intermediate on chip).
+ * workspace / workspace_bytes: optional device scratch.  With bf16 inputs, when
+ *   kda_prefill_workspace_bytes() is nonzero and the workspace holds at least that
+ *   many bytes, the producer/consumer kernel runs: per (sequence, head), producer
+ *   workgroups compute each chunk's d_v-independent tiles once and hand them to the
+ *   value-tile workgroups through a ring in the workspace.  Otherwise (NULL, too
+ *   small, fp32) the fused kernel runs, in which every value tile recomputes them.
+ *   The library owns the workspace's contents during the call (no initialisation
+ *   needed); calls that share one workspace must be ordered on one stream.  After
+ *   such a call completes, the workspace's first int32 is 0; nonzero means a
+ *   cross-workgroup hand-off wait timed out, the call stopped early and its
+ *   outputs are invalid.
  */
 int kda_prefill(int dtype,
                 const void* q, const void* k, const void* v,
@@ -93,12 +102,20 @@ int kda_prefill(int dtype,
                 void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
-/* Device workspace kda_prefill needs for these sizes (0 for this library). */
+/* Workspace bytes that select the producer/consumer prefill for these sizes on the
+ * current device (0: not applicable, the fused kernel runs).  Host-only apart from a
+ * cached device-attribute query. */
 size_t kda_prefill_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_t H,
                                    int32_t d_k, int32_t d_v);
 
+/* Geometry of the producer/consumer prefill on the current device: value-tile
+ * workgroups (consumers), producer workgroups per (sequence, head) and ring slots;
+ * all zero when it does not apply.  Output pointers may be NULL. */
+int kda_prefill_coop_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                          int32_t* consumers, int32_t* producers, int32_t* ring_slots);
+
 /*
- * Launch geometry kda_prefill would use on the current device: the number of
+ * Launch geometry of the fused prefill kernel on the current device: the number of
  * d_v tiles each (sequence, head) is split into (rows of S never mix, so the
  * tiles run independently) and the resulting workgroup count.  Either output
  * pointer may be NULL.  Host-only apart from a cached device-attribute query.

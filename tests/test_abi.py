@@ -38,7 +38,9 @@ def test_version_and_status_strings():
         s = L.kda_status_string(code).decode()
         assert s.startswith("KDA")
     assert "unknown" in L.kda_status_string(99).decode()
-    assert L.kda_prefill_workspace_bytes(1, 8, 1 << 20, 16, 128, 128) == 0
+    # fp32 inputs always take the fused kernel: no workspace
+    assert L.kda_prefill_workspace_bytes(0, 8, 1 << 20, 16, 128, 128) == 0
+    assert L.kda_prefill_workspace_bytes(1, 0, 0, 16, 128, 128) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first

@@ -14,12 +14,24 @@ from parity import check
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+# bf16 prefill runs on two kernels: "fused" (each value tile computes the chunk tiles)
+# and "coop" (producer workgroups hand the chunk tiles to the value tiles)
+PATHS = ["fused", "coop"]
 
 
-def run_gpu(x, **kw):
+def run_gpu(x, path="fused", **kw):
+    ws = None
+    if path == "coop":
+        N = x["cu_seqlens"].numel() - 1 if x["cu_seqlens"] is not None else x["q"].shape[0]
+        B, T, H, d_k = x["q"].shape
+        nb = kda.workspace_bytes(x["q"].dtype, N, B * T, H, d_k, x["v"].shape[-1])
+        assert nb > 0, "producer/consumer kernel not applicable to this case"
+        ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device=DEV)   # contents must not matter
     o, fs = kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=x["cu_seqlens"],
-                        initial_state=x["initial_state"], **kw)
+                        initial_state=x["initial_state"], workspace=ws, **kw)
     torch.cuda.synchronize()
+    if ws is not None:
+        assert not kda.workspace_aborted(ws), "producer/consumer hand-off aborted"
     return o, fs
 
 
@@ -64,31 +76,32 @@ def test_tiny_fp32_workload():
     compare_full(x, o, fs, o_ref, s_ref, "tiny fp32")
 
 
-@pytest.mark.parametrize("dtype,d_k,d_v", [("fp32", 64, 64), ("fp32", 128, 128),
-                                           ("fp32", 64, 128), ("bf16", 64, 64),
-                                           ("bf16", 128, 128), ("bf16", 128, 64),
-                                           ("bf16", 64, 128)])
-def test_varlen_ragged_with_initial_state(dtype, d_k, d_v):
+@pytest.mark.parametrize("dtype,d_k,d_v,path", [
+    ("fp32", 64, 64, "fused"), ("fp32", 128, 128, "fused"), ("fp32", 64, 128, "fused"),
+    ("bf16", 64, 64, "fused"), ("bf16", 128, 128, "fused"), ("bf16", 128, 64, "fused"),
+    ("bf16", 64, 128, "fused"), ("bf16", 64, 64, "coop"), ("bf16", 128, 128, "coop"),
+    ("bf16", 128, 64, "coop"), ("bf16", 64, 128, "coop")])
+def test_varlen_ragged_with_initial_state(dtype, d_k, d_v, path):
     """Packed sequences with empty, sub-chunk, exact-chunk and ragged lengths, nonzero
     initial state, H=3 (N*H not a multiple of 8: plain workgroup mapping)."""
     lengths = [1, 63, 0, 64, 65, 130, 200]
-    print(f"prefill varlen {dtype} d_k={d_k} d_v={d_v} lengths={lengths}", flush=True)
+    print(f"prefill varlen {dtype} d_k={d_k} d_v={d_v} {path} lengths={lengths}", flush=True)
     x = ki.make_prefill(H=3, d_k=d_k, d_v=d_v, dtype=dtype, gate="softplus", lengths=lengths,
                         init_state_std=0.02, seed=31, device=DEV)
-    o, fs = run_gpu(x)
+    o, fs = run_gpu(x, path)
     o_ref, s_ref = run_oracle(x)
     compare_full(x, o, fs, o_ref, s_ref, f"varlen {dtype}")
     # the empty sequence returns its initial state untouched
     assert torch.equal(fs[2], x["initial_state"][2])
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_batched_multi_chunk_xcd_mapping(dtype):
+@pytest.mark.parametrize("dtype,path", [("fp32", "fused"), ("bf16", "fused"), ("bf16", "coop")])
+def test_batched_multi_chunk_xcd_mapping(dtype, path):
     """B=2, H=4 (N*H = 8: XCD-grouped mapping), T=300 (4 full chunks + ragged tail)."""
-    print(f"prefill batched {dtype} B=2 H=4 T=300 d=128", flush=True)
+    print(f"prefill batched {dtype} {path} B=2 H=4 T=300 d=128", flush=True)
     x = ki.make_prefill(B=2, T=300, H=4, d_k=128, d_v=128, dtype=dtype, gate="uniform", seed=32,
                         device=DEV)
-    o, fs = run_gpu(x)
+    o, fs = run_gpu(x, path)
     o_ref, s_ref = run_oracle(x)
     compare_full(x, o, fs, o_ref, s_ref, f"batched {dtype}")
 
@@ -100,16 +113,16 @@ def test_value_tile_heights_agree(bv, monkeypatch):
     x = ki.make_prefill(B=1, T=160, H=2, d_k=128, d_v=128, dtype="bf16", seed=33,
                         init_state_std=0.02, lengths=[70, 90], device=DEV)
     print(f"prefill BV={bv}", flush=True)
-    o, fs = run_gpu(x)
+    o, fs = run_gpu(x, "fused")
     o_ref, s_ref = run_oracle(x)
     compare_full(x, o, fs, o_ref, s_ref, f"BV={bv}")
 
 
 # ------------------------------------------------------------------ full-size workloads
-def _sampled(w, units, label):
-    print(f"prefill full workload {w.name}: units {units}", flush=True)
+def _sampled(w, units, label, path):
+    print(f"prefill full workload {w.name} {path}: units {units}", flush=True)
     x = ki.make_prefill_workload(w, device=DEV)
-    o, fs = run_gpu(x)
+    o, fs = run_gpu(x, path)
     o_ref, s_ref = run_oracle(x, units=units)
     H, d_v = x["H"], x["d_v"]
     og = o.view(-1, H, d_v)
@@ -124,21 +137,25 @@ def _sampled(w, units, label):
     return x, o, fs
 
 
-def test_training_prefill_workload_sampled():
-    _sampled(ki.TRAIN_PREFILL, [(0, 0), (1, 7), (2, 15), (3, 3), (3, 11)], "B4 H16 T4096")
+@pytest.mark.parametrize("path", PATHS)
+def test_training_prefill_workload_sampled(path):
+    _sampled(ki.TRAIN_PREFILL, [(0, 0), (1, 7), (2, 15), (3, 3), (3, 11)], "B4 H16 T4096", path)
 
 
-def test_long_prefill_workload_sampled():
-    _sampled(ki.LONG_PREFILL, [(0, 0), (0, 17), (0, 31)], "H32 T65536")
+@pytest.mark.parametrize("path", PATHS)
+def test_long_prefill_workload_sampled(path):
+    _sampled(ki.LONG_PREFILL, [(0, 0), (0, 17), (0, 31)], "H32 T65536", path)
 
 
-def test_varlen_prefill_workload_sampled():
+@pytest.mark.parametrize("path", PATHS)
+def test_varlen_prefill_workload_sampled(path):
     w = ki.VARLEN_PREFILL
-    _sampled(w, [(0, 0), (1, 5), (3, 9), (5, 15), (7, 2)], "varlen N8")
+    _sampled(w, [(0, 0), (1, 5), (3, 9), (5, 15), (7, 2)], "varlen N8", path)
 
 
 # ------------------------------------------------------------------ method special cases
-def test_one_hot_retrieval_exact():
+@pytest.mark.parametrize("path", PATHS)
+def test_one_hot_retrieval_exact(path):
     """alpha = 1, beta = 1, distinct one-hot keys from a zero state, bf16-representable
     values; a later token with beta = 0, g = 0, q = k_i, scale = 1 reads v_i exactly.
     Writes in chunk 0 and 1, reads in chunk 2 (through the carried state) and in the
@@ -167,7 +184,7 @@ def test_one_hot_retrieval_exact():
     x = dict(q=q.to(torch.bfloat16).to(DEV), k=k.to(torch.bfloat16).to(DEV),
              v=v.to(torch.bfloat16).to(DEV), g=torch.zeros((1, T, 1, d), device=DEV),
              beta=beta.to(DEV), cu_seqlens=None, initial_state=None)
-    o, fs = run_gpu(x, scale=1.0)
+    o, fs = run_gpu(x, path, scale=1.0)
     for r, tgt in zip(reads, targets):
         assert torch.equal(o[0, r, 0].cpu(), vals[tgt]), f"token {r} should read value {tgt}"
     assert torch.equal(o[0, 10, 0].cpu(), vals[3])
@@ -176,14 +193,14 @@ def test_one_hot_retrieval_exact():
         assert torch.equal(fs[0, 0][:, keys[i]].cpu(), vals[i].float())
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_beta_zero_decays_only(dtype):
+@pytest.mark.parametrize("dtype,path", [("fp32", "fused"), ("bf16", "fused"), ("bf16", "coop")])
+def test_beta_zero_decays_only(dtype, path):
     """beta = 0: the state only decays (closed form), and with g = 0 too it comes back
     bit-for-bit."""
     x = ki.make_prefill(B=1, T=150, H=2, d_k=64, d_v=64, dtype=dtype, init_state_std=0.1,
                         seed=42, device=DEV)
     x["beta"] = torch.zeros_like(x["beta"])
-    o, fs = run_gpu(x)
+    o, fs = run_gpu(x, path)
     s0 = ki.to_f64(x["initial_state"])
     G = np.cumsum(ki.to_f64(x["g"])[0], axis=0)                      # [T, H, d_k]
     s_ref = s0[0] * np.exp(G[-1])[:, None, :]
@@ -191,25 +208,26 @@ def test_beta_zero_decays_only(dtype):
     check(dtype, ki.to_f64(fs[0]), s_ref, "beta=0 state")
     check(dtype, ki.to_f64(o[0]), o_ref, "beta=0 o")
     x["g"] = torch.zeros_like(x["g"])
-    o, fs = run_gpu(x)
+    o, fs = run_gpu(x, path)
     assert torch.equal(fs, x["initial_state"])
 
 
-def test_split_resume_and_state_aliasing():
+@pytest.mark.parametrize("path", PATHS)
+def test_split_resume_and_state_aliasing(path):
     """run(0..T) == run(0..t) then run(t..T) with initial = final; bit-for-bit when t is
     a chunk boundary.  final_state may alias initial_state."""
     x = ki.make_prefill(B=1, T=320, H=4, d_k=128, d_v=128, dtype="bf16", init_state_std=0.02,
                         seed=43, device=DEV)
-    o_full, s_full = run_gpu(x)
+    o_full, s_full = run_gpu(x, path)
     for t in (128, 100):
         a = {kk: (vv[:, :t].contiguous() if kk in ("q", "k", "v", "g", "beta") else vv)
              for kk, vv in x.items()}
         b = {kk: (vv[:, t:].contiguous() if kk in ("q", "k", "v", "g", "beta") else vv)
              for kk, vv in x.items()}
-        o1, s1 = run_gpu(a)
+        o1, s1 = run_gpu(a, path)
         st = s1.clone()
         o2, _ = kda.prefill(b["q"], b["k"], b["v"], b["g"], b["beta"], initial_state=st,
-                            final_state=st)          # in place
+                            final_state=st, workspace=None if path == "fused" else "auto")
         torch.cuda.synchronize()
         o_cat = torch.cat([o1, o2], dim=1)
         if t % 64 == 0:
@@ -220,30 +238,32 @@ def test_split_resume_and_state_aliasing():
             check("bf16", ki.to_f64(st), s_ref, f"split at {t} state")
 
 
-def test_packed_equals_separate_calls_and_deterministic():
+@pytest.mark.parametrize("path", PATHS)
+def test_packed_equals_separate_calls_and_deterministic(path):
     lengths = [77, 200, 5]
     x = ki.make_prefill(H=8, d_k=128, d_v=128, dtype="bf16", lengths=lengths,
                         init_state_std=0.02, seed=44, device=DEV)
-    o, fs = run_gpu(x)
-    o2, fs2 = run_gpu(x)
+    o, fs = run_gpu(x, path)
+    o2, fs2 = run_gpu(x, path)
     assert torch.equal(o, o2) and torch.equal(fs, fs2)          # run-to-run deterministic
     cu = x["cu_seqlens"].tolist()
     for n in range(len(lengths)):
         lo, hi = cu[n], cu[n + 1]
         y = {kk: (x[kk][:, lo:hi].contiguous()) for kk in ("q", "k", "v", "g", "beta")}
         y.update(cu_seqlens=None, initial_state=x["initial_state"][n:n + 1].contiguous())
-        on, fsn = run_gpu(y)
+        on, fsn = run_gpu(y, path)
         check("bf16", ki.to_f64(on), ki.to_f64(o[:, lo:hi]), f"separate seq {n} o")
         check("bf16", ki.to_f64(fsn[0]), ki.to_f64(fs[n]), f"separate seq {n} state")
 
 
-def test_decode_steps_match_prefill():
+@pytest.mark.parametrize("path", PATHS)
+def test_decode_steps_match_prefill(path):
     """T decode steps from S_0 give the same outputs and state as one prefill of the
     same T tokens (both against the oracle too)."""
     N, H, T, d = 4, 4, 70, 128
     x = ki.make_prefill(B=N, T=T, H=H, d_k=d, d_v=d, dtype="bf16", init_state_std=0.02,
                         seed=45, device=DEV)
-    o_pre, s_pre = run_gpu(x)
+    o_pre, s_pre = run_gpu(x, path)
     state = x["initial_state"].clone()
     outs = []
     for t in range(T):
