@@ -23,8 +23,12 @@ LIB = os.path.join(OUT_DIR, "libkda.so")
 
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip"]
 ARCH = "gfx950"
+# -packed-fp32-ops: no v_pk_*_f32 generation.  -amdgpu-mfma-vgpr-form: MFMA
+# accumulators in ordinary VGPRs, so loop-carried accumulators (the prefill state)
+# are scaled and packed in place instead of being copied out of and back into AGPRs.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -51,10 +51,12 @@ int env_int(const char* name, int dflt) {
 }
 
 // Producer/consumer geometry: W = CUs / units workgroups per unit (all resident at
-// once, one per CU), split into NC consumers (value tiles of d_v / NC rows, NC a
-// power of two, tiles of at least 16 rows) and NP = W - NC producers.  Needs bf16
-// inputs and W >= 2.  KDA_PREFILL_COOP=0 disables it; KDA_COOP_NC / KDA_COOP_NP /
-// KDA_COOP_R override the split and the ring depth (tuning only).
+// once, one per CU): NC consumers, each 4 waves owning d_v / (4 NC) value columns
+// (NC = 2 for d_v = 128 when W >= 6, else 1), and NP = min(W - NC, 5) producers
+// (measured: past five producers per unit the consumers set the pace); R = NP + 4
+// ring slots.  Needs bf16 inputs and W >= 2.  KDA_PREFILL_COOP=0 disables it;
+// KDA_COOP_NC / KDA_COOP_NP / KDA_COOP_R override the split and the ring depth
+// (tuning only).
 struct CoopPlan {
   int NC = 0, NP = 0, R = 0;
   bool ok() const { return NC > 0; }
@@ -65,16 +67,15 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t d_v, int cus) {
   int W = static_cast<int>(cus / units);
   if (W > 16) W = 16;
   if (W < 2) return p;
-  int nc = 1;
-  while (nc * 2 <= W / 2 && d_v / (nc * 2) >= 16) nc *= 2;
-  int np = W - nc;
+  int nc = (d_v == 128 && W >= 6) ? 2 : 1;
   const int enc = env_int("KDA_COOP_NC", 0), enp = env_int("KDA_COOP_NP", 0);
-  if (enc > 0 && (enc & (enc - 1)) == 0 && d_v / enc >= 16 && d_v % enc == 0) nc = enc;
+  if (enc > 0 && d_v % (4 * enc) == 0 && (d_v / (4 * enc) == 16 || d_v / (4 * enc) == 32)) nc = enc;
+  int np = W - nc < 5 ? W - nc : 5;
   if (enp > 0) np = enp;
-  if (static_cast<int64_t>(units) * (nc + np) > cus) return p;
+  if (np < 1 || static_cast<int64_t>(units) * (nc + np) > cus) return p;
   p.NC = nc;
   p.NP = np;
-  p.R = env_int("KDA_COOP_R", 8);
+  p.R = env_int("KDA_COOP_R", np + 4);
   if (p.R < 2) p.R = 2;
   return p;
 }
@@ -105,7 +106,7 @@ size_t kda_prefill_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_
   if (units > (1 << 24)) return 0;
   const CoopPlan p = coop_plan(dtype, units, d_v, cu_count());
   if (!p.ok()) return 0;
-  return kda::prefill_coop_workspace_bytes(d_k, static_cast<int>(units), p.R);
+  return kda::prefill_coop_workspace_bytes(d_k, d_v, static_cast<int>(units), p.R);
 }
 
 int kda_prefill_coop_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
@@ -171,7 +172,7 @@ int kda_prefill(int dtype, const void* q, const void* k, const void* v, const fl
   const int cus = cu_count();
   const CoopPlan p = coop_plan(dtype, units, d_v, cus);
   if (p.ok() && workspace != nullptr &&
-      workspace_bytes >= kda::prefill_coop_workspace_bytes(d_k, static_cast<int>(units), p.R)) {
+      workspace_bytes >= kda::prefill_coop_workspace_bytes(d_k, d_v, static_cast<int>(units), p.R)) {
     a.workspace = static_cast<unsigned char*>(workspace);
     a.NC = p.NC;
     a.NP = p.NP;

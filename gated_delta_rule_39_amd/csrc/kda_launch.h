@@ -34,8 +34,9 @@ hipError_t launch_decode(int dtype, int dk, int dv, const void* q, const void* k
 // Fused prefill: bv in {16, 32, 64}, bv <= prefill_max_bv(dtype, dk), a.NV = DV / bv.
 hipError_t launch_prefill(int dtype, int dk, int bv, const PrefillArgs& a, hipStream_t stream);
 int prefill_max_bv(int dtype, int dk);
-// Producer/consumer prefill (bf16): a.workspace holds prefill_coop_workspace_bytes bytes.
+// Producer/consumer prefill (bf16): a.workspace holds prefill_coop_workspace_bytes bytes;
+// a.DV / (4 * a.NC) in {16, 32}.
 hipError_t launch_prefill_coop(int dk, const PrefillArgs& a, hipStream_t stream);
-size_t prefill_coop_workspace_bytes(int dk, int units, int R);
+size_t prefill_coop_workspace_bytes(int dk, int dv, int units, int R);
 
 }  // namespace kda

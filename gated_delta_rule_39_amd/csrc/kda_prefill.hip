@@ -40,8 +40,21 @@
 
 #include "kda_chunk.h"
 #include "kda_launch.h"
+#include "kda_wy.h"
+
+#include <utility>
 
 namespace kda {
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 
 __device__ __forceinline__ void unit_bounds(const PrefillArgs& a, int unit, int& n_seq, int& h,
@@ -297,65 +310,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 }
 
 // ====================================================================================
-// Producer / consumer kernel (bf16)
+// Producer / consumer kernel (bf16, WY form; the algebra is in kda_wy.h)
 // ====================================================================================
 
-// One ring slot: the chunk's operands in MFMA fragment order.  A fragment block is
-// the 16 bytes each of the 64 lanes loads for one 16x32 operand step (1 KiB), so a
-// consumer wave reads every block as one contiguous 1 KiB load.
-template <int DK>
-struct SlotLayout {
-  static constexpr int kKs = DK / 32;                 // k steps of Kg / Qg
-  static constexpr int nKg = 4 * kKs;                 // (row block, k step)
-  static constexpr int nKiT = (DK / 16) * 2;          // (key block, token step)
-  static constexpr int nTm = 8;                       // (row block, token step)
-  static constexpr size_t kFrag = 1024;
-  static constexpr size_t oKg = 0;
-  static constexpr size_t oQg = oKg + nKg * kFrag;
-  static constexpr size_t oKiT = oQg + nKg * kFrag;
-  static constexpr size_t oTm = oKiT + nKiT * kFrag;
-  static constexpr size_t oM = oTm + nTm * kFrag;
-  static constexpr size_t oBeta = oM + nTm * kFrag;   // 64 fp32
-  static constexpr size_t oEgn = oBeta + 64 * 4;      // DK fp32
-  static constexpr size_t kBytes = (oEgn + DK * 4 + 255) & ~size_t(255);
-  static constexpr int nBlocks = 2 * nKg + nKiT + 2 * nTm;
-};
-
-// Workspace: [0, 256) header (word 0: abort), then per-unit flags ready[R], done[R]
-// (int32), then the ring slots.
+// Workspace: [0, 256) header (word 0: abort), then per-unit flags ready[R], done[R],
+// arrive, pad (int32), then the ring slots.
 constexpr size_t kWsHeader = 256;
+__host__ __device__ inline int coop_flag_words(int R) { return 2 * R + 2; }
 __host__ __device__ inline size_t coop_flags_bytes(int units, int R) {
-  return (size_t(units) * 2 * R * 4 + 255) & ~size_t(255);
+  return (size_t(units) * coop_flag_words(R) * 4 + 255) & ~size_t(255);
 }
-template <int DK>
+
+// s_getreg operand for the XCC_ID hardware register (id 20, bits 0..15): the XCD the
+// wave runs on.
+constexpr int kHwRegXccId = 20 | (0 << 6) | (15 << 11);
+template <int DK, int DV>
 __host__ __device__ inline size_t coop_workspace_bytes(int units, int R) {
-  return kWsHeader + coop_flags_bytes(units, R) + size_t(units) * R * SlotLayout<DK>::kBytes;
+  return kWsHeader + coop_flags_bytes(units, R) + size_t(units) * R * WySlot<DK, DV>::kBytes;
 }
 
 constexpr uint32_t kSpinLimit = 1u << 22;   // ~ a second of s_sleep polling
-
-// Ring slots are written and read with device-scope (sc1) buffer accesses: a store
-// is acknowledged only once it is visible device-wide and a load reads the
-// device-coherent copy, so the hand-off needs no cache write-back or invalidate.
-constexpr int kDeviceScope = 16;             // cache-policy bit SC1
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(unsigned char* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
-}
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void ring_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16x8 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDeviceScope);
-}
-__device__ __forceinline__ void ring_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kDeviceScope);
-}
-__device__ __forceinline__ bf16x8 ring_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope);
-  return __builtin_bit_cast(bf16x8, x);
-}
-__device__ __forceinline__ f32x4 ring_load16f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope);
-  return __builtin_bit_cast(f32x4, x);
-}
 
 // Wait (one lane) until *p >= target.  False if the wait ran out or the grid aborted;
 // a wait that runs out raises the abort word.
@@ -373,76 +347,44 @@ __device__ __forceinline__ bool wait_at_least(const int* p, int target, int* abo
   }
 }
 
-template <int DK, int BV>
-struct ConsumerLayout {
-  static constexpr int LDK = DK + 8, LDC = kChunk + 8;
-  static constexpr size_t oS = 0;                                         // [BV][LDK] bf16
-  static constexpr size_t oRT = (oS + size_t(BV) * LDK * 2 + 15) & ~size_t(15);   // [BV][LDC]
-  static constexpr size_t oET = (oRT + size_t(BV) * LDC * 2 + 15) & ~size_t(15);
-  static constexpr size_t oFlag = (oET + size_t(BV) * LDC * 2 + 15) & ~size_t(15);
+// Barrier after this wave's global accesses have completed (loads landed, LDS
+// copies written, stores acknowledged) and its LDS operations are done.
+__device__ __forceinline__ void vm_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Consumer LDS: two staging buffers, two output tiles [64][BV + 8] bf16, flags.
+template <int DK, int DV>
+struct WyConsumerLayout {
+  static constexpr int LDO = 128 + 8;   // output tile row (the widest value tile)
+  static constexpr size_t oStage = 0;
+  static constexpr size_t oO = 2 * WySlot<DK, DV>::kStage;
+  static constexpr size_t kOBytes = size_t(kChunk) * LDO * 2;
+  static constexpr size_t oFlag = oO + 2 * kOBytes;
   static constexpr size_t kBytes = oFlag + 16;
 };
 
-// A consumer's operand fragments for one chunk (wave w: row block w; key blocks of
-// its state tiles).
-template <int DK>
-struct ChunkFrags {
-  using SL = SlotLayout<DK>;
-  static constexpr int KPW = DK / 64;
-  bf16x8 kg[SL::kKs], qg[SL::kKs], tm[2], mm[2], kit[KPW][2];
-  f32x4 bt;          // beta of rows 16w + 4*lq .. +3
-  f32x4 egn[KPW];    // e^{G_n} of key channels 16*kb + 4*lq .. +3
-  // slot: byte offset of the slot in the unit's ring
-  __device__ __forceinline__ void load_kq(__amdgpu_buffer_rsrc_t r, uint32_t slot, int wave,
-                                          int lane) {
-#pragma unroll
-    for (int s = 0; s < SL::kKs; ++s) {
-      kg[s] = ring_load16(r, slot + SL::oKg + (wave * SL::kKs + s) * SL::kFrag + 16 * lane);
-      qg[s] = ring_load16(r, slot + SL::oQg + (wave * SL::kKs + s) * SL::kFrag + 16 * lane);
-    }
-    bt = ring_load16f(r, slot + SL::oBeta + (16 * wave + 4 * (lane >> 4)) * 4);
-  }
-  __device__ __forceinline__ void load_tm(__amdgpu_buffer_rsrc_t r, uint32_t slot, int wave,
-                                          int lane) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      tm[t] = ring_load16(r, slot + SL::oTm + (wave * 2 + t) * SL::kFrag + 16 * lane);
-  }
-  __device__ __forceinline__ void load_rest(__amdgpu_buffer_rsrc_t r, uint32_t slot, int wave,
-                                            int lane) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      mm[t] = ring_load16(r, slot + SL::oM + (wave * 2 + t) * SL::kFrag + 16 * lane);
-#pragma unroll
-    for (int j = 0; j < KPW; ++j) {
-      const int kb = wave * KPW + j;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        kit[j][t] = ring_load16(r, slot + SL::oKiT + (kb * 2 + t) * SL::kFrag + 16 * lane);
-      egn[j] = ring_load16f(r, slot + SL::oEgn + (16 * kb + 4 * (lane >> 4)) * 4);
-    }
-  }
-};
-
-template <int DK, int BV>
-struct CoopLayout {
-  static constexpr size_t a = ChunkLayout<bf16, DK>::kBytes;
-  static constexpr size_t b = ConsumerLayout<DK, BV>::kBytes;
-  static constexpr size_t kBytes = a > b ? a : b;
+template <int DK, int DV>
+struct WyLds {
+  static constexpr size_t kCons = WyConsumerLayout<DK, DV>::kBytes;
+  static constexpr size_t kProd = WyProducerLayout<DK, DV>::kBytes;
+  static constexpr size_t kBytes = kProd > kCons ? kProd : kCons;
   static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
 };
 
-template <int DK, int BV>
-__global__ __launch_bounds__(kThreads, 1) void prefill_coop_kernel(PrefillArgs a) {
-  using CP = ChunkProducer<bf16, DK>;
-  using M = Mfma<bf16>;
-  using SL = SlotLayout<DK>;
-  using CL = ConsumerLayout<DK, BV>;
-  using ST = StateTiles<DK, BV>;
-  constexpr int NVB = BV / 16;
-  constexpr int LDK = CL::LDK, LDC = CL::LDC;
+// Per unit: NC consumers of 4 * VBW value columns (wave w of consumer r owns columns
+// 4 VBW r + VBW w .. +VBW) and NP producers (producer p takes chunks p, p + NP, ...).
+template <int DK, int DV, int VBW>
+__global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) {
+  using PR = WyProducer<DK, DV>;
+  using SL = WySlot<DK, DV>;
+  using PL = WyProducerLayout<DK, DV>;
+  constexpr int KS = DK / 32, NKB = DK / 16, NVS = VBW / 16;
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[CoopLayout<DK, BV>::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[WyLds<DK, DV>::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -457,24 +399,54 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_coop_kernel(PrefillArgs a
   const int nch = static_cast<int>((eos - bos + kChunk - 1) / kChunk);
 
   int* abort_word = reinterpret_cast<int*>(a.workspace);
-  int* ready = reinterpret_cast<int*>(a.workspace + kWsHeader) + size_t(unit) * 2 * a.R;
+  int* ready = reinterpret_cast<int*>(a.workspace + kWsHeader) + size_t(unit) * coop_flag_words(a.R);
   int* done = ready + a.R;
+  int* arrive = done + a.R;
   unsigned char* ring = a.workspace + kWsHeader + coop_flags_bytes(a.units, a.R) +
                         size_t(unit) * a.R * SL::kBytes;
-  int* sFlag = reinterpret_cast<int*>(smem + CL::oFlag);   // consumer: wait result
   const __amdgpu_buffer_rsrc_t rr = ring_rsrc(ring, static_cast<uint32_t>(a.R * SL::kBytes));
+
+  // Co-location.  When every workgroup of the unit runs on the XCD its id was dealt
+  // to (ids congruent mod 8, read back from XCC_ID), they share one L2: producers then
+  // publish with plain stores, which the consumers' device-scope loads read from that
+  // L2.  Otherwise producers store device-scope (written through past the L2).  Each
+  // workgroup adds 1 (on its XCD) or 1 << 16 (elsewhere) to the unit's arrive word.
+  if (tid == 0) {
+    const int xcc = static_cast<int>(__builtin_amdgcn_s_getreg(kHwRegXccId) & 0xf);
+    const bool here = a.xcd_remap != 0 && xcc == static_cast<int>(blockIdx.x & 7);
+    __hip_atomic_fetch_add(arrive, here ? 1 : 0x10000, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   if (role >= a.NC) {
     // ================================ producer ==================================
     const int p = role - a.NC;
-    CP cp;
-    cp.init(smem, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), a.g, a.beta,
-            a.H, h, a.scale, tid, wave);
+    PR pr;
+    pr.init(smem, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+            static_cast<const bf16*>(a.v), a.g, a.beta, a.H, h, a.scale, tid, wave);
+    int* pFlag = reinterpret_cast<int*>(smem + PL::oFlag);
+    if (tid == 0) {
+      int mode = -1;
+      for (uint32_t it = 0; it < kSpinLimit; ++it) {
+        const int v = __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((v & 0xffff) + (v >> 16) >= W) {
+          mode = (v >> 16) == 0 ? 1 : 0;
+          break;
+        }
+        if ((it & 15) == 15 &&
+            __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+          break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (mode < 0) __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pFlag[1] = mode;
+    }
+    lds_barrier();
+    if (pFlag[1] < 0) return;
+    pr.local = pFlag[1] == 1;
     if (p < nch) {
       const int64_t c0 = bos + int64_t(p) * kChunk;
-      cp.load(c0, static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk))));
+      pr.load(c0, static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk))));
     }
-    int* pFlag = reinterpret_cast<int*>(smem + ChunkLayout<bf16, DK>::oScr);
     for (int c = p; c < nch; c += a.NP) {
       const int64_t c0 = bos + int64_t(c) * kChunk;
       const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
@@ -482,169 +454,260 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_coop_kernel(PrefillArgs a
       const bool has_next = cn < nch;
       const int64_t c1 = bos + int64_t(cn) * kChunk;
       const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
-      cp.factors(n, has_next, c1, n1);
-      cp.products();
-      cp.inverse();
-      // the slot must have been read by every consumer of its previous chunk
+      pr.factors(n);
+      // the slot must have been copied by every consumer of its previous chunk
       const int s = c % a.R;
       if (tid == 0) pFlag[0] = wait_at_least(done + s, a.NC * (c / a.R), abort_word) ? 1 : 0;
       lds_barrier();
-      const bool ok = pFlag[0] != 0;
-      lds_barrier();
-      if (!ok) break;
+      if (pFlag[0] == 0) break;
       const uint32_t slot = static_cast<uint32_t>(s) * SL::kBytes;
-      // fragment blocks: waves take blocks w, w+4, ...
-      for (int b = wave; b < SL::nBlocks; b += 4) {
-        bf16x8 f;
-        uint32_t off;
-        if (b < SL::nKg) {
-          f = frag_rows<M>(cp.sKg, CP::LDK, 16 * (b / SL::kKs), 32 * (b % SL::kKs), lane);
-          off = SL::oKg + b * SL::kFrag;
-        } else if (b < 2 * SL::nKg) {
-          const int i = b - SL::nKg;
-          f = frag_rows<M>(cp.sQg, CP::LDK, 16 * (i / SL::kKs), 32 * (i % SL::kKs), lane);
-          off = SL::oQg + i * SL::kFrag;
-        } else if (b < 2 * SL::nKg + SL::nKiT) {
-          const int i = b - 2 * SL::nKg;
-          f = frag_rows<M>(cp.sKiT, CP::LDC, 16 * (i / 2), 32 * (i % 2), lane);
-          off = SL::oKiT + i * SL::kFrag;
-        } else if (b < 2 * SL::nKg + SL::nKiT + SL::nTm) {
-          const int i = b - 2 * SL::nKg - SL::nKiT;
-          f = frag_rows<M>(cp.sTm, CP::LDC, 16 * (i / 2), 32 * (i % 2), lane);
-          off = SL::oTm + i * SL::kFrag;
-        } else {
-          const int i = b - 2 * SL::nKg - SL::nKiT - SL::nTm;
-          f = frag_rows<M>(cp.sM, CP::LDC, 16 * (i / 2), 32 * (i % 2), lane);
-          off = SL::oM + i * SL::kFrag;
-        }
-        ring_store16(rr, slot + off + 16 * lane, f);
-      }
-      if (tid < kChunk) ring_store4(rr, slot + SL::oBeta + 4 * tid, cp.sBeta[tid]);
-      if (tid < DK) ring_store4(rr, slot + SL::oEgn + 4 * tid, cp.sEgn[tid]);
-      // every store of the workgroup acknowledged (device-visible), then publish
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_waitcnt(0);
+      // the next chunk's inputs are requested in three parts between the phases
+      if (has_next) pr.load_part(0, c1, n1);
+      pr.products(rr, slot);
       lds_barrier();
+      if (has_next) pr.load_part(1, c1, n1);
+      if (wave == 0)
+        pr.inverse_diag();
+      else
+        pr.publish_qk(rr, slot);
+      lds_barrier();
+      pr.inverse_rest();
+      if (has_next) pr.load_part(2, c1, n1);
+      pr.publish_wu(rr, slot);
+      // every slot store of the workgroup acknowledged (device-visible), then publish
+      vm_barrier();
       if (tid == 0) __hip_atomic_store(ready + s, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
 
   // ================================== consumer =====================================
-  const int vt = role;
-  const int v0 = vt * BV;
-  bf16* sS = reinterpret_cast<bf16*>(smem + CL::oS);
-  bf16* sRT = reinterpret_cast<bf16*>(smem + CL::oRT);
-  bf16* sET = reinterpret_cast<bf16*>(smem + CL::oET);
-  const bf16* v = static_cast<const bf16*>(a.v);
-  bf16* o = static_cast<bf16*>(a.o);
+  const int vw0 = role * 4 * VBW + VBW * wave;     // this wave's first value column
+  using CL = WyConsumerLayout<DK, DV>;
+  int* cFlag = reinterpret_cast<int*>(smem + CL::oFlag);
+  const uint32_t rowO = static_cast<uint32_t>(a.H) * DV;
+  constexpr int BV = 4 * VBW;
+  const int v0 = role * BV;
+  // Output tiles go through LDS and leave as whole 2*BV-byte rows during the next
+  // chunk: wave w stores rows 16 w .. 16 w + 15, LPR lanes per row, NOI stores.
+  constexpr int LPR = BV / 8, RPI = 64 / LPR, NOI = 16 / RPI;
+  auto o_window = [&](int64_t cs, int rows) {   // rows >= `rows` fall outside
+    return __builtin_amdgcn_make_buffer_rsrc(static_cast<bf16*>(a.o) + (cs * a.H + h) * DV + v0, 0,
+                                             static_cast<int>(uint32_t(rows) * rowO * 2), 0x00020000);
+  };
+  auto o_read = [&](const unsigned char* ob, int i) -> u32x4 {
+    const int r = 16 * wave + RPI * i + lane / LPR, col = 8 * (lane % LPR);
+    return *reinterpret_cast<const u32x4*>(ob + (r * CL::LDO + col) * 2);
+  };
+  auto o_store = [&](__amdgpu_buffer_rsrc_t w, int i, u32x4 x) {
+    const int r = 16 * wave + RPI * i + lane / LPR, col = 8 * (lane % LPR);
+    __builtin_amdgcn_raw_buffer_store_b128(x, w, (r * rowO + col) * 2, 0, 0);
+  };
 
-  f32x4 sacc[ST::NST];
-  const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * a.DV * DK;
-  load_state<DK, BV, LDK>(sacc, a.initial_state, st_base, v0, sS, wave, lane);
+  // S^T tiles: S[kb][vs] holds S^T[16 kb + 4 lq + i][vw0 + 16 vs + lr]
+  f32x4 S[NKB][NVS];
+  bf16x8 Sb[KS][NVS];
+  const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * DV * DK;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs)
+      S[kb][vs] = a.initial_state
+                      ? *reinterpret_cast<const f32x4*>(a.initial_state + st_base +
+                                                        int64_t(vw0 + 16 * vs + lr) * DK +
+                                                        16 * kb + 4 * lq)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KS; ++j)
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs) Sb[j][vs] = pack_frag(S[2 * j][vs], S[2 * j + 1][vs]);
 
-  ChunkFrags<DK> fr;
-  ValueRegs<bf16, NVB> vr;
-  bool ok = true;
+  f32x4 U[4][NVS];
+  constexpr int kShare = SL::nStage / 4;   // staged blocks copied by each wave
+  auto stage_blk = [&](uint32_t slot, unsigned char* buf, int i) {
+    const int blk = wave + 4 * i;
+    ring_to_lds(rr, slot + blk * SL::kFrag, buf + blk * SL::kFrag, lane);
+  };
+  auto load_u = [&](uint32_t slot, int k) {   // k = tb * NVS + vs
+    const int tb = k / NVS, vs = k % NVS;
+    U[tb][vs] = ring_load16f(
+        rr, slot + SL::oU + (tb * SL::NVB + vw0 / 16 + vs) * SL::kFrag + 16 * lane);
+  };
+
+  bool ok = true, nok = true;
   if (nch > 0) {
-    if (tid == 0) sFlag[0] = wait_at_least(ready, 1, abort_word) ? 1 : 0;
+    if (tid == 0) cFlag[0] = wait_at_least(ready, 1, abort_word) ? 1 : 0;
     lds_barrier();
-    ok = sFlag[0] != 0;
+    ok = cFlag[0] != 0;
     if (ok) {
-      fr.load_kq(rr, 0, wave, lane);
-      fr.load_tm(rr, 0, wave, lane);
-      fr.load_rest(rr, 0, wave, lane);
-      vr.load(v, bos, static_cast<int>(min(eos - bos, static_cast<int64_t>(kChunk))), a.H, h,
-              a.DV, v0, wave, lane);
+#pragma unroll
+      for (int i = 0; i < kShare; ++i) stage_blk(0, smem, i);
+#pragma unroll
+      for (int k = 0; k < 4 * NVS; ++k) load_u(0, k);
     }
+    if (tid == 0) cFlag[1] = nch > 1 ? (wait_at_least(ready + 1 % a.R, 2, abort_word) ? 1 : 0) : 1;
+    vm_barrier();
+    nok = cFlag[1] != 0;
   }
 
+  // One chunk is a fixed stream of LDS fragment reads, each feeding NVS MFMAs, read
+  // P steps ahead of use:
+  //   W (j, tb)  E[tb]  += W S^T        Q (j, tb)  Ot[tb] += S Qg^T
+  //   M (tb, t)  Ot[tb] += E^T M^T      egn (kb)   row scales of S^T
+  //   KD (t, kb) S^T[kb] = D S^T[kb] (t = 0) + KD^T E
+  // The next chunk's U tiles and staged blocks are requested between the first
+  // steps, so the vector-memory traffic overlaps the MFMA and LDS work.
+  constexpr int NW = 4 * KS, NM = 6;
+  constexpr int iQ = NW, iM = iQ + NW, iE = iM + NM, iKD = iE + NKB, NF = iKD + 2 * NKB;
+  constexpr int P = 6;
+  // U loads at steps kU0 .. kU0 + 4 NVS - 1; then one staged block every kDs steps
+  constexpr int kU0 = 1, kD0 = kU0 + 4 * NVS, kDs = (NF - kD0 - 2) / kShare;
+  static_assert(kDs >= 1 && kD0 + kDs * (kShare - 1) < NF, "staging does not fit the stream");
+  auto frag_at = [&](const unsigned char* F, int i) -> u32x4 {
+    uint32_t off;
+    if (i < iQ) {
+      off = SL::oW + ((i % 4) * KS + i / 4) * SL::kFrag + 16 * lane;
+    } else if (i < iM) {
+      const int k = i - iQ;
+      off = SL::oQ + ((k % 4) * KS + k / 4) * SL::kFrag + 16 * lane;
+    } else if (i < iE) {
+      // blocks (tb, 0) for tb < 4, then (2, 1), (3, 1): stored in this order
+      off = SL::oM + (i - iM) * SL::kFrag + 16 * lane;
+    } else if (i < iKD) {
+      off = SL::oEgn + (16 * (i - iE) + 4 * lq) * 4;
+    } else {
+      const int k = i - iKD, t = k / NKB, kb = k % NKB;
+      off = SL::oKD + (kb * 2 + t) * SL::kFrag + 16 * lane;
+    }
+    return *reinterpret_cast<const u32x4*>(F + off);
+  };
+
+  // ring slot indices of chunks c, c + 1, c + 2
+  int s0 = 0, s1 = 1 % a.R, s2 = 2 % a.R;
   for (int c = 0; ok && c < nch; ++c) {
     const int64_t c0 = bos + int64_t(c) * kChunk;
     const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
-    const bool has_next = c + 1 < nch;
-    const int64_t c1 = c0 + kChunk;
-    const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
-    const uint32_t nslot = static_cast<uint32_t>((c + 1) % a.R) * SL::kBytes;
-    // wait for the next chunk's slot while this chunk computes
-    if (tid == 0 && has_next)
-      sFlag[1] = wait_at_least(ready + (c + 1) % a.R, c + 2, abort_word) ? 1 : 0;
+    const bool has_next = c + 1 < nch, has2 = c + 2 < nch;
+    const unsigned char* F = smem + (c & 1) * SL::kStage;
+    // chunk c is in LDS and U: its slot is free
+    if (tid == 0) __hip_atomic_fetch_add(done + s0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the flag of chunk c + 2, checked at the end of this chunk
+    int fv = 0;
+    if (tid == 0 && has2)
+      fv = __hip_atomic_load(ready + s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The next chunk is requested unconditionally (a slot that is not ready yet, or
+    // past the last chunk, only fills the idle buffer with unused bytes).
+    const uint32_t nslot = static_cast<uint32_t>(s1) * SL::kBytes;
+    unsigned char* nbuf = smem + ((c + 1) & 1) * SL::kStage;
+    // this chunk's output tile, and the previous chunk's (stored during this stream;
+    // an empty window for c = 0 drops those stores)
+    unsigned char* Ocur = smem + CL::oO + (c & 1) * CL::kOBytes;
+    const unsigned char* Oprev = smem + CL::oO + ((c + 1) & 1) * CL::kOBytes;
+    const __amdgpu_buffer_rsrc_t owin = o_window(c0 - kChunk, c > 0 ? kChunk : 0);
+    u32x4 ox[NOI];
 
-    // ---- P = Kg S^T, Qs = Qg S^T; R' = diag(beta)(V - P) -> R'^T ---------------------
-    f32x4 accQ[NVB];
-    {
-      f32x4 accP[NVB];
+    f32x4 E[4][NVS], Ot[4][NVS];
+    f32x4 d[NKB];
+    bf16x8 Eb[2][NVS];
 #pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) accP[vb] = accQ[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int ks = 0; ks < SL::kKs; ++ks) {
+      for (int vs = 0; vs < NVS; ++vs) {
+        E[tb][vs] = U[tb][vs];
+        Ot[tb][vs] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    u32x4 fb[P + 1];
+    static_for<P>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      fb[i] = frag_at(F, i);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NF>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + P < NF) fb[(i + P) % (P + 1)] = frag_at(F, i + P);
+      if constexpr (i >= kU0 && i < kD0) load_u(nslot, i - kU0);
+      if constexpr (i >= kD0 && (i - kD0) % kDs == 0 && (i - kD0) / kDs < kShare)
+        stage_blk(nslot, nbuf, (i - kD0) / kDs);
+      // the previous chunk's outputs: LDS reads at steps iQ + 2m, stores two steps later
+      if constexpr (i >= iQ && i < iQ + 2 * NOI && (i - iQ) % 2 == 0)
+        ox[(i - iQ) / 2] = o_read(Oprev, (i - iQ) / 2);
+      if constexpr (i >= iQ + 2 && i < iQ + 2 + 2 * NOI && (i - iQ) % 2 == 0)
+        o_store(owin, (i - iQ - 2) / 2, ox[(i - iQ - 2) / 2]);
+      const u32x4 raw = fb[i % (P + 1)];
+      const bf16x8 f = __builtin_bit_cast(bf16x8, raw);
+      if constexpr (i < iQ) {
+        constexpr int j = i / 4, tb = i % 4;
 #pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
-          const auto bS = frag_rows<M>(sS, LDK, 16 * vb, 32 * ks, lane);
-          accP[vb] = M::mma(fr.kg[ks], bS, accP[vb]);
-          accQ[vb] = M::mma(fr.qg[ks], bS, accQ[vb]);
+        for (int vs = 0; vs < NVS; ++vs) E[tb][vs] = mma_bf16(f, Sb[j][vs], E[tb][vs]);
+      } else if constexpr (i < iM) {
+        constexpr int k = i - iQ, j = k / 4, tb = k % 4;
+#pragma unroll
+        for (int vs = 0; vs < NVS; ++vs) Ot[tb][vs] = mma_bf16(Sb[j][vs], f, Ot[tb][vs]);
+      } else if constexpr (i < iE) {
+        if constexpr (i == iM) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int vs = 0; vs < NVS; ++vs) Eb[t][vs] = pack_frag(E[2 * t][vs], E[2 * t + 1][vs]);
+        }
+        constexpr int k = i - iM, tb = k < 4 ? k : k - 2, t = k < 4 ? 0 : 1;
+#pragma unroll
+        for (int vs = 0; vs < NVS; ++vs) Ot[tb][vs] = mma_bf16(Eb[t][vs], f, Ot[tb][vs]);
+      } else if constexpr (i < iKD) {
+        d[i - iE] = __builtin_bit_cast(f32x4, raw);
+      } else {
+        constexpr int k = i - iKD, t = k / NKB, kb = k % NKB;
+        if constexpr (k < 4 * NVS) {
+          // output tile (tb, vs) into LDS: 4 consecutive value columns of token 16 tb + lr
+          constexpr int tb = k / NVS, vs = k % NVS;
+          const f32x4 x = Ot[tb][vs];
+          *reinterpret_cast<bf16x4*>(Ocur + ((16 * tb + lr) * CL::LDO + VBW * wave + 16 * vs + 4 * lq) * 2) =
+              bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                     static_cast<bf16>(x[3])};
+        }
+#pragma unroll
+        for (int vs = 0; vs < NVS; ++vs) {
+          if constexpr (t == 0)
+            S[kb][vs] = mma_bf16(f, Eb[t][vs], S[kb][vs] * d[kb]);
+          else
+            S[kb][vs] = mma_bf16(f, Eb[t][vs], S[kb][vs]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+    });
 #pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        f32x4 rv;
+    for (int j = 0; j < KS; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool okr = 16 * wave + 4 * lq + i < n;
-          rv[i] = okr ? fr.bt[i] * (vr.f32(vb, i) - accP[vb][i]) : 0.f;
-        }
-        store4(sRT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, rv);
-      }
-    }
-    lds_barrier();
-    const bool nok = has_next ? sFlag[1] != 0 : true;
-    if (has_next && nok) {
-      fr.load_kq(rr, nslot, wave, lane);
-      vr.load(v, c1, n1, a.H, h, a.DV, v0, wave, lane);
-    }
+      for (int vs = 0; vs < NVS; ++vs) Sb[j][vs] = pack_frag(S[2 * j][vs], S[2 * j + 1][vs]);
 
-    // ---- E = X R' -> E^T ---------------------------------------------------------------
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc = M::mma(fr.tm[0], frag_rows<M>(sRT, LDC, 16 * vb, 0, lane), acc);
-      if (wave >= 2) acc = M::mma(fr.tm[1], frag_rows<M>(sRT, LDC, 16 * vb, 32, lane), acc);
-      store4(sET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, acc);
-    }
-    lds_barrier();
-    if (has_next && nok) fr.load_tm(rr, nslot, wave, lane);
-
-    // ---- O = Qs + M E (store); S^T = (S^T + Ki^T E) Diag(e^{G_n}) -----------------------
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      f32x4 acc = accQ[vb];
-      acc = M::mma(fr.mm[0], frag_rows<M>(sET, LDC, 16 * vb, 0, lane), acc);
-      if (wave >= 2) acc = M::mma(fr.mm[1], frag_rows<M>(sET, LDC, 16 * vb, 32, lane), acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * lq + i;
-        if (r < n) o[((c0 + r) * a.H + h) * a.DV + v0 + 16 * vb + lr] = from_f32<bf16>(acc[i]);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < ST::NST; ++s) {
-      const int j = s / NVB, vb = ST::vb(s);
-      const int kb = ST::kb(wave, s);
-      f32x4 acc = sacc[s];
-      acc = M::mma(fr.kit[j][0], frag_rows<M>(sET, LDC, 16 * vb, 0, lane), acc);
-      acc = M::mma(fr.kit[j][1], frag_rows<M>(sET, LDC, 16 * vb, 32, lane), acc);
-      acc *= fr.egn[j];
-      store4(sS + (16 * vb + lr) * LDK + 16 * kb + 4 * lq, acc);
-      sacc[s] = acc;
-    }
-    if (has_next && nok) fr.load_rest(rr, nslot, wave, lane);
-    lds_barrier();
-    // this chunk's fragments were all used: free its slot
-    if (tid == 0) __hip_atomic_fetch_add(done + c % a.R, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ok = nok;
+    if (tid == 0)
+      cFlag[c & 1] = !has2 ? 1
+                           : ((fv >= c + 3 || wait_at_least(ready + s2, c + 3, abort_word)) ? 1 : 0);
+    vm_barrier();
+    ok = has_next ? nok : true;
+    nok = cFlag[c & 1] != 0;
+    s0 = s1;
+    s1 = s2;
+    s2 = s2 + 1 == a.R ? 0 : s2 + 1;
   }
 
-  if (ok && a.final_state) store_state<DK, BV>(sacc, a.final_state, st_base, v0, wave, lane);
+  // the last chunk's outputs (its tile was completed before the loop's last barrier)
+  if (ok && nch > 0) {
+    const int64_t cl = bos + int64_t(nch - 1) * kChunk;
+    const __amdgpu_buffer_rsrc_t owin = o_window(cl, static_cast<int>(eos - cl));
+    const unsigned char* Olast = smem + CL::oO + ((nch - 1) & 1) * CL::kOBytes;
+#pragma unroll
+    for (int i = 0; i < NOI; ++i) o_store(owin, i, o_read(Olast, i));
+  }
+
+  if (ok && a.final_state) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int vs = 0; vs < NVS; ++vs)
+        *reinterpret_cast<f32x4*>(a.final_state + st_base + int64_t(vw0 + 16 * vs + lr) * DK +
+                                  16 * kb + 4 * lq) = S[kb][vs];
+  }
 }
 
 // Zero the abort word and the hand-off flags before a producer/consumer launch.
@@ -691,12 +754,14 @@ hipError_t launch_prefill(int dtype, int dk, int bv, const PrefillArgs& a, hipSt
                   : launch_fused_dk<float, 128>(bv, a, stream);
 }
 
-size_t prefill_coop_workspace_bytes(int dk, int units, int R) {
-  return dk == 64 ? coop_workspace_bytes<64>(units, R) : coop_workspace_bytes<128>(units, R);
+size_t prefill_coop_workspace_bytes(int dk, int dv, int units, int R) {
+  if (dk == 64)
+    return dv == 64 ? coop_workspace_bytes<64, 64>(units, R) : coop_workspace_bytes<64, 128>(units, R);
+  return dv == 64 ? coop_workspace_bytes<128, 64>(units, R) : coop_workspace_bytes<128, 128>(units, R);
 }
 
-template <int DK, int BV>
-static hipError_t launch_coop_t(const PrefillArgs& a, hipStream_t stream) {
+template <int DK, int DV, int VBW>
+static hipError_t launch_wy_t(const PrefillArgs& a, hipStream_t stream) {
   const int nwords = static_cast<int>((kWsHeader + coop_flags_bytes(a.units, a.R)) / 4);
   hipLaunchKernelGGL(coop_reset_kernel, dim3((nwords + 255) / 256), dim3(256), 0, stream,
                      reinterpret_cast<int*>(a.workspace), nwords);
@@ -704,24 +769,22 @@ static hipError_t launch_coop_t(const PrefillArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   PrefillArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&prefill_coop_kernel<DK, BV>),
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&prefill_wy_kernel<DK, DV, VBW>),
                                     dim3(a.units * (a.NC + a.NP)), dim3(kThreads), params, 0,
                                     stream);
 }
 
-// Producer/consumer kernel (bf16).  a.NC consumers of a.DV / a.NC rows, a.NP producers,
-// a.R ring slots per unit; a.workspace holds prefill_coop_workspace_bytes bytes.
+// Producer/consumer kernel (bf16).  a.NC consumers of a.DV / a.NC value columns
+// (4 waves x VBW, VBW in {16, 32}), a.NP producers, a.R ring slots per unit;
+// a.workspace holds prefill_coop_workspace_bytes bytes.
 hipError_t launch_prefill_coop(int dk, const PrefillArgs& a, hipStream_t stream) {
-  const int bv = a.DV / a.NC;
+  const int vbw = a.DV / (4 * a.NC);
   if (dk == 64) {
-    if (bv == 64) return launch_coop_t<64, 64>(a, stream);
-    if (bv == 32) return launch_coop_t<64, 32>(a, stream);
-    return launch_coop_t<64, 16>(a, stream);
+    if (a.DV == 64) return launch_wy_t<64, 64, 16>(a, stream);
+    return vbw == 32 ? launch_wy_t<64, 128, 32>(a, stream) : launch_wy_t<64, 128, 16>(a, stream);
   }
-  if (bv == 128) return launch_coop_t<128, 128>(a, stream);
-  if (bv == 64) return launch_coop_t<128, 64>(a, stream);
-  if (bv == 32) return launch_coop_t<128, 32>(a, stream);
-  return launch_coop_t<128, 16>(a, stream);
+  if (a.DV == 64) return launch_wy_t<128, 64, 16>(a, stream);
+  return vbw == 32 ? launch_wy_t<128, 128, 32>(a, stream) : launch_wy_t<128, 128, 16>(a, stream);
 }
 
 }  // namespace kda

@@ -1,0 +1,560 @@
+// The KDA chunk step in WY form, split between producer and consumer workgroups
+// (gfx950, bf16 operands, fp32 accumulation).
+//
+// With X = (I + A)^{-1} and the chunk factors of kda_chunk.h, the state step of one
+// chunk (n <= 64 rows) is
+//   E     = U - W S^T              U = X diag(beta) V,   W = X diag(beta) Kg
+//   O     = Qg S^T + M E
+//   S'^T  = D S^T + KD^T E         D = Diag(e^{G_n}),   KD_{r,j} = k_{r,j} e^{G_{n,j} - G_{r,j}}
+// (substitute E = X diag(beta)(V - Kg S^T) and S' = (S + E^T Ki) D of kda_chunk.h).
+// W, U, Qg, KD^T, M and e^{G_n} depend on the chunk's inputs only.  A producer
+// computes them once per (unit, chunk) and publishes them into a ring slot; a
+// consumer owning a block of value columns keeps its part of S^T in MFMA
+// accumulators and runs the chain E -> S' -> E ... with operands from registers:
+// the recurrent state stays in registers and the prediction, error, gate and write
+// of each token are fused into the chunk step, as the kernel-design notes of "Kimi
+// Delta Attention Technical Deep Dive" (mohalkarushikesh.github.io, "Systems and
+// implementation tradeoffs" -> "Kernel design") ask.
+//
+// Permuted-K fragments.  A 16x16 accumulator holds D[4g + i][l % 16] in lane l
+// (g = l / 16, i = 0..3).  Two accumulators of consecutive 16-row blocks 2j, 2j+1
+// packed into eight bf16 per lane form a 16x32 MFMA operand fragment whose lane l
+// covers row (or column) l % 16 and K indices
+//   32j + 4g + e        (e = 0..3,  from block 2j)
+//   32j + 16 + 4g + e-4 (e = 4..7,  from block 2j+1).
+// The MFMA sums over K, so any K order works as long as both operands use it.  All
+// published fragments use this order; then every accumulator a consumer produces
+// (S^T, E) is directly the next product's operand, as the A operand (rows = value
+// column) or the B operand (columns = value column): no LDS round trip in the chain.
+// The producer forms W and M transposed (W^T = Kg^T (X diag(beta))^T, M^T = Ki Qg^T)
+// so that their accumulators are the published fragments too.
+#pragma once
+
+#include "kda_chunk.h"
+
+namespace kda {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Two accumulators of row blocks 2j, 2j+1 -> one permuted-K operand fragment.
+__device__ __forceinline__ bf16x8 pack_frag(f32x4 lo, f32x4 hi) {
+  return bf16x8{static_cast<bf16>(lo[0]), static_cast<bf16>(lo[1]), static_cast<bf16>(lo[2]),
+                static_cast<bf16>(lo[3]), static_cast<bf16>(hi[0]), static_cast<bf16>(hi[1]),
+                static_cast<bf16>(hi[2]), static_cast<bf16>(hi[3])};
+}
+
+// The same fragment from a row-major bf16 LDS array: row row0 + l % 16, K from k0.
+__device__ __forceinline__ bf16x8 frag_perm(const bf16* base, int ld, int row0, int k0, int lane) {
+  const bf16* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j
+// supplies the address of four consecutive bf16 and lane i receives element i % 4 of
+// the vectors addressed by lanes 4e + i / 4, e = 0..3.  With lane j addressing row
+// R + j / 4, column n0 + 4 (j % 4) of a row-major array, lane i receives column n0 + i
+// of rows R .. R + 3.
+__device__ __forceinline__ bf16x4 read_tr4(const bf16* base, int ld, int row, int col) {
+  typedef __bf16 v4bf16 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+  const auto p = (__attribute__((address_space(3))) v4bf16*)(base + row * ld + col);
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
+}
+
+// MFMA operand fragment of a row-major K x N bf16 LDS array (K = row index): lane l
+// covers column n0 + l % 16 and K rows k0 + 8 (l / 16) .. +7 (the order frag_rows
+// uses for an N x K array).
+__device__ __forceinline__ bf16x8 frag_tr(const bf16* base, int ld, int k0, int n0, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const bf16x4 a = read_tr4(base, ld, k0 + 8 * g + (j >> 2), n0 + 4 * (j & 3));
+  const bf16x4 b = read_tr4(base, ld, k0 + 8 * g + 4 + (j >> 2), n0 + 4 * (j & 3));
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// The same in the permuted K order: rows k0 + 4 (l / 16) .. +3, then k0 + 16 + 4 (l / 16)
+// .. +3 (k0 = 32 j).
+__device__ __forceinline__ bf16x8 frag_tr_perm(const bf16* base, int ld, int k0, int n0, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const bf16x4 a = read_tr4(base, ld, k0 + 4 * g + (j >> 2), n0 + 4 * (j & 3));
+  const bf16x4 b = read_tr4(base, ld, k0 + 16 + 4 * g + (j >> 2), n0 + 4 * (j & 3));
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- ring slot ---------------------------------------------------------------------
+// One chunk's published operands.  Every fragment block is the 16 bytes each of 64
+// lanes holds (1 KiB, lane-major), so a block is copied with one 16-byte-per-lane
+// load and read with one conflict-free ds_read_b128.
+//   W   (tb, j)  tb < 4 token blocks, j < DK/32          rows = token
+//   Q   (tb, j)  the same for Qg
+//   KD  (kb, t)  kb < DK/16 key blocks, t < 2           rows = key channel
+//   M   (tb, t)  t = 0 for tb < 4, then t = 1 for tb = 2, 3 (the others are zero),
+//                block index tb for t = 0, 2 + tb for t = 1
+//   egn DK fp32 (in a 1 KiB block)
+//   U   (tb, vb) vb < DV/16: fp32 16x16 accumulator tiles (16 bytes per lane)
+// The consumer copies [0, kStage) -- fragments, egn and padding -- into LDS.
+template <int DK, int DV>
+struct WySlot {
+  static constexpr int KS = DK / 32;
+  static constexpr size_t kFrag = 1024;
+  static constexpr int nW = 4 * KS;
+  static constexpr int nKD = 2 * (DK / 16);
+  static constexpr int nM = 6;
+  static constexpr size_t oW = 0;
+  static constexpr size_t oQ = oW + nW * kFrag;
+  static constexpr size_t oKD = oQ + nW * kFrag;
+  static constexpr size_t oM = oKD + nKD * kFrag;
+  static constexpr size_t oEgn = oM + nM * kFrag;
+  // staged part padded to a multiple of 4 blocks: each consumer wave copies the same
+  // number of blocks
+  static constexpr int nStage = static_cast<int>((oEgn / kFrag + 1 + 3) / 4 * 4);
+  static constexpr size_t kStage = size_t(nStage) * kFrag;
+  static constexpr size_t oU = kStage;
+  static constexpr int NVB = DV / 16;
+  static constexpr size_t kBytes = oU + 4 * NVB * kFrag;
+  static_assert(DK * 4 <= static_cast<int>(kFrag), "egn block");
+};
+
+// ---- producer ----------------------------------------------------------------------
+template <int DK, int DV>
+struct WyProducerLayout {
+  static constexpr int LDK = DK + 8;        // bf16 [64][DK] rows, 16-byte pad
+  static constexpr int LDV = DV + 8;        // bf16 [64][DV] rows
+  static constexpr int LDC = kChunk + 8;    // bf16 [*][64] rows
+  static constexpr int LDF = kChunk + 4;    // fp32 [64][64]
+  static constexpr int CG = DK / 4, RG = kThreads / CG;
+  static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
+  static constexpr size_t tK = size_t(kChunk) * LDK * 2;
+  static constexpr size_t oKg = 0;
+  static constexpr size_t oQg = al(oKg + tK);
+  static constexpr size_t oKi = al(oQg + tK);
+  static constexpr size_t oKD = al(oKi + tK);                          // [64][LDK]
+  static constexpr size_t oV = al(oKD + tK);                           // [64][LDV]
+  static constexpr size_t oTm = al(oV + size_t(kChunk) * LDV * 2);     // X diag(beta), [64][LDC]
+  static constexpr size_t oA = al(oTm + size_t(kChunk) * LDC * 2);     // fp32 [64][LDF]
+  static constexpr size_t oX = al(oA + size_t(kChunk) * LDF * 4);      // fp32 [64][LDF]
+  static constexpr size_t scrTot = size_t(RG) * DK * 4;
+  static constexpr size_t scrY = size_t(4) * 16 * 17 * 4;
+  static constexpr size_t oScr = al(oX + size_t(kChunk) * LDF * 4);
+  static constexpr size_t oBeta = al(oScr + (scrTot > scrY ? scrTot : scrY));
+  static constexpr size_t oEgn = al(oBeta + kChunk * 4);
+  static constexpr size_t oFlag = al(oEgn + DK * 4);
+  static constexpr size_t kBytes = al(oFlag + 16);
+};
+
+// Device-scope (SC1) buffer accesses for ring slots: a store is acknowledged once it
+// is visible device-wide and a load reads the device-coherent copy, so the hand-off
+// needs no cache write-back or invalidate.
+constexpr int kDeviceScope = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(unsigned char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ void ring_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16x8 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ void ring_store16f(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ void ring_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ f32x4 ring_load16f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope);
+  return __builtin_bit_cast(f32x4, x);
+}
+// One 1 KiB block: 64 lanes x 16 bytes from the ring at off + 16 * lane into LDS at
+// dst + 16 * lane (dst wave-uniform).  Completion is counted by vmcnt, not lgkmcnt,
+// and the compiler does not order later LDS reads after it: wait explicitly.
+__device__ __forceinline__ void ring_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void* dst,
+                                            int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(dst), 16, off + 16 * lane, 0,
+      0, kDeviceScope);
+}
+
+template <int DK, int DV>
+struct WyProducer {
+  using L = WyProducerLayout<DK, DV>;
+  using SL = WySlot<DK, DV>;
+  using M = Mfma<bf16>;
+  static constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDF = L::LDF;
+  static constexpr int CG = DK / 4, RG = kThreads / CG, RPG = kChunk / RG;
+  static constexpr int CGV = DV / 4, RGV = kThreads / CGV, RPGV = kChunk / RGV;
+  static constexpr int KS = DK / 32;
+
+  bf16 *sKg, *sQg, *sKi, *sKD, *sV, *sTm;
+  float *sA, *sX, *sScr, *sBeta, *sEgn;
+  const bf16 *q, *k, *v;
+  const float *g, *beta;
+  int32_t H, h;
+  uint32_t rowK, rowV;
+  int tid, lane, wave, rg, j0, rgv, jv0;
+  float scale;
+  f32x4 gr[RPG];
+  bf16x4 kr[RPG], qr[RPG], vr[RPGV];
+  float br;
+  // slot stores: plain when the unit's workgroups share one L2, else device-scope
+  bool local;
+  __device__ __forceinline__ void st16(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16x8 v) const {
+    if (local)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+    else
+      ring_store16(r, off, v);
+  }
+  __device__ __forceinline__ void st16f(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) const {
+    if (local)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+    else
+      ring_store16f(r, off, v);
+  }
+  __device__ __forceinline__ void st4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) const {
+    if (local)
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+    else
+      ring_store4(r, off, v);
+  }
+
+  __device__ __forceinline__ void init(unsigned char* smem, const bf16* q_, const bf16* k_,
+                                       const bf16* v_, const float* g_, const float* beta_,
+                                       int32_t H_, int32_t h_, float scale_, int tid_, int wave_) {
+    sKg = reinterpret_cast<bf16*>(smem + L::oKg);
+    sQg = reinterpret_cast<bf16*>(smem + L::oQg);
+    sKi = reinterpret_cast<bf16*>(smem + L::oKi);
+    sKD = reinterpret_cast<bf16*>(smem + L::oKD);
+    sV = reinterpret_cast<bf16*>(smem + L::oV);
+    sTm = reinterpret_cast<bf16*>(smem + L::oTm);
+    sA = reinterpret_cast<float*>(smem + L::oA);
+    sX = reinterpret_cast<float*>(smem + L::oX);
+    sScr = reinterpret_cast<float*>(smem + L::oScr);
+    sBeta = reinterpret_cast<float*>(smem + L::oBeta);
+    sEgn = reinterpret_cast<float*>(smem + L::oEgn);
+    q = q_;
+    k = k_;
+    v = v_;
+    g = g_;
+    beta = beta_;
+    H = H_;
+    h = h_;
+    rowK = static_cast<uint32_t>(H_) * DK;
+    rowV = static_cast<uint32_t>(H_) * DV;
+    scale = scale_;
+    tid = tid_;
+    lane = tid_ & 63;
+    wave = wave_;
+    rg = tid_ / CG;
+    j0 = 4 * (tid_ % CG);
+    rgv = tid_ / CGV;
+    jv0 = 4 * (tid_ % CGV);
+    br = 0.f;
+    local = false;
+    // the strictly upper part of X diag(beta) is never written
+    for (int i = tid; i < kChunk * LDC; i += kThreads) sTm[i] = static_cast<bf16>(0.f);
+  }
+
+  // Rows c0 .. c0+n-1 (n >= 1) of the inputs into registers, in three parts that the
+  // caller issues at different points of a chunk (part 0: g; 1: k, q; 2: v, beta), so
+  // that no single burst fills the memory pipeline; rows past the end re-read the last
+  // valid row (masked at use).  Streaming (non-temporal) loads: the inputs are read once.
+  __device__ __forceinline__ void load_part(int part, int64_t c0, int n) {
+    if (part == 0) {
+      const float* gb = g + (c0 * H + h) * DK;
+#pragma unroll
+      for (int i = 0; i < RPG; ++i)
+        gr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
+            gb + static_cast<uint32_t>(min(rg * RPG + i, n - 1)) * rowK + j0));
+    } else if (part == 1) {
+      const bf16* kb = k + (c0 * H + h) * DK;
+      const bf16* qb = q + (c0 * H + h) * DK;
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const uint32_t off = static_cast<uint32_t>(min(rg * RPG + i, n - 1)) * rowK + j0;
+        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(kb + off));
+        qr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(qb + off));
+      }
+    } else {
+      const bf16* vb = v + (c0 * H + h) * DV;
+#pragma unroll
+      for (int i = 0; i < RPGV; ++i)
+        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(
+            vb + static_cast<uint32_t>(min(rgv * RPGV + i, n - 1)) * rowV + jv0));
+      br = __builtin_nontemporal_load(beta + (c0 + min(lane, n - 1)) * H + h);
+    }
+  }
+  __device__ __forceinline__ void load(int64_t c0, int n) {
+    load_part(0, c0, n);
+    load_part(1, c0, n);
+    load_part(2, c0, n);
+  }
+
+  // Kg, Qg, Ki, KD, V (row-major), beta and e^{G_n} of the loaded chunk into LDS.  The
+  // input registers are free afterwards.  No closing barrier.
+  __device__ __forceinline__ void factors(int n) {
+    f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const f32x4 gg = gr[i];
+      gr[i] = rg * RPG + i < n ? f32x4{exp_hw(gg[0]), exp_hw(gg[1]), exp_hw(gg[2]), exp_hw(gg[3])}
+                               : f32x4{1.f, 1.f, 1.f, 1.f};
+      tot *= gr[i];
+    }
+    store4(sScr + rg * DK + j0, tot);
+    if (tid < kChunk) sBeta[tid] = tid < n ? br : 0.f;
+    // V rows meanwhile (rows past the end are zero)
+#pragma unroll
+    for (int i = 0; i < RPGV; ++i) {
+      const bool ok = rgv * RPGV + i < n;
+      *reinterpret_cast<bf16x4*>(sV + (rgv * RPGV + i) * LDV + jv0) =
+          ok ? vr[i] : bf16x4{static_cast<bf16>(0.f), static_cast<bf16>(0.f),
+                              static_cast<bf16>(0.f), static_cast<bf16>(0.f)};
+    }
+    lds_barrier();
+    f32x4 tots[RG];
+#pragma unroll
+    for (int r2 = 0; r2 < RG; ++r2) tots[r2] = *reinterpret_cast<const f32x4*>(sScr + r2 * DK + j0);
+    f32x4 cp = f32x4{1.f, 1.f, 1.f, 1.f}, cs = f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int r2 = 0; r2 < RG; ++r2) {
+      if (r2 < rg) cp *= tots[r2];
+      if (r2 > rg) cs *= tots[r2];
+    }
+    const f32x4 egn = cp * tot * cs;   // e^{G_n}
+    // forward: e^{G_r} = cp * alpha_first .. alpha_r  ->  Kg, Qg
+    {
+      f32x4 run = cp;
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const bool ok = rg * RPG + i < n;
+        run *= gr[i];
+        const f32x4 k4 = ok ? widen(kr[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 q4 = ok ? widen(qr[i]) * scale : f32x4{0.f, 0.f, 0.f, 0.f};
+        store4(sKg + (rg * RPG + i) * LDK + j0, k4 * run);
+        store4(sQg + (rg * RPG + i) * LDK + j0, q4 * run);
+      }
+    }
+    // backward: e^{G_n - G_r} = alpha_{r+1} .. alpha_n (a suffix product)  ->  KD;
+    // Ki = KD / e^{G_n}
+    {
+      const f32x4 rn = f32x4{__builtin_amdgcn_rcpf(egn[0]), __builtin_amdgcn_rcpf(egn[1]),
+                             __builtin_amdgcn_rcpf(egn[2]), __builtin_amdgcn_rcpf(egn[3])};
+      f32x4 sfx = cs;
+#pragma unroll
+      for (int i = RPG - 1; i >= 0; --i) {
+        const bool ok = rg * RPG + i < n;
+        const f32x4 k4 = ok ? widen(kr[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 kd = k4 * sfx;
+        store4(sKD + (rg * RPG + i) * LDK + j0, kd);
+        store4(sKi + (rg * RPG + i) * LDK + j0, kd * rn);
+        sfx *= gr[i];
+      }
+    }
+    if (rg == 0) store4(sEgn + j0, egn);
+  }
+
+  // Waves 0, 1: A = strict-lower(diag(beta) Kg Ki^T) into LDS (fp32).
+  // Waves 2, 3: M^T = Ki Qg^T (tiles (a, b), a <= b, masked to a row <= column) and
+  // its M fragments straight to the ring slot.  No closing barrier.
+  __device__ __forceinline__ void products(__amdgpu_buffer_rsrc_t rr, uint32_t slot) {
+    const int lq = lane >> 4, lr = lane & 15;
+    f32x4 acc[5];
+    if (wave < 2) {
+      const f32x4 bta = *reinterpret_cast<const f32x4*>(sBeta + 16 * (wave ? 1 : 0) + 4 * lq);
+      const f32x4 btb = *reinterpret_cast<const f32x4*>(sBeta + 16 * (wave ? 2 : 3) + 4 * lq);
+      if (wave == 0) {
+        lower_blocks<M, DK, LDK, 0, 3>(acc, sKg, sKi, lane);
+        store_lower_blocks<true, bf16, LDF, LDC, 0, 3>(acc, bta, btb, sA, nullptr, lane);
+      } else {
+        lower_blocks<M, DK, LDK, 1, 2>(acc, sKg, sKi, lane);
+        store_lower_blocks<true, bf16, LDF, LDC, 1, 2>(acc, bta, btb, sA, nullptr, lane);
+      }
+      return;
+    }
+    // token blocks b of this wave: (0, 3) or (1, 2); tiles (a, b) for a <= b
+    const int b0 = wave == 2 ? 0 : 1, b1 = wave == 2 ? 3 : 2;
+    // acc[0..b0] = tiles (a, b0), acc[b0+1 .. b0+1+b1] = tiles (a, b1)
+#pragma unroll
+    for (int i = 0; i < 5; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < DK; kk += 32) {
+      const bf16x8 q0 = frag_rows<M>(sQg, LDK, 16 * b0, kk, lane);
+      const bf16x8 q1 = frag_rows<M>(sQg, LDK, 16 * b1, kk, lane);
+      bf16x8 ki[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) ki[a] = frag_rows<M>(sKi, LDK, 16 * a, kk, lane);
+      if (wave == 2) {
+        acc[0] = mma_bf16(ki[0], q0, acc[0]);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) acc[1 + a] = mma_bf16(ki[a], q1, acc[1 + a]);
+      } else {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) acc[a] = mma_bf16(ki[a], q0, acc[a]);
+#pragma unroll
+        for (int a = 0; a < 3; ++a) acc[2 + a] = mma_bf16(ki[a], q1, acc[2 + a]);
+      }
+    }
+    // causal mask on the diagonal tiles: row (token') 4*lq + i <= column (token) lr
+    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto diag = [&](f32x4 t) {
+      f32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = 4 * lq + i <= lr ? t[i] : 0.f;
+      return r;
+    };
+    const uint32_t base = slot + SL::oM + 16 * lane;
+    if (wave == 2) {
+      // b = 0: fragment (0, 0) = tiles (0, 0)diag, (1, 0) = 0
+      st16(rr, base + 0 * SL::kFrag, pack_frag(diag(acc[0]), z));
+      // b = 3: fragments (3, 0) = tiles (0, 3), (1, 3); (3, 1) = (2, 3), (3, 3)diag
+      st16(rr, base + 3 * SL::kFrag, pack_frag(acc[1], acc[2]));
+      st16(rr, base + 5 * SL::kFrag, pack_frag(acc[3], diag(acc[4])));
+    } else {
+      // b = 1: fragment (1, 0) = tiles (0, 1), (1, 1)diag
+      st16(rr, base + 1 * SL::kFrag, pack_frag(acc[0], diag(acc[1])));
+      // b = 2: fragments (2, 0) = tiles (0, 2), (1, 2); (2, 1) = (2, 2)diag, 0
+      st16(rr, base + 2 * SL::kFrag, pack_frag(acc[2], acc[3]));
+      st16(rr, base + 4 * SL::kFrag, pack_frag(diag(acc[4]), z));
+    }
+  }
+
+  // Wave 0: the four 16x16 diagonal blocks of X = (I + A)^{-1} (left-looking
+  // substitution, lane = (block, column), the block's rows preloaded from LDS), then
+  // X_10 = -X_11 A_10 X_00 and X_32 = -X_33 A_32 X_22.  X goes to LDS in fp32 and,
+  // times diag(beta), as the bf16 operand Tm.  No closing barrier.
+  __device__ __forceinline__ void inverse_diag() {
+    const int lr = lane & 15, lq = lane >> 4;
+    float* sY = sScr;
+    {
+      const int b = lane >> 4, c = lane & 15;
+      const float* Ab = sA + (16 * b) * LDF + 16 * b;
+      f32x4 ar[16][4];
+#pragma unroll
+      for (int r = 1; r < 16; ++r)
+#pragma unroll
+        for (int j4 = 0; j4 < r; j4 += 4) ar[r][j4 / 4] = *reinterpret_cast<const f32x4*>(Ab + r * LDF + j4);
+      // x[r] = delta(r, c) - sum_{j < r} A[r][j] x[j], the sum in four independent
+      // partial sums (j mod 4) to shorten the dependent chain
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < r; ++j) p[j % 4] += ar[r][j / 4][j % 4] * x[j];
+        x[r] = ((r == c) ? 1.f : 0.f) - ((p[0] + p[1]) + (p[2] + p[3]));
+      }
+      const float bc = sBeta[16 * b + c];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sX[(16 * b + r) * LDF + 16 * b + c] = x[r];
+        sTm[(16 * b + r) * LDC + 16 * b + c] = static_cast<bf16>(x[r] * bc);
+      }
+    }
+    wave_lds_sync();
+    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 y0 = mm16(z, sA + 16 * LDF, LDF, sX, LDF, lane);
+    const f32x4 y1 = mm16(z, sA + 48 * LDF + 32, LDF, sX + 32 * LDF + 32, LDF, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sY[(4 * lq + i) * 17 + lr] = y0[i];
+      sY[16 * 17 + (4 * lq + i) * 17 + lr] = y1[i];
+    }
+    wave_lds_sync();
+    const f32x4 x10 = mm16(z, sX + 16 * LDF + 16, LDF, sY, 17, lane);
+    const f32x4 x32 = mm16(z, sX + 48 * LDF + 48, LDF, sY + 16 * 17, 17, lane);
+    const float b0 = sBeta[lr], b2 = sBeta[32 + lr];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * lq + i;
+      sX[(16 + r) * LDF + lr] = -x10[i];
+      sX[(48 + r) * LDF + 32 + lr] = -x32[i];
+      sTm[(16 + r) * LDC + lr] = static_cast<bf16>(-x10[i] * b0);
+      sTm[(48 + r) * LDC + 32 + lr] = static_cast<bf16>(-x32[i] * b2);
+    }
+  }
+
+  // All waves, after a barrier that follows inverse_diag: the 32x32 block below the
+  // diagonal, X_lo = -X_B11 (A_lo X_B00); wave w forms block (w/2, w%2).  Ends with
+  // a barrier (Tm complete).
+  __device__ __forceinline__ void inverse_rest() {
+    const int lr = lane & 15, lq = lane >> 4;
+    float* sY = sScr;
+    const int bi = 2 + (wave >> 1), bj = wave & 1;
+    {
+      f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb >= bj) y = mm16(y, sA + (16 * bi) * LDF + 16 * kb, LDF,
+                               sX + (16 * kb) * LDF + 16 * bj, LDF, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sY[wave * 16 * 17 + (4 * lq + i) * 17 + lr] = y[i];
+    }
+    lds_barrier();
+    {
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 2; kb < 4; ++kb)
+        if (kb <= bi) x = mm16(x, sX + (16 * bi) * LDF + 16 * kb, LDF,
+                               sY + ((kb - 2) * 2 + bj) * 16 * 17, 17, lane);
+      const float bc = sBeta[16 * bj + lr];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * bi + 4 * lq + i, c = 16 * bj + lr;
+        sTm[r * LDC + c] = static_cast<bf16>(-x[i] * bc);
+      }
+    }
+    lds_barrier();
+  }
+
+  // Waves 1..3 (while wave 0 inverts): Qg and KD^T fragments and e^{G_n} to the slot.
+  __device__ __forceinline__ void publish_qk(__amdgpu_buffer_rsrc_t rr, uint32_t slot) {
+    constexpr int nQ = 4 * KS, nKD = 2 * (DK / 16);
+    for (int f = wave - 1; f < nQ + nKD; f += 3) {
+      if (f < nQ) {
+        const int tb = f / KS, j = f % KS;
+        st16(rr, slot + SL::oQ + f * SL::kFrag + 16 * lane,
+                     frag_perm(sQg, LDK, 16 * tb, 32 * j, lane));
+      } else {
+        const int i = f - nQ, kb = i >> 1, t = i & 1;
+        st16(rr, slot + SL::oKD + i * SL::kFrag + 16 * lane,
+             frag_tr_perm(sKD, LDK, 32 * t, 16 * kb, lane));
+      }
+    }
+    if (tid - 64 < DK && tid >= 64) st4(rr, slot + SL::oEgn + 4 * (tid - 64), sEgn[tid - 64]);
+  }
+
+  // All waves: W^T = -(Kg^T (X diag(beta))^T) as W fragments and U = X diag(beta) V as
+  // fp32 tiles, straight to the slot.  Row block tb of X diag(beta) is zero beyond
+  // column 16 tb + 15, so tb < 2 needs one K step.
+  __device__ __forceinline__ void publish_wu(__amdgpu_buffer_rsrc_t rr, uint32_t slot) {
+    for (int f = wave; f < 4 * KS; f += 4) {
+      const int tb = f / KS, j = f % KS;
+      f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (t == 1 && tb < 2) break;
+        const bf16x8 xb = frag_rows<M>(sTm, LDC, 16 * tb, 32 * t, lane);
+        lo = mma_bf16(frag_tr(sKg, LDK, 32 * t, 32 * j, lane), xb, lo);
+        hi = mma_bf16(frag_tr(sKg, LDK, 32 * t, 32 * j + 16, lane), xb, hi);
+      }
+      st16(rr, slot + SL::oW + f * SL::kFrag + 16 * lane, pack_frag(-lo, -hi));
+    }
+    for (int vb = wave; vb < SL::NVB; vb += 4) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if (t == 1 && tb < 2) break;
+          acc = mma_bf16(frag_rows<M>(sTm, LDC, 16 * tb, 32 * t, lane),
+                         frag_tr(sV, LDV, 32 * t, 16 * vb, lane), acc);
+        }
+        st16f(rr, slot + SL::oU + (tb * SL::NVB + vb) * SL::kFrag + 16 * lane, acc);
+      }
+    }
+  }
+};
+
+}  // namespace kda
