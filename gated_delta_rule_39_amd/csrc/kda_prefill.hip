@@ -461,18 +461,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       lds_barrier();
       if (pFlag[0] == 0) break;
       const uint32_t slot = static_cast<uint32_t>(s) * SL::kBytes;
-      // the next chunk's inputs are requested in three parts between the phases
-      if (has_next) pr.load_part(0, c1, n1);
+      // the next chunk's inputs are requested in five slices between the phases
+      constexpr int L = PR::kLoads, RPG = PR::RPG;
+      if (has_next) pr.template load_slice<0, RPG / 2>(c1, n1);            // g, first half
       pr.products(rr, slot);
+      if (has_next) pr.template load_slice<RPG / 2, RPG>(c1, n1);          // g, second half
       lds_barrier();
-      if (has_next) pr.load_part(1, c1, n1);
+      if (has_next) pr.template load_slice<RPG, 2 * RPG>(c1, n1);          // k
       if (wave == 0)
         pr.inverse_diag();
       else
         pr.publish_qk(rr, slot);
+      if (has_next) pr.template load_slice<2 * RPG, 3 * RPG>(c1, n1);      // q
       lds_barrier();
       pr.inverse_rest();
-      if (has_next) pr.load_part(2, c1, n1);
+      if (has_next) pr.template load_slice<3 * RPG, L>(c1, n1);            // v, beta
       pr.publish_wu(rr, slot);
       // every slot store of the workgroup acknowledged (device-visible), then publish
       vm_barrier();
@@ -550,31 +553,40 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
     nok = cFlag[1] != 0;
   }
 
-  // One chunk is a fixed stream of LDS fragment reads, each feeding NVS MFMAs, read
-  // P steps ahead of use:
-  //   W (j, tb)  E[tb]  += W S^T        Q (j, tb)  Ot[tb] += S Qg^T
-  //   M (tb, t)  Ot[tb] += E^T M^T      egn (kb)   row scales of S^T
-  //   KD (t, kb) S^T[kb] = D S^T[kb] (t = 0) + KD^T E
-  // The next chunk's U tiles and staged blocks are requested between the first
-  // steps, so the vector-memory traffic overlaps the MFMA and LDS work.
+  // One chunk is a fixed stream of LDS reads, each feeding NVS MFMAs (or a row scale),
+  // read P steps ahead of use:
+  //   W (j, tb)       E[tb]  += W S^T
+  //   Q (j, tb), egn  Ot[tb] += S Qg^T; every third step instead reads e^{G_n} for one
+  //                   key block and scales those rows of S^T (D S^T), in the shadow of
+  //                   the neighbouring MFMAs; E is packed to bf16 early in this phase
+  //   M (tb, t)       Ot[tb] += E^T M^T
+  //   KD (t, kb)      S^T[kb] += KD^T E; the next chunk's bf16 S^T operand is packed
+  //                   during the second pass
+  // The next chunk's U tiles and staged blocks are requested at evenly spaced steps,
+  // so the vector-memory traffic overlaps the MFMA and LDS work.
   constexpr int NW = 4 * KS, NM = 6;
-  constexpr int iQ = NW, iM = iQ + NW, iE = iM + NM, iKD = iE + NKB, NF = iKD + 2 * NKB;
+  constexpr int iQ = NW, iM = iQ + 3 * NKB, iKD = iM + NM, NF = iKD + 2 * NKB;
+  static_assert(NW == 2 * NKB, "Q and egn entries interleave two to one");
   constexpr int P = 6;
-  // U loads at steps kU0 .. kU0 + 4 NVS - 1; then one staged block every kDs steps
-  constexpr int kU0 = 1, kD0 = kU0 + 4 * NVS, kDs = (NF - kD0 - 2) / kShare;
-  static_assert(kDs >= 1 && kD0 + kDs * (kShare - 1) < NF, "staging does not fit the stream");
+  // U load k at step kU0 + 3 k; staged block i at step kD0 + kDs i
+  constexpr int kU0 = 1, kD0 = 2, kDs = (NF - kD0 - 2) / kShare;
+  static_assert(kDs >= 1 && kD0 + kDs * (kShare - 1) < NF && kU0 + 3 * (4 * NVS - 1) < NF,
+                "memory requests do not fit the stream");
   auto frag_at = [&](const unsigned char* F, int i) -> u32x4 {
     uint32_t off;
     if (i < iQ) {
       off = SL::oW + ((i % 4) * KS + i / 4) * SL::kFrag + 16 * lane;
     } else if (i < iM) {
-      const int k = i - iQ;
-      off = SL::oQ + ((k % 4) * KS + k / 4) * SL::kFrag + 16 * lane;
-    } else if (i < iE) {
+      const int r = i - iQ;
+      if (r % 3 == 2) {
+        off = SL::oEgn + (16 * (r / 3) + 4 * lq) * 4;
+      } else {
+        const int k = 2 * (r / 3) + r % 3;
+        off = SL::oQ + ((k % 4) * KS + k / 4) * SL::kFrag + 16 * lane;
+      }
+    } else if (i < iKD) {
       // blocks (tb, 0) for tb < 4, then (2, 1), (3, 1): stored in this order
       off = SL::oM + (i - iM) * SL::kFrag + 16 * lane;
-    } else if (i < iKD) {
-      off = SL::oEgn + (16 * (i - iE) + 4 * lq) * 4;
     } else {
       const int k = i - iKD, t = k / NKB, kb = k % NKB;
       off = SL::oKD + (kb * 2 + t) * SL::kFrag + 16 * lane;
@@ -607,7 +619,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
     u32x4 ox[NOI];
 
     f32x4 E[4][NVS], Ot[4][NVS];
-    f32x4 d[NKB];
     bf16x8 Eb[2][NVS];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -625,7 +636,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
     static_for<NF>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i + P < NF) fb[(i + P) % (P + 1)] = frag_at(F, i + P);
-      if constexpr (i >= kU0 && i < kD0) load_u(nslot, i - kU0);
+      if constexpr (i >= kU0 && (i - kU0) % 3 == 0 && (i - kU0) / 3 < 4 * NVS)
+        load_u(nslot, (i - kU0) / 3);
       if constexpr (i >= kD0 && (i - kD0) % kDs == 0 && (i - kD0) / kDs < kShare)
         stage_blk(nslot, nbuf, (i - kD0) / kDs);
       // the previous chunk's outputs: LDS reads at steps iQ + 2m, stores two steps later
@@ -640,21 +652,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
 #pragma unroll
         for (int vs = 0; vs < NVS; ++vs) E[tb][vs] = mma_bf16(f, Sb[j][vs], E[tb][vs]);
       } else if constexpr (i < iM) {
-        constexpr int k = i - iQ, j = k / 4, tb = k % 4;
+        constexpr int r = i - iQ;
+        if constexpr (r % 3 == 2) {
+          // rows 16 kb + 4 lq + i of S^T scaled by e^{G_n}
+          constexpr int kb = r / 3;
+          const f32x4 dd = __builtin_bit_cast(f32x4, raw);
 #pragma unroll
-        for (int vs = 0; vs < NVS; ++vs) Ot[tb][vs] = mma_bf16(Sb[j][vs], f, Ot[tb][vs]);
-      } else if constexpr (i < iE) {
-        if constexpr (i == iM) {
+          for (int vs = 0; vs < NVS; ++vs) S[kb][vs] *= dd;
+        } else {
+          constexpr int k = 2 * (r / 3) + r % 3, j = k / 4, tb = k % 4;
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int vs = 0; vs < NVS; ++vs) Eb[t][vs] = pack_frag(E[2 * t][vs], E[2 * t + 1][vs]);
+          for (int vs = 0; vs < NVS; ++vs) Ot[tb][vs] = mma_bf16(Sb[j][vs], f, Ot[tb][vs]);
         }
+        // E is final since the last W step: pack it while the Qg products run
+        if constexpr (r == 3 || r == 7) {
+          constexpr int t = r == 3 ? 0 : 1;
+#pragma unroll
+          for (int vs = 0; vs < NVS; ++vs) Eb[t][vs] = pack_frag(E[2 * t][vs], E[2 * t + 1][vs]);
+        }
+      } else if constexpr (i < iKD) {
         constexpr int k = i - iM, tb = k < 4 ? k : k - 2, t = k < 4 ? 0 : 1;
 #pragma unroll
         for (int vs = 0; vs < NVS; ++vs) Ot[tb][vs] = mma_bf16(Eb[t][vs], f, Ot[tb][vs]);
-      } else if constexpr (i < iKD) {
-        d[i - iE] = __builtin_bit_cast(f32x4, raw);
       } else {
         constexpr int k = i - iKD, t = k / NKB, kb = k % NKB;
         if constexpr (k < 4 * NVS) {
@@ -666,17 +685,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
                      static_cast<bf16>(x[3])};
         }
 #pragma unroll
-        for (int vs = 0; vs < NVS; ++vs) {
-          if constexpr (t == 0)
-            S[kb][vs] = mma_bf16(f, Eb[t][vs], S[kb][vs] * d[kb]);
-          else
-            S[kb][vs] = mma_bf16(f, Eb[t][vs], S[kb][vs]);
+        for (int vs = 0; vs < NVS; ++vs) S[kb][vs] = mma_bf16(f, Eb[t][vs], S[kb][vs]);
+        // second pass: key blocks 2j, 2j+1 are final two steps after 2j+1 was issued
+        if constexpr (t == 1 && kb >= 3 && kb % 2 == 1) {
+          constexpr int j = (kb - 3) / 2;
+#pragma unroll
+          for (int vs = 0; vs < NVS; ++vs) Sb[j][vs] = pack_frag(S[2 * j][vs], S[2 * j + 1][vs]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    // the key-block pairs not packed inside the stream
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
+    for (int j = (NKB - 2) / 2; j < KS; ++j)
 #pragma unroll
       for (int vs = 0; vs < NVS; ++vs) Sb[j][vs] = pack_frag(S[2 * j][vs], S[2 * j + 1][vs]);
 

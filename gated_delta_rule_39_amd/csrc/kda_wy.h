@@ -256,40 +256,37 @@ struct WyProducer {
     for (int i = tid; i < kChunk * LDC; i += kThreads) sTm[i] = static_cast<bf16>(0.f);
   }
 
-  // Rows c0 .. c0+n-1 (n >= 1) of the inputs into registers, in three parts that the
-  // caller issues at different points of a chunk (part 0: g; 1: k, q; 2: v, beta), so
-  // that no single burst fills the memory pipeline; rows past the end re-read the last
-  // valid row (masked at use).  Streaming (non-temporal) loads: the inputs are read once.
-  __device__ __forceinline__ void load_part(int part, int64_t c0, int n) {
-    if (part == 0) {
-      const float* gb = g + (c0 * H + h) * DK;
+  // Rows c0 .. c0+n-1 (n >= 1) of the inputs into registers.  The loads form one list
+  // (g rows, k rows, q rows, v rows, beta) of which the caller issues slices between the
+  // phases of a chunk, so that the per-CU memory pipeline never holds more than one
+  // slice of misses; rows past the end re-read the last valid row (masked at use).
+  // Streaming (non-temporal) loads: the inputs are read once.
+  static constexpr int kLoads = 3 * RPG + RPGV + 1;
+  template <int I0, int I1>
+  __device__ __forceinline__ void load_slice(int64_t c0, int n) {
+    const int64_t rk = (c0 * H + h) * DK;
 #pragma unroll
-      for (int i = 0; i < RPG; ++i)
-        gr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
-            gb + static_cast<uint32_t>(min(rg * RPG + i, n - 1)) * rowK + j0));
-    } else if (part == 1) {
-      const bf16* kb = k + (c0 * H + h) * DK;
-      const bf16* qb = q + (c0 * H + h) * DK;
-#pragma unroll
-      for (int i = 0; i < RPG; ++i) {
+    for (int e = I0; e < I1; ++e) {
+      if (e < 3 * RPG) {
+        const int i = e % RPG;
         const uint32_t off = static_cast<uint32_t>(min(rg * RPG + i, n - 1)) * rowK + j0;
-        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(kb + off));
-        qr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(qb + off));
-      }
-    } else {
-      const bf16* vb = v + (c0 * H + h) * DV;
-#pragma unroll
-      for (int i = 0; i < RPGV; ++i)
+        if (e < RPG)
+          gr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + rk + off));
+        else if (e < 2 * RPG)
+          kr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(k + rk + off));
+        else
+          qr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(q + rk + off));
+      } else if (e < 3 * RPG + RPGV) {
+        const int i = e - 3 * RPG;
         vr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(
-            vb + static_cast<uint32_t>(min(rgv * RPGV + i, n - 1)) * rowV + jv0));
-      br = __builtin_nontemporal_load(beta + (c0 + min(lane, n - 1)) * H + h);
+            v + (c0 * H + h) * DV + static_cast<uint32_t>(min(rgv * RPGV + i, n - 1)) * rowV +
+            jv0));
+      } else {
+        br = __builtin_nontemporal_load(beta + (c0 + min(lane, n - 1)) * H + h);
+      }
     }
   }
-  __device__ __forceinline__ void load(int64_t c0, int n) {
-    load_part(0, c0, n);
-    load_part(1, c0, n);
-    load_part(2, c0, n);
-  }
+  __device__ __forceinline__ void load(int64_t c0, int n) { load_slice<0, kLoads>(c0, n); }
 
   // Kg, Qg, Ki, KD, V (row-major), beta and e^{G_n} of the loaded chunk into LDS.  The
   // input registers are free afterwards.  No closing barrier.
@@ -509,19 +506,29 @@ struct WyProducer {
   }
 
   // Waves 1..3 (while wave 0 inverts): Qg and KD^T fragments and e^{G_n} to the slot.
+  // Wave w' = wave - 1 takes Qg fragments w', w' + 3, ... and then KD^T fragments
+  // w', w' + 3, ...; the trip counts are compile-time (indices past the end repeat the
+  // last fragment, an identical store), so each wave's reads and stores overlap.
   __device__ __forceinline__ void publish_qk(__amdgpu_buffer_rsrc_t rr, uint32_t slot) {
     constexpr int nQ = 4 * KS, nKD = 2 * (DK / 16);
-    for (int f = wave - 1; f < nQ + nKD; f += 3) {
-      if (f < nQ) {
-        const int tb = f / KS, j = f % KS;
-        st16(rr, slot + SL::oQ + f * SL::kFrag + 16 * lane,
-                     frag_perm(sQg, LDK, 16 * tb, 32 * j, lane));
-      } else {
-        const int i = f - nQ, kb = i >> 1, t = i & 1;
-        st16(rr, slot + SL::oKD + i * SL::kFrag + 16 * lane,
-             frag_tr_perm(sKD, LDK, 32 * t, 16 * kb, lane));
-      }
+    const int w1 = wave - 1;
+    bf16x8 fq[(nQ + 2) / 3], fk[(nKD + 2) / 3];
+#pragma unroll
+    for (int i = 0; i < (nQ + 2) / 3; ++i) {
+      const int f = min(w1 + 3 * i, nQ - 1), tb = f / KS, j = f % KS;
+      fq[i] = frag_perm(sQg, LDK, 16 * tb, 32 * j, lane);
     }
+#pragma unroll
+    for (int i = 0; i < (nKD + 2) / 3; ++i) {
+      const int f = min(w1 + 3 * i, nKD - 1), kb = f >> 1, t = f & 1;
+      fk[i] = frag_tr_perm(sKD, LDK, 32 * t, 16 * kb, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < (nQ + 2) / 3; ++i)
+      st16(rr, slot + SL::oQ + min(w1 + 3 * i, nQ - 1) * SL::kFrag + 16 * lane, fq[i]);
+#pragma unroll
+    for (int i = 0; i < (nKD + 2) / 3; ++i)
+      st16(rr, slot + SL::oKD + min(w1 + 3 * i, nKD - 1) * SL::kFrag + 16 * lane, fk[i]);
     if (tid - 64 < DK && tid >= 64) st4(rr, slot + SL::oEgn + 4 * (tid - 64), sEgn[tid - 64]);
   }
 
@@ -529,8 +536,9 @@ struct WyProducer {
   // fp32 tiles, straight to the slot.  Row block tb of X diag(beta) is zero beyond
   // column 16 tb + 15, so tb < 2 needs one K step.
   __device__ __forceinline__ void publish_wu(__amdgpu_buffer_rsrc_t rr, uint32_t slot) {
-    for (int f = wave; f < 4 * KS; f += 4) {
-      const int tb = f / KS, j = f % KS;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int f = wave + 4 * i, tb = f / KS, j = f % KS;
       f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -541,7 +549,9 @@ struct WyProducer {
       }
       st16(rr, slot + SL::oW + f * SL::kFrag + 16 * lane, pack_frag(-lo, -hi));
     }
-    for (int vb = wave; vb < SL::NVB; vb += 4) {
+#pragma unroll
+    for (int i = 0; i < SL::NVB / 4; ++i) {
+      const int vb = wave + 4 * i;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
