@@ -39,13 +39,19 @@ from scipy.linalg import solve_triangular
 def chunked(q, k, v, g, beta, scale, initial_state=None, chunk=64):
     """Chunkwise evaluation for one unit.
 
-    q, k, g: [T, d_k]; v: [T, d_v]; beta: [T]; initial_state [d_v, d_k] or None.
+    q, k: [T, d_k]; v: [T, d_v]; beta: [T]; initial_state [d_v, d_k] or None;
+    g: [T, d_k] (per key channel), [T] (one scalar per token: every channel decays
+    alike, so G, e^{G} are the same for all channels) or None (no decay, G = 0).
     Returns (o [T, d_v], final_state [d_v, d_k]) in float64.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
+    if g is None:
+        g = np.zeros(k.shape)
     g = np.asarray(g, dtype=np.float64)
+    if g.ndim == 1:
+        g = np.repeat(g[:, None], k.shape[1], axis=1)
     beta = np.asarray(beta, dtype=np.float64)
     n_tok, d_k = k.shape
     d_v = v.shape[1]

@@ -26,6 +26,15 @@ Readings taken where the pages leave a step open:
   memory": predict from the undecayed state, then decay) is a different function
   and is not what is built; the step-by-step page's order (decay first) is.
 
+The two simpler members of the same family (step-by-step page, "From quadratic
+attention to fixed state: a brief history" and "DeltaNet, Gated DeltaNet, and KDA:
+comparison table"; its FAQ "What's the concrete difference between Gated DeltaNet
+and KDA?") use the same cycle with a different step 1:
+
+* Gated DeltaNet: one scalar decay per token for the whole state (every entry of
+  S is multiplied by alpha_t = exp(g_t)); g has no key-channel axis.
+* DeltaNet: no decay at all (g is None).
+
 Everything is computed in float64 on whatever values are passed in; callers pass
 inputs already rounded to the kernel's input dtype so that input quantisation is
 not counted as error.
@@ -45,23 +54,30 @@ def recurrence(q, k, v, g, beta, scale=None, initial_state=None):
     """Run the recurrence over T tokens for U independent units at once.
 
     Shapes (any float dtype; promoted to float64):
-      q, k, g : [U, T, d_k]      v : [U, T, d_v]      beta : [U, T]
+      q, k : [U, T, d_k]      v : [U, T, d_v]      beta : [U, T]
+      g    : [U, T, d_k] (KDA, per key channel), [U, T] (Gated DeltaNet, one scalar
+             per token) or None (DeltaNet, no decay)
       initial_state : [U, d_v, d_k] or None (zeros)
     Returns (o [U, T, d_v], final_state [U, d_v, d_k]), both float64.
 
-    A 2-D call (no unit axis: q [T, d_k], beta [T], state [d_v, d_k]) is accepted
-    and returns 2-D results.
+    A 2-D call (no unit axis: q [T, d_k], beta [T], g [T, d_k] or [T], state
+    [d_v, d_k]) is accepted and returns 2-D results.
     """
     squeeze = np.ndim(beta) == 1
     if squeeze:
-        q, k, v, g, beta = (np.asarray(x)[None] for x in (q, k, v, g, beta))
+        q, k, v, beta = (np.asarray(x)[None] for x in (q, k, v, beta))
+        if g is not None:
+            g = np.asarray(g)[None]
         if initial_state is not None:
             initial_state = np.asarray(initial_state)[None]
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
     beta = np.asarray(beta, dtype=np.float64)
+    if g is not None:
+        g = np.asarray(g, dtype=np.float64)
+        if g.ndim not in (2, 3) or g.shape[:2] != beta.shape:
+            raise ValueError("g must be [U, T, d_k], [U, T] or None")
     n_units, n_tok, d_k = k.shape
     d_v = v.shape[2]
     if scale is None:
@@ -74,8 +90,13 @@ def recurrence(q, k, v, g, beta, scale=None, initial_state=None):
     out = np.empty((n_units, n_tok, d_v))
     for t in range(n_tok):
         key = k[:, t, :]                                       # [U, d_k]
-        # 1. decay each key channel (columns of S) by alpha_t = exp(g_t)
-        state *= np.exp(g[:, t, :])[:, None, :]
+        # 1. decay: each key channel (column of S) by its own alpha_t = exp(g_t)
+        #    (KDA), the whole state by one scalar alpha_t (Gated DeltaNet), or
+        #    nothing (DeltaNet)
+        if g is not None and g.ndim == 3:
+            state *= np.exp(g[:, t, :])[:, None, :]
+        elif g is not None:
+            state *= np.exp(g[:, t])[:, None, None]
         # 2. what the decayed memory returns for this key
         predicted = np.matmul(state, key[:, :, None])[:, :, 0]  # [U, d_v]
         # 3. error between the true value and the prediction, times beta_t
@@ -100,7 +121,8 @@ def forward(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
             units=None):
     """Whole-batch prefill in the packed ``[B, T, H, d]`` layout.
 
-    q, k, g: [B, T, H, d_k]; v: [B, T, H, d_v]; beta: [B, T, H].
+    q, k: [B, T, H, d_k]; v: [B, T, H, d_v]; beta: [B, T, H]; g: [B, T, H, d_k]
+    (KDA), [B, T, H] (Gated DeltaNet) or None (DeltaNet).
     With ``cu_seqlens`` ([N+1], non-decreasing, cu[0] = 0, cu[N] = B*T) the B*T
     token rows are split into N sequences; otherwise each batch row b is one
     sequence of length T.  Every sequence starts from its own initial state
@@ -118,7 +140,8 @@ def forward(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
     qf = np.asarray(q, dtype=np.float64).reshape(tok, H, d_k)
     kf = np.asarray(k, dtype=np.float64).reshape(tok, H, d_k)
     vf = np.asarray(v, dtype=np.float64).reshape(tok, H, d_v)
-    gf = np.asarray(g, dtype=np.float64).reshape(tok, H, d_k)
+    gf = None if g is None else np.asarray(g, dtype=np.float64).reshape(tok, H, -1)
+    per_channel = gf is not None and np.ndim(g) == 4
     bf = np.asarray(beta, dtype=np.float64).reshape(tok, H)
     seqs = _sequence_bounds(cu_seqlens, B, T)
     N = len(seqs)
@@ -138,7 +161,9 @@ def forward(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
         # unit axis = heads of this sequence
         o_seq, s_seq = recurrence(
             qf[lo:hi, heads].transpose(1, 0, 2), kf[lo:hi, heads].transpose(1, 0, 2),
-            vf[lo:hi, heads].transpose(1, 0, 2), gf[lo:hi, heads].transpose(1, 0, 2),
+            vf[lo:hi, heads].transpose(1, 0, 2),
+            None if gf is None else (gf[lo:hi, heads].transpose(1, 0, 2) if per_channel
+                                     else gf[lo:hi, heads, 0].T),
             bf[lo:hi, heads].T, scale=scale if scale is not None else default_scale(d_k),
             initial_state=s0)
         o[lo:hi, heads] = o_seq.transpose(1, 0, 2)
@@ -149,7 +174,8 @@ def forward(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
 def decode_step(q, k, v, g, beta, state, scale=None):
     """One decode step: one token per (sequence, head), state advanced by one.
 
-    q, k, g: [N, H, d_k]; v: [N, H, d_v]; beta: [N, H]; state: [N, H, d_v, d_k].
+    q, k: [N, H, d_k]; v: [N, H, d_v]; beta: [N, H]; state: [N, H, d_v, d_k];
+    g: [N, H, d_k] (KDA), [N, H] (Gated DeltaNet) or None (DeltaNet).
     This is the recurrence with T = 1 (deep-dive page, "Decoding": one state
     update plus one query-state product per token).  The input ``state`` is not
     modified; the new state is returned.
@@ -161,7 +187,9 @@ def decode_step(q, k, v, g, beta, state, scale=None):
     U = N * H
     o, s = recurrence(
         np.asarray(q).reshape(U, 1, d_k), np.asarray(k).reshape(U, 1, d_k),
-        np.asarray(v).reshape(U, 1, d_v), np.asarray(g).reshape(U, 1, d_k),
+        np.asarray(v).reshape(U, 1, d_v),
+        None if g is None else (np.asarray(g).reshape(U, 1, d_k) if np.ndim(g) == 3
+                                else np.asarray(g).reshape(U, 1)),
         np.asarray(beta).reshape(U, 1), scale=scale,
         initial_state=np.asarray(state).reshape(U, d_v, d_k))
     return o.reshape(N, H, d_v), s.reshape(N, H, d_v, d_k)
