@@ -20,6 +20,9 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+# decay kinds: per key channel (KDA), one scalar per token and head (Gated DeltaNet), none
+# (DeltaNet)
+KDA_DECAY_CHANNEL, KDA_DECAY_HEAD, KDA_DECAY_NONE = 0, 1, 2
 
 _lib = None
 
@@ -55,9 +58,15 @@ def lib() -> ctypes.CDLL:
     L.kda_prefill_coop_plan.restype = ctypes.c_int
     L.kda_prefill_coop_plan.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.POINTER(i32),
                                         ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.kda_prefill_ex.restype = ctypes.c_int
+    L.kda_prefill_ex.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32,
+                                 i64, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                   f32, vp]
+    L.kda_decode_step_ex.restype = ctypes.c_int
+    L.kda_decode_step_ex.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, i32,
+                                     i32, i32, i32, f32, vp]
     _lib = L
     return L
 
@@ -123,6 +132,19 @@ def _auto_workspace(device, nbytes: int):
     return ws
 
 
+def _decay_kind(g, qshape) -> int:
+    """Decay kind from g's shape: q's shape = per key channel, q's shape without the
+    last axis = one scalar per (token, head), None = no decay."""
+    if g is None:
+        return KDA_DECAY_NONE
+    if tuple(g.shape) == tuple(qshape):
+        return KDA_DECAY_CHANNEL
+    if tuple(g.shape) == tuple(qshape[:-1]):
+        return KDA_DECAY_HEAD
+    raise ValueError(f"g must have shape {tuple(qshape)} (per key channel), "
+                     f"{tuple(qshape[:-1])} (per head) or be None, got {tuple(g.shape)}")
+
+
 def workspace_aborted(ws: torch.Tensor) -> bool:
     """True if the last producer/consumer call on ``ws`` stopped early (synchronises)."""
     return int(ws[:4].view(torch.int32).item()) != 0
@@ -132,8 +154,9 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None
             output_final_state=True, out=None, final_state=None, workspace="auto"):
     """Chunked KDA forward over packed sequences.
 
-    q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (all fp32 or all bf16); g (log alpha):
-    [B, T, H, d_k] fp32; beta: [B, T, H] fp32; cu_seqlens: int32 [N+1] device tensor
+    q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (all fp32 or all bf16); g (log alpha) fp32:
+    [B, T, H, d_k] (per key channel, KDA), [B, T, H] (one decay per token and head,
+    Gated DeltaNet) or None (no decay, DeltaNet); beta: [B, T, H] fp32; cu_seqlens: int32 [N+1] device tensor
     (B must be 1) or None (N = B); initial_state: [N, H, d_v, d_k] fp32 or None.
     ``final_state`` may be passed (and may be ``initial_state`` itself) to write the
     state in place.  ``workspace``: "auto" (a cached device buffer when the
@@ -147,14 +170,15 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None
         raise TypeError(f"q/k/v must be float32 or bfloat16, got {dt}")
     for t, nm in ((k, "k"), (v, "v")):
         _need(t, nm, dtype=dt, device=dev)
-    _need(g, "g", dtype=torch.float32, device=dev)
+    if g is not None:
+        _need(g, "g", dtype=torch.float32, device=dev)
     _need(beta, "beta", dtype=torch.float32, device=dev)
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, d_k]")
     B, T, H, d_k = q.shape
     d_v = v.shape[-1]
-    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, d_v) \
-            or beta.shape != (B, T, H):
+    decay = _decay_kind(g, q.shape)
+    if k.shape != q.shape or v.shape != (B, T, H, d_v) or beta.shape != (B, T, H):
         raise ValueError("inconsistent q/k/v/g/beta shapes")
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=dev)
@@ -187,17 +211,18 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None
     elif workspace is not None:
         _need(workspace, "workspace", dtype=torch.uint8, device=dev)
         ws = workspace
-    _check(lib().kda_prefill(_DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                             _ptr(cu_seqlens), N, B, T, H, d_k, d_v, float(scale),
-                             _ptr(initial_state), _ptr(fs), _ptr(o), _ptr(ws),
-                             0 if ws is None else ws.numel(), _stream(dev)))
+    _check(lib().kda_prefill_ex(_DTYPE_CODE[dt], decay, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                _ptr(beta), _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
+                                float(scale), _ptr(initial_state), _ptr(fs), _ptr(o), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(dev)))
     return o, fs
 
 
 def decode_step(q, k, v, g, beta, state, *, scale=None, out=None):
     """One decode token per (sequence, head); ``state`` [N, H, d_v, d_k] fp32 is
-    updated in place.  q, k: [N, H, d_k]; v: [N, H, d_v]; g: [N, H, d_k] fp32;
-    beta: [N, H] fp32.  Returns o [N, H, d_v]."""
+    updated in place.  q, k: [N, H, d_k]; v: [N, H, d_v]; g fp32: [N, H, d_k] (per key
+    channel), [N, H] (per head) or None (no decay); beta: [N, H] fp32.
+    Returns o [N, H, d_v]."""
     dev = q.device
     _need(q, "q", device=dev)
     dt = q.dtype
@@ -205,18 +230,23 @@ def decode_step(q, k, v, g, beta, state, *, scale=None, out=None):
         raise TypeError(f"q/k/v must be float32 or bfloat16, got {dt}")
     for t, nm in ((k, "k"), (v, "v")):
         _need(t, nm, dtype=dt, device=dev)
-    _need(g, "g", dtype=torch.float32, device=dev)
+    if g is not None:
+        _need(g, "g", dtype=torch.float32, device=dev)
     _need(beta, "beta", dtype=torch.float32, device=dev)
     _need(state, "state", dtype=torch.float32, device=dev)
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
     N, H, d_k = q.shape
     d_v = v.shape[-1]
-    if k.shape != q.shape or g.shape != q.shape or v.shape != (N, H, d_v) \
+    decay = _decay_kind(g, q.shape)
+    if k.shape != q.shape or v.shape != (N, H, d_v) \
             or beta.shape != (N, H) or state.shape != (N, H, d_v, d_k):
         raise ValueError("inconsistent decode shapes")
     if scale is None:
         scale = d_k ** -0.5
     o = out if out is not None else torch.empty((N, H, d_v), dtype=dt, device=dev)
     _need(o, "out", dtype=dt, device=dev)
-    _check(lib().kda_decode_step(_DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                 _ptr(state), _ptr(o), N, H, d_k, d_v, float(scale), _stream(dev)))
+    _check(lib().kda_decode_step_ex(_DTYPE_CODE[dt], decay, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                    _ptr(beta), _ptr(state), _ptr(o), N, H, d_k, d_v,
+                                    float(scale), _stream(dev)))
     return o

@@ -270,16 +270,24 @@ struct ChunkProducer {
     }
   }
 
-  // Load rows c0 .. c0+n-1 (n >= 1) of g, k, q, beta into registers.
+  // Load rows c0 .. c0+n-1 (n >= 1) of g, k, q, beta into registers.  DECAY: 0 = g per
+  // key channel, 1 = one g per (row, head) broadcast to the channels, 2 = no g (zero).
+  template <int DECAY>
   __device__ __forceinline__ void load(int64_t c0, int n) {
     const int64_t base = (c0 * H + h) * DK;
-    const float* gb = g + base;
     const Tin* kb = k + base;
     const Tin* qb = q + base;
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const uint32_t off = static_cast<uint32_t>(min(rg * RPG + i, n - 1)) * rowK + j0;
-      gr[i] = *reinterpret_cast<const f32x4*>(gb + off);
+      if constexpr (DECAY == 0) {
+        gr[i] = *reinterpret_cast<const f32x4*>(g + base + off);
+      } else if constexpr (DECAY == 1) {
+        // lane l loads row l's g; factors() hands the rows to the threads that use them
+        if (i == 0) gr[0][0] = g[(c0 + min(lane, n - 1)) * H + h];
+      } else {
+        gr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       kr[i] = *reinterpret_cast<const raw4*>(kb + off);
       qr[i] = *reinterpret_cast<const raw4*>(qb + off);
     }
@@ -288,7 +296,16 @@ struct ChunkProducer {
 
   // Kg, Qg, Ki, Ki^T, beta, e^{G_n} of the loaded chunk (n rows) into LDS; then, if
   // has_next, load rows c1 .. c1+n1-1.  Ends with a barrier.
+  template <int DECAY>
   __device__ __forceinline__ void factors(int n, bool has_next, int64_t c1, int n1) {
+    if constexpr (DECAY == 1) {
+      const float x = gr[0][0];
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const float y = __shfl(x, rg * RPG + i);
+        gr[i] = f32x4{y, y, y, y};
+      }
+    }
     // alpha = e^g in place (1 for rows past the end); per-thread product of its rows
     f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
@@ -350,7 +367,7 @@ struct ChunkProducer {
     }
     if (rg == 0) store4(sEgn + j0, egn);
     // the registers are free: load the next chunk's g, k, q, beta
-    if (has_next) load(c1, n1);
+    if (has_next) load<DECAY>(c1, n1);
     lds_barrier();
   }
 

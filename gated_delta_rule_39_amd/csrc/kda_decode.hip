@@ -3,7 +3,9 @@
 //
 // Per (sequence, head) the state S (d_v rows x d_k columns, fp32, d_k contiguous)
 // is read once and written once.  For each row i (value index):
-//   decayed_i = s_i * alpha            (alpha = exp(g) per key channel)
+//   decayed_i = s_i * alpha            (alpha = exp(g) per key channel; one scalar
+//                                       exp(g) per (sequence, head) for Gated
+//                                       DeltaNet; 1 for DeltaNet)
 //   p_i       = decayed_i . k          (prediction for the key)
 //   r_i       = decayed_i . (scale q)  (read of the decayed state)
 //   e_i       = beta (v_i - p_i)
@@ -28,7 +30,7 @@
 
 namespace kda {
 
-template <typename Tin, int DK, int DV>
+template <typename Tin, int DK, int DV, int DECAY>
 __global__ __launch_bounds__(256) void decode_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
@@ -56,7 +58,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const f32x4 kk = load4(k + kbase);
   f32x4 qq = load4(q + kbase);
   qq *= scale;
-  const f32x4 gg = load4(g + kbase);
+  f32x4 gg = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (DECAY == 0) {
+    gg = load4(g + kbase);
+  } else if constexpr (DECAY == 1) {
+    const float x = g[unit];
+    gg = f32x4{x, x, x, x};
+  }
   const f32x4 a = f32x4{exp_hw(gg[0]), exp_hw(gg[1]), exp_hw(gg[2]), exp_hw(gg[3])};
   const float b = beta[unit];
   float vv[NP];
@@ -80,30 +88,44 @@ __global__ __launch_bounds__(256) void decode_kernel(
 template <typename Tin, int DK, int DV>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
                                   const float* beta, float* state, void* o, int32_t units,
-                                  float scale, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<Tin, DK, DV>), dim3(units), dim3(256), 0, stream,
-                     static_cast<const Tin*>(q), static_cast<const Tin*>(k),
-                     static_cast<const Tin*>(v), g, beta, state, static_cast<Tin*>(o), scale);
+                                  float scale, int decay, hipStream_t stream) {
+  const Tin* qt = static_cast<const Tin*>(q);
+  const Tin* kt = static_cast<const Tin*>(k);
+  const Tin* vt = static_cast<const Tin*>(v);
+  Tin* ot = static_cast<Tin*>(o);
+  if (decay == 1)
+    hipLaunchKernelGGL((decode_kernel<Tin, DK, DV, 1>), dim3(units), dim3(256), 0, stream, qt, kt,
+                       vt, g, beta, state, ot, scale);
+  else if (decay == 2)
+    hipLaunchKernelGGL((decode_kernel<Tin, DK, DV, 2>), dim3(units), dim3(256), 0, stream, qt, kt,
+                       vt, g, beta, state, ot, scale);
+  else
+    hipLaunchKernelGGL((decode_kernel<Tin, DK, DV, 0>), dim3(units), dim3(256), 0, stream, qt, kt,
+                       vt, g, beta, state, ot, scale);
   return hipGetLastError();
 }
 
 template <typename Tin>
 static hipError_t launch_decode_d(int dk, int dv, const void* q, const void* k, const void* v,
                                   const float* g, const float* beta, float* state, void* o,
-                                  int32_t units, float scale, hipStream_t stream) {
-  if (dk == 64 && dv == 64) return launch_decode_t<Tin, 64, 64>(q, k, v, g, beta, state, o, units, scale, stream);
-  if (dk == 64 && dv == 128) return launch_decode_t<Tin, 64, 128>(q, k, v, g, beta, state, o, units, scale, stream);
-  if (dk == 128 && dv == 64) return launch_decode_t<Tin, 128, 64>(q, k, v, g, beta, state, o, units, scale, stream);
-  return launch_decode_t<Tin, 128, 128>(q, k, v, g, beta, state, o, units, scale, stream);
+                                  int32_t units, float scale, int decay, hipStream_t stream) {
+  if (dk == 64 && dv == 64)
+    return launch_decode_t<Tin, 64, 64>(q, k, v, g, beta, state, o, units, scale, decay, stream);
+  if (dk == 64 && dv == 128)
+    return launch_decode_t<Tin, 64, 128>(q, k, v, g, beta, state, o, units, scale, decay, stream);
+  if (dk == 128 && dv == 64)
+    return launch_decode_t<Tin, 128, 64>(q, k, v, g, beta, state, o, units, scale, decay, stream);
+  return launch_decode_t<Tin, 128, 128>(q, k, v, g, beta, state, o, units, scale, decay, stream);
 }
 
-// Called by the C ABI after validation: dtype 0 = fp32, 1 = bf16; dk, dv in {64, 128}.
-hipError_t launch_decode(int dtype, int dk, int dv, const void* q, const void* k, const void* v,
-                         const float* g, const float* beta, float* state, void* o,
-                         int32_t units, float scale, hipStream_t stream) {
+// Called by the C ABI after validation: dtype 0 = fp32, 1 = bf16; dk, dv in {64, 128};
+// decay 0 = per key channel, 1 = one scalar per unit, 2 = none.
+hipError_t launch_decode(int dtype, int decay, int dk, int dv, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta, float* state,
+                         void* o, int32_t units, float scale, hipStream_t stream) {
   if (dtype == 1)
-    return launch_decode_d<bf16>(dk, dv, q, k, v, g, beta, state, o, units, scale, stream);
-  return launch_decode_d<float>(dk, dv, q, k, v, g, beta, state, o, units, scale, stream);
+    return launch_decode_d<bf16>(dk, dv, q, k, v, g, beta, state, o, units, scale, decay, stream);
+  return launch_decode_d<float>(dk, dv, q, k, v, g, beta, state, o, units, scale, decay, stream);
 }
 
 }  // namespace kda

@@ -24,13 +24,15 @@ struct PrefillArgs {
   int32_t NV;                 // fused kernel: value tiles per unit
   int32_t NC, NP, R;          // producer/consumer kernel: consumers, producers, ring slots
   int32_t xcd_remap;          // units % 8 == 0: keep a unit's workgroups on one XCD
+  int32_t decay;              // 0: g per key channel, 1: one g per (token, head), 2: none
   float scale;
 };
 
 // dtype: 0 = fp32, 1 = bf16; dk, dv in {64, 128}.
-hipError_t launch_decode(int dtype, int dk, int dv, const void* q, const void* k, const void* v,
-                         const float* g, const float* beta, float* state, void* o,
-                         int32_t units, float scale, hipStream_t stream);
+// decay: 0 = g per key channel [units, dk], 1 = one g per unit [units], 2 = none.
+hipError_t launch_decode(int dtype, int decay, int dk, int dv, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta, float* state,
+                         void* o, int32_t units, float scale, hipStream_t stream);
 // Fused prefill: bv in {16, 32, 64}, bv <= prefill_max_bv(dtype, dk), a.NV = DV / bv.
 hipError_t launch_prefill(int dtype, int dk, int bv, const PrefillArgs& a, hipStream_t stream);
 int prefill_max_bv(int dtype, int dk);

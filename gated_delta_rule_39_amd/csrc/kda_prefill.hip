@@ -170,7 +170,9 @@ struct FusedLayout {
   static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
 };
 
-template <typename Tin, int DK, int BV>
+// DECAY: 0 = g per key channel (KDA), 1 = one g per token and head (Gated DeltaNet),
+// 2 = no decay (DeltaNet).  Only the gate loads differ.
+template <typename Tin, int DK, int BV, int DECAY>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   using CP = ChunkProducer<Tin, DK>;
   using M = typename CP::M;
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   ValueRegs<Tin, NVB> vr;
   if (bos < eos) {
     const int n0 = static_cast<int>(min(eos - bos, static_cast<int64_t>(kChunk)));
-    cp.load(bos, n0);
+    cp.template load<DECAY>(bos, n0);
     vr.load(v, bos, n0, a.H, h, a.DV, v0, wave, lane);
   }
 
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const bool has_next = c1 < eos;
     const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
 
-    cp.factors(n, has_next, c1, n1);
+    cp.template factors<DECAY>(n, has_next, c1, n1);
     cp.products();
     cp.inverse();
 
@@ -377,7 +379,8 @@ struct WyLds {
 
 // Per unit: NC consumers of 4 * VBW value columns (wave w of consumer r owns columns
 // 4 VBW r + VBW w .. +VBW) and NP producers (producer p takes chunks p, p + NP, ...).
-template <int DK, int DV, int VBW>
+// DECAY as for prefill_kernel.
+template <int DK, int DV, int VBW, int DECAY>
 __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) {
   using PR = WyProducer<DK, DV>;
   using SL = WySlot<DK, DV>;
@@ -445,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
     pr.local = pFlag[1] == 1;
     if (p < nch) {
       const int64_t c0 = bos + int64_t(p) * kChunk;
-      pr.load(c0, static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk))));
+      pr.template load<DECAY>(c0, static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk))));
     }
     for (int c = p; c < nch; c += a.NP) {
       const int64_t c0 = bos + int64_t(c) * kChunk;
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       const bool has_next = cn < nch;
       const int64_t c1 = bos + int64_t(cn) * kChunk;
       const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
-      pr.factors(n);
+      pr.template factors<DECAY>(n);
       // the slot must have been copied by every consumer of its previous chunk
       const int s = c % a.R;
       if (tid == 0) pFlag[0] = wait_at_least(done + s, a.NC * (c / a.R), abort_word) ? 1 : 0;
@@ -463,19 +466,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       const uint32_t slot = static_cast<uint32_t>(s) * SL::kBytes;
       // the next chunk's inputs are requested in five slices between the phases
       constexpr int L = PR::kLoads, RPG = PR::RPG;
-      if (has_next) pr.template load_slice<0, RPG / 2>(c1, n1);            // g, first half
+      if (has_next) pr.template load_slice<DECAY, 0, RPG / 2>(c1, n1);            // g, first half
       pr.products(rr, slot);
-      if (has_next) pr.template load_slice<RPG / 2, RPG>(c1, n1);          // g, second half
+      if (has_next) pr.template load_slice<DECAY, RPG / 2, RPG>(c1, n1);          // g, second half
       lds_barrier();
-      if (has_next) pr.template load_slice<RPG, 2 * RPG>(c1, n1);          // k
+      if (has_next) pr.template load_slice<DECAY, RPG, 2 * RPG>(c1, n1);          // k
       if (wave == 0)
         pr.inverse_diag();
       else
         pr.publish_qk(rr, slot);
-      if (has_next) pr.template load_slice<2 * RPG, 3 * RPG>(c1, n1);      // q
+      if (has_next) pr.template load_slice<DECAY, 2 * RPG, 3 * RPG>(c1, n1);      // q
       lds_barrier();
       pr.inverse_rest();
-      if (has_next) pr.template load_slice<3 * RPG, L>(c1, n1);            // v, beta
+      if (has_next) pr.template load_slice<DECAY, 3 * RPG, L>(c1, n1);            // v, beta
       pr.publish_wu(rr, slot);
       // every slot store of the workgroup acknowledged (device-visible), then publish
       vm_barrier();
@@ -746,33 +749,43 @@ __global__ void coop_reset_kernel(int* words, int n) {
 constexpr int max_bv(bool fp32, int dk) { return fp32 ? (dk == 128 ? 16 : 32) : 64; }
 int prefill_max_bv(int dtype, int dk) { return max_bv(dtype == 0, dk); }
 
-template <typename Tin, int DK>
+template <typename Tin, int DK, int DECAY>
 static hipError_t launch_fused_dk(int bv, const PrefillArgs& a, hipStream_t stream) {
   constexpr int kMax = max_bv(sizeof(Tin) == 4, DK);
   const dim3 grid(a.units * a.NV), block(kThreads);
   if constexpr (kMax >= 64) {
     if (bv == 64) {
-      hipLaunchKernelGGL((prefill_kernel<Tin, DK, 64>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_kernel<Tin, DK, 64, DECAY>), grid, block, 0, stream, a);
       return hipGetLastError();
     }
   }
   if constexpr (kMax >= 32) {
     if (bv == 32) {
-      hipLaunchKernelGGL((prefill_kernel<Tin, DK, 32>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_kernel<Tin, DK, 32, DECAY>), grid, block, 0, stream, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<Tin, DK, 16>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<Tin, DK, 16, DECAY>), grid, block, 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename Tin, int DECAY>
+static hipError_t launch_fused_t(int dk, int bv, const PrefillArgs& a, hipStream_t stream) {
+  return dk == 64 ? launch_fused_dk<Tin, 64, DECAY>(bv, a, stream)
+                  : launch_fused_dk<Tin, 128, DECAY>(bv, a, stream);
+}
+
+template <typename Tin>
+static hipError_t launch_fused_d(int dk, int bv, const PrefillArgs& a, hipStream_t stream) {
+  if (a.decay == 1) return launch_fused_t<Tin, 1>(dk, bv, a, stream);
+  if (a.decay == 2) return launch_fused_t<Tin, 2>(dk, bv, a, stream);
+  return launch_fused_t<Tin, 0>(dk, bv, a, stream);
 }
 
 // Fused kernel.  bv in {16, 32, 64}, bv <= prefill_max_bv; a.NV = DV / bv.
 hipError_t launch_prefill(int dtype, int dk, int bv, const PrefillArgs& a, hipStream_t stream) {
-  if (dtype == 1)
-    return dk == 64 ? launch_fused_dk<bf16, 64>(bv, a, stream)
-                    : launch_fused_dk<bf16, 128>(bv, a, stream);
-  return dk == 64 ? launch_fused_dk<float, 64>(bv, a, stream)
-                  : launch_fused_dk<float, 128>(bv, a, stream);
+  if (dtype == 1) return launch_fused_d<bf16>(dk, bv, a, stream);
+  return launch_fused_d<float>(dk, bv, a, stream);
 }
 
 size_t prefill_coop_workspace_bytes(int dk, int dv, int units, int R) {
@@ -781,8 +794,8 @@ size_t prefill_coop_workspace_bytes(int dk, int dv, int units, int R) {
   return dv == 64 ? coop_workspace_bytes<128, 64>(units, R) : coop_workspace_bytes<128, 128>(units, R);
 }
 
-template <int DK, int DV, int VBW>
-static hipError_t launch_wy_t(const PrefillArgs& a, hipStream_t stream) {
+template <int DK, int DV, int VBW, int DECAY>
+static hipError_t launch_wy_k(const PrefillArgs& a, hipStream_t stream) {
   const int nwords = static_cast<int>((kWsHeader + coop_flags_bytes(a.units, a.R)) / 4);
   hipLaunchKernelGGL(coop_reset_kernel, dim3((nwords + 255) / 256), dim3(256), 0, stream,
                      reinterpret_cast<int*>(a.workspace), nwords);
@@ -790,9 +803,16 @@ static hipError_t launch_wy_t(const PrefillArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   PrefillArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&prefill_wy_kernel<DK, DV, VBW>),
-                                    dim3(a.units * (a.NC + a.NP)), dim3(kThreads), params, 0,
-                                    stream);
+  const void* kernel = reinterpret_cast<const void*>(&prefill_wy_kernel<DK, DV, VBW, DECAY>);
+  return hipLaunchCooperativeKernel(kernel, dim3(a.units * (a.NC + a.NP)), dim3(kThreads), params,
+                                    0, stream);
+}
+
+template <int DK, int DV, int VBW>
+static hipError_t launch_wy_t(const PrefillArgs& a, hipStream_t stream) {
+  if (a.decay == 1) return launch_wy_k<DK, DV, VBW, 1>(a, stream);
+  if (a.decay == 2) return launch_wy_k<DK, DV, VBW, 2>(a, stream);
+  return launch_wy_k<DK, DV, VBW, 0>(a, stream);
 }
 
 // Producer/consumer kernel (bf16).  a.NC consumers of a.DV / a.NC value columns

@@ -262,7 +262,7 @@ struct WyProducer {
   // slice of misses; rows past the end re-read the last valid row (masked at use).
   // Streaming (non-temporal) loads: the inputs are read once.
   static constexpr int kLoads = 3 * RPG + RPGV + 1;
-  template <int I0, int I1>
+  template <int DECAY, int I0, int I1>
   __device__ __forceinline__ void load_slice(int64_t c0, int n) {
     const int64_t rk = (c0 * H + h) * DK;
 #pragma unroll
@@ -270,8 +270,17 @@ struct WyProducer {
       if (e < 3 * RPG) {
         const int i = e % RPG;
         const uint32_t off = static_cast<uint32_t>(min(rg * RPG + i, n - 1)) * rowK + j0;
-        if (e < RPG)
-          gr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + rk + off));
+        if (e < RPG) {
+          // g per key channel; with one g per (row, head), lane l loads row l's and
+          // factors() hands the rows to the threads that use them; no g: zeros
+          if constexpr (DECAY == 0) {
+            gr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + rk + off));
+          } else if constexpr (DECAY == 1) {
+            if (i == 0) gr[0][0] = g[(c0 + min(lane, n - 1)) * H + h];
+          } else {
+            gr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
         else if (e < 2 * RPG)
           kr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(k + rk + off));
         else
@@ -286,11 +295,21 @@ struct WyProducer {
       }
     }
   }
-  __device__ __forceinline__ void load(int64_t c0, int n) { load_slice<0, kLoads>(c0, n); }
+  template <int DECAY>
+  __device__ __forceinline__ void load(int64_t c0, int n) { load_slice<DECAY, 0, kLoads>(c0, n); }
 
   // Kg, Qg, Ki, KD, V (row-major), beta and e^{G_n} of the loaded chunk into LDS.  The
   // input registers are free afterwards.  No closing barrier.
+  template <int DECAY>
   __device__ __forceinline__ void factors(int n) {
+    if constexpr (DECAY == 1) {
+      const float x = gr[0][0];
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const float y = __shfl(x, rg * RPG + i);
+        gr[i] = f32x4{y, y, y, y};
+      }
+    }
     f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {

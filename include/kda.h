@@ -41,16 +41,28 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 /* dtype of q, k, v and o.  g, beta and all states are always fp32. */
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
+
+/*
+ * How the state decays at each token (the `_ex` entry points; the plain ones are
+ * KDA_DECAY_CHANNEL).  The three members of the family share the decay -> predict ->
+ * correct -> read cycle and differ in the decay ("Kimi Delta Attention: The Linear
+ * Attention Behind Kimi K2 and Qwen3", "From quadratic attention to fixed state: a
+ * brief history" and "DeltaNet, Gated DeltaNet, and KDA: comparison table"):
+ *   KDA_DECAY_CHANNEL  KDA: per key channel, g is [.., H, d_k]
+ *   KDA_DECAY_HEAD     Gated DeltaNet: one scalar per (token, head), g is [.., H]
+ *   KDA_DECAY_NONE     DeltaNet: no decay, g is not read (may be NULL)
+ */
+enum { KDA_DECAY_CHANNEL = 0, KDA_DECAY_HEAD = 1, KDA_DECAY_NONE = 2 };
 
 enum {
   KDA_OK = 0,
   KDA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                          */
   KDA_ERR_BAD_SHAPE = 2,    /* negative or inconsistent sizes                      */
-  KDA_ERR_UNSUPPORTED = 3,  /* d_k or d_v not in {64, 128}                         */
+  KDA_ERR_UNSUPPORTED = 3,  /* d_k or d_v not in {64, 128}, or unknown decay kind   */
   KDA_ERR_BAD_DTYPE = 4,    /* dtype not KDA_F32 / KDA_BF16                         */
   KDA_ERR_HIP = 5           /* kernel launch failed (hipGetLastError)              */
 };
@@ -102,6 +114,22 @@ int kda_prefill(int dtype,
                 void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/*
+ * kda_prefill_ex -- kda_prefill with the decay kind as an argument.  With
+ * KDA_DECAY_HEAD, g is [B, T, H] fp32 (one log-decay per token row and head); with
+ * KDA_DECAY_NONE, g is not read and may be NULL.  Everything else is as kda_prefill.
+ */
+int kda_prefill_ex(int dtype, int decay,
+                   const void* q, const void* k, const void* v,
+                   const float* g, const float* beta,
+                   const int32_t* cu_seqlens,
+                   int32_t N, int32_t B, int64_t T, int32_t H, int32_t d_k, int32_t d_v,
+                   float scale,
+                   const float* initial_state, float* final_state,
+                   void* o,
+                   void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
 /* Workspace bytes that select the producer/consumer prefill for these sizes on the
  * current device (0: not applicable, the fused kernel runs).  Host-only apart from a
  * cached device-attribute query. */
@@ -138,6 +166,18 @@ int kda_decode_step(int dtype,
                     float* state, void* o,
                     int32_t N, int32_t H, int32_t d_k, int32_t d_v,
                     float scale, hipStream_t stream);
+
+/*
+ * kda_decode_step_ex -- kda_decode_step with the decay kind as an argument.  With
+ * KDA_DECAY_HEAD, g is [N, H] fp32; with KDA_DECAY_NONE, g is not read and may be
+ * NULL.  Everything else is as kda_decode_step.
+ */
+int kda_decode_step_ex(int dtype, int decay,
+                       const void* q, const void* k, const void* v,
+                       const float* g, const float* beta,
+                       float* state, void* o,
+                       int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                       float scale, hipStream_t stream);
 
 #ifdef __cplusplus
 }

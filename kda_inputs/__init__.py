@@ -14,6 +14,10 @@ gate is g = log(alpha) in fp32, either -U(0.001, 0.1) ("uniform") or
 states, where present, are N(0, 0.02^2) fp32 (0.02 read as the standard
 deviation).  The draw order is fixed: sequence lengths (varlen only), q, k, v,
 g, beta, initial state.
+
+Decay kinds: "channel" (KDA: g per key channel, [.., H, d_k]), "head" (Gated
+DeltaNet: one g per token and head, [.., H], same distribution) and "none"
+(DeltaNet: no g is drawn and g is None).
 """
 
 from __future__ import annotations
@@ -105,8 +109,18 @@ def varlen_lengths(n_seqs: int, lo: int, hi: int, seed: int):
     return torch.randint(lo, hi + 1, (n_seqs,), generator=gen).tolist()
 
 
+def _gate_for(gen, lead, d_k, kind, decay, device):
+    if decay == "channel":
+        return _gate(gen, (*lead, d_k), kind, device)
+    if decay == "head":
+        return _gate(gen, lead, kind, device)
+    if decay == "none":
+        return None
+    raise ValueError(f"unknown decay kind {decay!r}")
+
+
 def make_prefill(B=1, T=64, H=1, d_k=64, d_v=64, dtype="fp32", gate="uniform",
-                 init_state_std=None, lengths=None, seed=0, device="cpu"):
+                 init_state_std=None, lengths=None, seed=0, device="cpu", decay="channel"):
     """Draw one prefill batch.
 
     With ``lengths`` (a list of sequence lengths, zeros allowed) the batch is
@@ -114,8 +128,8 @@ def make_prefill(B=1, T=64, H=1, d_k=64, d_v=64, dtype="fp32", gate="uniform",
     holds the offsets.  Otherwise ``cu_seqlens`` is None and each of the B rows is
     one sequence of length T.
 
-    Returns a dict with q, k, v ([B, T, H, d], dtype), g ([B, T, H, d_k] fp32),
-    beta ([B, T, H] fp32), cu_seqlens, initial_state ([N, H, d_v, d_k] fp32 or
+    Returns a dict with q, k, v ([B, T, H, d], dtype), g ([B, T, H, d_k] fp32 for
+    decay "channel", [B, T, H] for "head", None for "none"), beta ([B, T, H] fp32), cu_seqlens, initial_state ([N, H, d_v, d_k] fp32 or
     None), N, lengths and the shape fields.
     """
     if lengths is not None:
@@ -127,7 +141,7 @@ def make_prefill(B=1, T=64, H=1, d_k=64, d_v=64, dtype="fp32", gate="uniform",
     q = _randn(gen, (B, T, H, d_k), device).to(tdt)
     k = _unit_keys(gen, (B, T, H, d_k), device).to(tdt)
     v = _randn(gen, (B, T, H, d_v), device).to(tdt)
-    g = _gate(gen, (B, T, H, d_k), gate, device)
+    g = _gate_for(gen, (B, T, H), d_k, gate, decay, device)
     beta = torch.sigmoid(_randn(gen, (B, T, H), device))
     s0 = None
     if init_state_std is not None:
@@ -139,26 +153,29 @@ def make_prefill(B=1, T=64, H=1, d_k=64, d_v=64, dtype="fp32", gate="uniform",
             offs.append(offs[-1] + n)
         cu = torch.tensor(offs, dtype=torch.int32, device=device)
     return dict(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu, initial_state=s0,
-                N=N, B=B, T=T, H=H, d_k=d_k, d_v=d_v, dtype=dtype, lengths=lengths)
+                N=N, B=B, T=T, H=H, d_k=d_k, d_v=d_v, dtype=dtype, lengths=lengths,
+                decay=decay)
 
 
-def make_prefill_workload(w: PrefillWorkload, device="cpu"):
-    """Draw the named workload (varlen lengths first, from the same seed)."""
+def make_prefill_workload(w: PrefillWorkload, device="cpu", decay="channel"):
+    """Draw the named workload (varlen lengths first, from the same seed); ``decay``
+    selects the gate's form (see the module docstring)."""
     lengths = None
     if w.n_seqs:
         lengths = varlen_lengths(w.n_seqs, w.len_lo, w.len_hi, w.seed)
     return make_prefill(B=w.B, T=w.T, H=w.H, d_k=w.d_k, d_v=w.d_v, dtype=w.dtype,
                         gate=w.gate, init_state_std=w.init_state_std, lengths=lengths,
-                        seed=w.seed, device=device)
+                        seed=w.seed, device=device, decay=decay)
 
 
 def make_decode(N=4, H=2, d_k=64, d_v=64, steps=1, dtype="bf16", gate="uniform",
-                state_std=0.02, seed=0, device="cpu"):
+                state_std=0.02, seed=0, device="cpu", decay="channel"):
     """Draw a decode run: initial state plus ``steps`` one-token inputs per
     (sequence, head).
 
     Returns a dict with state ([N, H, d_v, d_k] fp32), q, k, v
-    ([steps, N, H, d], dtype), g ([steps, N, H, d_k] fp32), beta ([steps, N, H]).
+    ([steps, N, H, d], dtype), g ([steps, N, H, d_k] fp32; [steps, N, H] for decay
+    "head"; None for "none"), beta ([steps, N, H]).
     """
     gen = _gen(seed, device)
     tdt = _DTYPES[dtype]
@@ -166,16 +183,17 @@ def make_decode(N=4, H=2, d_k=64, d_v=64, steps=1, dtype="bf16", gate="uniform",
     q = _randn(gen, (steps, N, H, d_k), device).to(tdt)
     k = _unit_keys(gen, (steps, N, H, d_k), device).to(tdt)
     v = _randn(gen, (steps, N, H, d_v), device).to(tdt)
-    g = _gate(gen, (steps, N, H, d_k), gate, device)
+    g = _gate_for(gen, (steps, N, H), d_k, gate, decay, device)
     beta = torch.sigmoid(_randn(gen, (steps, N, H), device))
     return dict(state=state, q=q, k=k, v=v, g=g, beta=beta, N=N, H=H, d_k=d_k, d_v=d_v,
-                steps=steps, dtype=dtype)
+                steps=steps, dtype=dtype, decay=decay)
 
 
-def make_decode_workload(w: DecodeWorkload, device="cpu", steps=None):
+def make_decode_workload(w: DecodeWorkload, device="cpu", steps=None, decay="channel"):
     return make_decode(N=w.N, H=w.H, d_k=w.d_k, d_v=w.d_v,
                        steps=w.steps if steps is None else steps, dtype=w.dtype,
-                       gate=w.gate, state_std=w.state_std, seed=w.seed, device=device)
+                       gate=w.gate, state_std=w.state_std, seed=w.seed, device=device,
+                       decay=decay)
 
 
 def to_f64(t):

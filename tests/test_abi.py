@@ -25,7 +25,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"kda_prefill", "kda_decode_step", "kda_abi_version", "kda_status_string",
-            "kda_prefill_workspace_bytes", "kda_prefill_plan"} <= set(names)
+            "kda_prefill_workspace_bytes", "kda_prefill_plan", "kda_prefill_coop_plan",
+            "kda_prefill_ex", "kda_decode_step_ex"} <= set(names)
     L = kda.lib()
     for name in names:
         assert hasattr(L, name), f"{name} declared in kda.h but not exported"
@@ -33,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = kda.lib()
-    assert L.kda_abi_version() == 1
+    assert L.kda_abi_version() == 2
     for code in range(6):
         s = L.kda_status_string(code).decode()
         assert s.startswith("KDA")
@@ -81,6 +82,37 @@ def test_decode_validation_codes():
     assert st(H=0) == 2
     assert st(state=None) == 1
     assert st(N=0) == 0
+
+
+def test_decay_kind_validation_codes():
+    L = kda.lib()
+
+    def pf(decay, g=FAKE):
+        return L.kda_prefill_ex(1, decay, FAKE, FAKE, FAKE, g, FAKE, None, 1, 1, 64, 2, 64, 64,
+                                0.125, None, None, FAKE, None, 0, None)
+
+    def dc(decay, g=FAKE):
+        return L.kda_decode_step_ex(1, decay, FAKE, FAKE, FAKE, g, FAKE, FAKE, FAKE, 4, 2, 64,
+                                    64, 0.1, None)
+
+    for f in (pf, dc):
+        assert f(3) == 3 and f(-1) == 3          # unknown decay kind: unsupported
+        assert f(0, g=None) == 1                 # per-channel decay needs g
+        assert f(1, g=None) == 1                 # per-head decay needs g
+    # no decay with g NULL passes validation; with T = 0 and no final state nothing launches
+    assert L.kda_prefill_ex(1, 2, FAKE, FAKE, FAKE, None, FAKE, None, 1, 1, 0, 2, 64, 64, 0.125,
+                            None, None, FAKE, None, 0, None) == 0
+    assert L.kda_decode_step_ex(1, 2, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, 2, 64, 64,
+                                0.1, None) == 0
+
+
+def test_binding_decay_kind_from_g_shape():
+    assert kda._decay_kind(None, (1, 4, 2, 8)) == kda.KDA_DECAY_NONE
+    import torch
+    assert kda._decay_kind(torch.zeros(1, 4, 2, 8), (1, 4, 2, 8)) == kda.KDA_DECAY_CHANNEL
+    assert kda._decay_kind(torch.zeros(1, 4, 2), (1, 4, 2, 8)) == kda.KDA_DECAY_HEAD
+    with pytest.raises(ValueError, match="g must have shape"):
+        kda._decay_kind(torch.zeros(1, 4, 8), (1, 4, 2, 8))
 
 
 def test_python_binding_rejects_host_tensors():

@@ -38,8 +38,9 @@ def run_gpu(x, path="fused", **kw):
 def run_oracle(x, units=None, scale=None):
     cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu().numpy()
     s0 = None if x["initial_state"] is None else ki.to_f64(x["initial_state"])
+    g = None if x["g"] is None else ki.to_f64(x["g"])
     return oracle_forward(ki.to_f64(x["q"]), ki.to_f64(x["k"]), ki.to_f64(x["v"]),
-                          ki.to_f64(x["g"]), ki.to_f64(x["beta"]), cu_seqlens=cu, scale=scale,
+                          g, ki.to_f64(x["beta"]), cu_seqlens=cu, scale=scale,
                           initial_state=s0, units=units)
 
 
@@ -119,9 +120,9 @@ def test_value_tile_heights_agree(bv, monkeypatch):
 
 
 # ------------------------------------------------------------------ full-size workloads
-def _sampled(w, units, label, path):
-    print(f"prefill full workload {w.name} {path}: units {units}", flush=True)
-    x = ki.make_prefill_workload(w, device=DEV)
+def _sampled(w, units, label, path, decay="channel"):
+    print(f"prefill full workload {w.name} {path} decay={decay}: units {units}", flush=True)
+    x = ki.make_prefill_workload(w, device=DEV, decay=decay)
     o, fs = run_gpu(x, path)
     o_ref, s_ref = run_oracle(x, units=units)
     H, d_v = x["H"], x["d_v"]

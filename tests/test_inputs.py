@@ -33,3 +33,12 @@ def test_decode_shapes():
     d = ki.make_decode(N=3, H=2, d_k=8, d_v=4, steps=5, seed=1)
     assert d["state"].shape == (3, 2, 4, 8) and d["q"].shape == (5, 3, 2, 8)
     assert d["v"].shape == (5, 3, 2, 4) and d["beta"].shape == (5, 3, 2)
+
+
+def test_decay_kinds():
+    h = ki.make_prefill(B=1, T=9, H=3, d_k=8, d_v=4, decay="head", seed=2)
+    assert h["g"].shape == (1, 9, 3) and (h["g"] < 0).all()
+    n = ki.make_prefill(B=1, T=9, H=3, d_k=8, d_v=4, decay="none", seed=2)
+    assert n["g"] is None and n["decay"] == "none"
+    d = ki.make_decode(N=2, H=3, d_k=8, d_v=4, steps=2, decay="head", seed=1)
+    assert d["g"].shape == (2, 2, 3)
