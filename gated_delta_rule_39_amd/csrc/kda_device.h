@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace kda {
 
 typedef __bf16 bf16;
@@ -44,6 +46,16 @@ __device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
   for (int m = width / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, width);
   return x;
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace kda

@@ -42,19 +42,8 @@
 #include "kda_launch.h"
 #include "kda_wy.h"
 
-#include <utility>
 
 namespace kda {
-
-// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 
 __device__ __forceinline__ void unit_bounds(const PrefillArgs& a, int unit, int& n_seq, int& h,
@@ -471,10 +460,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       if (has_next) pr.template load_slice<DECAY, RPG / 2, RPG>(c1, n1);          // g, second half
       lds_barrier();
       if (has_next) pr.template load_slice<DECAY, RPG, 2 * RPG>(c1, n1);          // k
-      if (wave == 0)
-        pr.inverse_diag();
+      pr.inverse_blocks();
+      lds_barrier();
+      if (wave < 2)
+        pr.inverse_pairs();
       else
-        pr.publish_qk(rr, slot);
+        pr.template publish_qk<2, 2>(rr, slot);
       if (has_next) pr.template load_slice<DECAY, 2 * RPG, 3 * RPG>(c1, n1);      // q
       lds_barrier();
       pr.inverse_rest();

@@ -436,62 +436,68 @@ struct WyProducer {
     }
   }
 
-  // Wave 0: the four 16x16 diagonal blocks of X = (I + A)^{-1} (left-looking
-  // substitution, lane = (block, column), the block's rows preloaded from LDS), then
-  // X_10 = -X_11 A_10 X_00 and X_32 = -X_33 A_32 X_22.  X goes to LDS in fp32 and,
-  // times diag(beta), as the bf16 operand Tm.  No closing barrier.
-  __device__ __forceinline__ void inverse_diag() {
-    const int lr = lane & 15, lq = lane >> 4;
-    float* sY = sScr;
-    {
-      const int b = lane >> 4, c = lane & 15;
-      const float* Ab = sA + (16 * b) * LDF + 16 * b;
-      f32x4 ar[16][4];
+  // All waves: wave b inverts diagonal block b of I + A (unit lower triangular) by
+  // right-looking substitution.  Lane 4c + q owns column c and rows q, q + 4, q + 8,
+  // q + 12 of the block; at step j the finished entry x_j of column c is broadcast
+  // within the lane's quad (DPP) and every row below subtracts A[r][j] x_j (A holds
+  // zeros on and above its diagonal, so rows above j are left as they are).  The
+  // dependent chain is 16 steps of one broadcast and one FMA.  X_bb goes to sX (fp32)
+  // and, times diag(beta), to sTm (bf16).  No closing barrier.
+  __device__ __forceinline__ void inverse_blocks() {
+    const int b = wave, c = lane >> 2, q = lane & 3;
+    const float* Ab = sA + (16 * b + q) * LDF + 16 * b;
+    // a[m][j4] = A[4 m + q][4 j4 .. 4 j4 + 3]: columns past 4 m + 3 are zero for every q
+    f32x4 a[4][4];
 #pragma unroll
-      for (int r = 1; r < 16; ++r)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int j4 = 0; j4 < r; j4 += 4) ar[r][j4 / 4] = *reinterpret_cast<const f32x4*>(Ab + r * LDF + j4);
-      // x[r] = delta(r, c) - sum_{j < r} A[r][j] x[j], the sum in four independent
-      // partial sums (j mod 4) to shorten the dependent chain
-      float x[16];
+      for (int j4 = 0; j4 <= m; ++j4)
+        a[m][j4] = *reinterpret_cast<const f32x4*>(Ab + 4 * m * LDF + 4 * j4);
+    float x[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 4; ++m) x[m] = 4 * m + q == c ? 1.f : 0.f;
+    static_for<15>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const float xj = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[j >> 2]), (j & 3) * 0x55,
+                                          0xf, 0xf, false));
 #pragma unroll
-        for (int j = 0; j < r; ++j) p[j % 4] += ar[r][j / 4][j % 4] * x[j];
-        x[r] = ((r == c) ? 1.f : 0.f) - ((p[0] + p[1]) + (p[2] + p[3]));
-      }
-      const float bc = sBeta[16 * b + c];
+      for (int m = 0; m < 4; ++m)
+        if (4 * m + 3 > j) x[m] = __builtin_fmaf(-a[m][j >> 2][j & 3], xj, x[m]);
+    });
+    const float bc = sBeta[16 * b + c];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sX[(16 * b + r) * LDF + 16 * b + c] = x[r];
-        sTm[(16 * b + r) * LDC + 16 * b + c] = static_cast<bf16>(x[r] * bc);
-      }
-    }
-    wave_lds_sync();
-    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4 y0 = mm16(z, sA + 16 * LDF, LDF, sX, LDF, lane);
-    const f32x4 y1 = mm16(z, sA + 48 * LDF + 32, LDF, sX + 32 * LDF + 32, LDF, lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sY[(4 * lq + i) * 17 + lr] = y0[i];
-      sY[16 * 17 + (4 * lq + i) * 17 + lr] = y1[i];
-    }
-    wave_lds_sync();
-    const f32x4 x10 = mm16(z, sX + 16 * LDF + 16, LDF, sY, 17, lane);
-    const f32x4 x32 = mm16(z, sX + 48 * LDF + 48, LDF, sY + 16 * 17, 17, lane);
-    const float b0 = sBeta[lr], b2 = sBeta[32 + lr];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * lq + i;
-      sX[(16 + r) * LDF + lr] = -x10[i];
-      sX[(48 + r) * LDF + 32 + lr] = -x32[i];
-      sTm[(16 + r) * LDC + lr] = static_cast<bf16>(-x10[i] * b0);
-      sTm[(48 + r) * LDC + 32 + lr] = static_cast<bf16>(-x32[i] * b2);
+    for (int m = 0; m < 4; ++m) {
+      const int r = 16 * b + 4 * m + q;
+      sX[r * LDF + 16 * b + c] = x[m];
+      sTm[r * LDC + 16 * b + c] = static_cast<bf16>(x[m] * bc);
     }
   }
 
-  // All waves, after a barrier that follows inverse_diag: the 32x32 block below the
+  // Waves 0, 1, after a barrier that follows inverse_blocks: X_10 = -X_11 A_10 X_00
+  // (wave 0) or X_32 = -X_33 A_32 X_22 (wave 1), to sX and, times diag(beta), sTm.
+  // No closing barrier.
+  __device__ __forceinline__ void inverse_pairs() {
+    const int lr = lane & 15, lq = lane >> 4;
+    const int rb = 2 * wave + 1, cb = 2 * wave;
+    float* sY = sScr + wave * 16 * 17;
+    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 y = mm16(z, sA + 16 * rb * LDF + 16 * cb, LDF, sX + 16 * cb * LDF + 16 * cb, LDF,
+                         lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sY[(4 * lq + i) * 17 + lr] = y[i];
+    wave_lds_sync();
+    const f32x4 x = mm16(z, sX + 16 * rb * LDF + 16 * rb, LDF, sY, 17, lane);
+    const float bc = sBeta[16 * cb + lr];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + 4 * lq + i;
+      sX[r * LDF + 16 * cb + lr] = -x[i];
+      sTm[r * LDC + 16 * cb + lr] = static_cast<bf16>(-x[i] * bc);
+    }
+  }
+
+  // All waves, after a barrier that follows inverse_pairs: the 32x32 block below the
   // diagonal, X_lo = -X_B11 (A_lo X_B00); wave w forms block (w/2, w%2).  Ends with
   // a barrier (Tm complete).
   __device__ __forceinline__ void inverse_rest() {
@@ -524,31 +530,34 @@ struct WyProducer {
     lds_barrier();
   }
 
-  // Waves 1..3 (while wave 0 inverts): Qg and KD^T fragments and e^{G_n} to the slot.
-  // Wave w' = wave - 1 takes Qg fragments w', w' + 3, ... and then KD^T fragments
-  // w', w' + 3, ...; the trip counts are compile-time (indices past the end repeat the
+  // Waves W0 .. W0 + NW - 1: Qg and KD^T fragments and e^{G_n} to the slot.  Wave
+  // w' = wave - W0 takes Qg fragments w', w' + NW, ... and then KD^T fragments w',
+  // w' + NW, ...; the trip counts are compile-time (indices past the end repeat the
   // last fragment, an identical store), so each wave's reads and stores overlap.
+  template <int W0, int NW>
   __device__ __forceinline__ void publish_qk(__amdgpu_buffer_rsrc_t rr, uint32_t slot) {
     constexpr int nQ = 4 * KS, nKD = 2 * (DK / 16);
-    const int w1 = wave - 1;
-    bf16x8 fq[(nQ + 2) / 3], fk[(nKD + 2) / 3];
+    constexpr int TQ = (nQ + NW - 1) / NW, TK = (nKD + NW - 1) / NW;
+    const int w1 = wave - W0;
+    bf16x8 fq[TQ], fk[TK];
 #pragma unroll
-    for (int i = 0; i < (nQ + 2) / 3; ++i) {
-      const int f = min(w1 + 3 * i, nQ - 1), tb = f / KS, j = f % KS;
+    for (int i = 0; i < TQ; ++i) {
+      const int f = min(w1 + NW * i, nQ - 1), tb = f / KS, j = f % KS;
       fq[i] = frag_perm(sQg, LDK, 16 * tb, 32 * j, lane);
     }
 #pragma unroll
-    for (int i = 0; i < (nKD + 2) / 3; ++i) {
-      const int f = min(w1 + 3 * i, nKD - 1), kb = f >> 1, t = f & 1;
+    for (int i = 0; i < TK; ++i) {
+      const int f = min(w1 + NW * i, nKD - 1), kb = f >> 1, t = f & 1;
       fk[i] = frag_tr_perm(sKD, LDK, 32 * t, 16 * kb, lane);
     }
 #pragma unroll
-    for (int i = 0; i < (nQ + 2) / 3; ++i)
-      st16(rr, slot + SL::oQ + min(w1 + 3 * i, nQ - 1) * SL::kFrag + 16 * lane, fq[i]);
+    for (int i = 0; i < TQ; ++i)
+      st16(rr, slot + SL::oQ + min(w1 + NW * i, nQ - 1) * SL::kFrag + 16 * lane, fq[i]);
 #pragma unroll
-    for (int i = 0; i < (nKD + 2) / 3; ++i)
-      st16(rr, slot + SL::oKD + min(w1 + 3 * i, nKD - 1) * SL::kFrag + 16 * lane, fk[i]);
-    if (tid - 64 < DK && tid >= 64) st4(rr, slot + SL::oEgn + 4 * (tid - 64), sEgn[tid - 64]);
+    for (int i = 0; i < TK; ++i)
+      st16(rr, slot + SL::oKD + min(w1 + NW * i, nKD - 1) * SL::kFrag + 16 * lane, fk[i]);
+    const int e = tid - 64 * W0;
+    if (e >= 0 && e < DK) st4(rr, slot + SL::oEgn + 4 * e, sEgn[e]);
   }
 
   // All waves: W^T = -(Kg^T (X diag(beta))^T) as W fragments and U = X diag(beta) V as
