@@ -358,9 +358,259 @@ struct WyConsumerLayout {
   static constexpr size_t kBytes = oFlag + 16;
 };
 
+// Split consumer LDS: the bf16 S^T operand fragments [KS][4] (1 KiB each), the bf16 E
+// operand fragments [2][4], one output tile [64][64 + 8] bf16, flags.
+struct WySplitLayout {
+  static constexpr int NVT = 4;                 // 64 value columns per consumer
+  static constexpr int LDO = 16 * NVT + 8;
+  static constexpr size_t oSb = 0;
+  static constexpr size_t oEb = oSb + size_t(4) * NVT * 1024;
+  static constexpr size_t oO = oEb + size_t(2) * NVT * 1024;
+  static constexpr size_t oFlag = oO + size_t(kChunk) * LDO * 2;
+  static constexpr size_t kBytes = oFlag + 16;
+};
+
+// Consumer with the work split by token and key blocks (d_k = 128, 64 value columns):
+// wave w forms the rows of token block w of E = U - W S^T and O = Qg S^T + M E, and
+// owns key blocks 2w, 2w+1 of S^T (keys 32w .. 32w + 31) in fp32 accumulators.  Per
+// chunk the waves exchange only the bf16 operands of the chain through LDS: wave w
+// packs its keys into the S^T fragments of K step w, and its E rows into half w % 2 of
+// the E fragments of K step w / 2 (permuted-K order).  Each wave loads just the
+// published operands it uses (its token block of W, Qg, M, U; its key blocks of KD^T,
+// e^{G_n}) straight from the ring slot into registers, one chunk ahead.  The slot of
+// chunk c is released after chunk c's end-of-chunk barrier, when every wave has used
+// those registers.
+template <int DK, int DV>
+__device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned char* smem,
+                                                 __amdgpu_buffer_rsrc_t rr, int* ready,
+                                                 int* done, int* abort_word, int role,
+                                                 int n_seq, int h, int64_t bos, int64_t eos,
+                                                 int nch, int tid, int wave, int lane) {
+  using SL = WySlot<DK, DV>;
+  using CL = WySplitLayout;
+  constexpr int KS = DK / 32, NVT = CL::NVT;
+  static_assert(KS == 4, "one K step of keys per wave");
+  const int lr = lane & 15, lq = lane >> 4;
+  const int v0 = role * 16 * NVT;
+  int* cFlag = reinterpret_cast<int*>(smem + CL::oFlag);
+  const uint32_t rowO = static_cast<uint32_t>(a.H) * DV;
+  auto ld16 = [&](uint32_t off) -> u32x4 {
+    return __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, kDeviceScope);
+  };
+  auto ldf = [&](uint32_t off) -> bf16x8 { return __builtin_bit_cast(bf16x8, ld16(off)); };
+  auto ldv = [&](uint32_t off) -> f32x4 { return __builtin_bit_cast(f32x4, ld16(off)); };
+  const uint32_t fl = 16 * lane;
+  // slot offsets of this wave's operands
+  auto offU = [&](int vt) { return uint32_t(SL::oU + (wave * SL::NVB + v0 / 16 + vt) * SL::kFrag) + fl; };
+  auto offW = [&](int j) { return uint32_t(SL::oW + (wave * KS + j) * SL::kFrag) + fl; };
+  auto offQ = [&](int j) { return uint32_t(SL::oQ + (wave * KS + j) * SL::kFrag) + fl; };
+  // M (w, 0) is block w; (w, 1) is block 2 + w and exists for w >= 2 (else re-read (w, 0))
+  auto offM = [&](int t) {
+    return uint32_t(SL::oM + (t == 0 || wave < 2 ? wave : 2 + wave) * SL::kFrag) + fl;
+  };
+  auto offKD = [&](int b, int t) {
+    return uint32_t(SL::oKD + ((2 * wave + b) * 2 + t) * SL::kFrag) + fl;
+  };
+  auto offEg = [&](int b) { return uint32_t(SL::oEgn + (16 * (2 * wave + b) + 4 * lq) * 4); };
+  unsigned char* sSb = smem + CL::oSb + fl;
+  unsigned char* sEb = smem + CL::oEb + fl;
+  unsigned char* sO = smem + CL::oO;
+  auto sb_at = [&](int j, int vt) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(sSb + (j * NVT + vt) * 1024);
+  };
+  auto eb_at = [&](int t, int vt) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(sEb + (t * NVT + vt) * 1024);
+  };
+  // output rows of this wave (token block w) from the LDS tile to o; rows >= `rows` of
+  // the window starting at token row cs are dropped
+  auto store_rows = [&](int64_t cs, int rows) {
+    const __amdgpu_buffer_rsrc_t win = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<bf16*>(a.o) + (cs * a.H + h) * DV + v0, 0,
+        static_cast<int>(uint32_t(rows) * rowO * 2), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * wave + 8 * i + lane / 8, col = 8 * (lane % 8);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(sO + (r * CL::LDO + col) * 2);
+      __builtin_amdgcn_raw_buffer_store_b128(x, win, (r * rowO + col) * 2, 0, 0);
+    }
+  };
+
+  // S^T rows of this wave: S[b][vt] holds S^T[32 w + 16 b + 4 lq + i][v0 + 16 vt + lr]
+  f32x4 S[2][NVT];
+  const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * DV * DK;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt)
+      S[b][vt] = a.initial_state
+                     ? *reinterpret_cast<const f32x4*>(a.initial_state + st_base +
+                                                       int64_t(v0 + 16 * vt + lr) * DK +
+                                                       32 * wave + 16 * b + 4 * lq)
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt)
+    *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = pack_frag(S[0][vt], S[1][vt]);
+
+  // this chunk's operands; each is reloaded from the next chunk's slot right after its
+  // last use here, so a request has about one chunk of time to arrive
+  f32x4 U[NVT], eg[2];
+  bf16x8 Wf[KS], Qf[KS], Mf[2], KDf[2][2];
+  auto load_w = [&](uint32_t slot) {
+#pragma unroll
+    for (int j = 0; j < KS; ++j) Wf[j] = ldf(slot + offW(j));
+  };
+  auto load_q = [&](uint32_t slot) {
+#pragma unroll
+    for (int j = 0; j < KS; ++j) Qf[j] = ldf(slot + offQ(j));
+  };
+  auto load_m = [&](uint32_t slot) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) Mf[t] = ldf(slot + offM(t));
+  };
+  auto load_kd = [&](uint32_t slot) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) KDf[b][t] = ldf(slot + offKD(b, t));
+      eg[b] = ldv(slot + offEg(b));
+    }
+  };
+
+  bool ok = true, nok = true;
+  if (nch > 0) {
+    if (tid == 0) cFlag[0] = wait_at_least(ready, 1, abort_word) ? 1 : 0;
+    lds_barrier();
+    ok = cFlag[0] != 0;
+    if (ok) {
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) U[vt] = ldv(offU(vt));
+      load_w(0);
+      load_q(0);
+      load_m(0);
+      load_kd(0);
+    }
+    if (tid == 0) cFlag[1] = nch > 1 ? (wait_at_least(ready + 1 % a.R, 2, abort_word) ? 1 : 0) : 1;
+    lds_barrier();
+    nok = cFlag[1] != 0;
+  }
+
+  // ring slot indices of chunks c - 1, c, c + 1, c + 2
+  int sp = 0, s0 = 0, s1 = 1 % a.R, s2 = 2 % a.R;
+  const int t_own = wave >> 1, h_own = wave & 1;
+  for (int c = 0; ok && c < nch; ++c) {
+    const int64_t c0 = bos + int64_t(c) * kChunk;
+    const bool has_next = c + 1 < nch, has2 = c + 2 < nch;
+    // every wave has used chunk c - 1's operands: its slot is free
+    if (tid == 0 && c > 0) __hip_atomic_fetch_add(done + sp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int fv = 0;
+    if (tid == 0 && has2)
+      fv = __hip_atomic_load(ready + s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The next chunk's operands are requested unconditionally (past the last chunk
+    // they are unused bytes of an idle slot).
+    const uint32_t nslot = static_cast<uint32_t>(s1) * SL::kBytes;
+
+    f32x4 E[NVT], Ot[NVT];
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt) {
+      E[vt] = U[vt];
+      Ot[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      U[vt] = ldv(nslot + offU(vt));
+    }
+    // E = U - W S^T for token block w; the S^T fragments stay for O
+    bf16x8 sb[KS][NVT];
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) sb[j][vt] = sb_at(j, vt);
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) E[vt] = mma_bf16(Wf[j], sb[j][vt], E[vt]);
+    load_w(nslot);
+    // this wave's E rows into its half of the E operand fragments
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt) {
+      const f32x4 e = E[vt];
+      *reinterpret_cast<bf16x4*>(sEb + (t_own * NVT + vt) * 1024 + 8 * h_own) =
+          bf16x4{static_cast<bf16>(e[0]), static_cast<bf16>(e[1]), static_cast<bf16>(e[2]),
+                 static_cast<bf16>(e[3])};
+    }
+    // D S^T for this wave's keys, while the other waves finish E
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) S[b][vt] *= eg[b];
+    lds_barrier();
+    bf16x8 eb[2][NVT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) eb[t][vt] = eb_at(t, vt);
+    // the previous chunk's output rows (a full chunk), from this wave's LDS rows
+    if (c > 0) store_rows(c0 - kChunk, kChunk);
+    // O = Qg S^T + M E (token block w reads E blocks <= w: K step 1 only for w >= 2)
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) Ot[vt] = mma_bf16(sb[j][vt], Qf[j], Ot[vt]);
+    load_q(nslot);
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt) Ot[vt] = mma_bf16(eb[0][vt], Mf[0], Ot[vt]);
+    if (wave >= 2) {
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) Ot[vt] = mma_bf16(eb[1][vt], Mf[1], Ot[vt]);
+    }
+    load_m(nslot);
+    // S^T += KD^T E for this wave's keys
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) S[b][vt] = mma_bf16(KDf[b][t], eb[t][vt], S[b][vt]);
+    load_kd(nslot);
+    // the next chunk's S^T operand (K step w) and this chunk's output rows
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt) {
+      *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = pack_frag(S[0][vt], S[1][vt]);
+      const f32x4 x = Ot[vt];
+      *reinterpret_cast<bf16x4*>(sO + ((16 * wave + lr) * CL::LDO + 16 * vt + 4 * lq) * 2) =
+          bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                 static_cast<bf16>(x[3])};
+    }
+
+    if (tid == 0)
+      cFlag[c & 1] = !has2 ? 1
+                           : ((fv >= c + 3 || wait_at_least(ready + s2, c + 3, abort_word)) ? 1 : 0);
+    lds_barrier();
+    ok = has_next ? nok : true;
+    nok = cFlag[c & 1] != 0;
+    sp = s0;
+    s0 = s1;
+    s1 = s2;
+    s2 = s2 + 1 == a.R ? 0 : s2 + 1;
+  }
+
+  // the last chunk's output rows (written before the loop's last barrier)
+  if (ok && nch > 0) {
+    const int64_t cl = bos + int64_t(nch - 1) * kChunk;
+    store_rows(cl, static_cast<int>(eos - cl));
+  }
+  if (ok && a.final_state) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt)
+        *reinterpret_cast<f32x4*>(a.final_state + st_base + int64_t(v0 + 16 * vt + lr) * DK +
+                                  32 * wave + 16 * b + 4 * lq) = S[b][vt];
+  }
+}
+
 template <int DK, int DV>
 struct WyLds {
-  static constexpr size_t kCons = WyConsumerLayout<DK, DV>::kBytes;
+  static constexpr size_t kCons = WyConsumerLayout<DK, DV>::kBytes > WySplitLayout::kBytes
+                                      ? WyConsumerLayout<DK, DV>::kBytes
+                                      : WySplitLayout::kBytes;
   static constexpr size_t kProd = WyProducerLayout<DK, DV>::kBytes;
   static constexpr size_t kBytes = kProd > kCons ? kProd : kCons;
   static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
@@ -479,6 +729,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
   }
 
   // ================================== consumer =====================================
+  if constexpr (DK == 128 && VBW == 16) {
+    wy_consume_split<DK, DV>(a, smem, rr, ready, done, abort_word, role, n_seq, h, bos, eos, nch,
+                             tid, wave, lane);
+    return;
+  }
   const int vw0 = role * 4 * VBW + VBW * wave;     // this wave's first value column
   using CL = WyConsumerLayout<DK, DV>;
   int* cFlag = reinterpret_cast<int*>(smem + CL::oFlag);
