@@ -21,10 +21,13 @@ Modules:
 * :mod:`oracle.kda_ref`        -- the token-by-token recurrence (the definition).
 * :mod:`oracle.kda_chunk_ref`  -- the chunkwise algebra in fp64 (what a chunked
   kernel computes), checked against the recurrence.
+* :mod:`oracle.kda_prologue`   -- raw projections to the recurrence's inputs (key
+  L2 normalisation, sigmoid write strength, sigmoid retention gate).
 * :mod:`oracle.pool`           -- fans independent (sequence, head) units out over
   host cores, for the CPU baseline.
 
-Parity pins (all in ``tests/test_oracle_pins.py``): every function here is pinned
+Parity pins (``tests/test_oracle_pins.py``, ``tests/test_oracle_decay_variants.py``,
+``tests/test_oracle_prologue.py``): every function here is pinned
 by closed forms, special cases that reduce to a library routine, exact rational
 brute force, a hand-derived worked example and invariants; none is "parity unpinned".
 """
@@ -36,3 +39,9 @@ from .kda_ref import (  # noqa: F401
     decode_step,
 )
 from .kda_chunk_ref import chunked  # noqa: F401
+from .kda_prologue import (  # noqa: F401
+    BETA_LOGIT,
+    GATE_LOGIT,
+    NORM_K,
+    prologue,
+)

@@ -44,6 +44,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .kda_prologue import prologue
+
 
 def default_scale(d_k: int) -> float:
     """Query scaling d_k^{-1/2} (step-by-step page, "read" step)."""
@@ -118,7 +120,7 @@ def _sequence_bounds(cu_seqlens, B, T):
 
 
 def forward(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
-            units=None):
+            units=None, flags=0):
     """Whole-batch prefill in the packed ``[B, T, H, d]`` layout.
 
     q, k: [B, T, H, d_k]; v: [B, T, H, d_v]; beta: [B, T, H]; g: [B, T, H, d_k]
@@ -131,12 +133,17 @@ def forward(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
     ``units`` optionally restricts the work to a list of (n, h) pairs; outputs of
     other units are left as NaN and their final states as NaN.
 
+    ``flags`` (``oracle.kda_prologue``) marks k, beta and g as raw projections that
+    the prologue turns into unit keys, sigmoid(beta) and log(sigmoid(g)) first.
+
     Returns (o [B, T, H, d_v] float64, final_state [N, H, d_v, d_k] float64).
     """
     q = np.asarray(q)
     B, T, H, d_k = q.shape
     d_v = np.asarray(v).shape[3]
     tok = B * T
+    if flags:
+        k, g, beta = prologue(k, g, beta, flags)
     qf = np.asarray(q, dtype=np.float64).reshape(tok, H, d_k)
     kf = np.asarray(k, dtype=np.float64).reshape(tok, H, d_k)
     vf = np.asarray(v, dtype=np.float64).reshape(tok, H, d_v)
@@ -171,20 +178,22 @@ def forward(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
     return o.reshape(B, T, H, d_v), final
 
 
-def decode_step(q, k, v, g, beta, state, scale=None):
+def decode_step(q, k, v, g, beta, state, scale=None, flags=0):
     """One decode step: one token per (sequence, head), state advanced by one.
 
     q, k: [N, H, d_k]; v: [N, H, d_v]; beta: [N, H]; state: [N, H, d_v, d_k];
     g: [N, H, d_k] (KDA), [N, H] (Gated DeltaNet) or None (DeltaNet).
     This is the recurrence with T = 1 (deep-dive page, "Decoding": one state
     update plus one query-state product per token).  The input ``state`` is not
-    modified; the new state is returned.
+    modified; the new state is returned.  ``flags`` as for ``forward``.
     Returns (o [N, H, d_v], new_state [N, H, d_v, d_k]) in float64.
     """
     q = np.asarray(q)
     N, H, d_k = q.shape
     d_v = np.asarray(v).shape[2]
     U = N * H
+    if flags:
+        k, g, beta = prologue(k, g, beta, flags)
     o, s = recurrence(
         np.asarray(q).reshape(U, 1, d_k), np.asarray(k).reshape(U, 1, d_k),
         np.asarray(v).reshape(U, 1, d_v),
