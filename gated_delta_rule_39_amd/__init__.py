@@ -23,6 +23,8 @@ _DTYPE_CODE = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 # decay kinds: per key channel (KDA), one scalar per token and head (Gated DeltaNet), none
 # (DeltaNet)
 KDA_DECAY_CHANNEL, KDA_DECAY_HEAD, KDA_DECAY_NONE = 0, 1, 2
+# prologue flags: k raw (L2-normalised in the kernel), beta and g given as logits
+KDA_PRO_NORM_K, KDA_PRO_BETA_LOGIT, KDA_PRO_GATE_LOGIT = 1, 2, 4
 
 _lib = None
 
@@ -59,14 +61,14 @@ def lib() -> ctypes.CDLL:
     L.kda_prefill_coop_plan.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.POINTER(i32),
                                         ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.kda_prefill_ex.restype = ctypes.c_int
-    L.kda_prefill_ex.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32,
-                                 i64, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.kda_prefill_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp,
+                                 vp, i32, i32, i64, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                   f32, vp]
     L.kda_decode_step_ex.restype = ctypes.c_int
-    L.kda_decode_step_ex.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, i32,
-                                     i32, i32, i32, f32, vp]
+    L.kda_decode_step_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp,
+                                     vp, vp, i32, i32, i32, i32, f32, vp]
     _lib = L
     return L
 
@@ -145,13 +147,19 @@ def _decay_kind(g, qshape) -> int:
                      f"{tuple(qshape[:-1])} (per head) or be None, got {tuple(g.shape)}")
 
 
+def _flags(normalize_k: bool, beta_logit: bool, gate_logit: bool) -> int:
+    return ((KDA_PRO_NORM_K if normalize_k else 0) | (KDA_PRO_BETA_LOGIT if beta_logit else 0)
+            | (KDA_PRO_GATE_LOGIT if gate_logit else 0))
+
+
 def workspace_aborted(ws: torch.Tensor) -> bool:
     """True if the last producer/consumer call on ``ws`` stopped early (synchronises)."""
     return int(ws[:4].view(torch.int32).item()) != 0
 
 
 def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None,
-            output_final_state=True, out=None, final_state=None, workspace="auto"):
+            output_final_state=True, out=None, final_state=None, workspace="auto",
+            normalize_k=False, beta_logit=False, gate_logit=False):
     """Chunked KDA forward over packed sequences.
 
     q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (all fp32 or all bf16); g (log alpha) fp32:
@@ -161,6 +169,9 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None
     ``final_state`` may be passed (and may be ``initial_state`` itself) to write the
     state in place.  ``workspace``: "auto" (a cached device buffer when the
     producer/consumer kernel applies), None (fused kernel), or a uint8 device tensor.
+    Prologue (fused into the kernels): ``normalize_k`` L2-normalises each raw key row,
+    ``beta_logit`` takes beta = sigmoid(beta), ``gate_logit`` takes the retention
+    alpha = sigmoid(g) instead of exp(g).
     Returns (o [B, T, H, d_v], final_state or None).
     """
     dev = q.device
@@ -211,18 +222,20 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None
     elif workspace is not None:
         _need(workspace, "workspace", dtype=torch.uint8, device=dev)
         ws = workspace
-    _check(lib().kda_prefill_ex(_DTYPE_CODE[dt], decay, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+    _check(lib().kda_prefill_ex(_DTYPE_CODE[dt], decay,
+                                _flags(normalize_k, beta_logit, gate_logit), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                 _ptr(beta), _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
                                 float(scale), _ptr(initial_state), _ptr(fs), _ptr(o), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(dev)))
     return o, fs
 
 
-def decode_step(q, k, v, g, beta, state, *, scale=None, out=None):
+def decode_step(q, k, v, g, beta, state, *, scale=None, out=None, normalize_k=False,
+                beta_logit=False, gate_logit=False):
     """One decode token per (sequence, head); ``state`` [N, H, d_v, d_k] fp32 is
     updated in place.  q, k: [N, H, d_k]; v: [N, H, d_v]; g fp32: [N, H, d_k] (per key
-    channel), [N, H] (per head) or None (no decay); beta: [N, H] fp32.
-    Returns o [N, H, d_v]."""
+    channel), [N, H] (per head) or None (no decay); beta: [N, H] fp32.  The prologue
+    flags are as for ``prefill``.  Returns o [N, H, d_v]."""
     dev = q.device
     _need(q, "q", device=dev)
     dt = q.dtype
@@ -246,7 +259,8 @@ def decode_step(q, k, v, g, beta, state, *, scale=None, out=None):
         scale = d_k ** -0.5
     o = out if out is not None else torch.empty((N, H, d_v), dtype=dt, device=dev)
     _need(o, "out", dtype=dt, device=dev)
-    _check(lib().kda_decode_step_ex(_DTYPE_CODE[dt], decay, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+    _check(lib().kda_decode_step_ex(_DTYPE_CODE[dt], decay,
+                                    _flags(normalize_k, beta_logit, gate_logit), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                     _ptr(beta), _ptr(state), _ptr(o), N, H, d_k, d_v,
                                     float(scale), _stream(dev)))
     return o

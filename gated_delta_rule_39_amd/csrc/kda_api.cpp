@@ -12,6 +12,11 @@
 
 namespace {
 
+constexpr int kAllFlags = KDA_PRO_NORM_K | KDA_PRO_BETA_LOGIT | KDA_PRO_GATE_LOGIT;
+static_assert(KDA_PRO_NORM_K == kda::kNormK && KDA_PRO_BETA_LOGIT == kda::kBetaLogit &&
+                  KDA_PRO_GATE_LOGIT == kda::kGateLogit,
+              "prologue flags of the C ABI and the kernels agree");
+
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not yet queried
 
@@ -136,14 +141,15 @@ int kda_prefill_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
   return KDA_OK;
 }
 
-int kda_prefill_ex(int dtype, int decay, const void* q, const void* k, const void* v,
-                   const float* g, const float* beta, const int32_t* cu_seqlens, int32_t N,
-                   int32_t B, int64_t T, int32_t H, int32_t d_k, int32_t d_v, float scale,
-                   const float* initial_state, float* final_state, void* o, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+int kda_prefill_ex(int dtype, int decay, int flags, const void* q, const void* k,
+                   const void* v, const float* g, const float* beta, const int32_t* cu_seqlens,
+                   int32_t N, int32_t B, int64_t T, int32_t H, int32_t d_k, int32_t d_v,
+                   float scale, const float* initial_state, float* final_state, void* o,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
   if (decay != KDA_DECAY_CHANNEL && decay != KDA_DECAY_HEAD && decay != KDA_DECAY_NONE)
     return KDA_ERR_UNSUPPORTED;
+  if (flags & ~kAllFlags) return KDA_ERR_UNSUPPORTED;
   if (N < 0 || B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
   if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
   if (cu_seqlens == nullptr && N != B) return KDA_ERR_BAD_SHAPE;
@@ -173,6 +179,7 @@ int kda_prefill_ex(int dtype, int decay, const void* q, const void* k, const voi
   a.xcd_remap = (units % 8 == 0) ? 1 : 0;
   a.scale = scale;
   a.decay = decay;
+  a.flags = flags;
   const int cus = cu_count();
   const CoopPlan p = coop_plan(dtype, units, d_v, cus);
   if (p.ok() && workspace != nullptr &&
@@ -196,17 +203,19 @@ int kda_prefill(int dtype, const void* q, const void* k, const void* v, const fl
                 int32_t H, int32_t d_k, int32_t d_v, float scale, const float* initial_state,
                 float* final_state, void* o, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
-  return kda_prefill_ex(dtype, KDA_DECAY_CHANNEL, q, k, v, g, beta, cu_seqlens, N, B, T, H, d_k,
+  return kda_prefill_ex(dtype, KDA_DECAY_CHANNEL, 0, q, k, v, g, beta, cu_seqlens, N, B, T, H, d_k,
                         d_v, scale, initial_state, final_state, o, workspace, workspace_bytes,
                         stream);
 }
 
-int kda_decode_step_ex(int dtype, int decay, const void* q, const void* k, const void* v,
-                       const float* g, const float* beta, float* state, void* o, int32_t N,
-                       int32_t H, int32_t d_k, int32_t d_v, float scale, hipStream_t stream) {
+int kda_decode_step_ex(int dtype, int decay, int flags, const void* q, const void* k,
+                       const void* v, const float* g, const float* beta, float* state, void* o,
+                       int32_t N, int32_t H, int32_t d_k, int32_t d_v, float scale,
+                       hipStream_t stream) {
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
   if (decay != KDA_DECAY_CHANNEL && decay != KDA_DECAY_HEAD && decay != KDA_DECAY_NONE)
     return KDA_ERR_UNSUPPORTED;
+  if (flags & ~kAllFlags) return KDA_ERR_UNSUPPORTED;
   if (N < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
   if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
   const int64_t units = static_cast<int64_t>(N) * H;
@@ -214,7 +223,7 @@ int kda_decode_step_ex(int dtype, int decay, const void* q, const void* k, const
   if (N == 0) return KDA_OK;
   if (!q || !k || !v || (!g && decay != KDA_DECAY_NONE) || !beta || !state || !o)
     return KDA_ERR_NULL_ARG;
-  hipError_t err = kda::launch_decode(dtype, decay, d_k, d_v, q, k, v, g, beta, state, o,
+  hipError_t err = kda::launch_decode(dtype, decay, flags, d_k, d_v, q, k, v, g, beta, state, o,
                                       static_cast<int32_t>(units), scale, stream);
   return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -222,7 +231,7 @@ int kda_decode_step_ex(int dtype, int decay, const void* q, const void* k, const
 int kda_decode_step(int dtype, const void* q, const void* k, const void* v, const float* g,
                     const float* beta, float* state, void* o, int32_t N, int32_t H,
                     int32_t d_k, int32_t d_v, float scale, hipStream_t stream) {
-  return kda_decode_step_ex(dtype, KDA_DECAY_CHANNEL, q, k, v, g, beta, state, o, N, H, d_k,
+  return kda_decode_step_ex(dtype, KDA_DECAY_CHANNEL, 0, q, k, v, g, beta, state, o, N, H, d_k,
                             d_v, scale, stream);
 }
 

@@ -234,10 +234,12 @@ struct ChunkProducer {
   f32x4 gr[RPG];
   raw4 kr[RPG], qr[RPG];
   float br;
+  int32_t flags;   // prologue flags (kNormK, kBetaLogit, kGateLogit)
 
   __device__ __forceinline__ void init(unsigned char* smem, const Tin* q_, const Tin* k_,
                                        const float* g_, const float* beta_, int32_t H_, int32_t h_,
-                                       float scale_, int tid_, int wave_) {
+                                       float scale_, int tid_, int wave_, int32_t flags_) {
+    flags = flags_;
     sKg = reinterpret_cast<TC*>(smem + L::oKg);
     sQg = reinterpret_cast<TC*>(smem + L::oQg);
     sKi = reinterpret_cast<TC*>(smem + L::oKi);
@@ -296,8 +298,33 @@ struct ChunkProducer {
 
   // Kg, Qg, Ki, Ki^T, beta, e^{G_n} of the loaded chunk (n rows) into LDS; then, if
   // has_next, load rows c1 .. c1+n1-1.  Ends with a barrier.
+  // Raw keys to unit keys: row norms over the CG threads of a row group; bf16 keys are
+  // rounded to bf16 again (what a caller-side normalisation hands over).
+  __device__ __forceinline__ void normalise_keys() {
+    float ss[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const f32x4 k4 = widen(kr[i]);
+      ss[i] = dot4(k4, k4);
+    }
+#pragma unroll
+    for (int m = CG / 2; m >= 1; m >>= 1)
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) ss[i] += __shfl_xor(ss[i], m, CG);
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const f32x4 k4 = widen(kr[i]) * __builtin_amdgcn_rsqf(ss[i] + kNormEps);
+      if constexpr (sizeof(TC) == 4)
+        kr[i] = k4;
+      else
+        kr[i] = raw4{static_cast<bf16>(k4[0]), static_cast<bf16>(k4[1]),
+                     static_cast<bf16>(k4[2]), static_cast<bf16>(k4[3])};
+    }
+  }
+
   template <int DECAY>
   __device__ __forceinline__ void factors(int n, bool has_next, int64_t c1, int n1) {
+    if (flags & kNormK) normalise_keys();
     if constexpr (DECAY == 1) {
       const float x = gr[0][0];
 #pragma unroll
@@ -307,6 +334,11 @@ struct ChunkProducer {
       }
     }
     // alpha = e^g in place (1 for rows past the end); per-thread product of its rows
+    // retention logits to log-decays (no decay: alpha = 1 whatever the flag says)
+    if (DECAY != 2 && (flags & kGateLogit)) {
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) gr[i] = log_sigmoid4(gr[i]);
+    }
     f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
@@ -316,7 +348,8 @@ struct ChunkProducer {
       tot *= gr[i];
     }
     store4(sScr + rg * DK + j0, tot);
-    if (tid < kChunk) sBeta[tid] = tid < n ? br : 0.f;
+    if (tid < kChunk)
+      sBeta[tid] = tid < n ? ((flags & kBetaLogit) ? sigmoid_hw(br) : br) : 0.f;
     lds_barrier();
     // products of the other row groups' totals: before (cp) and after (cs) this one
     f32x4 tots[RG];

@@ -34,7 +34,7 @@ template <typename Tin, int DK, int DV, int DECAY>
 __global__ __launch_bounds__(256) void decode_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    Tin* __restrict__ o, float scale) {
+    Tin* __restrict__ o, float scale, int flags) {
   constexpr int LPR = DK / 4;      // lanes covering one state row
   constexpr int RPP = 256 / LPR;   // rows per pass of the workgroup
   constexpr int NP = DV / RPP;     // passes (rows per thread)
@@ -55,7 +55,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
   for (int i = 0; i < NP; ++i)
     s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (r0 + RPP * i) * DK));
 
-  const f32x4 kk = load4(k + kbase);
+  f32x4 kk = load4(k + kbase);
+  if (flags & kNormK) kk *= __builtin_amdgcn_rsqf(group_sum<LPR>(dot4(kk, kk)) + kNormEps);
   f32x4 qq = load4(q + kbase);
   qq *= scale;
   f32x4 gg = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -65,8 +66,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const float x = g[unit];
     gg = f32x4{x, x, x, x};
   }
+  // retention logits to log-decays (no decay: alpha = 1 whatever the flag says)
+  if (DECAY != 2 && (flags & kGateLogit)) gg = log_sigmoid4(gg);
   const f32x4 a = f32x4{exp_hw(gg[0]), exp_hw(gg[1]), exp_hw(gg[2]), exp_hw(gg[3])};
-  const float b = beta[unit];
+  const float b = (flags & kBetaLogit) ? sigmoid_hw(beta[unit]) : beta[unit];
   float vv[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) vv[i] = to_f32(v[vbase + r0 + RPP * i]);
@@ -88,44 +91,51 @@ __global__ __launch_bounds__(256) void decode_kernel(
 template <typename Tin, int DK, int DV>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
                                   const float* beta, float* state, void* o, int32_t units,
-                                  float scale, int decay, hipStream_t stream) {
+                                  float scale, int decay, int flags, hipStream_t stream) {
   const Tin* qt = static_cast<const Tin*>(q);
   const Tin* kt = static_cast<const Tin*>(k);
   const Tin* vt = static_cast<const Tin*>(v);
   Tin* ot = static_cast<Tin*>(o);
   if (decay == 1)
     hipLaunchKernelGGL((decode_kernel<Tin, DK, DV, 1>), dim3(units), dim3(256), 0, stream, qt, kt,
-                       vt, g, beta, state, ot, scale);
+                       vt, g, beta, state, ot, scale, flags);
   else if (decay == 2)
     hipLaunchKernelGGL((decode_kernel<Tin, DK, DV, 2>), dim3(units), dim3(256), 0, stream, qt, kt,
-                       vt, g, beta, state, ot, scale);
+                       vt, g, beta, state, ot, scale, flags);
   else
     hipLaunchKernelGGL((decode_kernel<Tin, DK, DV, 0>), dim3(units), dim3(256), 0, stream, qt, kt,
-                       vt, g, beta, state, ot, scale);
+                       vt, g, beta, state, ot, scale, flags);
   return hipGetLastError();
 }
 
 template <typename Tin>
 static hipError_t launch_decode_d(int dk, int dv, const void* q, const void* k, const void* v,
                                   const float* g, const float* beta, float* state, void* o,
-                                  int32_t units, float scale, int decay, hipStream_t stream) {
+                                  int32_t units, float scale, int decay, int flags,
+                                  hipStream_t stream) {
   if (dk == 64 && dv == 64)
-    return launch_decode_t<Tin, 64, 64>(q, k, v, g, beta, state, o, units, scale, decay, stream);
+    return launch_decode_t<Tin, 64, 64>(q, k, v, g, beta, state, o, units, scale, decay, flags,
+                                        stream);
   if (dk == 64 && dv == 128)
-    return launch_decode_t<Tin, 64, 128>(q, k, v, g, beta, state, o, units, scale, decay, stream);
+    return launch_decode_t<Tin, 64, 128>(q, k, v, g, beta, state, o, units, scale, decay, flags,
+                                         stream);
   if (dk == 128 && dv == 64)
-    return launch_decode_t<Tin, 128, 64>(q, k, v, g, beta, state, o, units, scale, decay, stream);
-  return launch_decode_t<Tin, 128, 128>(q, k, v, g, beta, state, o, units, scale, decay, stream);
+    return launch_decode_t<Tin, 128, 64>(q, k, v, g, beta, state, o, units, scale, decay, flags,
+                                         stream);
+  return launch_decode_t<Tin, 128, 128>(q, k, v, g, beta, state, o, units, scale, decay, flags,
+                                        stream);
 }
 
 // Called by the C ABI after validation: dtype 0 = fp32, 1 = bf16; dk, dv in {64, 128};
-// decay 0 = per key channel, 1 = one scalar per unit, 2 = none.
-hipError_t launch_decode(int dtype, int decay, int dk, int dv, const void* q, const void* k,
-                         const void* v, const float* g, const float* beta, float* state,
-                         void* o, int32_t units, float scale, hipStream_t stream) {
+// decay 0 = per key channel, 1 = one scalar per unit, 2 = none; flags: prologue flags.
+hipError_t launch_decode(int dtype, int decay, int flags, int dk, int dv, const void* q,
+                         const void* k, const void* v, const float* g, const float* beta,
+                         float* state, void* o, int32_t units, float scale, hipStream_t stream) {
   if (dtype == 1)
-    return launch_decode_d<bf16>(dk, dv, q, k, v, g, beta, state, o, units, scale, decay, stream);
-  return launch_decode_d<float>(dk, dv, q, k, v, g, beta, state, o, units, scale, decay, stream);
+    return launch_decode_d<bf16>(dk, dv, q, k, v, g, beta, state, o, units, scale, decay, flags,
+                                 stream);
+  return launch_decode_d<float>(dk, dv, q, k, v, g, beta, state, o, units, scale, decay, flags,
+                                stream);
 }
 
 }  // namespace kda

@@ -7,6 +7,8 @@
 
 #include <utility>
 
+#include "kda_launch.h"
+
 namespace kda {
 
 typedef __bf16 bf16;
@@ -26,6 +28,21 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 // round-to-nearest-even through the gfx950 conversion instruction
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// 1 / (1 + e^{-x}) through the hardware exponential and reciprocal (0 and 1 at the
+// extremes, no overflow trap).
+__device__ __forceinline__ float sigmoid_hw(float x) {
+  return __builtin_amdgcn_rcpf(1.f + exp_hw(-x));
+}
+// log(sigmoid(a)) = -log(1 + e^{-a}): a retention logit as a log-decay g (0 when
+// e^{-a} is below fp32 resolution, -inf for a below about -88, so e^g is 1 or 0).
+__device__ __forceinline__ float log_sigmoid_hw(float a) {
+  return -__builtin_amdgcn_logf(1.f + exp_hw(-a)) * 0.6931471805599453f;
+}
+__device__ __forceinline__ f32x4 log_sigmoid4(f32x4 a) {
+  return f32x4{log_sigmoid_hw(a[0]), log_sigmoid_hw(a[1]), log_sigmoid_hw(a[2]),
+               log_sigmoid_hw(a[3])};
+}
 
 // Four consecutive elements of an fp32 or bf16 array, widened to fp32.
 __device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }

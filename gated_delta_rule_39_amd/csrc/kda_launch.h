@@ -7,6 +7,12 @@
 
 namespace kda {
 
+// Prologue flags: inputs given as raw projections.  kNormK: k is L2-normalised per
+// (token, head) over d_k, k / sqrt(sum k^2 + kNormEps); kBetaLogit: beta = sigmoid(beta);
+// kGateLogit: the gate input a gives the retention alpha = sigmoid(a) (g = log alpha).
+constexpr int kNormK = 1, kBetaLogit = 2, kGateLogit = 4;
+constexpr float kNormEps = 1e-6f;
+
 // Arguments of both prefill kernels (validated by the C ABI).
 struct PrefillArgs {
   const void* q;
@@ -25,14 +31,15 @@ struct PrefillArgs {
   int32_t NC, NP, R;          // producer/consumer kernel: consumers, producers, ring slots
   int32_t xcd_remap;          // units % 8 == 0: keep a unit's workgroups on one XCD
   int32_t decay;              // 0: g per key channel, 1: one g per (token, head), 2: none
+  int32_t flags;              // prologue flags (kda_device.h: kNormK, kBetaLogit, kGateLogit)
   float scale;
 };
 
 // dtype: 0 = fp32, 1 = bf16; dk, dv in {64, 128}.
 // decay: 0 = g per key channel [units, dk], 1 = one g per unit [units], 2 = none.
-hipError_t launch_decode(int dtype, int decay, int dk, int dv, const void* q, const void* k,
-                         const void* v, const float* g, const float* beta, float* state,
-                         void* o, int32_t units, float scale, hipStream_t stream);
+hipError_t launch_decode(int dtype, int decay, int flags, int dk, int dv, const void* q,
+                         const void* k, const void* v, const float* g, const float* beta,
+                         float* state, void* o, int32_t units, float scale, hipStream_t stream);
 // Fused prefill: bv in {16, 32, 64}, bv <= prefill_max_bv(dtype, dk), a.NV = DV / bv.
 hipError_t launch_prefill(int dtype, int dk, int bv, const PrefillArgs& a, hipStream_t stream);
 int prefill_max_bv(int dtype, int dk);

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 
   CP cp;
   cp.init(smem, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, a.H, h,
-          a.scale, tid, wave);
+          a.scale, tid, wave, a.flags);
   f32x4 sacc[ST::NST];
   const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * a.DV * DK;
   load_state<DK, BV, LDK>(sacc, a.initial_state, st_base, v0, sS, wave, lane);
@@ -664,7 +664,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
     const int p = role - a.NC;
     PR pr;
     pr.init(smem, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-            static_cast<const bf16*>(a.v), a.g, a.beta, a.H, h, a.scale, tid, wave);
+            static_cast<const bf16*>(a.v), a.g, a.beta, a.H, h, a.scale, tid, wave, a.flags);
     int* pFlag = reinterpret_cast<int*>(smem + PL::oFlag);
     if (tid == 0) {
       int mode = -1;

@@ -198,6 +198,7 @@ struct WyProducer {
   f32x4 gr[RPG];
   bf16x4 kr[RPG], qr[RPG], vr[RPGV];
   float br;
+  int32_t flags;   // prologue flags (kNormK, kBetaLogit, kGateLogit)
   // slot stores: plain when the unit's workgroups share one L2, else device-scope
   bool local;
   __device__ __forceinline__ void st16(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16x8 v) const {
@@ -221,7 +222,9 @@ struct WyProducer {
 
   __device__ __forceinline__ void init(unsigned char* smem, const bf16* q_, const bf16* k_,
                                        const bf16* v_, const float* g_, const float* beta_,
-                                       int32_t H_, int32_t h_, float scale_, int tid_, int wave_) {
+                                       int32_t H_, int32_t h_, float scale_, int tid_, int wave_,
+                                       int32_t flags_) {
+    flags = flags_;
     sKg = reinterpret_cast<bf16*>(smem + L::oKg);
     sQg = reinterpret_cast<bf16*>(smem + L::oQg);
     sKi = reinterpret_cast<bf16*>(smem + L::oKi);
@@ -300,8 +303,30 @@ struct WyProducer {
 
   // Kg, Qg, Ki, KD, V (row-major), beta and e^{G_n} of the loaded chunk into LDS.  The
   // input registers are free afterwards.  No closing barrier.
+  // Raw keys to unit keys: row norms over the CG threads of a row group, then the
+  // normalised key rounded to bf16 again (what a caller-side normalisation hands over).
+  __device__ __forceinline__ void normalise_keys() {
+    float ss[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const f32x4 k4 = widen(kr[i]);
+      ss[i] = dot4(k4, k4);
+    }
+#pragma unroll
+    for (int m = CG / 2; m >= 1; m >>= 1)
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) ss[i] += __shfl_xor(ss[i], m, CG);
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const f32x4 k4 = widen(kr[i]) * __builtin_amdgcn_rsqf(ss[i] + kNormEps);
+      kr[i] = bf16x4{static_cast<bf16>(k4[0]), static_cast<bf16>(k4[1]),
+                     static_cast<bf16>(k4[2]), static_cast<bf16>(k4[3])};
+    }
+  }
+
   template <int DECAY>
   __device__ __forceinline__ void factors(int n) {
+    if (flags & kNormK) normalise_keys();
     if constexpr (DECAY == 1) {
       const float x = gr[0][0];
 #pragma unroll
@@ -309,6 +334,11 @@ struct WyProducer {
         const float y = __shfl(x, rg * RPG + i);
         gr[i] = f32x4{y, y, y, y};
       }
+    }
+    // retention logits to log-decays (no decay: alpha = 1 whatever the flag says)
+    if (DECAY != 2 && (flags & kGateLogit)) {
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) gr[i] = log_sigmoid4(gr[i]);
     }
     f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
@@ -319,7 +349,8 @@ struct WyProducer {
       tot *= gr[i];
     }
     store4(sScr + rg * DK + j0, tot);
-    if (tid < kChunk) sBeta[tid] = tid < n ? br : 0.f;
+    if (tid < kChunk)
+      sBeta[tid] = tid < n ? ((flags & kBetaLogit) ? sigmoid_hw(br) : br) : 0.f;
     // V rows meanwhile (rows past the end are zero)
 #pragma unroll
     for (int i = 0; i < RPGV; ++i) {

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 /* dtype of q, k, v and o.  g, beta and all states are always fp32. */
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
@@ -58,11 +58,29 @@ enum { KDA_F32 = 0, KDA_BF16 = 1 };
  */
 enum { KDA_DECAY_CHANNEL = 0, KDA_DECAY_HEAD = 1, KDA_DECAY_NONE = 2 };
 
+/*
+ * Prologue flags (the `_ex` entry points; 0 = inputs as the plain entry points take
+ * them).  They fuse the step just before the recurrence, which turns a layer's raw
+ * projections into its inputs: unit keys (the delta rule assumes them: "Kimi Delta
+ * Attention: The Linear Attention Behind Kimi K2 and Qwen3", warning in "How Kimi
+ * Delta Attention works step by step" and FAQ "Why does DeltaNet need keys to be
+ * normalized?"), a sigmoid-like retention and a positive write strength ("Kimi
+ * Delta Attention Technical Deep Dive", "From attention to recurrent state").
+ *   KDA_PRO_NORM_K      k is raw: each (token, head) row is replaced by
+ *                       k / sqrt(sum_j k_j^2 + 1e-6) before use (bf16 keys are
+ *                       rounded to bf16 again after the division)
+ *   KDA_PRO_BETA_LOGIT  beta holds logits: beta <- 1 / (1 + exp(-beta))
+ *   KDA_PRO_GATE_LOGIT  g holds retention logits a: alpha = 1 / (1 + exp(-a))
+ *                       (instead of alpha = exp(g)); ignored with KDA_DECAY_NONE
+ * q is never normalised (it is scaled by `scale`).
+ */
+enum { KDA_PRO_NORM_K = 1, KDA_PRO_BETA_LOGIT = 2, KDA_PRO_GATE_LOGIT = 4 };
 enum {
   KDA_OK = 0,
   KDA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                          */
   KDA_ERR_BAD_SHAPE = 2,    /* negative or inconsistent sizes                      */
-  KDA_ERR_UNSUPPORTED = 3,  /* d_k or d_v not in {64, 128}, or unknown decay kind   */
+  KDA_ERR_UNSUPPORTED = 3,  /* d_k or d_v not in {64, 128}, unknown decay kind or
+                               prologue flag                                        */
   KDA_ERR_BAD_DTYPE = 4,    /* dtype not KDA_F32 / KDA_BF16                         */
   KDA_ERR_HIP = 5           /* kernel launch failed (hipGetLastError)              */
 };
@@ -115,11 +133,12 @@ int kda_prefill(int dtype,
                 hipStream_t stream);
 
 /*
- * kda_prefill_ex -- kda_prefill with the decay kind as an argument.  With
- * KDA_DECAY_HEAD, g is [B, T, H] fp32 (one log-decay per token row and head); with
- * KDA_DECAY_NONE, g is not read and may be NULL.  Everything else is as kda_prefill.
+ * kda_prefill_ex -- kda_prefill with the decay kind and the prologue flags as
+ * arguments.  With KDA_DECAY_HEAD, g is [B, T, H] fp32 (one log-decay, or retention
+ * logit, per token row and head); with KDA_DECAY_NONE, g is not read and may be
+ * NULL.  Everything else is as kda_prefill.
  */
-int kda_prefill_ex(int dtype, int decay,
+int kda_prefill_ex(int dtype, int decay, int flags,
                    const void* q, const void* k, const void* v,
                    const float* g, const float* beta,
                    const int32_t* cu_seqlens,
@@ -168,11 +187,11 @@ int kda_decode_step(int dtype,
                     float scale, hipStream_t stream);
 
 /*
- * kda_decode_step_ex -- kda_decode_step with the decay kind as an argument.  With
- * KDA_DECAY_HEAD, g is [N, H] fp32; with KDA_DECAY_NONE, g is not read and may be
- * NULL.  Everything else is as kda_decode_step.
+ * kda_decode_step_ex -- kda_decode_step with the decay kind and the prologue flags
+ * as arguments.  With KDA_DECAY_HEAD, g is [N, H] fp32; with KDA_DECAY_NONE, g is
+ * not read and may be NULL.  Everything else is as kda_decode_step.
  */
-int kda_decode_step_ex(int dtype, int decay,
+int kda_decode_step_ex(int dtype, int decay, int flags,
                        const void* q, const void* k, const void* v,
                        const float* g, const float* beta,
                        float* state, void* o,

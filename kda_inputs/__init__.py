@@ -18,6 +18,11 @@ g, beta, initial state.
 Decay kinds: "channel" (KDA: g per key channel, [.., H, d_k]), "head" (Gated
 DeltaNet: one g per token and head, [.., H], same distribution) and "none"
 (DeltaNet: no g is drawn and g is None).
+
+Raw projections (``raw=True``, for the fused prologue): k ~ N(0, 1) is not
+normalised, beta holds logits ~ N(0, 1) (sigmoid gives the recipe's beta) and g
+holds retention logits a ~ U(2, 7), so that log(sigmoid(a)) spans about the same
+range as the uniform gate, -0.127 .. -0.0009.
 """
 
 from __future__ import annotations
@@ -109,7 +114,10 @@ def varlen_lengths(n_seqs: int, lo: int, hi: int, seed: int):
     return torch.randint(lo, hi + 1, (n_seqs,), generator=gen).tolist()
 
 
-def _gate_for(gen, lead, d_k, kind, decay, device):
+def _gate_for(gen, lead, d_k, kind, decay, device, raw=False):
+    if raw and decay in ("channel", "head"):
+        shape = (*lead, d_k) if decay == "channel" else lead
+        return 2.0 + 5.0 * torch.rand(*shape, generator=gen, device=device, dtype=torch.float32)
     if decay == "channel":
         return _gate(gen, (*lead, d_k), kind, device)
     if decay == "head":
@@ -120,7 +128,8 @@ def _gate_for(gen, lead, d_k, kind, decay, device):
 
 
 def make_prefill(B=1, T=64, H=1, d_k=64, d_v=64, dtype="fp32", gate="uniform",
-                 init_state_std=None, lengths=None, seed=0, device="cpu", decay="channel"):
+                 init_state_std=None, lengths=None, seed=0, device="cpu", decay="channel",
+                 raw=False):
     """Draw one prefill batch.
 
     With ``lengths`` (a list of sequence lengths, zeros allowed) the batch is
@@ -139,10 +148,13 @@ def make_prefill(B=1, T=64, H=1, d_k=64, d_v=64, dtype="fp32", gate="uniform",
     gen = _gen(seed, device)
     tdt = _DTYPES[dtype]
     q = _randn(gen, (B, T, H, d_k), device).to(tdt)
-    k = _unit_keys(gen, (B, T, H, d_k), device).to(tdt)
+    k = (_randn(gen, (B, T, H, d_k), device) if raw
+         else _unit_keys(gen, (B, T, H, d_k), device)).to(tdt)
     v = _randn(gen, (B, T, H, d_v), device).to(tdt)
-    g = _gate_for(gen, (B, T, H), d_k, gate, decay, device)
-    beta = torch.sigmoid(_randn(gen, (B, T, H), device))
+    g = _gate_for(gen, (B, T, H), d_k, gate, decay, device, raw)
+    beta = _randn(gen, (B, T, H), device)
+    if not raw:
+        beta = torch.sigmoid(beta)
     s0 = None
     if init_state_std is not None:
         s0 = _randn(gen, (N, H, d_v, d_k), device) * float(init_state_std)
@@ -154,10 +166,10 @@ def make_prefill(B=1, T=64, H=1, d_k=64, d_v=64, dtype="fp32", gate="uniform",
         cu = torch.tensor(offs, dtype=torch.int32, device=device)
     return dict(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu, initial_state=s0,
                 N=N, B=B, T=T, H=H, d_k=d_k, d_v=d_v, dtype=dtype, lengths=lengths,
-                decay=decay)
+                decay=decay, raw=raw)
 
 
-def make_prefill_workload(w: PrefillWorkload, device="cpu", decay="channel"):
+def make_prefill_workload(w: PrefillWorkload, device="cpu", decay="channel", raw=False):
     """Draw the named workload (varlen lengths first, from the same seed); ``decay``
     selects the gate's form (see the module docstring)."""
     lengths = None
@@ -165,11 +177,11 @@ def make_prefill_workload(w: PrefillWorkload, device="cpu", decay="channel"):
         lengths = varlen_lengths(w.n_seqs, w.len_lo, w.len_hi, w.seed)
     return make_prefill(B=w.B, T=w.T, H=w.H, d_k=w.d_k, d_v=w.d_v, dtype=w.dtype,
                         gate=w.gate, init_state_std=w.init_state_std, lengths=lengths,
-                        seed=w.seed, device=device, decay=decay)
+                        seed=w.seed, device=device, decay=decay, raw=raw)
 
 
 def make_decode(N=4, H=2, d_k=64, d_v=64, steps=1, dtype="bf16", gate="uniform",
-                state_std=0.02, seed=0, device="cpu", decay="channel"):
+                state_std=0.02, seed=0, device="cpu", decay="channel", raw=False):
     """Draw a decode run: initial state plus ``steps`` one-token inputs per
     (sequence, head).
 
@@ -181,12 +193,15 @@ def make_decode(N=4, H=2, d_k=64, d_v=64, steps=1, dtype="bf16", gate="uniform",
     tdt = _DTYPES[dtype]
     state = _randn(gen, (N, H, d_v, d_k), device) * float(state_std)
     q = _randn(gen, (steps, N, H, d_k), device).to(tdt)
-    k = _unit_keys(gen, (steps, N, H, d_k), device).to(tdt)
+    k = (_randn(gen, (steps, N, H, d_k), device) if raw
+         else _unit_keys(gen, (steps, N, H, d_k), device)).to(tdt)
     v = _randn(gen, (steps, N, H, d_v), device).to(tdt)
-    g = _gate_for(gen, (steps, N, H), d_k, gate, decay, device)
-    beta = torch.sigmoid(_randn(gen, (steps, N, H), device))
+    g = _gate_for(gen, (steps, N, H), d_k, gate, decay, device, raw)
+    beta = _randn(gen, (steps, N, H), device)
+    if not raw:
+        beta = torch.sigmoid(beta)
     return dict(state=state, q=q, k=k, v=v, g=g, beta=beta, N=N, H=H, d_k=d_k, d_v=d_v,
-                steps=steps, dtype=dtype, decay=decay)
+                steps=steps, dtype=dtype, decay=decay, raw=raw)
 
 
 def make_decode_workload(w: DecodeWorkload, device="cpu", steps=None, decay="channel"):

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = kda.lib()
-    assert L.kda_abi_version() == 2
+    assert L.kda_abi_version() == 3
     for code in range(6):
         s = L.kda_status_string(code).decode()
         assert s.startswith("KDA")
@@ -88,11 +88,11 @@ def test_decay_kind_validation_codes():
     L = kda.lib()
 
     def pf(decay, g=FAKE):
-        return L.kda_prefill_ex(1, decay, FAKE, FAKE, FAKE, g, FAKE, None, 1, 1, 64, 2, 64, 64,
-                                0.125, None, None, FAKE, None, 0, None)
+        return L.kda_prefill_ex(1, decay, 0, FAKE, FAKE, FAKE, g, FAKE, None, 1, 1, 64, 2, 64,
+                                64, 0.125, None, None, FAKE, None, 0, None)
 
     def dc(decay, g=FAKE):
-        return L.kda_decode_step_ex(1, decay, FAKE, FAKE, FAKE, g, FAKE, FAKE, FAKE, 4, 2, 64,
+        return L.kda_decode_step_ex(1, decay, 0, FAKE, FAKE, FAKE, g, FAKE, FAKE, FAKE, 4, 2, 64,
                                     64, 0.1, None)
 
     for f in (pf, dc):
@@ -100,10 +100,26 @@ def test_decay_kind_validation_codes():
         assert f(0, g=None) == 1                 # per-channel decay needs g
         assert f(1, g=None) == 1                 # per-head decay needs g
     # no decay with g NULL passes validation; with T = 0 and no final state nothing launches
-    assert L.kda_prefill_ex(1, 2, FAKE, FAKE, FAKE, None, FAKE, None, 1, 1, 0, 2, 64, 64, 0.125,
-                            None, None, FAKE, None, 0, None) == 0
-    assert L.kda_decode_step_ex(1, 2, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, 2, 64, 64,
+    assert L.kda_prefill_ex(1, 2, 0, FAKE, FAKE, FAKE, None, FAKE, None, 1, 1, 0, 2, 64, 64,
+                            0.125, None, None, FAKE, None, 0, None) == 0
+    assert L.kda_decode_step_ex(1, 2, 0, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, 2, 64, 64,
                                 0.1, None) == 0
+
+
+def test_prologue_flag_validation():
+    L = kda.lib()
+    # known flags pass validation (T = 0 / N = 0: nothing launches); unknown bits are refused
+    for f in (1, 2, 4, 7):
+        assert L.kda_prefill_ex(1, 0, f, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 0, 2, 64, 64,
+                                0.125, None, None, FAKE, None, 0, None) == 0
+        assert L.kda_decode_step_ex(1, 0, f, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 64,
+                                    64, 0.1, None) == 0
+    for f in (8, 16, -1):
+        assert L.kda_prefill_ex(1, 0, f, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 2, 64, 64,
+                                0.125, None, None, FAKE, None, 0, None) == 3
+        assert L.kda_decode_step_ex(1, 0, f, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 64,
+                                    64, 0.1, None) == 3
+    assert kda._flags(True, False, True) == kda.KDA_PRO_NORM_K | kda.KDA_PRO_GATE_LOGIT
 
 
 def test_binding_decay_kind_from_g_shape():

@@ -1,0 +1,132 @@
+"""GPU parity of the fused prologue (raw keys L2-normalised in the kernels, beta and
+the retention gate given as logits) against the fp64 oracle's prologue + recurrence,
+for both prefill kernels, every decay kind and decode."""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_39_amd as kda
+import kda_inputs as ki
+from oracle import BETA_LOGIT, GATE_LOGIT, NORM_K
+from oracle import decode_step as oracle_decode
+from oracle import forward as oracle_forward
+from parity import check
+from test_gpu_prefill import DEV, compare_full, run_gpu, seq_bounds
+
+pytestmark = pytest.mark.gpu
+ALL = dict(normalize_k=True, beta_logit=True, gate_logit=True)
+
+
+def oracle_flags(kw):
+    return ((NORM_K if kw.get("normalize_k") else 0) | (BETA_LOGIT if kw.get("beta_logit") else 0)
+            | (GATE_LOGIT if kw.get("gate_logit") else 0))
+
+
+def run_oracle(x, kw, units=None):
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu().numpy()
+    s0 = None if x["initial_state"] is None else ki.to_f64(x["initial_state"])
+    g = None if x["g"] is None else ki.to_f64(x["g"])
+    return oracle_forward(ki.to_f64(x["q"]), ki.to_f64(x["k"]), ki.to_f64(x["v"]), g,
+                          ki.to_f64(x["beta"]), cu_seqlens=cu, initial_state=s0, units=units,
+                          flags=oracle_flags(kw))
+
+
+@pytest.mark.parametrize("decay", ["channel", "head", "none"])
+@pytest.mark.parametrize("dtype,d_k,d_v,path", [
+    ("fp32", 64, 64, "fused"), ("fp32", 128, 128, "fused"), ("bf16", 128, 128, "fused"),
+    ("bf16", 128, 128, "coop"), ("bf16", 64, 128, "coop")])
+def test_varlen_ragged_all_flags(decay, dtype, d_k, d_v, path):
+    lengths = [1, 63, 0, 64, 65, 130, 200]
+    print(f"prologue {decay} {dtype} d_k={d_k} d_v={d_v} {path}", flush=True)
+    x = ki.make_prefill(H=3, d_k=d_k, d_v=d_v, dtype=dtype, lengths=lengths, init_state_std=0.02,
+                        seed=71, device=DEV, decay=decay, raw=True)
+    o, fs = run_gpu(x, path, **ALL)
+    o_ref, s_ref = run_oracle(x, ALL)
+    compare_full(x, o, fs, o_ref, s_ref, f"prologue {decay} {dtype}")
+
+
+@pytest.mark.parametrize("kw", [dict(normalize_k=True), dict(beta_logit=True),
+                                dict(gate_logit=True)], ids=["norm_k", "beta_logit", "gate_logit"])
+@pytest.mark.parametrize("dtype,path", [("fp32", "fused"), ("bf16", "coop")])
+def test_each_flag_alone(kw, dtype, path):
+    """One transformation on, the other inputs in their ordinary form."""
+    print(f"prologue flag {kw} {dtype} {path}", flush=True)
+    x = ki.make_prefill(B=2, T=150, H=4, d_k=128, d_v=128, dtype=dtype, init_state_std=0.02,
+                        seed=72, device=DEV)
+    xr = ki.make_prefill(B=2, T=150, H=4, d_k=128, d_v=128, dtype=dtype, seed=72, device=DEV,
+                         raw=True)
+    if kw.get("normalize_k"):
+        x["k"] = xr["k"]
+    if kw.get("beta_logit"):
+        x["beta"] = xr["beta"]
+    if kw.get("gate_logit"):
+        x["g"] = xr["g"]
+    o, fs = run_gpu(x, path, **kw)
+    o_ref, s_ref = run_oracle(x, kw)
+    compare_full(x, o, fs, o_ref, s_ref, f"flag {kw}")
+
+
+def test_long_workload_sampled_all_flags():
+    """H32 T65536 d128 bf16 raw projections on the producer/consumer kernel."""
+    w = ki.LONG_PREFILL
+    units = [(0, 0), (0, 19)]
+    print(f"prologue long workload units {units}", flush=True)
+    x = ki.make_prefill_workload(w, device=DEV, raw=True)
+    o, fs = run_gpu(x, "coop", **ALL)
+    o_ref, s_ref = run_oracle(x, ALL, units=units)
+    H, d_v = x["H"], x["d_v"]
+    og = o.view(-1, H, d_v)
+    orf = o_ref.reshape(-1, H, d_v)
+    for n, h in units:
+        check("bf16", ki.to_f64(og[:, h]), orf[:, h], f"long o head {h}")
+        check("bf16", ki.to_f64(fs[n, h]), s_ref[n, h], f"long state head {h}")
+
+
+@pytest.mark.parametrize("decay", ["channel", "head", "none"])
+@pytest.mark.parametrize("dtype,d_k,d_v", [("fp32", 64, 64), ("fp32", 128, 128),
+                                           ("bf16", 128, 128)])
+def test_decode_all_flags(decay, dtype, d_k, d_v):
+    print(f"prologue decode {decay} {dtype} d_k={d_k} d_v={d_v}", flush=True)
+    d = ki.make_decode(N=5, H=3, d_k=d_k, d_v=d_v, steps=5, dtype=dtype, seed=73, device=DEV,
+                       decay=decay, raw=True)
+    state = d["state"].clone()
+    ref = ki.to_f64(d["state"])
+    f = oracle_flags(ALL)
+    for t in range(5):
+        g = None if d["g"] is None else d["g"][t]
+        o = kda.decode_step(d["q"][t], d["k"][t], d["v"][t], g, d["beta"][t], state, **ALL)
+        o_ref, ref = oracle_decode(ki.to_f64(d["q"][t]), ki.to_f64(d["k"][t]),
+                                   ki.to_f64(d["v"][t]), None if g is None else ki.to_f64(g),
+                                   ki.to_f64(d["beta"][t]), ref, flags=f)
+        torch.cuda.synchronize()
+        check(dtype, ki.to_f64(o), o_ref, f"decode o step {t}")
+        check(dtype, ki.to_f64(state), ref, f"decode state step {t}")
+
+
+def test_decode_steps_match_prefill_with_prologue():
+    N, H, T, d = 2, 4, 70, 128
+    x = ki.make_prefill(B=N, T=T, H=H, d_k=d, d_v=d, dtype="bf16", init_state_std=0.02, seed=74,
+                        device=DEV, raw=True)
+    o_pre, s_pre = run_gpu(x, "coop", **ALL)
+    state = x["initial_state"].clone()
+    outs = [kda.decode_step(x["q"][:, t].contiguous(), x["k"][:, t].contiguous(),
+                            x["v"][:, t].contiguous(), x["g"][:, t].contiguous(),
+                            x["beta"][:, t].contiguous(), state, **ALL) for t in range(T)]
+    torch.cuda.synchronize()
+    check("bf16", ki.to_f64(torch.stack(outs, dim=1)), ki.to_f64(o_pre), "decode vs prefill o")
+    check("bf16", ki.to_f64(state), ki.to_f64(s_pre), "decode vs prefill state")
+
+
+def test_zero_key_rows_stay_finite():
+    """A raw key row of zeros normalises to zero (eps), writes nothing, and produces
+    no NaN."""
+    x = ki.make_prefill(B=1, T=100, H=2, d_k=128, d_v=128, dtype="bf16", seed=75, device=DEV,
+                        raw=True)
+    x["k"][:, 10:30] = 0
+    for path in ("fused", "coop"):
+        o, fs = run_gpu(x, path, **ALL)
+        assert torch.isfinite(o.float()).all() and torch.isfinite(fs).all()
+        o_ref, s_ref = run_oracle(x, ALL)
+        check("bf16", ki.to_f64(o), o_ref, f"zero keys {path} o")
+        check("bf16", ki.to_f64(fs), s_ref, f"zero keys {path} state")

@@ -42,3 +42,13 @@ def test_decay_kinds():
     assert n["g"] is None and n["decay"] == "none"
     d = ki.make_decode(N=2, H=3, d_k=8, d_v=4, steps=2, decay="head", seed=1)
     assert d["g"].shape == (2, 2, 3)
+
+
+def test_raw_projections():
+    r = ki.make_prefill(B=1, T=20, H=2, d_k=16, d_v=4, raw=True, seed=3)
+    norms = r["k"].float().norm(dim=-1)
+    assert (norms > 1.5).any()                                  # keys are not unit
+    assert (r["beta"] < 0).any() and (r["beta"] > 0).any()      # logits, both signs
+    assert ((r["g"] >= 2) & (r["g"] <= 7)).all()                # retention logits
+    d = ki.make_decode(N=2, H=2, d_k=8, d_v=4, steps=2, raw=True, decay="head", seed=1)
+    assert d["g"].shape == (2, 2, 2) and (d["g"] >= 2).all()
