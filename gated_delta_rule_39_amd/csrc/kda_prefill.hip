@@ -696,10 +696,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       const bool has_next = cn < nch;
       const int64_t c1 = bos + int64_t(cn) * kChunk;
       const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
-      pr.template factors<DECAY>(n);
-      // the slot must have been copied by every consumer of its previous chunk
+      // the slot must have been released by every consumer of its previous chunk; its
+      // counter is read before the factors, so the check after them rarely waits
       const int s = c % a.R;
-      if (tid == 0) pFlag[0] = wait_at_least(done + s, a.NC * (c / a.R), abort_word) ? 1 : 0;
+      const int need = a.NC * (c / a.R);
+      int dv = 0;
+      if (tid == 0) dv = __hip_atomic_load(done + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pr.template factors<DECAY>(n);
+      if (tid == 0) pFlag[0] = (dv >= need || wait_at_least(done + s, need, abort_word)) ? 1 : 0;
       lds_barrier();
       if (pFlag[0] == 0) break;
       const uint32_t slot = static_cast<uint32_t>(s) * SL::kBytes;
