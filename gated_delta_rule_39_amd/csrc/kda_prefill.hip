@@ -401,7 +401,10 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   auto ldv = [&](uint32_t off) -> f32x4 { return __builtin_bit_cast(f32x4, ld16(off)); };
   const uint32_t fl = 16 * lane;
   // slot offsets of this wave's operands
-  auto offU = [&](int vt) { return uint32_t(SL::oU + (wave * SL::NVB + v0 / 16 + vt) * SL::kFrag) + fl; };
+  // U tiles of value blocks v0/16 + 2p, + 2p + 1 (bf16, one 16-byte piece per pair)
+  auto offU = [&](int p) {
+    return uint32_t(SL::oU + (wave * (SL::NVB / 2) + v0 / 32 + p) * SL::kFrag) + fl;
+  };
   auto offW = [&](int j) { return uint32_t(SL::oW + (wave * KS + j) * SL::kFrag) + fl; };
   auto offQ = [&](int j) { return uint32_t(SL::oQ + (wave * KS + j) * SL::kFrag) + fl; };
   // M (w, 0) is block w; (w, 1) is block 2 + w and exists for w >= 2 (else re-read (w, 0))
@@ -453,7 +456,8 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 
   // this chunk's operands; each is reloaded from the next chunk's slot right after its
   // last use here, so a request has about one chunk of time to arrive
-  f32x4 U[NVT], eg[2];
+  bf16x8 U[NVT / 2];
+  f32x4 eg[2];
   bf16x8 Wf[KS], Qf[KS], Mf[2], KDf[2][2];
   auto load_w = [&](uint32_t slot) {
 #pragma unroll
@@ -483,7 +487,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     ok = cFlag[0] != 0;
     if (ok) {
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) U[vt] = ldv(offU(vt));
+      for (int p = 0; p < NVT / 2; ++p) U[p] = ldf(offU(p));
       load_w(0);
       load_q(0);
       load_m(0);
@@ -512,10 +516,12 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     f32x4 E[NVT], Ot[NVT];
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt) {
-      E[vt] = U[vt];
+      const bf16x8 u = U[vt / 2];
+      E[vt] = vt % 2 ? widen(bf16x4{u[4], u[5], u[6], u[7]}) : widen(bf16x4{u[0], u[1], u[2], u[3]});
       Ot[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      U[vt] = ldv(nslot + offU(vt));
     }
+#pragma unroll
+    for (int p = 0; p < NVT / 2; ++p) U[p] = ldf(nslot + offU(p));
     // E = U - W S^T for token block w; the S^T fragments stay for O
     bf16x8 sb[KS][NVT];
 #pragma unroll
@@ -786,8 +792,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
   };
   auto load_u = [&](uint32_t slot, int k) {   // k = tb * NVS + vs
     const int tb = k / NVS, vs = k % NVS;
-    U[tb][vs] = ring_load16f(
-        rr, slot + SL::oU + (tb * SL::NVB + vw0 / 16 + vs) * SL::kFrag + 16 * lane);
+    const int vb = vw0 / 16 + vs;
+    const bf16x8 u = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+        rr, slot + SL::oU + (tb * (SL::NVB / 2) + vb / 2) * SL::kFrag + 16 * lane, 0,
+        kDeviceScope));
+    U[tb][vs] = vb % 2 ? widen(bf16x4{u[4], u[5], u[6], u[7]}) : widen(bf16x4{u[0], u[1], u[2], u[3]});
   };
 
   bool ok = true, nok = true;

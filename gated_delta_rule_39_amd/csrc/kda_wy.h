@@ -96,7 +96,8 @@ __device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 //   M   (tb, t)  t = 0 for tb < 4, then t = 1 for tb = 2, 3 (the others are zero),
 //                block index tb for t = 0, 2 + tb for t = 1
 //   egn DK fp32 (in a 1 KiB block)
-//   U   (tb, vb) vb < DV/16: fp32 16x16 accumulator tiles (16 bytes per lane)
+//   U   (tb, p)  p < DV/32: the 16x16 accumulator tiles of value blocks 2p and 2p + 1
+//                rounded to bf16, lane l holding its four values of each (16 bytes)
 // The consumer copies [0, kStage) -- fragments, egn and padding -- into LDS.
 template <int DK, int DV>
 struct WySlot {
@@ -116,7 +117,7 @@ struct WySlot {
   static constexpr size_t kStage = size_t(nStage) * kFrag;
   static constexpr size_t oU = kStage;
   static constexpr int NVB = DV / 16;
-  static constexpr size_t kBytes = oU + 4 * NVB * kFrag;
+  static constexpr size_t kBytes = oU + 4 * (NVB / 2) * kFrag;
   static_assert(DK * 4 <= static_cast<int>(kFrag), "egn block");
 };
 
@@ -157,15 +158,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(unsigned char* base,
 __device__ __forceinline__ void ring_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16x8 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDeviceScope);
 }
-__device__ __forceinline__ void ring_store16f(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDeviceScope);
-}
 __device__ __forceinline__ void ring_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kDeviceScope);
-}
-__device__ __forceinline__ f32x4 ring_load16f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope);
-  return __builtin_bit_cast(f32x4, x);
 }
 // One 1 KiB block: 64 lanes x 16 bytes from the ring at off + 16 * lane into LDS at
 // dst + 16 * lane (dst wave-uniform).  Completion is counted by vmcnt, not lgkmcnt,
@@ -206,12 +200,6 @@ struct WyProducer {
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
     else
       ring_store16(r, off, v);
-  }
-  __device__ __forceinline__ void st16f(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) const {
-    if (local)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
-    else
-      ring_store16f(r, off, v);
   }
   __device__ __forceinline__ void st4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) const {
     if (local)
@@ -608,19 +596,21 @@ struct WyProducer {
       }
       st16(rr, slot + SL::oW + f * SL::kFrag + 16 * lane, pack_frag(-lo, -hi));
     }
-#pragma unroll
-    for (int i = 0; i < SL::NVB / 4; ++i) {
-      const int vb = wave + 4 * i;
+    // U: wave w forms value-block pairs w, w + 4, ... (blocks 2p, 2p + 1)
+    for (int pv = wave; pv < SL::NVB / 2; pv += 4) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           if (t == 1 && tb < 2) break;
-          acc = mma_bf16(frag_rows<M>(sTm, LDC, 16 * tb, 32 * t, lane),
-                         frag_tr(sV, LDV, 32 * t, 16 * vb, lane), acc);
+          const bf16x8 xb = frag_rows<M>(sTm, LDC, 16 * tb, 32 * t, lane);
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            acc[hb] = mma_bf16(xb, frag_tr(sV, LDV, 32 * t, 16 * (2 * pv + hb), lane), acc[hb]);
         }
-        st16f(rr, slot + SL::oU + (tb * SL::NVB + vb) * SL::kFrag + 16 * lane, acc);
+        st16(rr, slot + SL::oU + (tb * (SL::NVB / 2) + pv) * SL::kFrag + 16 * lane,
+             pack_frag(acc[0], acc[1]));
       }
     }
   }
