@@ -308,9 +308,7 @@ struct ChunkProducer {
       ss[i] = dot4(k4, k4);
     }
 #pragma unroll
-    for (int m = CG / 2; m >= 1; m >>= 1)
-#pragma unroll
-      for (int i = 0; i < RPG; ++i) ss[i] += __shfl_xor(ss[i], m, CG);
+    for (int i = 0; i < RPG; ++i) ss[i] = row_sum<CG>(ss[i]);
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const f32x4 k4 = widen(kr[i]) * __builtin_amdgcn_rsqf(ss[i] + kNormEps);
@@ -333,12 +331,12 @@ struct ChunkProducer {
         gr[i] = f32x4{y, y, y, y};
       }
     }
-    // alpha = e^g in place (1 for rows past the end); per-thread product of its rows
     // retention logits to log-decays (no decay: alpha = 1 whatever the flag says)
     if (DECAY != 2 && (flags & kGateLogit)) {
 #pragma unroll
       for (int i = 0; i < RPG; ++i) gr[i] = log_sigmoid4(gr[i]);
     }
+    // alpha = e^g in place (1 for rows past the end); per-thread product of its rows
     f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {

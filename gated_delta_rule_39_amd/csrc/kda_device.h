@@ -34,6 +34,27 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return sta
 __device__ __forceinline__ float sigmoid_hw(float x) {
   return __builtin_amdgcn_rcpf(1.f + exp_hw(-x));
 }
+// v of the lane selected by the DPP control CTRL (all rows and banks enabled).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                            0xf, 0xf, false));
+}
+// Sum over aligned groups of `width` (16 or 32) lanes, every lane receiving the total:
+// within each 16-lane row by DPP (neighbour swap, pair swap, half-row and row mirror:
+// each step adds a lane whose partial covers the other half of the current block),
+// then one cross-row exchange for width 32.
+template <int width>
+__device__ __forceinline__ float row_sum(float x) {
+  static_assert(width == 16 || width == 32, "row_sum over 16 or 32 lanes");
+  x += dpp_mov<0xb1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp_mov<0x4e>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_mov<0x141>(x);   // row_half_mirror
+  x += dpp_mov<0x140>(x);   // row_mirror
+  if constexpr (width == 32) x += __shfl_xor(x, 16, 32);
+  return x;
+}
+
 // log(sigmoid(a)) = -log(1 + e^{-a}): a retention logit as a log-decay g (0 when
 // e^{-a} is below fp32 resolution, -inf for a below about -88, so e^g is 1 or 0).
 __device__ __forceinline__ float log_sigmoid_hw(float a) {

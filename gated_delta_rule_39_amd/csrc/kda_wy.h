@@ -301,9 +301,7 @@ struct WyProducer {
       ss[i] = dot4(k4, k4);
     }
 #pragma unroll
-    for (int m = CG / 2; m >= 1; m >>= 1)
-#pragma unroll
-      for (int i = 0; i < RPG; ++i) ss[i] += __shfl_xor(ss[i], m, CG);
+    for (int i = 0; i < RPG; ++i) ss[i] = row_sum<CG>(ss[i]);
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const f32x4 k4 = widen(kr[i]) * __builtin_amdgcn_rsqf(ss[i] + kNormEps);
@@ -328,6 +326,7 @@ struct WyProducer {
 #pragma unroll
       for (int i = 0; i < RPG; ++i) gr[i] = log_sigmoid4(gr[i]);
     }
+    // alpha = e^g in place (1 for rows past the end); per-thread product of its rows
     f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
