@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (r0 + RPP * i) * DK));
 
   f32x4 kk = load4(k + kbase);
-  if (flags & kNormK) kk *= __builtin_amdgcn_rsqf(group_sum<LPR>(dot4(kk, kk)) + kNormEps);
+  if (flags & kNormK) kk *= __builtin_amdgcn_rsqf(row_sum<LPR>(dot4(kk, kk)) + kNormEps);
   f32x4 qq = load4(q + kbase);
   qq *= scale;
   f32x4 gg = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -74,13 +74,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
   for (int i = 0; i < NP; ++i) vv[i] = to_f32(v[vbase + r0 + RPP * i]);
 
-  const float kq = group_sum<LPR>(dot4(kk, qq));
+  const float kq = row_sum<LPR>(dot4(kk, qq));
 
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const f32x4 d = s[i] * a;
-    const float p = group_sum<LPR>(dot4(d, kk));
-    const float r = group_sum<LPR>(dot4(d, qq));
+    const float p = row_sum<LPR>(dot4(d, kk));
+    const float r = row_sum<LPR>(dot4(d, qq));
     const float e = b * (vv[i] - p);
     const f32x4 sn = d + e * kk;
     __builtin_nontemporal_store(sn, reinterpret_cast<f32x4*>(S + (r0 + RPP * i) * DK));

@@ -77,15 +77,6 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
   return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64); every lane
-// of the group receives the total.
-template <int width>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int m = width / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, width);
-  return x;
-}
-
 // f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
