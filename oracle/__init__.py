@@ -23,11 +23,15 @@ Modules:
   kernel computes), checked against the recurrence.
 * :mod:`oracle.kda_prologue`   -- raw projections to the recurrence's inputs (key
   L2 normalisation, sigmoid write strength, sigmoid retention gate).
+* :mod:`oracle.kda_bwd_ref`    -- the gradients of the recurrence (reverse-mode chain
+  rule through the token cycle), for training; ``kda_chunk_ref.chunked_backward``
+  is the same through the chunk algebra.
 * :mod:`oracle.pool`           -- fans independent (sequence, head) units out over
   host cores, for the CPU baseline.
 
 Parity pins (``tests/test_oracle_pins.py``, ``tests/test_oracle_decay_variants.py``,
-``tests/test_oracle_prologue.py``): every function here is pinned
+``tests/test_oracle_prologue.py``, ``tests/test_oracle_backward.py``): every function
+here is pinned
 by closed forms, special cases that reduce to a library routine, exact rational
 brute force, a hand-derived worked example and invariants; none is "parity unpinned".
 """
@@ -38,10 +42,11 @@ from .kda_ref import (  # noqa: F401
     forward,
     decode_step,
 )
-from .kda_chunk_ref import chunked  # noqa: F401
+from .kda_chunk_ref import chunked, chunked_backward  # noqa: F401
 from .kda_prologue import (  # noqa: F401
     BETA_LOGIT,
     GATE_LOGIT,
     NORM_K,
     prologue,
 )
+from .kda_bwd_ref import backward, recurrence_backward  # noqa: F401
