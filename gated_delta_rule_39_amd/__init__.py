@@ -1,4 +1,5 @@
-"""MI355X (gfx950) Kimi Delta Attention forward: chunked prefill and in-place decode.
+"""MI355X (gfx950) Kimi Delta Attention: chunked prefill, in-place decode and the
+prefill's backward (gradients for training).
 
 Thin Python binding over the C ABI in ``include/kda.h`` (``libkda.so``).  It only
 marshals arguments: checks dtypes, devices and contiguity, allocates outputs with
@@ -66,6 +67,12 @@ def lib() -> ctypes.CDLL:
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                   f32, vp]
+    L.kda_backward.restype = ctypes.c_int
+    L.kda_backward.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                               i32, i32, i64, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
+                               vp, vp, sz, vp]
+    L.kda_backward_workspace_bytes.restype = sz
+    L.kda_backward_workspace_bytes.argtypes = [ctypes.c_int, i32, i64, i32, i32, i32]
     L.kda_decode_step_ex.restype = ctypes.c_int
     L.kda_decode_step_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp,
                                      vp, vp, i32, i32, i32, i32, f32, vp]
@@ -123,10 +130,10 @@ def workspace_bytes(dtype: torch.dtype, N: int, T_total: int, H: int, d_k: int, 
 _workspaces = {}
 
 
-def _auto_workspace(device, nbytes: int):
-    """A workspace of at least ``nbytes`` cached per (device, stream): calls that share
-    it are ordered on that stream."""
-    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+def _auto_workspace(device, nbytes: int, purpose: str = "prefill"):
+    """A workspace of at least ``nbytes`` cached per (purpose, device, stream): calls
+    that share it are ordered on that stream."""
+    key = (purpose, device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
@@ -264,3 +271,71 @@ def decode_step(q, k, v, g, beta, state, *, scale=None, out=None, normalize_k=Fa
                                     _ptr(beta), _ptr(state), _ptr(o), N, H, d_k, d_v,
                                     float(scale), _stream(dev)))
     return o
+
+
+def backward_workspace_bytes(N: int, T_total: int, H: int, d_k: int, d_v: int) -> int:
+    """Workspace bytes ``backward`` needs (bf16 chunk states and state gradients)."""
+    return int(lib().kda_backward_workspace_bytes(KDA_BF16, N, T_total, H, d_k, d_v))
+
+
+def backward(q, k, v, g, beta, do, *, cu_seqlens=None, scale=None, initial_state=None,
+             dfinal_state=None, need_dinitial_state=True, workspace="auto"):
+    """Gradients of ``prefill`` (bf16 inputs, no prologue flags).
+
+    The inputs are those of the forward call; ``do`` [B, T, H, d_v] bf16 is dL/do and
+    ``dfinal_state`` [N, H, d_v, d_k] fp32 (or None: zero) is dL/d(final state).
+    ``workspace``: "auto" (a cached device buffer) or a uint8 device tensor of at least
+    ``backward_workspace_bytes`` bytes.
+    Returns (dq, dk, dv [bf16], dg [fp32, g's shape, or None], dbeta [fp32],
+    dinitial_state [fp32, or None]).
+    """
+    dev = q.device
+    _need(q, "q", dtype=torch.bfloat16, device=dev)
+    for t, nm in ((k, "k"), (v, "v"), (do, "do")):
+        _need(t, nm, dtype=torch.bfloat16, device=dev)
+    if g is not None:
+        _need(g, "g", dtype=torch.float32, device=dev)
+    _need(beta, "beta", dtype=torch.float32, device=dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    decay = _decay_kind(g, q.shape)
+    if k.shape != q.shape or v.shape != (B, T, H, d_v) or do.shape != v.shape \
+            or beta.shape != (B, T, H):
+        raise ValueError("inconsistent q/k/v/do/g/beta shapes")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=dev)
+        N = cu_seqlens.numel() - 1
+        if B != 1:
+            raise ValueError("packed sequences (cu_seqlens) need B == 1")
+    else:
+        N = B
+    for t, nm in ((initial_state, "initial_state"), (dfinal_state, "dfinal_state")):
+        if t is not None:
+            _need(t, nm, dtype=torch.float32, device=dev)
+            if t.shape != (N, H, d_v, d_k):
+                raise ValueError(f"{nm} must be [N, H, d_v, d_k]")
+    if scale is None:
+        scale = d_k ** -0.5
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dg = None if g is None else torch.empty_like(g)
+    dbeta = torch.empty_like(beta)
+    ds0 = torch.empty((N, H, d_v, d_k), dtype=torch.float32, device=dev) \
+        if need_dinitial_state else None
+    nb = backward_workspace_bytes(max(N, 1), B * T, H, d_k, d_v)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto' or a uint8 device tensor")
+        ws = _auto_workspace(dev, nb, "backward")
+    else:
+        _need(workspace, "workspace", dtype=torch.uint8, device=dev)
+        ws = workspace
+    _check(lib().kda_backward(KDA_BF16, decay, 0, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                              _ptr(cu_seqlens), N, B, T, H, d_k, d_v, float(scale),
+                              _ptr(initial_state), _ptr(do), _ptr(dfinal_state), _ptr(dq),
+                              _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(ws),
+                              ws.numel(), _stream(dev)))
+    return dq, dk, dv, dg, dbeta, ds0

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libkda.so")
 
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_backward.hip"]
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_*_f32 generation.  -amdgpu-mfma-vgpr-form: MFMA
 # accumulators in ordinary VGPRs, so loop-carried accumulators (the prefill state)

@@ -99,6 +99,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: d_k and d_v must each be 64 or 128";
     case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: dtype must be KDA_F32 (0) or KDA_BF16 (1)";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP kernel launch failed";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
     default: return "KDA: unknown status code";
   }
 }
@@ -233,6 +234,98 @@ int kda_decode_step(int dtype, const void* q, const void* k, const void* v, cons
                     int32_t d_k, int32_t d_v, float scale, hipStream_t stream) {
   return kda_decode_step_ex(dtype, KDA_DECAY_CHANNEL, 0, q, k, v, g, beta, state, o, N, H, d_k,
                             d_v, scale, stream);
+}
+
+size_t kda_backward_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_t H, int32_t d_k,
+                                    int32_t d_v) {
+  if (dtype != KDA_BF16 || N <= 0 || T_total < 0 || H <= 0 || !supported_dim(d_k) ||
+      !supported_dim(d_v))
+    return 0;
+  const int64_t slots = kda::chunk_slots_host(T_total, N);
+  return static_cast<size_t>(2 * slots * H * d_v * d_k * 2);
+}
+
+int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, const void* v,
+                 const float* g, const float* beta, const int32_t* cu_seqlens, int32_t N,
+                 int32_t B, int64_t T, int32_t H, int32_t d_k, int32_t d_v, float scale,
+                 const float* initial_state, const void* dout, const float* dfinal_state,
+                 void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dinitial_state,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (decay != KDA_DECAY_CHANNEL && decay != KDA_DECAY_HEAD && decay != KDA_DECAY_NONE)
+    return KDA_ERR_UNSUPPORTED;
+  if (flags != 0) return KDA_ERR_UNSUPPORTED;
+  if (N < 0 || B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
+  if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
+  if (cu_seqlens == nullptr && N != B) return KDA_ERR_BAD_SHAPE;
+  if (cu_seqlens != nullptr && B != 1) return KDA_ERR_BAD_SHAPE;
+  const int64_t units = static_cast<int64_t>(N) * H;
+  if (units > (1 << 24)) return KDA_ERR_BAD_SHAPE;
+  if (N == 0) return KDA_OK;
+  const int64_t tot = static_cast<int64_t>(B) * T;
+  const int64_t slots = kda::chunk_slots_host(tot, N);
+  if (slots * H > 0x7fffffff) return KDA_ERR_BAD_SHAPE;
+  if (tot > 0 && (!q || !k || !v || (decay != KDA_DECAY_NONE && (!g || !dg)) || !beta || !dout ||
+                  !dq || !dk || !dv || !dbeta))
+    return KDA_ERR_NULL_ARG;
+  const size_t need = kda_backward_workspace_bytes(dtype, N, tot, H, d_k, d_v);
+  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  if (tot == 0 && !dinitial_state) return KDA_OK;
+  unsigned char* states = static_cast<unsigned char*>(workspace);
+  unsigned char* dstates = states + need / 2;
+  const int cus = cu_count();
+  if (tot > 0) {
+    kda::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.cu_seqlens = cu_seqlens;
+    a.initial_state = initial_state;
+    a.T = T;
+    a.H = H;
+    a.DV = d_v;
+    a.units = static_cast<int32_t>(units);
+    a.xcd_remap = (units % 8 == 0) ? 1 : 0;
+    a.scale = scale;
+    a.decay = decay;
+    a.workspace = states;
+    const int bv = choose_bv(KDA_BF16, static_cast<int32_t>(units), d_k, d_v, cus);
+    a.NV = d_v / bv;
+    if (kda::launch_prefill_states(d_k, bv, a, stream) != hipSuccess) return KDA_ERR_HIP;
+  }
+  kda::BwdArgs b{};
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.g = g;
+  b.beta = beta;
+  b.dout = dout;
+  b.cu_seqlens = cu_seqlens;
+  b.dfinal_state = dfinal_state;
+  b.dinitial_state = dinitial_state;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dg = dg;
+  b.dbeta = dbeta;
+  b.states = states;
+  b.dstates = dstates;
+  b.T = T;
+  b.slots = slots;
+  b.H = H;
+  b.DV = d_v;
+  b.N = N;
+  b.units = static_cast<int32_t>(units);
+  b.NV = d_v / kda::kBwdChainBV;
+  b.xcd_remap = (units % 8 == 0) ? 1 : 0;
+  b.decay = decay;
+  b.scale = scale;
+  if (kda::launch_backward_chain(d_k, b, stream) != hipSuccess) return KDA_ERR_HIP;
+  if (tot > 0 && kda::launch_backward_grads(d_k, b, stream) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
 }
 
 }  // extern "C"

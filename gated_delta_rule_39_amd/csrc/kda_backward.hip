@@ -1,0 +1,604 @@
+// Backward (training) pass of the chunked KDA prefill on gfx950, bf16 inputs.
+//
+// The gradient of the chunk algebra of kda_chunk.h.  With H = S^T (d_k x d_v) the
+// state at a chunk's start, W = X diag(beta) Kg, U = X diag(beta) V, Kh = k e^{G_n - G}
+// and D = Diag(e^{G_n}), one chunk maps
+//   E = U - W H,   O = Qg H + M E,   H' = D H + Kh^T E.
+// Given dO and dH' (the gradient of the state after the chunk), the reverse step is
+//   dE  = Kh dH' + M^T dO                dH = D dH' + Qg^T dO - W^T dE       (the chain)
+//   dQg = dO H^T + dM Ki,  dM = lower(dO E^T),   dW = -dE H^T,   dKh = E dH'^T,
+//   d e^{G_n}_j = sum_v dH'[j, v] H[j, v],
+//   dX  = dE (beta V)^T + dW (beta Kg)^T,   dA = -strict_lower(X^T dX X^T),
+//   d(beta V) = X^T dE,   d(beta Kg) = X^T dW + dA Ki,   dKi = dA^T (beta Kg) + dM^T Qg,
+// then through Kg = k e^G, Ki = k e^{-G}, Qg = scale q e^G, Kh = k e^{G_n - G} and the
+// prefix sums G of g.  The pages tie the chunkwise form to training ("Kimi Delta
+// Attention Technical Deep Dive", "Systems and implementation tradeoffs" ->
+// "Training"); the derivation is the chain rule through the forward recurrence of
+// "Kimi Delta Attention: The Linear Attention Behind Kimi K2 and Qwen3", "How Kimi
+// Delta Attention works step by step".
+//
+// Three launches on one stream:
+//   1. forward sweep (prefill_kernel with STATES): the state at every chunk start,
+//      bf16, into the workspace;
+//   2. bwd_chain_kernel: per (unit, 16 value rows), the chunks in reverse order; the
+//      chain above only (its value columns are independent), writing dH' of every
+//      chunk (bf16) and dL/dS_0;
+//   3. bwd_grad_kernel: one workgroup per (chunk, head), all chunks at once; reads H
+//      and dH', forms E and dE in 32-wide value slices and accumulates every
+//      d_v-contraction in registers, then the chunk-local algebra and the gradients.
+// Every product runs on the bf16 MFMA (16x16x32, fp32 accumulation); operands that
+// are needed transposed are read with ds_read_b64_tr_b16 (frag_tr).
+
+#include "kda_chunk.h"
+#include "kda_launch.h"
+#include "kda_tiles.h"
+#include "kda_wy.h"
+
+namespace kda {
+
+using MB = Mfma<bf16>;
+
+__device__ __forceinline__ bf16x8 frow(const bf16* base, int ld, int row0, int k0, int lane) {
+  return frag_rows<MB>(base, ld, row0, k0, lane);
+}
+
+// ====================================================================================
+// Reverse chain
+// ====================================================================================
+
+template <int DK, int BV>
+struct ChainLayout {
+  using CL = ChunkLayout<bf16, DK, false>;
+  static constexpr int LDK = CL::LDK, LDC = CL::LDC;
+  static constexpr size_t oP = CL::kBytes;   // [BV][LDK]: (D dH')^T snapshot
+  static constexpr size_t kBytes = CL::al(oP + size_t(BV) * LDK * 2);
+  // dO^T, dE^T, G^T ([BV][LDC]) in the A / inverse region, dead after the inverse
+  static constexpr size_t oDOT = CL::oA;
+  static constexpr size_t oDET = CL::al(oDOT + size_t(BV) * LDC * 2);
+  static constexpr size_t oGT = CL::al(oDET + size_t(BV) * LDC * 2);
+  static_assert(oGT + size_t(BV) * LDC * 2 <= CL::oScr, "chain tiles overflow");
+  static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <int DK, int BV, int DECAY>
+__global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
+  using CP = ChunkProducer<bf16, DK, false>;
+  using CL = ChainLayout<DK, BV>;
+  using ST = StateTiles<DK, BV>;
+  constexpr int LDK = CL::LDK, LDC = CL::LDC, NVB = BV / 16;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[CL::kBytes];
+  bf16* sP = reinterpret_cast<bf16*>(smem + CL::oP);
+  bf16* sDOT = reinterpret_cast<bf16*>(smem + CL::oDOT);
+  bf16* sDET = reinterpret_cast<bf16*>(smem + CL::oDET);
+  bf16* sGT = reinterpret_cast<bf16*>(smem + CL::oGT);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+
+  int unit, vt, n_seq, h;
+  int64_t bos, eos;
+  unit_role(blockIdx.x, a.NV, a.units, a.xcd_remap, unit, vt);
+  unit_bounds(a, unit, n_seq, h, bos, eos);
+  const int v0 = vt * BV;
+  const bf16* dout = static_cast<const bf16*>(a.dout);
+  bf16* dstates = static_cast<bf16*>(a.dstates);
+
+  CP cp;
+  cp.init(smem, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), a.g, a.beta, a.H,
+          h, a.scale, tid, wave, 0);
+  f32x4 sacc[ST::NST];   // dH^T tiles of this value tile (rows = key), fp32
+  const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * a.DV * DK;
+  load_state<DK, BV, LDK>(sacc, a.dfinal_state, st_base, v0, sP, wave, lane);
+
+  const int nch = static_cast<int>((eos - bos + kChunk - 1) / kChunk);
+  const int64_t slot0 = chunk_slot_base(n_seq, bos);
+  ValueRegs<bf16, NVB> dr;   // dO rows of the chunk, accumulator layout
+  if (nch > 0) {
+    const int64_t cl = bos + int64_t(nch - 1) * kChunk;
+    const int nl = static_cast<int>(eos - cl);
+    cp.template load<DECAY>(cl, nl);
+    dr.load(dout, cl, nl, a.H, h, a.DV, v0, wave, lane);
+  }
+  const int k0m = (16 * wave) & ~31;   // first K step that meets a triangular row block
+
+  for (int c = nch - 1; c >= 0; --c) {
+    const int64_t c0 = bos + int64_t(c) * kChunk;
+    const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
+    const bool has_next = c > 0;   // the previous chunk in token order (always full)
+    // dL/d(state after chunk c)
+    store_state_bf16<DK, BV>(sacc, dstates, ((slot0 + c) * a.H + h) * a.DV * DK, v0, wave,
+                             lane);
+
+    cp.template factors<DECAY>(n, has_next, c0 - kChunk, kChunk);
+    cp.products();
+    cp.inverse();
+
+    // P = D dH' (accumulators and snapshot), dO^T tile
+#pragma unroll
+    for (int s = 0; s < ST::NST; ++s) {
+      const int kb = ST::kb(wave, s), vb = ST::vb(s);
+      sacc[s] *= *reinterpret_cast<const f32x4*>(cp.sEgn + 16 * kb + 4 * lq);
+      store4(sP + (16 * vb + lr) * LDK + 16 * kb + 4 * lq, sacc[s]);
+    }
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      f32x4 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = 16 * wave + 4 * lq + i < n ? dr.f32(vb, i) : 0.f;
+      store4(sDOT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, x);
+    }
+    if (has_next) dr.load(dout, c0 - kChunk, kChunk, a.H, h, a.DV, v0, wave, lane);
+    lds_barrier();
+
+    // dE = Ki P + M^T dO for token block `wave` -> dE^T
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < DK; kk += 32)
+        acc = mma_bf16(frow(cp.sKi, LDK, 16 * wave, kk, lane), frow(sP, LDK, 16 * vb, kk, lane), acc);
+      for (int kk = k0m; kk < kChunk; kk += 32)
+        acc = mma_bf16(frag_tr(cp.sM, LDC, kk, 16 * wave, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
+                       acc);
+      store4(sDET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, acc);
+    }
+    lds_barrier();
+
+    // G = -beta X^T dE -> G^T
+    {
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(cp.sBeta + 16 * wave + 4 * lq);
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kk = k0m; kk < kChunk; kk += 32)
+          acc = mma_bf16(frag_tr(cp.sTm, LDC, kk, 16 * wave, lane),
+                         frow(sDET, LDC, 16 * vb, kk, lane), acc);
+        store4(sGT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, -(bt * acc));
+      }
+    }
+    lds_barrier();
+
+    // dH = P + Qg^T dO + Kg^T G
+#pragma unroll
+    for (int s = 0; s < ST::NST; ++s) {
+      const int kb = ST::kb(wave, s), vb = ST::vb(s);
+      f32x4 acc = sacc[s];
+#pragma unroll
+      for (int kk = 0; kk < kChunk; kk += 32) {
+        acc = mma_bf16(frag_tr(cp.sQg, LDK, kk, 16 * kb, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
+                       acc);
+        acc = mma_bf16(frag_tr(cp.sKg, LDK, kk, 16 * kb, lane), frow(sGT, LDC, 16 * vb, kk, lane),
+                       acc);
+      }
+      sacc[s] = acc;
+    }
+    lds_barrier();
+  }
+
+  if (a.dinitial_state) store_state<DK, BV>(sacc, a.dinitial_state, st_base, v0, wave, lane);
+}
+
+// ====================================================================================
+// Chunk-parallel gradients
+// ====================================================================================
+
+template <int DK>
+struct GradLayout {
+  using CL = ChunkLayout<bf16, DK, false>;
+  static constexpr int LDK = CL::LDK, LDC = CL::LDC;
+  static constexpr int LDEG = ChunkProducer<bf16, DK, false>::LDEG;
+  static constexpr int VS = 32;                                   // value slice
+  static constexpr size_t oEG = CL::kBytes;                       // fp32 e^{G} [64][LDEG]
+  static constexpr size_t kBytes = CL::al(oEG + size_t(kChunk) * LDEG * 4);
+  static constexpr size_t kLds = 160 * 1024;
+  // area 1: A and the fp32 inverse (dead after the inverse); area 2: the rest of LDS
+  static constexpr size_t a1 = CL::oA, a1end = CL::oScr;
+  static constexpr size_t a2 = kBytes, a2end = kLds;
+  static constexpr size_t tV = size_t(VS) * LDK * 2;              // [VS][LDK] bf16
+  static constexpr size_t tT = size_t(VS) * LDC * 2;              // [VS][LDC] bf16
+  static constexpr size_t tC = size_t(kChunk) * LDC * 2;          // [64][LDC] bf16
+  static constexpr size_t tW = size_t(DK) * LDC * 2;              // [DK][LDC] bf16
+  // value-slice phase
+  static constexpr size_t oH = a1, oDH = a1 + tV, oP = a1 + 2 * tV, oRT = a1 + 3 * tV;
+  static constexpr size_t oET = a2, oDET = a2 + tT, oDOT = a2 + 2 * tT, oVT = a2 + 3 * tT;
+  static_assert(oRT + tT <= a1end && oVT + tT <= a2end, "value-slice tiles overflow");
+  // chunk-local phase
+  static constexpr size_t oDWT = a1, oDMT = a1 + tW;
+  static constexpr size_t oCC1 = a2, oCC2 = a2 + tC, oCC3 = CL::oM;
+  static_assert(oDMT + tC <= a1end && oCC2 + tC <= a2end, "chunk tiles overflow");
+  static constexpr size_t oGm = a1;                               // fp32 [64][LDEG]
+  static_assert(oGm + size_t(kChunk) * LDEG * 4 <= a1end, "dG tile overflow");
+  static_assert(kBytes <= kLds, "LDS budget exceeded");
+};
+
+// Sequence and chunk of a chunk slot (see chunk_slot_base); false for an unused slot.
+__device__ __forceinline__ bool slot_chunk(const BwdArgs& a, int64_t slot, int& n_seq,
+                                           int64_t& bos, int64_t& eos, int& c) {
+  auto bos_of = [&](int n) -> int64_t {
+    return a.cu_seqlens ? static_cast<int64_t>(a.cu_seqlens[n]) : static_cast<int64_t>(n) * a.T;
+  };
+  int lo = 0, hi = a.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunk_slot_base(mid, bos_of(mid)) <= slot) lo = mid; else hi = mid - 1;
+  }
+  n_seq = lo;
+  bos = bos_of(lo);
+  eos = a.cu_seqlens ? static_cast<int64_t>(a.cu_seqlens[lo + 1]) : bos + a.T;
+  const int64_t cc = slot - chunk_slot_base(lo, bos);
+  c = static_cast<int>(cc);
+  return cc >= 0 && cc * kChunk < eos - bos;
+}
+
+template <int DK, int DV, int DECAY>
+__global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
+  using CP = ChunkProducer<bf16, DK, false>;
+  using GL = GradLayout<DK>;
+  constexpr int LDK = GL::LDK, LDC = GL::LDC, LDEG = GL::LDEG, VS = GL::VS;
+  constexpr int NKB = DK / 16;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[GL::kLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+
+  const int h = blockIdx.x % a.H;
+  const int64_t slot = blockIdx.x / a.H;
+  int n_seq, c;
+  int64_t bos, eos;
+  if (!slot_chunk(a, slot, n_seq, bos, eos, c)) return;   // uniform over the workgroup
+  const int64_t c0 = bos + int64_t(c) * kChunk;
+  const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
+  const int64_t sbase = ((slot * a.H + h) * a.DV) * DK;
+  const bf16* states = static_cast<const bf16*>(a.states) + sbase;
+  const bf16* dstates = static_cast<const bf16*>(a.dstates) + sbase;
+  const bf16* vin = static_cast<const bf16*>(a.v);
+  const bf16* dout = static_cast<const bf16*>(a.dout);
+  const bf16* kin = static_cast<const bf16*>(a.k);
+  const bf16* qin = static_cast<const bf16*>(a.q);
+  bf16* dvout = static_cast<bf16*>(a.dv);
+  const uint32_t rowV = static_cast<uint32_t>(a.H) * DV;
+  const uint32_t rowK = static_cast<uint32_t>(a.H) * DK;
+
+  CP cp;
+  cp.init(smem, qin, kin, a.g, a.beta, a.H, h, a.scale, tid, wave, 0);
+  cp.sEG = reinterpret_cast<float*>(smem + GL::oEG);
+  cp.template load<DECAY>(c0, n);
+  cp.template factors<DECAY, true>(n, false, 0, 0);
+  cp.products();
+  cp.inverse();
+
+  const int k0m = (16 * wave) & ~31;
+  const int kend = 16 * (wave + 1);
+  const f32x4 bt = *reinterpret_cast<const f32x4*>(cp.sBeta + 16 * wave + 4 * lq);
+
+  // ---- value slices: E, dE, and every contraction over d_v ----------------------------
+  bf16* sH = reinterpret_cast<bf16*>(smem + GL::oH);
+  bf16* sDH = reinterpret_cast<bf16*>(smem + GL::oDH);
+  bf16* sP = reinterpret_cast<bf16*>(smem + GL::oP);
+  bf16* sRT = reinterpret_cast<bf16*>(smem + GL::oRT);
+  bf16* sET = reinterpret_cast<bf16*>(smem + GL::oET);
+  bf16* sDET = reinterpret_cast<bf16*>(smem + GL::oDET);
+  bf16* sDOT = reinterpret_cast<bf16*>(smem + GL::oDOT);
+  bf16* sVT = reinterpret_cast<bf16*>(smem + GL::oVT);
+
+  f32x4 dQg[NKB], dWn[NKB], dKh[NKB], dM[4], dXU[4];
+#pragma unroll
+  for (int i = 0; i < NKB; ++i) dQg[i] = dWn[i] = dKh[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dM[i] = dXU[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 dbu = f32x4{0.f, 0.f, 0.f, 0.f};   // sum_v d(beta V) V for this lane's rows
+  float ddp = 0.f;                         // partial d e^{G_n}_j from H and dH'
+  constexpr int KPT = DK * VS / kThreads;  // (key, value) pairs per thread for ddp
+  const int dj = tid % DK, dpart = tid / DK;
+
+  for (int vs = 0; vs < DV / VS; ++vs) {
+    const int v0 = vs * VS;
+    // H, dH' (and P = D dH') slices [VS][DK]; V^T and dO^T slices [VS][64]
+    for (int i = tid; i < VS * DK / 8; i += kThreads) {
+      const int r = i / (DK / 8), c8 = 8 * (i % (DK / 8));
+      const bf16x8 hv = *reinterpret_cast<const bf16x8*>(states + int64_t(v0 + r) * DK + c8);
+      const bf16x8 dh = *reinterpret_cast<const bf16x8*>(dstates + int64_t(v0 + r) * DK + c8);
+      *reinterpret_cast<bf16x8*>(sH + r * LDK + c8) = hv;
+      *reinterpret_cast<bf16x8*>(sDH + r * LDK + c8) = dh;
+      bf16x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = static_cast<bf16>(static_cast<float>(dh[e]) * cp.sEgn[c8 + e]);
+      *reinterpret_cast<bf16x8*>(sP + r * LDK + c8) = p;
+    }
+    f32x4 vreg[VS / 16];
+#pragma unroll
+    for (int vb = 0; vb < VS / 16; ++vb) {
+      f32x4 x, d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * lq + i;
+        const uint32_t off = static_cast<uint32_t>(min(r, n - 1)) * rowV + v0 + 16 * vb + lr;
+        const int64_t base = (c0 * a.H + h) * DV;
+        x[i] = r < n ? static_cast<float>(vin[base + off]) : 0.f;
+        d[i] = r < n ? static_cast<float>(dout[base + off]) : 0.f;
+      }
+      vreg[vb] = x;
+      store4(sVT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, x);
+      store4(sDOT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, d);
+    }
+    lds_barrier();
+
+    // R' = beta (V - Kg H) -> R'^T;  dE = Ki P + M^T dO -> dE^T
+#pragma unroll
+    for (int vb = 0; vb < VS / 16; ++vb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, de = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < DK; kk += 32) {
+        acc = mma_bf16(frow(cp.sKg, LDK, 16 * wave, kk, lane), frow(sH, LDK, 16 * vb, kk, lane), acc);
+        de = mma_bf16(frow(cp.sKi, LDK, 16 * wave, kk, lane), frow(sP, LDK, 16 * vb, kk, lane), de);
+      }
+      for (int kk = k0m; kk < kChunk; kk += 32)
+        de = mma_bf16(frag_tr(cp.sM, LDC, kk, 16 * wave, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
+                      de);
+      store4(sRT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, bt * (vreg[vb] - acc));
+      store4(sDET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, de);
+    }
+    lds_barrier();
+
+    // E = X R' -> E^T;  d(beta V) = X^T dE -> dv, and its dot with V
+#pragma unroll
+    for (int vb = 0; vb < VS / 16; ++vb) {
+      f32x4 e = f32x4{0.f, 0.f, 0.f, 0.f}, dbv = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < kend; kk += 32)
+        e = mma_bf16(frow(cp.sTm, LDC, 16 * wave, kk, lane), frow(sRT, LDC, 16 * vb, kk, lane), e);
+      for (int kk = k0m; kk < kChunk; kk += 32)
+        dbv = mma_bf16(frag_tr(cp.sTm, LDC, kk, 16 * wave, lane),
+                       frow(sDET, LDC, 16 * vb, kk, lane), dbv);
+      store4(sET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, e);
+      dbu += dbv * vreg[vb];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * lq + i;
+        if (r < n)
+          dvout[(c0 + r) * rowV + int64_t(h) * DV + v0 + 16 * vb + lr] =
+              static_cast<bf16>(bt[i] * dbv[i]);
+      }
+    }
+    // d e^{G_n}: sum over this slice's values of dH' H, per key
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      const int r = dpart * KPT + e;
+      ddp += static_cast<float>(sDH[r * LDK + dj]) * static_cast<float>(sH[r * LDK + dj]);
+    }
+    lds_barrier();
+
+    // contractions over this slice's values (K = 32 = one MFMA step)
+    {
+      const bf16x8 aDO = frag_tr(sDOT, LDC, 0, 16 * wave, lane);
+      const bf16x8 aDE = frag_tr(sDET, LDC, 0, 16 * wave, lane);
+      const bf16x8 aE = frag_tr(sET, LDC, 0, 16 * wave, lane);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 bH = frag_tr(sH, LDK, 0, 16 * kb, lane);
+        dQg[kb] = mma_bf16(aDO, bH, dQg[kb]);
+        dWn[kb] = mma_bf16(aDE, bH, dWn[kb]);
+        dKh[kb] = mma_bf16(aE, frag_tr(sDH, LDK, 0, 16 * kb, lane), dKh[kb]);
+      }
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        dM[sb] = mma_bf16(aDO, frag_tr(sET, LDC, 0, 16 * sb, lane), dM[sb]);
+        dXU[sb] = mma_bf16(aDE, frag_tr(sVT, LDC, 0, 16 * sb, lane), dXU[sb]);
+      }
+    }
+    lds_barrier();
+  }
+
+  // ---- chunk-local algebra -------------------------------------------------------------
+  bf16* sDWT = reinterpret_cast<bf16*>(smem + GL::oDWT);   // dW^T [DK][64]
+  bf16* sDMT = reinterpret_cast<bf16*>(smem + GL::oDMT);   // dM^T [64][64]
+  bf16* sC1 = reinterpret_cast<bf16*>(smem + GL::oCC1);
+  bf16* sC2 = reinterpret_cast<bf16*>(smem + GL::oCC2);
+  bf16* sC3 = reinterpret_cast<bf16*>(smem + GL::oCC3);
+  // dW = -dE H^T (transposed), dM = lower(dO E^T) (transposed)
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+    store4(sDWT + (16 * kb + lr) * LDC + 16 * wave + 4 * lq, -dWn[kb]);
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    f32x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = 16 * sb + lr <= 16 * wave + 4 * lq + i ? dM[sb][i] : 0.f;
+    store4(sDMT + (16 * sb + lr) * LDC + 16 * wave + 4 * lq, x);
+  }
+  lds_barrier();
+
+  // dX = (dE V^T + dW Kg^T) Diag(beta), strictly lower -> dX^T (sC1)
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    f32x4 acc = dXU[sb];
+#pragma unroll
+    for (int kk = 0; kk < DK; kk += 32)
+      acc = mma_bf16(frag_tr(sDWT, LDC, kk, 16 * wave, lane), frow(cp.sKg, LDK, 16 * sb, kk, lane),
+                     acc);
+    const float bs = cp.sBeta[16 * sb + lr];
+    f32x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = 16 * sb + lr < 16 * wave + 4 * lq + i ? acc[i] * bs : 0.f;
+    store4(sC1 + (16 * sb + lr) * LDC + 16 * wave + 4 * lq, x);
+  }
+  lds_barrier();
+
+  // Y = dX X^T -> Y^T (sC2)
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < kend; kk += 32)
+      acc = mma_bf16(frag_tr(sC1, LDC, kk, 16 * wave, lane), frow(cp.sTm, LDC, 16 * jb, kk, lane),
+                     acc);
+    store4(sC2 + (16 * jb + lr) * LDC + 16 * wave + 4 * lq, acc);
+  }
+  lds_barrier();
+
+  // dA = -strict_lower(X^T Y) -> dA^T (sC1) and (Diag(beta) dA)^T (sC3)
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = k0m; kk < kChunk; kk += 32)
+      acc = mma_bf16(frag_tr(cp.sTm, LDC, kk, 16 * wave, lane), frow(sC2, LDC, 16 * jb, kk, lane),
+                     acc);
+    f32x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = 16 * jb + lr < 16 * wave + 4 * lq + i ? -acc[i] : 0.f;
+    store4(sC1 + (16 * jb + lr) * LDC + 16 * wave + 4 * lq, x);
+    store4(sC3 + (16 * jb + lr) * LDC + 16 * wave + 4 * lq, x * bt);
+  }
+  lds_barrier();
+
+  // d(beta Kg) = X^T dW + dA Ki;  dKi = dA^T (beta Kg) + dM^T Qg;  dQg += dM Ki
+  f32x4 dBk[NKB], dKi[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    f32x4 b = f32x4{0.f, 0.f, 0.f, 0.f}, ki = f32x4{0.f, 0.f, 0.f, 0.f}, qg = dQg[kb];
+    for (int kk = k0m; kk < kChunk; kk += 32) {
+      b = mma_bf16(frag_tr(cp.sTm, LDC, kk, 16 * wave, lane), frow(sDWT, LDC, 16 * kb, kk, lane), b);
+      ki = mma_bf16(frow(sC3, LDC, 16 * wave, kk, lane), frag_tr(cp.sKg, LDK, kk, 16 * kb, lane), ki);
+      ki = mma_bf16(frow(sDMT, LDC, 16 * wave, kk, lane), frag_tr(cp.sQg, LDK, kk, 16 * kb, lane), ki);
+    }
+    for (int kk = 0; kk < kend; kk += 32) {
+      const bf16x8 bKi = frag_tr(cp.sKi, LDK, kk, 16 * kb, lane);
+      b = mma_bf16(frag_tr(sC1, LDC, kk, 16 * wave, lane), bKi, b);
+      qg = mma_bf16(frag_tr(sDMT, LDC, kk, 16 * wave, lane), bKi, qg);
+    }
+    dBk[kb] = b;
+    dKi[kb] = ki;
+    dQg[kb] = qg;
+  }
+  lds_barrier();
+
+  // ---- gradients of k, q, beta, g ----------------------------------------------------
+  float* sGm = reinterpret_cast<float*>(smem + GL::oGm);   // dL/dG [64][LDEG] fp32
+  float* sRed = cp.sScr;                                    // [4][DK] + [kThreads / DK][DK]
+  bf16* dqout = static_cast<bf16*>(a.dq);
+  bf16* dkout = static_cast<bf16*>(a.dk);
+  f32x4 dbk = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int j = 16 * kb + lr;
+    const float egn = cp.sEgn[j];
+    float gn = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * lq + i;
+      const int64_t off = (c0 + min(r, n - 1)) * rowK + int64_t(h) * DK + j;
+      const float kf = r < n ? static_cast<float>(kin[off]) : 0.f;
+      const float qf = r < n ? static_cast<float>(qin[off]) : 0.f;
+      const float eg = cp.sEG[r * LDEG + j];
+      const float ieg = __builtin_amdgcn_rcpf(eg);
+      const float eh = egn * ieg;   // e^{G_n - G_r}
+      const float dkg = bt[i] * dBk[kb][i];
+      const float kg = kf * eg, ki = kf * ieg, kh = kf * eh, qg = a.scale * qf * eg;
+      dbk[i] += dBk[kb][i] * kg;
+      gn += dKh[kb][i] * kh;
+      sGm[r * LDEG + j] = dkg * kg + dQg[kb][i] * qg - dKi[kb][i] * ki - dKh[kb][i] * kh;
+      if (r < n) {
+        dkout[off] = static_cast<bf16>(dkg * eg + dKi[kb][i] * ieg + dKh[kb][i] * eh);
+        dqout[off] = static_cast<bf16>(a.scale * dQg[kb][i] * eg);
+      }
+    }
+    gn += __shfl_xor(gn, 16);
+    gn += __shfl_xor(gn, 32);
+    if (lq == 0) sRed[wave * DK + j] = gn;
+  }
+  sRed[4 * DK + dpart * DK + dj] = ddp;
+  // d beta: the V and the Kg terms, summed over this row's values / keys
+  {
+    f32x4 tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tot[i] = row_sum<16>(dbu[i] + dbk[i]);
+    if (lr == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * lq + i;
+        if (r < n) a.dbeta[(c0 + r) * a.H + h] = tot[i];
+      }
+    }
+  }
+  lds_barrier();
+
+  // dg: G_r = g_1 + ... + g_r and G_n = G_last, so dg_s = sum_{r >= s} dG_r + dG_n with
+  // dG_n = sum_r dKh Kh + d e^{G_n} e^{G_n}
+  if constexpr (DECAY != 2) {
+    constexpr int NPART = kThreads / DK, RPP = kChunk / NPART;
+    const int j = tid % DK, part = tid / DK;
+    float dd = 0.f;
+#pragma unroll
+    for (int p = 0; p < NPART; ++p) dd += sRed[4 * DK + p * DK + j];
+    const float dgn = sRed[j] + sRed[DK + j] + sRed[2 * DK + j] + sRed[3 * DK + j] +
+                      dd * cp.sEgn[j];
+    float own = 0.f;
+    for (int r = part * RPP; r < part * RPP + RPP; ++r) own += sGm[r * LDEG + j];
+    lds_barrier();
+    sRed[part * DK + j] = own;   // the dG_n partials are consumed above
+    lds_barrier();
+    float run = dgn;
+    for (int p = part + 1; p < NPART; ++p) run += sRed[p * DK + j];
+    for (int r = part * RPP + RPP - 1; r >= part * RPP; --r) {
+      run += sGm[r * LDEG + j];
+      if constexpr (DECAY == 0) {
+        if (r < n) a.dg[(c0 + r) * rowK + int64_t(h) * DK + j] = run;
+      } else {
+        sGm[r * LDEG + j] = run;
+      }
+    }
+    if constexpr (DECAY == 1) {
+      lds_barrier();
+      // one scalar decay per (token, head): the channel gradients summed
+      if (tid < kChunk && tid < n) {
+        float s = 0.f;
+        for (int jj = 0; jj < DK; ++jj) s += sGm[tid * LDEG + jj];
+        a.dg[(c0 + tid) * a.H + h] = s;
+      }
+    }
+  }
+}
+
+// ====================================================================================
+// Launch
+// ====================================================================================
+
+template <int DK, int DECAY>
+static hipError_t launch_chain_k(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_chain_kernel<DK, kBwdChainBV, DECAY>), dim3(a.units * a.NV),
+                     dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_chain(int dk, const BwdArgs& a, hipStream_t stream) {
+  if (dk == 64) {
+    if (a.decay == 1) return launch_chain_k<64, 1>(a, stream);
+    if (a.decay == 2) return launch_chain_k<64, 2>(a, stream);
+    return launch_chain_k<64, 0>(a, stream);
+  }
+  if (a.decay == 1) return launch_chain_k<128, 1>(a, stream);
+  if (a.decay == 2) return launch_chain_k<128, 2>(a, stream);
+  return launch_chain_k<128, 0>(a, stream);
+}
+
+template <int DK, int DV>
+static hipError_t launch_grads_d(const BwdArgs& a, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(a.slots * a.H)), block(kThreads);
+  if (a.decay == 1)
+    hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, 1>), grid, block, 0, stream, a);
+  else if (a.decay == 2)
+    hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, 2>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, 0>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_grads(int dk, const BwdArgs& a, hipStream_t stream) {
+  if (dk == 64) return a.DV == 64 ? launch_grads_d<64, 64>(a, stream) : launch_grads_d<64, 128>(a, stream);
+  return a.DV == 64 ? launch_grads_d<128, 64>(a, stream) : launch_grads_d<128, 128>(a, stream);
+}
+
+}  // namespace kda

@@ -177,8 +177,9 @@ __device__ __forceinline__ void store_lower_blocks(const f32x4 (&acc)[5], f32x4 
   }
 }
 
-// Byte layout of the chunk-local tiles and scratch in LDS.
-template <typename Tin, int DK>
+// Byte layout of the chunk-local tiles and scratch in LDS.  KIT = false drops the
+// Ki^T copy (kernels that read transposed operands with ds_read_b64_tr_b16).
+template <typename Tin, int DK, bool KIT = true>
 struct ChunkLayout {
   using TC = typename Mfma<Tin>::TC;
   static constexpr bool kBf16 = sizeof(TC) == 2;
@@ -187,7 +188,7 @@ struct ChunkLayout {
   static constexpr int LDC = kChunk + PADC;         // [*][64] operand tiles
   static constexpr int LDF = kChunk + 4;            // fp32 [64][64] (A, inverse), 16 B rows
   static constexpr int LDX = kBf16 ? LDF : LDC;     // fp32 path: the inverse is the operand
-  static constexpr bool kKiT = kBf16;               // bf16 keeps Ki^T (16 B fragments)
+  static constexpr bool kKiT = kBf16 && KIT;        // bf16 keeps Ki^T (16 B fragments)
   static constexpr int CG = DK / 4, RG = kThreads / CG, RPG = kChunk / RG;
 
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
@@ -211,17 +212,19 @@ struct ChunkLayout {
 };
 
 // Computes one chunk's tiles into LDS.  Holds the next chunk's inputs in registers.
-template <typename Tin, int DK>
+template <typename Tin, int DK, bool KIT = true>
 struct ChunkProducer {
   using M = Mfma<Tin>;
   using TC = typename M::TC;
   using raw4 = typename M::raw4;
-  using L = ChunkLayout<Tin, DK>;
+  using L = ChunkLayout<Tin, DK, KIT>;
+  static constexpr int LDEG = DK + 4;   // row stride of the optional fp32 e^{G} tile
   static constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF, LDX = L::LDX;
   static constexpr int CG = L::CG, RG = L::RG, RPG = L::RPG;
 
   TC *sKg, *sQg, *sKi, *sKiT, *sTm, *sM;
   float *sA, *sX, *sScr, *sBeta, *sEgn;
+  float* sEG = nullptr;     // fp32 e^{G_r} tile [64][LDEG] (factors<DECAY, true> only)
   const float* g;
   const Tin* k;
   const Tin* q;
@@ -320,7 +323,8 @@ struct ChunkProducer {
     }
   }
 
-  template <int DECAY>
+  // KEEP_EG: also write e^{G_r} (fp32) into sEG.
+  template <int DECAY, bool KEEP_EG = false>
   __device__ __forceinline__ void factors(int n, bool has_next, int64_t c1, int n1) {
     if (flags & kNormK) normalise_keys();
     if constexpr (DECAY == 1) {
@@ -370,6 +374,7 @@ struct ChunkProducer {
       const f32x4 q4 = ok ? widen(qr[i]) * scale : f32x4{0.f, 0.f, 0.f, 0.f};
       store4(sKg + (rg * RPG + i) * LDK + j0, k4 * run);
       store4(sQg + (rg * RPG + i) * LDK + j0, q4 * run);
+      if constexpr (KEEP_EG) *reinterpret_cast<f32x4*>(sEG + (rg * RPG + i) * LDEG + j0) = run;
     }
     // backward pass: e^{-G_r} = (alpha_{r+1} ... alpha_n) / e^{G_n}  ->  Ki, Ki^T
     run = cs * f32x4{__builtin_amdgcn_rcpf(egn[0]), __builtin_amdgcn_rcpf(egn[1]),

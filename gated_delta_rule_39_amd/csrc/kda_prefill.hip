@@ -40,107 +40,10 @@
 
 #include "kda_chunk.h"
 #include "kda_launch.h"
+#include "kda_tiles.h"
 #include "kda_wy.h"
 
-
 namespace kda {
-
-
-__device__ __forceinline__ void unit_bounds(const PrefillArgs& a, int unit, int& n_seq, int& h,
-                                            int64_t& bos, int64_t& eos) {
-  n_seq = unit / a.H;
-  h = unit % a.H;
-  if (a.cu_seqlens) {
-    bos = a.cu_seqlens[n_seq];
-    eos = a.cu_seqlens[n_seq + 1];
-  } else {
-    bos = static_cast<int64_t>(n_seq) * a.T;
-    eos = bos + a.T;
-  }
-}
-
-// Workgroup id -> (unit, role index) with W workgroups per unit.  With xcd_remap the
-// W workgroups of a unit get ids congruent modulo 8 (the same XCD).
-__device__ __forceinline__ void unit_role(int x, int W, int units, int xcd_remap, int& unit,
-                                          int& role) {
-  if (xcd_remap) {
-    const int xcd = x & 7, y = x >> 3;
-    unit = xcd * (units >> 3) + y / W;
-    role = y % W;
-  } else {
-    unit = x / W;
-    role = x % W;
-  }
-}
-
-// S^T accumulator tiles of a value tile: wave w owns key blocks
-// [w * KPW, (w + 1) * KPW) for every 16-row value block, KPW = DK / 64.
-template <int DK, int BV>
-struct StateTiles {
-  static constexpr int NVB = BV / 16;
-  static constexpr int KPW = DK / 64;
-  static constexpr int NST = KPW * NVB;
-  static __device__ __forceinline__ int kb(int wave, int s) { return wave * KPW + s / NVB; }
-  static __device__ __forceinline__ int vb(int s) { return s % NVB; }
-};
-
-// Load the initial state tile (or zeros) into accumulators and its snapshot into LDS.
-template <int DK, int BV, int LDK, typename TC, int NST>
-__device__ __forceinline__ void load_state(f32x4 (&sacc)[NST], const float* s0, int64_t st_base,
-                                           int v0, TC* sS, int wave, int lane) {
-  using ST = StateTiles<DK, BV>;
-  static_assert(NST == ST::NST, "state tile count");
-  const int lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-  for (int s = 0; s < ST::NST; ++s) {
-    const int kb = ST::kb(wave, s), vb = ST::vb(s);
-    const int vrow = v0 + 16 * vb + lr, kcol = 16 * kb + 4 * lq;
-    sacc[s] = s0 ? *reinterpret_cast<const f32x4*>(s0 + st_base + int64_t(vrow) * DK + kcol)
-                 : f32x4{0.f, 0.f, 0.f, 0.f};
-    store4(sS + (16 * vb + lr) * LDK + kcol, sacc[s]);
-  }
-}
-
-template <int DK, int BV, int NST>
-__device__ __forceinline__ void store_state(const f32x4 (&sacc)[NST], float* s1, int64_t st_base,
-                                            int v0, int wave, int lane) {
-  using ST = StateTiles<DK, BV>;
-  static_assert(NST == ST::NST, "state tile count");
-  const int lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-  for (int s = 0; s < ST::NST; ++s) {
-    const int kb = ST::kb(wave, s), vb = ST::vb(s);
-    const int vrow = v0 + 16 * vb + lr, kcol = 16 * kb + 4 * lq;
-    *reinterpret_cast<f32x4*>(s1 + st_base + int64_t(vrow) * DK + kcol) = sacc[s];
-  }
-}
-
-// The value tile of one chunk in accumulator layout (row block = wave), loaded ahead
-// as raw bits: bf16 in the low half of a 32-bit register, or fp32.
-template <typename Tin, int NVB>
-struct ValueRegs {
-  uint32_t r[NVB][4];
-  __device__ __forceinline__ void load(const Tin* v, int64_t c0, int n, int32_t H, int h,
-                                       int32_t DV, int v0, int wave, int lane) {
-    const Tin* vb0 = v + (c0 * H + h) * DV + v0;
-    const uint32_t rowV = static_cast<uint32_t>(H) * DV;
-    const int lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t off =
-            static_cast<uint32_t>(min(16 * wave + 4 * lq + i, n - 1)) * rowV + 16 * vb + lr;
-        if constexpr (sizeof(Tin) == 2)
-          r[vb][i] = *reinterpret_cast<const unsigned short*>(vb0 + off);
-        else
-          r[vb][i] = *reinterpret_cast<const uint32_t*>(vb0 + off);
-      }
-  }
-  __device__ __forceinline__ float f32(int vb, int i) const {
-    return sizeof(Tin) == 2 ? __uint_as_float(r[vb][i] << 16) : __uint_as_float(r[vb][i]);
-  }
-};
 
 // ====================================================================================
 // Fused kernel
@@ -161,7 +64,10 @@ struct FusedLayout {
 
 // DECAY: 0 = g per key channel (KDA), 1 = one g per token and head (Gated DeltaNet),
 // 2 = no decay (DeltaNet).  Only the gate loads differ.
-template <typename Tin, int DK, int BV, int DECAY>
+// STATES (the backward's forward sweep): instead of o, write the state at the start of
+// every chunk, bf16, to a.workspace as [slot][H][d_v][d_k] with
+// slot = chunk_slot_base(sequence) + chunk index (kda_tiles.h).
+template <typename Tin, int DK, int BV, int DECAY, bool STATES = false>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   using CP = ChunkProducer<Tin, DK>;
   using M = typename CP::M;
@@ -208,6 +114,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const int64_t c1 = c0 + kChunk;
     const bool has_next = c1 < eos;
     const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
+    if constexpr (STATES) {
+      const int64_t slot = chunk_slot_base(n_seq, bos) + (c0 - bos) / kChunk;
+      store_state_bf16<DK, BV>(sacc, reinterpret_cast<bf16*>(a.workspace),
+                               ((slot * a.H + h) * a.DV) * DK, v0, wave, lane);
+    }
 
     cp.template factors<DECAY>(n, has_next, c1, n1);
     cp.products();
@@ -269,10 +180,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         for (int kk = 0; kk < kend; kk += M::KSTEP)
           acc = M::mma(frag_rows<M>(cp.sM, LDC, 16 * wave, kk, lane),
                        frag_rows<M>(sET, LDC, 16 * vb, kk, lane), acc);
+        if constexpr (!STATES) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * wave + 4 * lq + i;
-          if (r < n) o[((c0 + r) * a.H + h) * a.DV + v0 + 16 * vb + lr] = from_f32<Tin>(acc[i]);
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * wave + 4 * lq + i;
+            if (r < n) o[((c0 + r) * a.H + h) * a.DV + v0 + 16 * vb + lr] = from_f32<Tin>(acc[i]);
+          }
         }
       }
 #pragma unroll
@@ -1045,6 +958,31 @@ static hipError_t launch_fused_d(int dk, int bv, const PrefillArgs& a, hipStream
 hipError_t launch_prefill(int dtype, int dk, int bv, const PrefillArgs& a, hipStream_t stream) {
   if (dtype == 1) return launch_fused_d<bf16>(dk, bv, a, stream);
   return launch_fused_d<float>(dk, bv, a, stream);
+}
+
+template <int DK, int DECAY>
+static hipError_t launch_states_dk(int bv, const PrefillArgs& a, hipStream_t stream) {
+  const dim3 grid(a.units * a.NV), block(kThreads);
+  if (bv == 64)
+    hipLaunchKernelGGL((prefill_kernel<bf16, DK, 64, DECAY, true>), grid, block, 0, stream, a);
+  else if (bv == 32)
+    hipLaunchKernelGGL((prefill_kernel<bf16, DK, 32, DECAY, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<bf16, DK, 16, DECAY, true>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DECAY>
+static hipError_t launch_states_t(int dk, int bv, const PrefillArgs& a, hipStream_t stream) {
+  return dk == 64 ? launch_states_dk<64, DECAY>(bv, a, stream)
+                  : launch_states_dk<128, DECAY>(bv, a, stream);
+}
+
+// Forward sweep of the backward (bf16): chunk-start states into a.workspace, no o.
+hipError_t launch_prefill_states(int dk, int bv, const PrefillArgs& a, hipStream_t stream) {
+  if (a.decay == 1) return launch_states_t<1>(dk, bv, a, stream);
+  if (a.decay == 2) return launch_states_t<2>(dk, bv, a, stream);
+  return launch_states_t<0>(dk, bv, a, stream);
 }
 
 size_t prefill_coop_workspace_bytes(int dk, int dv, int units, int R) {

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 /* dtype of q, k, v and o.  g, beta and all states are always fp32. */
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
@@ -82,7 +82,8 @@ enum {
   KDA_ERR_UNSUPPORTED = 3,  /* d_k or d_v not in {64, 128}, unknown decay kind or
                                prologue flag                                        */
   KDA_ERR_BAD_DTYPE = 4,    /* dtype not KDA_F32 / KDA_BF16                         */
-  KDA_ERR_HIP = 5           /* kernel launch failed (hipGetLastError)              */
+  KDA_ERR_HIP = 5,          /* kernel launch failed (hipGetLastError)              */
+  KDA_ERR_WORKSPACE = 6     /* workspace NULL or smaller than the call needs       */
 };
 
 /* Returns KDA_ABI_VERSION of the built library. */
@@ -197,6 +198,45 @@ int kda_decode_step_ex(int dtype, int decay, int flags,
                        float* state, void* o,
                        int32_t N, int32_t H, int32_t d_k, int32_t d_v,
                        float scale, hipStream_t stream);
+
+/*
+ * kda_backward -- gradients of kda_prefill_ex (training).  The pages tie the chunkwise
+ * form to training ("Kimi Delta Attention Technical Deep Dive", "Systems and
+ * implementation tradeoffs" -> "Training") and give no gradient formulas; this is the
+ * exact gradient of the recurrence of "Kimi Delta Attention: The Linear Attention
+ * Behind Kimi K2 and Qwen3", "How Kimi Delta Attention works step by step", for a
+ * loss whose gradients with respect to o and to the final state are given.
+ *   dtype: KDA_BF16 only (KDA_F32 returns KDA_ERR_UNSUPPORTED); flags must be 0.
+ *   Inputs q, k, v, g, beta, cu_seqlens, N, B, T, H, d_k, d_v, scale, initial_state:
+ *     exactly as passed to the forward call.
+ *   dout : [B, T, H, d_v] bf16, dL/do.
+ *   dfinal_state : [N, H, d_v, d_k] fp32, dL/d(final state), or NULL (zero).
+ *   Outputs (caller-allocated, written for every token row of a sequence):
+ *     dq, dk : [B, T, H, d_k] bf16      dv : [B, T, H, d_v] bf16
+ *     dg     : layout of g, fp32 (not read or written with KDA_DECAY_NONE; may be NULL)
+ *     dbeta  : [B, T, H] fp32
+ *     dinitial_state : [N, H, d_v, d_k] fp32, dL/d(initial state), or NULL (not written).
+ *   workspace: device memory of at least kda_backward_workspace_bytes() bytes (else
+ *     KDA_ERR_WORKSPACE); it receives the state at every chunk start and the state
+ *     gradient at every chunk end (bf16), and is owned by the library during the call.
+ * N = 0 is a no-op returning KDA_OK.  The keys must be unit rows as for the forward.
+ */
+int kda_backward(int dtype, int decay, int flags,
+                 const void* q, const void* k, const void* v,
+                 const float* g, const float* beta,
+                 const int32_t* cu_seqlens,
+                 int32_t N, int32_t B, int64_t T, int32_t H, int32_t d_k, int32_t d_v,
+                 float scale, const float* initial_state,
+                 const void* dout, const float* dfinal_state,
+                 void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                 float* dinitial_state,
+                 void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Workspace bytes kda_backward needs: 2 * (T_total / 64 + N + 1) * H * d_v * d_k * 2
+ * (0 for unsupported arguments).  Host-only. */
+size_t kda_backward_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_t H,
+                                    int32_t d_k, int32_t d_v);
 
 #ifdef __cplusplus
 }

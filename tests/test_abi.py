@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"kda_prefill", "kda_decode_step", "kda_abi_version", "kda_status_string",
             "kda_prefill_workspace_bytes", "kda_prefill_plan", "kda_prefill_coop_plan",
-            "kda_prefill_ex", "kda_decode_step_ex"} <= set(names)
+            "kda_prefill_ex", "kda_decode_step_ex", "kda_backward",
+            "kda_backward_workspace_bytes"} <= set(names)
     L = kda.lib()
     for name in names:
         assert hasattr(L, name), f"{name} declared in kda.h but not exported"
@@ -34,8 +35,8 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = kda.lib()
-    assert L.kda_abi_version() == 3
-    for code in range(6):
+    assert L.kda_abi_version() == 4
+    for code in range(7):
         s = L.kda_status_string(code).decode()
         assert s.startswith("KDA")
     assert "unknown" in L.kda_status_string(99).decode()
@@ -136,3 +137,30 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError, match="device"):
         kda.prefill(x, x, x, x, torch.zeros(1, 4, 1))
+
+
+def backward_status(dtype=1, decay=0, flags=0, N=1, B=1, T=64, H=2, dk=64, dv=64, cu=None,
+                    dq=FAKE, ws=FAKE, ws_bytes=1 << 40, g=FAKE, dg=FAKE):
+    L = kda.lib()
+    return L.kda_backward(dtype, decay, flags, FAKE, FAKE, FAKE, g, FAKE, cu, N, B, T, H, dk, dv,
+                          0.125, None, FAKE, None, dq, FAKE, FAKE, dg, FAKE, None, ws, ws_bytes,
+                          None)
+
+
+def test_backward_validation_codes():
+    assert backward_status(dtype=7) == 4                # bad dtype
+    assert backward_status(dtype=0) == 3                # fp32 backward: unsupported
+    assert backward_status(decay=5) == 3
+    assert backward_status(flags=1) == 3                # prologue flags: unsupported
+    assert backward_status(dk=96) == 3
+    assert backward_status(N=2, B=1) == 2               # N != B without cu_seqlens
+    assert backward_status(dq=None) == 1
+    assert backward_status(g=None) == 1                 # per-channel decay needs g and dg
+    assert backward_status(dg=None) == 1
+    assert backward_status(ws=None) == 6                # no workspace
+    assert backward_status(ws_bytes=16) == 6            # too small
+    assert backward_status(N=0, B=0) == 0               # nothing to do
+    L = kda.lib()
+    # two bf16 buffers of (T_total / 64 + N + 1) chunk slots of d_v x d_k per head
+    assert L.kda_backward_workspace_bytes(1, 3, 1000, 4, 128, 64) == 2 * (1000 // 64 + 4) * 4 * 64 * 128 * 2
+    assert L.kda_backward_workspace_bytes(0, 3, 1000, 4, 128, 64) == 0
