@@ -236,13 +236,34 @@ int kda_decode_step(int dtype, const void* q, const void* k, const void* v, cons
                             d_v, scale, stream);
 }
 
+namespace {
+// Backward workspace: [producer/consumer ring of the forward sweep, when that kernel
+// applies (d_k = d_v = 128, two consumers) | chunk states | state gradients].
+struct BwdPlan {
+  CoopPlan coop;
+  size_t ring = 0, states = 0;
+  size_t total() const { return ring + 2 * states; }
+};
+BwdPlan bwd_plan(int32_t N, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v) {
+  BwdPlan b;
+  const int64_t units = static_cast<int64_t>(N) * H;
+  b.states = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H * d_v * d_k * 2);
+  const CoopPlan p = coop_plan(KDA_BF16, units, d_v, cu_count());
+  if (p.ok() && d_k == 128 && d_v == 128 && p.NC == 2 && units <= (1 << 24)) {
+    b.coop = p;
+    b.ring = (kda::prefill_coop_workspace_bytes(d_k, d_v, static_cast<int>(units), p.R) + 255) &
+             ~size_t(255);
+  }
+  return b;
+}
+}  // namespace
+
 size_t kda_backward_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_t H, int32_t d_k,
                                     int32_t d_v) {
   if (dtype != KDA_BF16 || N <= 0 || T_total < 0 || H <= 0 || !supported_dim(d_k) ||
       !supported_dim(d_v))
     return 0;
-  const int64_t slots = kda::chunk_slots_host(T_total, N);
-  return static_cast<size_t>(2 * slots * H * d_v * d_k * 2);
+  return bwd_plan(N, T_total, H, d_k, d_v).total();
 }
 
 int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, const void* v,
@@ -269,11 +290,11 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
   if (tot > 0 && (!q || !k || !v || (decay != KDA_DECAY_NONE && (!g || !dg)) || !beta || !dout ||
                   !dq || !dk || !dv || !dbeta))
     return KDA_ERR_NULL_ARG;
-  const size_t need = kda_backward_workspace_bytes(dtype, N, tot, H, d_k, d_v);
-  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  const BwdPlan plan = bwd_plan(N, tot, H, d_k, d_v);
+  if (workspace == nullptr || workspace_bytes < plan.total()) return KDA_ERR_WORKSPACE;
   if (tot == 0 && !dinitial_state) return KDA_OK;
-  unsigned char* states = static_cast<unsigned char*>(workspace);
-  unsigned char* dstates = states + need / 2;
+  unsigned char* states = static_cast<unsigned char*>(workspace) + plan.ring;
+  unsigned char* dstates = states + plan.states;
   const int cus = cu_count();
   if (tot > 0) {
     kda::PrefillArgs a{};
@@ -291,10 +312,22 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
     a.xcd_remap = (units % 8 == 0) ? 1 : 0;
     a.scale = scale;
     a.decay = decay;
-    a.workspace = states;
-    const int bv = choose_bv(KDA_BF16, static_cast<int32_t>(units), d_k, d_v, cus);
-    a.NV = d_v / bv;
-    if (kda::launch_prefill_states(d_k, bv, a, stream) != hipSuccess) return KDA_ERR_HIP;
+    a.chunk_states = states;
+    bool done = false;
+    if (plan.ring > 0) {
+      a.workspace = static_cast<unsigned char*>(workspace);
+      a.NC = plan.coop.NC;
+      a.NP = plan.coop.NP;
+      a.R = plan.coop.R;
+      done = kda::launch_prefill_coop_states(a, stream) == hipSuccess;
+      if (!done) (void)hipGetLastError();   // not launchable as one resident grid
+    }
+    if (!done) {
+      a.workspace = nullptr;
+      const int bv = choose_bv(KDA_BF16, static_cast<int32_t>(units), d_k, d_v, cus);
+      a.NV = d_v / bv;
+      if (kda::launch_prefill_states(d_k, bv, a, stream) != hipSuccess) return KDA_ERR_HIP;
+    }
   }
   kda::BwdArgs b{};
   b.q = q;

@@ -33,6 +33,7 @@ struct PrefillArgs {
   int32_t decay;              // 0: g per key channel, 1: one g per (token, head), 2: none
   int32_t flags;              // prologue flags (kda_device.h: kNormK, kBetaLogit, kGateLogit)
   float scale;
+  void* chunk_states;         // STATES instantiations: bf16 state at every chunk start
 };
 
 // Arguments of the backward kernels (bf16 inputs; validated by the C ABI).
@@ -65,6 +66,9 @@ struct BwdArgs {
 // Backward: the forward sweep that writes the chunk-start states (fused kernel, bf16,
 // a.workspace = states), then the reverse chain and the chunk-parallel gradients.
 hipError_t launch_prefill_states(int dk, int bv, const PrefillArgs& a, hipStream_t stream);
+// The same from the producer/consumer kernel (d_k = d_v = 128, two consumers of 64 value
+// columns; a.o may be nullptr); a.workspace as for launch_prefill_coop.
+hipError_t launch_prefill_coop_states(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_backward_chain(int dk, const BwdArgs& a, hipStream_t stream);
 hipError_t launch_backward_grads(int dk, const BwdArgs& a, hipStream_t stream);
 constexpr int kBwdChainBV = 16;   // value rows per reverse-chain workgroup

@@ -65,7 +65,7 @@ struct FusedLayout {
 // DECAY: 0 = g per key channel (KDA), 1 = one g per token and head (Gated DeltaNet),
 // 2 = no decay (DeltaNet).  Only the gate loads differ.
 // STATES (the backward's forward sweep): instead of o, write the state at the start of
-// every chunk, bf16, to a.workspace as [slot][H][d_v][d_k] with
+// every chunk, bf16, to a.chunk_states as [slot][H][d_v][d_k] with
 // slot = chunk_slot_base(sequence) + chunk index (kda_tiles.h).
 template <typename Tin, int DK, int BV, int DECAY, bool STATES = false>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
     if constexpr (STATES) {
       const int64_t slot = chunk_slot_base(n_seq, bos) + (c0 - bos) / kChunk;
-      store_state_bf16<DK, BV>(sacc, reinterpret_cast<bf16*>(a.workspace),
+      store_state_bf16<DK, BV>(sacc, static_cast<bf16*>(a.chunk_states),
                                ((slot * a.H + h) * a.DV) * DK, v0, wave, lane);
     }
 
@@ -293,7 +293,9 @@ struct WySplitLayout {
 // e^{G_n}) straight from the ring slot into registers, one chunk ahead.  The slot of
 // chunk c is released after chunk c's end-of-chunk barrier, when every wave has used
 // those registers.
-template <int DK, int DV>
+// STATES: also write the state at every chunk start (bf16, as prefill_kernel's STATES),
+// and write o only when a.o is set.
+template <int DK, int DV, bool STATES = false>
 __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned char* smem,
                                                  __amdgpu_buffer_rsrc_t rr, int* ready,
                                                  int* done, int* abort_word, int role,
@@ -414,9 +416,24 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   // ring slot indices of chunks c - 1, c, c + 1, c + 2
   int sp = 0, s0 = 0, s1 = 1 % a.R, s2 = 2 % a.R;
   const int t_own = wave >> 1, h_own = wave & 1;
+  const bool write_o = !STATES || a.o != nullptr;
+  [[maybe_unused]] const int64_t slot0 = chunk_slot_base(n_seq, bos);
   for (int c = 0; ok && c < nch; ++c) {
     const int64_t c0 = bos + int64_t(c) * kChunk;
     const bool has_next = c + 1 < nch, has2 = c + 2 < nch;
+    if constexpr (STATES) {
+      bf16* cs = static_cast<bf16*>(a.chunk_states) + ((slot0 + c) * a.H + h) * DV * DK;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+          const f32x4 x = S[b][vt];
+          *reinterpret_cast<bf16x4*>(cs + int64_t(v0 + 16 * vt + lr) * DK + 32 * wave + 16 * b +
+                                     4 * lq) =
+              bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                     static_cast<bf16>(x[3])};
+        }
+    }
     // every wave has used chunk c - 1's operands: its slot is free
     if (tid == 0 && c > 0) __hip_atomic_fetch_add(done + sp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int fv = 0;
@@ -466,7 +483,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) eb[t][vt] = eb_at(t, vt);
     // the previous chunk's output rows (a full chunk), from this wave's LDS rows
-    if (c > 0) store_rows(c0 - kChunk, kChunk);
+    if (c > 0 && write_o) store_rows(c0 - kChunk, kChunk);
     // O = Qg S^T + M E (token block w reads E blocks <= w: K step 1 only for w >= 2)
 #pragma unroll
     for (int j = 0; j < KS; ++j)
@@ -511,7 +528,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   }
 
   // the last chunk's output rows (written before the loop's last barrier)
-  if (ok && nch > 0) {
+  if (ok && nch > 0 && write_o) {
     const int64_t cl = bos + int64_t(nch - 1) * kChunk;
     store_rows(cl, static_cast<int>(eos - cl));
   }
@@ -538,8 +555,10 @@ struct WyLds {
 // Per unit: NC consumers of 4 * VBW value columns (wave w of consumer r owns columns
 // 4 VBW r + VBW w .. +VBW) and NP producers (producer p takes chunks p, p + NP, ...).
 // DECAY as for prefill_kernel.
-template <int DK, int DV, int VBW, int DECAY>
+// STATES: see wy_consume_split (d_k = 128 with 16-column waves only).
+template <int DK, int DV, int VBW, int DECAY, bool STATES = false>
 __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) {
+  static_assert(!STATES || (DK == 128 && VBW == 16), "chunk states from the split consumer only");
   using PR = WyProducer<DK, DV>;
   using SL = WySlot<DK, DV>;
   using PL = WyProducerLayout<DK, DV>;
@@ -653,8 +672,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
 
   // ================================== consumer =====================================
   if constexpr (DK == 128 && VBW == 16) {
-    wy_consume_split<DK, DV>(a, smem, rr, ready, done, abort_word, role, n_seq, h, bos, eos, nch,
-                             tid, wave, lane);
+    wy_consume_split<DK, DV, STATES>(a, smem, rr, ready, done, abort_word, role, n_seq, h, bos,
+                                     eos, nch, tid, wave, lane);
     return;
   }
   const int vw0 = role * 4 * VBW + VBW * wave;     // this wave's first value column
@@ -991,7 +1010,7 @@ size_t prefill_coop_workspace_bytes(int dk, int dv, int units, int R) {
   return dv == 64 ? coop_workspace_bytes<128, 64>(units, R) : coop_workspace_bytes<128, 128>(units, R);
 }
 
-template <int DK, int DV, int VBW, int DECAY>
+template <int DK, int DV, int VBW, int DECAY, bool STATES = false>
 static hipError_t launch_wy_k(const PrefillArgs& a, hipStream_t stream) {
   const int nwords = static_cast<int>((kWsHeader + coop_flags_bytes(a.units, a.R)) / 4);
   hipLaunchKernelGGL(coop_reset_kernel, dim3((nwords + 255) / 256), dim3(256), 0, stream,
@@ -1000,7 +1019,8 @@ static hipError_t launch_wy_k(const PrefillArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   PrefillArgs arg = a;
   void* params[] = {&arg};
-  const void* kernel = reinterpret_cast<const void*>(&prefill_wy_kernel<DK, DV, VBW, DECAY>);
+  const void* kernel =
+      reinterpret_cast<const void*>(&prefill_wy_kernel<DK, DV, VBW, DECAY, STATES>);
   return hipLaunchCooperativeKernel(kernel, dim3(a.units * (a.NC + a.NP)), dim3(kThreads), params,
                                     0, stream);
 }
@@ -1023,6 +1043,14 @@ hipError_t launch_prefill_coop(int dk, const PrefillArgs& a, hipStream_t stream)
   }
   if (a.DV == 64) return launch_wy_t<128, 64, 16>(a, stream);
   return vbw == 32 ? launch_wy_t<128, 128, 32>(a, stream) : launch_wy_t<128, 128, 16>(a, stream);
+}
+
+// Producer/consumer kernel with chunk states (d_k = d_v = 128, a.NC = 2).
+hipError_t launch_prefill_coop_states(const PrefillArgs& a, hipStream_t stream) {
+  if (a.DV != 128 || a.NC != 2) return hipErrorInvalidValue;
+  if (a.decay == 1) return launch_wy_k<128, 128, 16, 1, true>(a, stream);
+  if (a.decay == 2) return launch_wy_k<128, 128, 16, 2, true>(a, stream);
+  return launch_wy_k<128, 128, 16, 0, true>(a, stream);
 }
 
 }  // namespace kda
