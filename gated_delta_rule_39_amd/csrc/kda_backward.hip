@@ -209,8 +209,12 @@ struct GradLayout {
   static constexpr size_t oDWT = a1, oDMT = a1 + tW;
   static constexpr size_t oCC1 = a2, oCC2 = a2 + tC, oCC3 = CL::oM;
   static_assert(oDMT + tC <= a1end && oCC2 + tC <= a2end, "chunk tiles overflow");
-  static constexpr size_t oGm = a1;                               // fp32 [64][LDEG]
-  static_assert(oGm + size_t(kChunk) * LDEG * 4 <= a1end, "dG tile overflow");
+  // gradients: raw k, q tiles (then dk, dq) and the reduction scratch
+  static constexpr size_t tK = size_t(kChunk) * LDK * 2;
+  static constexpr size_t oK = a1, oQ = a1 + tK;
+  static constexpr size_t oRed = a2;                              // fp32 [8 + NPART][DK]
+  static_assert(oQ + tK <= a1end, "k/q tiles overflow");
+  static_assert(oRed + size_t(8 + kThreads / DK) * DK * 4 <= a2end, "reduction overflow");
   static_assert(kBytes <= kLds, "LDS budget exceeded");
 };
 
@@ -310,23 +314,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       for (int e = 0; e < 8; ++e) p[e] = static_cast<bf16>(static_cast<float>(dh[e]) * cp.sEgn[c8 + e]);
       *reinterpret_cast<bf16x8*>(sP + r * LDK + c8) = p;
     }
-    f32x4 vreg[VS / 16];
-#pragma unroll
-    for (int vb = 0; vb < VS / 16; ++vb) {
-      f32x4 x, d;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * lq + i;
-        const uint32_t off = static_cast<uint32_t>(min(r, n - 1)) * rowV + v0 + 16 * vb + lr;
-        const int64_t base = (c0 * a.H + h) * DV;
-        x[i] = r < n ? static_cast<float>(vin[base + off]) : 0.f;
-        d[i] = r < n ? static_cast<float>(dout[base + off]) : 0.f;
+    // V and dO slices, one 16-byte piece of each per thread, into V^T and dO^T
+    static_assert(kChunk * VS / 8 == kThreads, "one piece per thread");
+    {
+      const int r = tid / (VS / 8), c8 = 8 * (tid % (VS / 8));
+      bf16x8 xv = {}, xd = {};
+      if (r < n) {
+        const int64_t off = (c0 + r) * rowV + int64_t(h) * DV + v0 + c8;
+        xv = *reinterpret_cast<const bf16x8*>(vin + off);
+        xd = *reinterpret_cast<const bf16x8*>(dout + off);
       }
-      vreg[vb] = x;
-      store4(sVT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, x);
-      store4(sDOT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, d);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sVT[(c8 + e) * LDC + r] = xv[e];
+        sDOT[(c8 + e) * LDC + r] = xd[e];
+      }
     }
     lds_barrier();
+    f32x4 vreg[VS / 16];   // V in accumulator layout (rows of this wave)
+#pragma unroll
+    for (int vb = 0; vb < VS / 16; ++vb)
+      vreg[vb] = widen(*reinterpret_cast<const bf16x4*>(sVT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq));
 
     // R' = beta (V - Kg H) -> R'^T;  dE = Ki P + M^T dO -> dE^T
 #pragma unroll
@@ -476,11 +484,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   lds_barrier();
 
   // ---- gradients of k, q, beta, g ----------------------------------------------------
-  float* sGm = reinterpret_cast<float*>(smem + GL::oGm);   // dL/dG [64][LDEG] fp32
-  float* sRed = cp.sScr;                                    // [4][DK] + [kThreads / DK][DK]
-  bf16* dqout = static_cast<bf16*>(a.dq);
-  bf16* dkout = static_cast<bf16*>(a.dk);
+  // the chunk's raw k and q (bf16, exact) into LDS; each element's gradient then
+  // replaces it in place (one owner per element), and the rows leave as 16-byte stores
+  bf16* sK = reinterpret_cast<bf16*>(smem + GL::oK);
+  bf16* sQ = reinterpret_cast<bf16*>(smem + GL::oQ);
+  for (int i = tid; i < kChunk * DK / 8; i += kThreads) {
+    const int r = i / (DK / 8), c8 = 8 * (i % (DK / 8));
+    bf16x8 kv = {}, qv = {};
+    if (r < n) {
+      const int64_t off = (c0 + r) * rowK + int64_t(h) * DK + c8;
+      kv = *reinterpret_cast<const bf16x8*>(kin + off);
+      qv = *reinterpret_cast<const bf16x8*>(qin + off);
+    }
+    *reinterpret_cast<bf16x8*>(sK + r * LDK + c8) = kv;
+    *reinterpret_cast<bf16x8*>(sQ + r * LDK + c8) = qv;
+  }
+  lds_barrier();
+
+  // per element: dk, dq, and dL/dG = dKg Kg + dQg Qg - dKi Ki - dKh Kh, summed over the
+  // rows at or below it within this wave's token block (suffix); the block totals, the
+  // dG_n partials and the d e^{G_n} partials go to LDS
+  float* sRed = reinterpret_cast<float*>(smem + GL::oRed);   // [4][DK] [4][DK] [NPART][DK]
+  constexpr int NPART = kThreads / DK;
   f32x4 dbk = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 gm[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const int j = 16 * kb + lr;
@@ -489,9 +516,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * wave + 4 * lq + i;
-      const int64_t off = (c0 + min(r, n - 1)) * rowK + int64_t(h) * DK + j;
-      const float kf = r < n ? static_cast<float>(kin[off]) : 0.f;
-      const float qf = r < n ? static_cast<float>(qin[off]) : 0.f;
+      const float kf = static_cast<float>(sK[r * LDK + j]);
+      const float qf = static_cast<float>(sQ[r * LDK + j]);
       const float eg = cp.sEG[r * LDEG + j];
       const float ieg = __builtin_amdgcn_rcpf(eg);
       const float eh = egn * ieg;   // e^{G_n - G_r}
@@ -499,17 +525,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       const float kg = kf * eg, ki = kf * ieg, kh = kf * eh, qg = a.scale * qf * eg;
       dbk[i] += dBk[kb][i] * kg;
       gn += dKh[kb][i] * kh;
-      sGm[r * LDEG + j] = dkg * kg + dQg[kb][i] * qg - dKi[kb][i] * ki - dKh[kb][i] * kh;
-      if (r < n) {
-        dkout[off] = static_cast<bf16>(dkg * eg + dKi[kb][i] * ieg + dKh[kb][i] * eh);
-        dqout[off] = static_cast<bf16>(a.scale * dQg[kb][i] * eg);
-      }
+      gm[kb][i] = dkg * kg + dQg[kb][i] * qg - dKi[kb][i] * ki - dKh[kb][i] * kh;
+      sK[r * LDK + j] = static_cast<bf16>(dkg * eg + dKi[kb][i] * ieg + dKh[kb][i] * eh);
+      sQ[r * LDK + j] = static_cast<bf16>(a.scale * dQg[kb][i] * eg);
     }
+    // suffix over this lane's four rows, then over the lane groups below it
+    gm[kb][2] += gm[kb][3];
+    gm[kb][1] += gm[kb][2];
+    gm[kb][0] += gm[kb][1];
+    const float t = gm[kb][0];
+    const float t1 = __shfl(t, (lane + 16) & 63), t2 = __shfl(t, (lane + 32) & 63),
+                t3 = __shfl(t, (lane + 48) & 63);
+    const float below = (lq < 3 ? t1 : 0.f) + (lq < 2 ? t2 : 0.f) + (lq < 1 ? t3 : 0.f);
+    gm[kb] += below;
     gn += __shfl_xor(gn, 16);
     gn += __shfl_xor(gn, 32);
-    if (lq == 0) sRed[wave * DK + j] = gn;
+    if (lq == 0) {
+      sRed[wave * DK + j] = t + below;          // this token block's column total
+      sRed[(4 + wave) * DK + j] = gn;
+    }
   }
-  sRed[4 * DK + dpart * DK + dj] = ddp;
+  sRed[(8 + dpart) * DK + dj] = ddp;
   // d beta: the V and the Kg terms, summed over this row's values / keys
   {
     f32x4 tot;
@@ -525,38 +561,56 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   }
   lds_barrier();
 
+  // dq, dk rows
+  {
+    bf16* dqout = static_cast<bf16*>(a.dq);
+    bf16* dkout = static_cast<bf16*>(a.dk);
+    for (int i = tid; i < kChunk * DK / 8; i += kThreads) {
+      const int r = i / (DK / 8), c8 = 8 * (i % (DK / 8));
+      if (r < n) {
+        const int64_t off = (c0 + r) * rowK + int64_t(h) * DK + c8;
+        *reinterpret_cast<bf16x8*>(dkout + off) = *reinterpret_cast<const bf16x8*>(sK + r * LDK + c8);
+        *reinterpret_cast<bf16x8*>(dqout + off) = *reinterpret_cast<const bf16x8*>(sQ + r * LDK + c8);
+      }
+    }
+  }
+
   // dg: G_r = g_1 + ... + g_r and G_n = G_last, so dg_s = sum_{r >= s} dG_r + dG_n with
   // dG_n = sum_r dKh Kh + d e^{G_n} e^{G_n}
   if constexpr (DECAY != 2) {
-    constexpr int NPART = kThreads / DK, RPP = kChunk / NPART;
-    const int j = tid % DK, part = tid / DK;
-    float dd = 0.f;
+    f32x4 rows = f32x4{0.f, 0.f, 0.f, 0.f};   // one scalar decay: sums over the channels
 #pragma unroll
-    for (int p = 0; p < NPART; ++p) dd += sRed[4 * DK + p * DK + j];
-    const float dgn = sRed[j] + sRed[DK + j] + sRed[2 * DK + j] + sRed[3 * DK + j] +
-                      dd * cp.sEgn[j];
-    float own = 0.f;
-    for (int r = part * RPP; r < part * RPP + RPP; ++r) own += sGm[r * LDEG + j];
-    lds_barrier();
-    sRed[part * DK + j] = own;   // the dG_n partials are consumed above
-    lds_barrier();
-    float run = dgn;
-    for (int p = part + 1; p < NPART; ++p) run += sRed[p * DK + j];
-    for (int r = part * RPP + RPP - 1; r >= part * RPP; --r) {
-      run += sGm[r * LDEG + j];
-      if constexpr (DECAY == 0) {
-        if (r < n) a.dg[(c0 + r) * rowK + int64_t(h) * DK + j] = run;
-      } else {
-        sGm[r * LDEG + j] = run;
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int j = 16 * kb + lr;
+      float dd = 0.f;
+#pragma unroll
+      for (int p = 0; p < NPART; ++p) dd += sRed[(8 + p) * DK + j];
+      float add = dd * cp.sEgn[j];
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        add += sRed[(4 + w2) * DK + j];
+        if (w2 > wave) add += sRed[w2 * DK + j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = gm[kb][i] + add;
+        if constexpr (DECAY == 0) {
+          const int r = 16 * wave + 4 * lq + i;
+          if (r < n) a.dg[(c0 + r) * rowK + int64_t(h) * DK + j] = v;
+        } else {
+          rows[i] += v;
+        }
       }
     }
     if constexpr (DECAY == 1) {
-      lds_barrier();
-      // one scalar decay per (token, head): the channel gradients summed
-      if (tid < kChunk && tid < n) {
-        float s = 0.f;
-        for (int jj = 0; jj < DK; ++jj) s += sGm[tid * LDEG + jj];
-        a.dg[(c0 + tid) * a.H + h] = s;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rows[i] = row_sum<16>(rows[i]);
+      if (lr == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * wave + 4 * lq + i;
+          if (r < n) a.dg[(c0 + r) * a.H + h] = rows[i];
+        }
       }
     }
   }
