@@ -238,16 +238,18 @@ int kda_decode_step(int dtype, const void* q, const void* k, const void* v, cons
 
 namespace {
 // Backward workspace: [producer/consumer ring of the forward sweep, when that kernel
-// applies (d_k = d_v = 128, two consumers) | chunk states | state gradients].
+// applies (d_k = d_v = 128, two consumers) | chunk states | state gradients | chunk
+// tiles of the reverse chain].
 struct BwdPlan {
   CoopPlan coop;
-  size_t ring = 0, states = 0;
-  size_t total() const { return ring + 2 * states; }
+  size_t ring = 0, states = 0, tiles = 0;
+  size_t total() const { return ring + 2 * states + tiles; }
 };
 BwdPlan bwd_plan(int32_t N, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v) {
   BwdPlan b;
   const int64_t units = static_cast<int64_t>(N) * H;
   b.states = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H * d_v * d_k * 2);
+  b.tiles = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H) * kda::chain_tile_bytes(d_k);
   const CoopPlan p = coop_plan(KDA_BF16, units, d_v, cu_count());
   if (p.ok() && d_k == 128 && d_v == 128 && p.NC == 2 && units <= (1 << 24)) {
     b.coop = p;
@@ -346,6 +348,7 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
   b.dbeta = dbeta;
   b.states = states;
   b.dstates = dstates;
+  b.tiles = dstates + plan.states;
   b.T = T;
   b.slots = slots;
   b.H = H;
@@ -356,7 +359,7 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
   b.xcd_remap = (units % 8 == 0) ? 1 : 0;
   b.decay = decay;
   b.scale = scale;
-  if (kda::launch_backward_chain(d_k, b, stream) != hipSuccess) return KDA_ERR_HIP;
+  if (kda::launch_backward_chain(d_k, b, stream) != hipSuccess) return KDA_ERR_HIP;   // tiles + chain
   if (tot > 0 && kda::launch_backward_grads(d_k, b, stream) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }

@@ -17,12 +17,14 @@
 // "Kimi Delta Attention: The Linear Attention Behind Kimi K2 and Qwen3", "How Kimi
 // Delta Attention works step by step".
 //
-// Three launches on one stream:
+// Four launches on one stream:
 //   1. forward sweep (prefill_kernel with STATES): the state at every chunk start,
 //      bf16, into the workspace;
-//   2. bwd_chain_kernel: per (unit, 16 value rows), the chunks in reverse order; the
-//      chain above only (its value columns are independent), writing dH' of every
-//      chunk (bf16) and dL/dS_0;
+//   2. bwd_tiles_kernel: one workgroup per (chunk, head) computes the chunk's factors
+//      (Ki, Qg, Kg, X, M, beta, e^{G_n}) once into the workspace; then bwd_chain_kernel:
+//      per (unit, 16 value rows), the chunks in reverse order, streaming those tiles
+//      through two LDS buffers; the chain above only (its value columns are
+//      independent), writing dH' of every chunk (bf16) and dL/dS_0;
 //   3. bwd_grad_kernel: one workgroup per (chunk, head), all chunks at once; reads H
 //      and dH', forms E and dE in 32-wide value slices and accumulates every
 //      d_v-contraction in registers, then the chunk-local algebra and the gradients.
@@ -43,35 +45,129 @@ __device__ __forceinline__ bf16x8 frow(const bf16* base, int ld, int row0, int k
 }
 
 // ====================================================================================
+// Chunk tiles of the reverse chain
+// ====================================================================================
+
+// Sequence and chunk of a chunk slot (see chunk_slot_base); false for an unused slot.
+__device__ __forceinline__ bool slot_chunk(const BwdArgs& a, int64_t slot, int& n_seq,
+                                           int64_t& bos, int64_t& eos, int& c) {
+  auto bos_of = [&](int n) -> int64_t {
+    return a.cu_seqlens ? static_cast<int64_t>(a.cu_seqlens[n]) : static_cast<int64_t>(n) * a.T;
+  };
+  int lo = 0, hi = a.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunk_slot_base(mid, bos_of(mid)) <= slot) lo = mid; else hi = mid - 1;
+  }
+  n_seq = lo;
+  bos = bos_of(lo);
+  eos = a.cu_seqlens ? static_cast<int64_t>(a.cu_seqlens[lo + 1]) : bos + a.T;
+  const int64_t cc = slot - chunk_slot_base(lo, bos);
+  c = static_cast<int>(cc);
+  return cc >= 0 && cc * kChunk < eos - bos;
+}
+
+// Per (chunk slot, head), in the workspace, as 16-byte pieces: Ki, Qg, Kg [64][DK] bf16,
+// X, M [64][64] bf16, beta [64] fp32, e^{G_n} [DK] fp32 (rows past a ragged chunk's end
+// are zero; X has identity rows there).  The chain reads them into LDS tiles with the
+// row padding of kda_chunk.h.
+template <int DK>
+struct ChainTiles {
+  static constexpr int PK = kChunk * DK / 8;       // pieces of a [64][DK] tile
+  static constexpr int PC = kChunk * kChunk / 8;   // of a [64][64] tile
+  static constexpr int PB = kChunk * 4 / 16, PE = DK * 4 / 16;
+  static constexpr int kPieces = 3 * PK + 2 * PC + PB + PE;
+  static constexpr size_t kBytes = size_t(kPieces) * 16;
+  static_assert(kBytes == chain_tile_bytes(DK), "host and device tile sizes agree");
+};
+
+// LDS byte offset of piece p, given the byte offsets of the seven tiles (Ki, Qg, Kg, X,
+// M, beta, e^{G_n}) with row strides DK + 8 and 64 + 8 (bf16).
+template <int DK>
+__device__ __forceinline__ uint32_t piece_lds(const uint32_t (&off)[7], int p) {
+  using TL = ChainTiles<DK>;
+  constexpr int RK = DK / 8;
+  if (p < 3 * TL::PK) {
+    const int t = p / TL::PK, q = p % TL::PK;
+    return off[t] + ((q / RK) * (DK + 8) + 8 * (q % RK)) * 2;
+  }
+  p -= 3 * TL::PK;
+  if (p < 2 * TL::PC) {
+    const int t = p / TL::PC, q = p % TL::PC;
+    return off[3 + t] + ((q / 8) * (kChunk + 8) + 8 * (q % 8)) * 2;
+  }
+  p -= 2 * TL::PC;
+  return p < TL::PB ? off[5] + 16 * p : off[6] + 16 * (p - TL::PB);
+}
+
+// One workgroup per (chunk slot, head): the chunk's factors (as the forward computes
+// them), copied to the workspace.
+template <int DK, int DECAY>
+__global__ __launch_bounds__(kThreads, 1) void bwd_tiles_kernel(BwdArgs a) {
+  using CP = ChunkProducer<bf16, DK, false>;
+  using CL = ChunkLayout<bf16, DK, false>;
+  using TL = ChainTiles<DK>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[CL::kBytes];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x % a.H;
+  const int64_t slot = blockIdx.x / a.H;
+  int n_seq, c;
+  int64_t bos, eos;
+  if (!slot_chunk(a, slot, n_seq, bos, eos, c)) return;   // uniform over the workgroup
+  const int64_t c0 = bos + int64_t(c) * kChunk;
+  const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
+  CP cp;
+  cp.init(smem, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), a.g, a.beta, a.H,
+          h, a.scale, tid, wave, 0);
+  cp.template load<DECAY>(c0, n);
+  cp.template factors<DECAY>(n, false, 0, 0);
+  cp.products();
+  cp.inverse();   // ends with a barrier
+  constexpr uint32_t off[7] = {CL::oKi, CL::oQg, CL::oKg, CL::oTm, CL::oM, CL::oBeta, CL::oEgn};
+  u32x4* dst = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.tiles) +
+                                        (slot * a.H + h) * TL::kBytes);
+  for (int p = tid; p < TL::kPieces; p += kThreads)
+    dst[p] = *reinterpret_cast<const u32x4*>(smem + piece_lds<DK>(off, p));
+}
+
+// ====================================================================================
 // Reverse chain
 // ====================================================================================
 
 template <int DK, int BV>
 struct ChainLayout {
-  using CL = ChunkLayout<bf16, DK, false>;
-  static constexpr int LDK = CL::LDK, LDC = CL::LDC;
-  static constexpr size_t oP = CL::kBytes;   // [BV][LDK]: (D dH')^T snapshot
-  static constexpr size_t kBytes = CL::al(oP + size_t(BV) * LDK * 2);
-  // dO^T, dE^T, G^T ([BV][LDC]) in the A / inverse region, dead after the inverse
-  static constexpr size_t oDOT = CL::oA;
-  static constexpr size_t oDET = CL::al(oDOT + size_t(BV) * LDC * 2);
-  static constexpr size_t oGT = CL::al(oDET + size_t(BV) * LDC * 2);
-  static_assert(oGT + size_t(BV) * LDC * 2 <= CL::oScr, "chain tiles overflow");
+  static constexpr int LDK = DK + 8, LDC = kChunk + 8;
+  static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
+  static constexpr size_t tK = size_t(kChunk) * LDK * 2, tC = size_t(kChunk) * LDC * 2;
+  // one buffer of chunk tiles: Ki, Qg, Kg, X, M, beta, e^{G_n}
+  static constexpr size_t oKi = 0, oQg = tK, oKg = 2 * tK, oX = 3 * tK, oM = 3 * tK + tC;
+  static constexpr size_t oB = 3 * tK + 2 * tC, oE = oB + kChunk * 4;
+  static constexpr size_t kBuf = al(oE + DK * 4);
+  static constexpr size_t oP = 2 * kBuf;                               // [BV][LDK]
+  static constexpr size_t oDOT = al(oP + size_t(BV) * LDK * 2);       // [BV][LDC] each
+  static constexpr size_t oDET = al(oDOT + size_t(BV) * LDC * 2);
+  static constexpr size_t oGT = al(oDET + size_t(BV) * LDC * 2);
+  static constexpr size_t kBytes = al(oGT + size_t(BV) * LDC * 2);
   static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
 };
 
+// Per (unit, BV value rows), the chunks in reverse order; each chunk's tiles are read
+// from the workspace one chunk ahead into the other of two LDS buffers.
 template <int DK, int BV, int DECAY>
 __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
-  using CP = ChunkProducer<bf16, DK, false>;
   using CL = ChainLayout<DK, BV>;
+  using TL = ChainTiles<DK>;
   using ST = StateTiles<DK, BV>;
   constexpr int LDK = CL::LDK, LDC = CL::LDC, NVB = BV / 16;
+  constexpr int NPT = (TL::kPieces + kThreads - 1) / kThreads;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[CL::kBytes];
   bf16* sP = reinterpret_cast<bf16*>(smem + CL::oP);
   bf16* sDOT = reinterpret_cast<bf16*>(smem + CL::oDOT);
   bf16* sDET = reinterpret_cast<bf16*>(smem + CL::oDET);
   bf16* sGT = reinterpret_cast<bf16*>(smem + CL::oGT);
+  constexpr uint32_t off[7] = {CL::oKi, CL::oQg, CL::oKg, CL::oX, CL::oM, CL::oB, CL::oE};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,42 +181,63 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
   const int v0 = vt * BV;
   const bf16* dout = static_cast<const bf16*>(a.dout);
   bf16* dstates = static_cast<bf16*>(a.dstates);
+  const u32x4* tiles = static_cast<const u32x4*>(a.tiles);
 
-  CP cp;
-  cp.init(smem, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), a.g, a.beta, a.H,
-          h, a.scale, tid, wave, 0);
   f32x4 sacc[ST::NST];   // dH^T tiles of this value tile (rows = key), fp32
   const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * a.DV * DK;
   load_state<DK, BV, LDK>(sacc, a.dfinal_state, st_base, v0, sP, wave, lane);
 
   const int nch = static_cast<int>((eos - bos + kChunk - 1) / kChunk);
   const int64_t slot0 = chunk_slot_base(n_seq, bos);
+  u32x4 stage[NPT];
+  auto fetch = [&](int c) {
+    const u32x4* src = tiles + ((slot0 + c) * a.H + h) * (TL::kBytes / 16);
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int p = tid + i * kThreads;
+      if (p < TL::kPieces) stage[i] = src[p];
+    }
+  };
+  auto deposit = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int p = tid + i * kThreads;
+      if (p < TL::kPieces)
+        *reinterpret_cast<u32x4*>(smem + buf * CL::kBuf + piece_lds<DK>(off, p)) = stage[i];
+    }
+  };
   ValueRegs<bf16, NVB> dr;   // dO rows of the chunk, accumulator layout
   if (nch > 0) {
     const int64_t cl = bos + int64_t(nch - 1) * kChunk;
-    const int nl = static_cast<int>(eos - cl);
-    cp.template load<DECAY>(cl, nl);
-    dr.load(dout, cl, nl, a.H, h, a.DV, v0, wave, lane);
+    fetch(nch - 1);
+    dr.load(dout, cl, static_cast<int>(eos - cl), a.H, h, a.DV, v0, wave, lane);
+    deposit(0);
   }
+  lds_barrier();
   const int k0m = (16 * wave) & ~31;   // first K step that meets a triangular row block
 
   for (int c = nch - 1; c >= 0; --c) {
+    const int cur = (nch - 1 - c) & 1;
+    const unsigned char* buf = smem + cur * CL::kBuf;
+    const bf16* sKi = reinterpret_cast<const bf16*>(buf + CL::oKi);
+    const bf16* sQg = reinterpret_cast<const bf16*>(buf + CL::oQg);
+    const bf16* sKg = reinterpret_cast<const bf16*>(buf + CL::oKg);
+    const bf16* sX = reinterpret_cast<const bf16*>(buf + CL::oX);
+    const bf16* sM = reinterpret_cast<const bf16*>(buf + CL::oM);
+    const float* sBeta = reinterpret_cast<const float*>(buf + CL::oB);
+    const float* sEgn = reinterpret_cast<const float*>(buf + CL::oE);
     const int64_t c0 = bos + int64_t(c) * kChunk;
     const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
-    const bool has_next = c > 0;   // the previous chunk in token order (always full)
+    if (c > 0) fetch(c - 1);   // the previous chunk in token order (always full)
     // dL/d(state after chunk c)
     store_state_bf16<DK, BV>(sacc, dstates, ((slot0 + c) * a.H + h) * a.DV * DK, v0, wave,
                              lane);
-
-    cp.template factors<DECAY>(n, has_next, c0 - kChunk, kChunk);
-    cp.products();
-    cp.inverse();
 
     // P = D dH' (accumulators and snapshot), dO^T tile
 #pragma unroll
     for (int s = 0; s < ST::NST; ++s) {
       const int kb = ST::kb(wave, s), vb = ST::vb(s);
-      sacc[s] *= *reinterpret_cast<const f32x4*>(cp.sEgn + 16 * kb + 4 * lq);
+      sacc[s] *= *reinterpret_cast<const f32x4*>(sEgn + 16 * kb + 4 * lq);
       store4(sP + (16 * vb + lr) * LDK + 16 * kb + 4 * lq, sacc[s]);
     }
 #pragma unroll
@@ -130,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) x[i] = 16 * wave + 4 * lq + i < n ? dr.f32(vb, i) : 0.f;
       store4(sDOT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, x);
     }
-    if (has_next) dr.load(dout, c0 - kChunk, kChunk, a.H, h, a.DV, v0, wave, lane);
+    if (c > 0) dr.load(dout, c0 - kChunk, kChunk, a.H, h, a.DV, v0, wave, lane);
     lds_barrier();
 
     // dE = Ki P + M^T dO for token block `wave` -> dE^T
@@ -139,9 +256,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < DK; kk += 32)
-        acc = mma_bf16(frow(cp.sKi, LDK, 16 * wave, kk, lane), frow(sP, LDK, 16 * vb, kk, lane), acc);
+        acc = mma_bf16(frow(sKi, LDK, 16 * wave, kk, lane), frow(sP, LDK, 16 * vb, kk, lane), acc);
       for (int kk = k0m; kk < kChunk; kk += 32)
-        acc = mma_bf16(frag_tr(cp.sM, LDC, kk, 16 * wave, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
+        acc = mma_bf16(frag_tr(sM, LDC, kk, 16 * wave, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
                        acc);
       store4(sDET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, acc);
     }
@@ -149,13 +266,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
 
     // G = -beta X^T dE -> G^T
     {
-      const f32x4 bt = *reinterpret_cast<const f32x4*>(cp.sBeta + 16 * wave + 4 * lq);
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(sBeta + 16 * wave + 4 * lq);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int kk = k0m; kk < kChunk; kk += 32)
-          acc = mma_bf16(frag_tr(cp.sTm, LDC, kk, 16 * wave, lane),
-                         frow(sDET, LDC, 16 * vb, kk, lane), acc);
+          acc = mma_bf16(frag_tr(sX, LDC, kk, 16 * wave, lane), frow(sDET, LDC, 16 * vb, kk, lane),
+                         acc);
         store4(sGT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, -(bt * acc));
       }
     }
@@ -168,13 +285,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
       f32x4 acc = sacc[s];
 #pragma unroll
       for (int kk = 0; kk < kChunk; kk += 32) {
-        acc = mma_bf16(frag_tr(cp.sQg, LDK, kk, 16 * kb, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
+        acc = mma_bf16(frag_tr(sQg, LDK, kk, 16 * kb, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
                        acc);
-        acc = mma_bf16(frag_tr(cp.sKg, LDK, kk, 16 * kb, lane), frow(sGT, LDC, 16 * vb, kk, lane),
+        acc = mma_bf16(frag_tr(sKg, LDK, kk, 16 * kb, lane), frow(sGT, LDC, 16 * vb, kk, lane),
                        acc);
       }
       sacc[s] = acc;
     }
+    if (c > 0) deposit(cur ^ 1);
     lds_barrier();
   }
 
@@ -217,25 +335,6 @@ struct GradLayout {
   static_assert(oRed + size_t(8 + kThreads / DK) * DK * 4 <= a2end, "reduction overflow");
   static_assert(kBytes <= kLds, "LDS budget exceeded");
 };
-
-// Sequence and chunk of a chunk slot (see chunk_slot_base); false for an unused slot.
-__device__ __forceinline__ bool slot_chunk(const BwdArgs& a, int64_t slot, int& n_seq,
-                                           int64_t& bos, int64_t& eos, int& c) {
-  auto bos_of = [&](int n) -> int64_t {
-    return a.cu_seqlens ? static_cast<int64_t>(a.cu_seqlens[n]) : static_cast<int64_t>(n) * a.T;
-  };
-  int lo = 0, hi = a.N - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (chunk_slot_base(mid, bos_of(mid)) <= slot) lo = mid; else hi = mid - 1;
-  }
-  n_seq = lo;
-  bos = bos_of(lo);
-  eos = a.cu_seqlens ? static_cast<int64_t>(a.cu_seqlens[lo + 1]) : bos + a.T;
-  const int64_t cc = slot - chunk_slot_base(lo, bos);
-  c = static_cast<int>(cc);
-  return cc >= 0 && cc * kChunk < eos - bos;
-}
 
 template <int DK, int DV, int DECAY>
 __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
@@ -622,6 +721,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
 
 template <int DK, int DECAY>
 static hipError_t launch_chain_k(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_tiles_kernel<DK, DECAY>), dim3(static_cast<unsigned>(a.slots * a.H)),
+                     dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_chain_kernel<DK, kBwdChainBV, DECAY>), dim3(a.units * a.NV),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -54,6 +54,7 @@ struct BwdArgs {
   float* dbeta;
   const void* states;          // bf16 [slot][H][d_v][d_k]: state at each chunk start
   void* dstates;               // bf16 [slot][H][d_v][d_k]: dL/d(state at each chunk end)
+  void* tiles;                 // [slot][H] chunk tiles of the reverse chain
   int64_t T;
   int64_t slots;               // chunk_slots_host(T_total, N)
   int32_t H, DV, N, units;
@@ -75,6 +76,11 @@ constexpr int kBwdChainBV = 16;   // value rows per reverse-chain workgroup
 // Chunk slots of the backward's per-chunk buffers for T_total packed rows and N
 // sequences (slot indexing: chunk_slot_base in kda_tiles.h).
 inline int64_t chunk_slots_host(int64_t T_total, int32_t N) { return T_total / 64 + N + 1; }
+// Bytes of one chunk's reverse-chain tiles: Ki, Qg, Kg [64][dk] and X, M [64][64] bf16,
+// beta [64] and e^{G_n} [dk] fp32.
+constexpr size_t chain_tile_bytes(int dk) {
+  return size_t(3 * 64 * dk * 2 + 2 * 64 * 64 * 2 + 64 * 4 + dk * 4);
+}
 
 // dtype: 0 = fp32, 1 = bf16; dk, dv in {64, 128}.
 // decay: 0 = g per key channel [units, dk], 1 = one g per unit [units], 2 = none.

@@ -217,8 +217,9 @@ int kda_decode_step_ex(int dtype, int decay, int flags,
  *     dbeta  : [B, T, H] fp32
  *     dinitial_state : [N, H, d_v, d_k] fp32, dL/d(initial state), or NULL (not written).
  *   workspace: device memory of at least kda_backward_workspace_bytes() bytes (else
- *     KDA_ERR_WORKSPACE); it receives the state at every chunk start and the state
- *     gradient at every chunk end (bf16), and is owned by the library during the call.
+ *     KDA_ERR_WORKSPACE); it receives the state at every chunk start, the state
+ *     gradient at every chunk end (bf16) and every chunk's factor tiles, and is owned
+ *     by the library during the call.
  *     With d_k = d_v = 128 and the producer/consumer plan of kda_prefill_coop_plan()
  *     (two consumers), the forward sweep that recomputes the chunk states runs on that
  *     kernel and the workspace starts with its ring: after the call, a nonzero first
@@ -238,10 +239,11 @@ int kda_backward(int dtype, int decay, int flags,
                  void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
-/* Workspace bytes kda_backward needs: 2 * (T_total / 64 + N + 1) * H * d_v * d_k * 2 for
- * the chunk states and state gradients, plus the producer/consumer ring when that
- * forward sweep applies (0 for unsupported arguments).  Host-only apart from a cached
- * device-attribute query. */
+/* Workspace bytes kda_backward needs, with S = (T_total / 64 + N + 1) * H chunk slots:
+ * 2 * S * d_v * d_k * 2 for the chunk states and state gradients (bf16), plus
+ * S * (388 d_k + 16640) for each chunk's factor tiles (bf16 Ki, Qg, Kg, X, M; fp32 beta,
+ * e^{G_n}), plus the producer/consumer ring when that forward sweep applies (0 for
+ * unsupported arguments).  Host-only apart from a cached device-attribute query. */
 size_t kda_backward_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_t H,
                                     int32_t d_k, int32_t d_v);
 
