@@ -367,6 +367,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   const uint32_t rowV = static_cast<uint32_t>(a.H) * DV;
   const uint32_t rowK = static_cast<uint32_t>(a.H) * DK;
 
+  // value slices of H, dH', V and dO: each slice's pieces are requested into registers
+  // one slice ahead (the first while the chunk's factors are computed)
+  constexpr int HPT = VS * DK / 8 / kThreads;   // 16-byte pieces of H (and of dH') per thread
+  static_assert(HPT * kThreads * 8 == VS * DK && kChunk * VS / 8 == kThreads, "slice pieces");
+  bf16x8 ph[HPT], pdh[HPT], pv, pdo;
+  auto fetch_slice = [&](int vs) {
+    const int v0 = vs * VS;
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+      const int idx = tid + i * kThreads;
+      const int r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+      ph[i] = *reinterpret_cast<const bf16x8*>(states + int64_t(v0 + r) * DK + c8);
+      pdh[i] = *reinterpret_cast<const bf16x8*>(dstates + int64_t(v0 + r) * DK + c8);
+    }
+    const int r = tid / (VS / 8), c8 = 8 * (tid % (VS / 8));
+    pv = bf16x8{};
+    pdo = bf16x8{};
+    if (r < n) {
+      const int64_t o = (c0 + r) * rowV + int64_t(h) * DV + v0 + c8;
+      pv = *reinterpret_cast<const bf16x8*>(vin + o);
+      pdo = *reinterpret_cast<const bf16x8*>(dout + o);
+    }
+  };
+  fetch_slice(0);
+
   CP cp;
   cp.init(smem, qin, kin, a.g, a.beta, a.H, h, a.scale, tid, wave, 0);
   cp.sEG = reinterpret_cast<float*>(smem + GL::oEG);
@@ -402,33 +427,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   for (int vs = 0; vs < DV / VS; ++vs) {
     const int v0 = vs * VS;
     // H, dH' (and P = D dH') slices [VS][DK]; V^T and dO^T slices [VS][64]
-    for (int i = tid; i < VS * DK / 8; i += kThreads) {
-      const int r = i / (DK / 8), c8 = 8 * (i % (DK / 8));
-      const bf16x8 hv = *reinterpret_cast<const bf16x8*>(states + int64_t(v0 + r) * DK + c8);
-      const bf16x8 dh = *reinterpret_cast<const bf16x8*>(dstates + int64_t(v0 + r) * DK + c8);
-      *reinterpret_cast<bf16x8*>(sH + r * LDK + c8) = hv;
-      *reinterpret_cast<bf16x8*>(sDH + r * LDK + c8) = dh;
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+      const int idx = tid + i * kThreads;
+      const int r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+      *reinterpret_cast<bf16x8*>(sH + r * LDK + c8) = ph[i];
+      *reinterpret_cast<bf16x8*>(sDH + r * LDK + c8) = pdh[i];
       bf16x8 p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = static_cast<bf16>(static_cast<float>(dh[e]) * cp.sEgn[c8 + e]);
+      for (int e = 0; e < 8; ++e)
+        p[e] = static_cast<bf16>(static_cast<float>(pdh[i][e]) * cp.sEgn[c8 + e]);
       *reinterpret_cast<bf16x8*>(sP + r * LDK + c8) = p;
     }
-    // V and dO slices, one 16-byte piece of each per thread, into V^T and dO^T
-    static_assert(kChunk * VS / 8 == kThreads, "one piece per thread");
     {
       const int r = tid / (VS / 8), c8 = 8 * (tid % (VS / 8));
-      bf16x8 xv = {}, xd = {};
-      if (r < n) {
-        const int64_t off = (c0 + r) * rowV + int64_t(h) * DV + v0 + c8;
-        xv = *reinterpret_cast<const bf16x8*>(vin + off);
-        xd = *reinterpret_cast<const bf16x8*>(dout + off);
-      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        sVT[(c8 + e) * LDC + r] = xv[e];
-        sDOT[(c8 + e) * LDC + r] = xd[e];
+        sVT[(c8 + e) * LDC + r] = pv[e];
+        sDOT[(c8 + e) * LDC + r] = pdo[e];
       }
     }
+    if (vs + 1 < DV / VS) fetch_slice(vs + 1);
     lds_barrier();
     f32x4 vreg[VS / 16];   // V in accumulator layout (rows of this wave)
 #pragma unroll
@@ -501,6 +520,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   }
 
   // ---- chunk-local algebra -------------------------------------------------------------
+  // the chunk's raw k and q rows, requested now for the gradients at the end
+  constexpr int KPT2 = kChunk * DK / 8 / kThreads;
+  bf16x8 pk[KPT2], pq[KPT2];
+#pragma unroll
+  for (int i = 0; i < KPT2; ++i) {
+    const int idx = tid + i * kThreads;
+    const int r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+    pk[i] = bf16x8{};
+    pq[i] = bf16x8{};
+    if (r < n) {
+      const int64_t o = (c0 + r) * rowK + int64_t(h) * DK + c8;
+      pk[i] = *reinterpret_cast<const bf16x8*>(kin + o);
+      pq[i] = *reinterpret_cast<const bf16x8*>(qin + o);
+    }
+  }
   bf16* sDWT = reinterpret_cast<bf16*>(smem + GL::oDWT);   // dW^T [DK][64]
   bf16* sDMT = reinterpret_cast<bf16*>(smem + GL::oDMT);   // dM^T [64][64]
   bf16* sC1 = reinterpret_cast<bf16*>(smem + GL::oCC1);
@@ -587,16 +621,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   // replaces it in place (one owner per element), and the rows leave as 16-byte stores
   bf16* sK = reinterpret_cast<bf16*>(smem + GL::oK);
   bf16* sQ = reinterpret_cast<bf16*>(smem + GL::oQ);
-  for (int i = tid; i < kChunk * DK / 8; i += kThreads) {
-    const int r = i / (DK / 8), c8 = 8 * (i % (DK / 8));
-    bf16x8 kv = {}, qv = {};
-    if (r < n) {
-      const int64_t off = (c0 + r) * rowK + int64_t(h) * DK + c8;
-      kv = *reinterpret_cast<const bf16x8*>(kin + off);
-      qv = *reinterpret_cast<const bf16x8*>(qin + off);
-    }
-    *reinterpret_cast<bf16x8*>(sK + r * LDK + c8) = kv;
-    *reinterpret_cast<bf16x8*>(sQ + r * LDK + c8) = qv;
+#pragma unroll
+  for (int i = 0; i < KPT2; ++i) {
+    const int idx = tid + i * kThreads;
+    const int r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+    *reinterpret_cast<bf16x8*>(sK + r * LDK + c8) = pk[i];
+    *reinterpret_cast<bf16x8*>(sQ + r * LDK + c8) = pq[i];
   }
   lds_barrier();
 
