@@ -172,3 +172,32 @@ def test_backward_dv_matches_directional_derivative_of_forward_kernel():
     fd = (loss(v32 + eps * direction) - loss(v32 - eps * direction)) / (2 * eps)
     an = float((got[2].float() * direction).sum())
     assert abs(fd - an) <= 2e-2 * max(abs(fd), 1.0), (fd, an)
+
+
+def test_backward_full_size_sampled_window():
+    """The long-context workload (B=1, H=32, T=65536, d=128, bf16) in the launch
+    configuration bench.py times.  Without a final-state gradient, the gradients of
+    the last W tokens depend only on the state at T - W and on those tokens, so the
+    oracle runs the forward recurrence to T - W (state only) and the exact backward of
+    the last W tokens from there, for two heads."""
+    from oracle import recurrence, recurrence_backward
+    W, heads = 320, [0, 21]
+    print("backward full size, sampled window", flush=True)
+    x = ki.make_prefill_workload(ki.LONG_PREFILL, device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(178)
+    do = torch.randn(x["v"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    got = kda.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, need_dinitial_state=False)
+    torch.cuda.synchronize()
+    T = x["T"]
+    f = lambda t: ki.to_f64(t[0, :, heads].transpose(0, 1))            # [U, T, ...]
+    q, k, v, g, do64 = f(x["q"]), f(x["k"]), f(x["v"]), f(x["g"]), f(do)
+    beta = ki.to_f64(x["beta"][0, :, heads].transpose(0, 1))
+    _, s_mid = recurrence(q[:, :T - W], k[:, :T - W], v[:, :T - W], g[:, :T - W],
+                          beta[:, :T - W])
+    ref = recurrence_backward(q[:, T - W:], k[:, T - W:], v[:, T - W:], g[:, T - W:],
+                              beta[:, T - W:], do64[:, T - W:], initial_state=s_mid)
+    for name, a, r in zip(NAMES[:5], got[:5], ref[:5]):
+        a = ki.to_f64(a[0, T - W:, heads].transpose(0, 1))
+        err = check("bf16", a, r, f"full-size window {name}")
+        print(f"  full-size window {name}: rms-rel {err:.2e}", flush=True)
