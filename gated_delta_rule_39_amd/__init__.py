@@ -279,8 +279,11 @@ def backward_workspace_bytes(N: int, T_total: int, H: int, d_k: int, d_v: int) -
 
 
 def backward(q, k, v, g, beta, do, *, cu_seqlens=None, scale=None, initial_state=None,
-             dfinal_state=None, need_dinitial_state=True, workspace="auto"):
-    """Gradients of ``prefill`` (bf16 inputs, no prologue flags).
+             dfinal_state=None, need_dinitial_state=True, workspace="auto",
+             normalize_k=False, beta_logit=False, gate_logit=False):
+    """Gradients of ``prefill`` (bf16 inputs).  The prologue flags must be those of the
+    forward call; the gradients are then with respect to the raw k, beta logits and
+    retention logits.
 
     The inputs are those of the forward call; ``do`` [B, T, H, d_v] bf16 is dL/do and
     ``dfinal_state`` [N, H, d_v, d_k] fp32 (or None: zero) is dL/d(final state).
@@ -333,7 +336,8 @@ def backward(q, k, v, g, beta, do, *, cu_seqlens=None, scale=None, initial_state
     else:
         _need(workspace, "workspace", dtype=torch.uint8, device=dev)
         ws = workspace
-    _check(lib().kda_backward(KDA_BF16, decay, 0, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+    _check(lib().kda_backward(KDA_BF16, decay, _flags(normalize_k, beta_logit, gate_logit),
+                              _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                               _ptr(cu_seqlens), N, B, T, H, d_k, d_v, float(scale),
                               _ptr(initial_state), _ptr(do), _ptr(dfinal_state), _ptr(dq),
                               _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(ws),

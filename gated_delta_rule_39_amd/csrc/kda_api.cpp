@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <hip/hip_runtime_api.h>
 
+#include "kda_bwd_launch.h"
 #include "kda_launch.h"
 
 namespace {
@@ -278,7 +279,7 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
   if (dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (decay != KDA_DECAY_CHANNEL && decay != KDA_DECAY_HEAD && decay != KDA_DECAY_NONE)
     return KDA_ERR_UNSUPPORTED;
-  if (flags != 0) return KDA_ERR_UNSUPPORTED;
+  if (flags & ~kAllFlags) return KDA_ERR_UNSUPPORTED;
   if (N < 0 || B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
   if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
   if (cu_seqlens == nullptr && N != B) return KDA_ERR_BAD_SHAPE;
@@ -314,6 +315,7 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
     a.xcd_remap = (units % 8 == 0) ? 1 : 0;
     a.scale = scale;
     a.decay = decay;
+    a.flags = flags;
     a.chunk_states = states;
     bool done = false;
     if (plan.ring > 0) {
@@ -358,6 +360,7 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
   b.NV = d_v / kda::kBwdChainBV;
   b.xcd_remap = (units % 8 == 0) ? 1 : 0;
   b.decay = decay;
+  b.flags = flags;
   b.scale = scale;
   if (kda::launch_backward_chain(d_k, b, stream) != hipSuccess) return KDA_ERR_HIP;   // tiles + chain
   if (tot > 0 && kda::launch_backward_grads(d_k, b, stream) != hipSuccess) return KDA_ERR_HIP;

@@ -31,6 +31,7 @@
 // Every product runs on the bf16 MFMA (16x16x32, fp32 accumulation); operands that
 // are needed transposed are read with ds_read_b64_tr_b16 (frag_tr).
 
+#include "kda_bwd_launch.h"
 #include "kda_chunk.h"
 #include "kda_launch.h"
 #include "kda_tiles.h"
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_tiles_kernel(BwdArgs a) {
   const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
   CP cp;
   cp.init(smem, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), a.g, a.beta, a.H,
-          h, a.scale, tid, wave, 0);
+          h, a.scale, tid, wave, a.flags);
   cp.template load<DECAY>(c0, n);
   cp.template factors<DECAY>(n, false, 0, 0);
   cp.products();
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   fetch_slice(0);
 
   CP cp;
-  cp.init(smem, qin, kin, a.g, a.beta, a.H, h, a.scale, tid, wave, 0);
+  cp.init(smem, qin, kin, a.g, a.beta, a.H, h, a.scale, tid, wave, a.flags);
   cp.sEG = reinterpret_cast<float*>(smem + GL::oEG);
   cp.template load<DECAY>(c0, n);
   cp.template factors<DECAY, true>(n, false, 0, 0);
@@ -637,6 +638,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   constexpr int NPART = kThreads / DK;
   f32x4 dbk = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 gm[NKB];
+  // raw keys: the factors used the unit key bf16(k / n), n = sqrt(|k|^2 + eps) per row;
+  // its gradient dk^ is carried back to k as (dk^ - k^ (k^ . dk^)) / n
+  const bool norm_k = (a.flags & kNormK) != 0;
+  f32x4 rn = f32x4{1.f, 1.f, 1.f, 1.f}, kdot = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 dkh[NKB];
+  if (norm_k) {
+    f32x4 ss = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float kf = static_cast<float>(sK[(16 * wave + 4 * lq + i) * LDK + 16 * kb + lr]);
+        ss[i] += kf * kf;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rn[i] = __builtin_amdgcn_rsqf(row_sum<16>(ss[i]) + kNormEps);
+  }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const int j = 16 * kb + lr;
@@ -645,7 +663,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * wave + 4 * lq + i;
-      const float kf = static_cast<float>(sK[r * LDK + j]);
+      float kf = static_cast<float>(sK[r * LDK + j]);
+      if (norm_k) kf = static_cast<float>(static_cast<bf16>(kf * rn[i]));
       const float qf = static_cast<float>(sQ[r * LDK + j]);
       const float eg = cp.sEG[r * LDEG + j];
       const float ieg = __builtin_amdgcn_rcpf(eg);
@@ -655,7 +674,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       dbk[i] += dBk[kb][i] * kg;
       gn += dKh[kb][i] * kh;
       gm[kb][i] = dkg * kg + dQg[kb][i] * qg - dKi[kb][i] * ki - dKh[kb][i] * kh;
-      sK[r * LDK + j] = static_cast<bf16>(dkg * eg + dKi[kb][i] * ieg + dKh[kb][i] * eh);
+      const float dkv = dkg * eg + dKi[kb][i] * ieg + dKh[kb][i] * eh;
+      if (norm_k) {
+        dkh[kb][i] = dkv;
+        kdot[i] += dkv * kf;
+      } else {
+        sK[r * LDK + j] = static_cast<bf16>(dkv);
+      }
       sQ[r * LDK + j] = static_cast<bf16>(a.scale * dQg[kb][i] * eg);
     }
     // suffix over this lane's four rows, then over the lane groups below it
@@ -675,11 +700,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
     }
   }
   sRed[(8 + dpart) * DK + dj] = ddp;
-  // d beta: the V and the Kg terms, summed over this row's values / keys
+  if (norm_k) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kdot[i] = row_sum<16>(kdot[i]);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bf16& e = sK[(16 * wave + 4 * lq + i) * LDK + 16 * kb + lr];
+        const float kh = static_cast<float>(static_cast<bf16>(static_cast<float>(e) * rn[i]));
+        e = static_cast<bf16>((dkh[kb][i] - kh * kdot[i]) * rn[i]);
+      }
+  }
+  // d beta: the V and the Kg terms, summed over this row's values / keys (beta from a
+  // logit b: times d sigmoid(b) / db = beta (1 - beta))
   {
     f32x4 tot;
 #pragma unroll
     for (int i = 0; i < 4; ++i) tot[i] = row_sum<16>(dbu[i] + dbk[i]);
+    if (a.flags & kBetaLogit) tot *= bt * (1.f - bt);
     if (lr == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -707,6 +746,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   // dg: G_r = g_1 + ... + g_r and G_n = G_last, so dg_s = sum_{r >= s} dG_r + dG_n with
   // dG_n = sum_r dKh Kh + d e^{G_n} e^{G_n}
   if constexpr (DECAY != 2) {
+    const bool gate_logit = (a.flags & kGateLogit) != 0;
     f32x4 rows = f32x4{0.f, 0.f, 0.f, 0.f};   // one scalar decay: sums over the channels
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -725,7 +765,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
         const float v = gm[kb][i] + add;
         if constexpr (DECAY == 0) {
           const int r = 16 * wave + 4 * lq + i;
-          if (r < n) a.dg[(c0 + r) * rowK + int64_t(h) * DK + j] = v;
+          if (r < n) {
+            const int64_t o = (c0 + r) * rowK + int64_t(h) * DK + j;
+            // g = log sigmoid(a) from a retention logit a: dg/da = sigmoid(-a)
+            a.dg[o] = gate_logit ? v * __builtin_amdgcn_rcpf(1.f + exp_hw(a.g[o])) : v;
+          }
         } else {
           rows[i] += v;
         }
@@ -738,7 +782,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * wave + 4 * lq + i;
-          if (r < n) a.dg[(c0 + r) * a.H + h] = rows[i];
+          if (r < n) {
+            const int64_t o = (c0 + r) * a.H + h;
+            a.dg[o] = gate_logit ? rows[i] * __builtin_amdgcn_rcpf(1.f + exp_hw(a.g[o])) : rows[i];
+          }
         }
       }
     }

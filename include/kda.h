@@ -206,9 +206,11 @@ int kda_decode_step_ex(int dtype, int decay, int flags,
  * exact gradient of the recurrence of "Kimi Delta Attention: The Linear Attention
  * Behind Kimi K2 and Qwen3", "How Kimi Delta Attention works step by step", for a
  * loss whose gradients with respect to o and to the final state are given.
- *   dtype: KDA_BF16 only (KDA_F32 returns KDA_ERR_UNSUPPORTED); flags must be 0.
- *   Inputs q, k, v, g, beta, cu_seqlens, N, B, T, H, d_k, d_v, scale, initial_state:
- *     exactly as passed to the forward call.
+ *   dtype: KDA_BF16 only (KDA_F32 returns KDA_ERR_UNSUPPORTED).
+ *   Inputs decay, flags, q, k, v, g, beta, cu_seqlens, N, B, T, H, d_k, d_v, scale,
+ *     initial_state: exactly as passed to the forward call (kda_prefill_ex).  With
+ *     prologue flags the gradients are with respect to the raw inputs: dk through the
+ *     key normalisation, dbeta through the sigmoid, dg through g = log sigmoid(a).
  *   dout : [B, T, H, d_v] bf16, dL/do.
  *   dfinal_state : [N, H, d_v, d_k] fp32, dL/d(final state), or NULL (zero).
  *   Outputs (caller-allocated, written for every token row of a sequence):

@@ -151,7 +151,7 @@ def test_backward_validation_codes():
     assert backward_status(dtype=7) == 4                # bad dtype
     assert backward_status(dtype=0) == 3                # fp32 backward: unsupported
     assert backward_status(decay=5) == 3
-    assert backward_status(flags=1) == 3                # prologue flags: unsupported
+    assert backward_status(flags=8) == 3                # unknown prologue flag
     assert backward_status(dk=96) == 3
     assert backward_status(N=2, B=1) == 2               # N != B without cu_seqlens
     assert backward_status(dq=None) == 1

@@ -34,17 +34,18 @@ def grads_in(x, seed, dfinal=True):
     return do, ds
 
 
-def run_both(x, do, ds):
+def run_both(x, do, ds, flags=0):
     got = kda.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do,
                        cu_seqlens=x["cu_seqlens"], initial_state=x["initial_state"],
-                       dfinal_state=ds)
+                       dfinal_state=ds, normalize_k=bool(flags & 1), beta_logit=bool(flags & 2),
+                       gate_logit=bool(flags & 4))
     torch.cuda.synchronize()
     f = ki.to_f64
     ref = oracle_backward(
         f(x["q"]), f(x["k"]), f(x["v"]), None if x["g"] is None else f(x["g"]), f(x["beta"]),
         f(do), cu_seqlens=None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu().numpy(),
         initial_state=None if x["initial_state"] is None else f(x["initial_state"]),
-        dfinal_state=None if ds is None else f(ds))
+        dfinal_state=None if ds is None else f(ds), flags=flags)
     return got, ref
 
 
@@ -201,3 +202,23 @@ def test_backward_full_size_sampled_window():
         a = ki.to_f64(a[0, T - W:, heads].transpose(0, 1))
         err = check("bf16", a, r, f"full-size window {name}")
         print(f"  full-size window {name}: rms-rel {err:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("decay,flags", [("channel", 7), ("head", 7), ("none", 7),
+                                         ("channel", 1), ("channel", 2), ("channel", 4)])
+def test_backward_prologue(decay, flags):
+    """Gradients with respect to the raw projections of the fused prologue: raw keys
+    (through the L2 normalisation), beta logits (through the sigmoid) and retention
+    logits (through g = log sigmoid(a)); the oracle chains its own prologue."""
+    print(f"backward prologue decay={decay} flags={flags}", flush=True)
+    x = ki.make_prefill(H=3, d_k=128, d_v=128, dtype="bf16", lengths=[70, 1, 130], seed=79,
+                        init_state_std=0.02, device=DEV, decay=decay, raw=True)
+    if not flags & 1:   # keys as the plain entry points take them: unit rows
+        x["k"] = (x["k"].float() / x["k"].float().norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    if not flags & 2:
+        x["beta"] = torch.sigmoid(x["beta"])
+    if not flags & 4 and x["g"] is not None:
+        x["g"] = -torch.nn.functional.softplus(-x["g"])
+    do, ds = grads_in(x, 179)
+    got, ref = run_both(x, do, ds, flags)
+    compare(x, got, ref, f"prologue {decay} {flags}")
