@@ -299,6 +299,7 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
   unsigned char* states = static_cast<unsigned char*>(workspace) + plan.ring;
   unsigned char* dstates = states + plan.states;
   const int cus = cu_count();
+  bool tiles_done = false;   // the producer/consumer sweep also wrote the chunk tiles
   if (tot > 0) {
     kda::PrefillArgs a{};
     a.q = q;
@@ -317,6 +318,7 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
     a.decay = decay;
     a.flags = flags;
     a.chunk_states = states;
+    a.chunk_tiles = dstates + plan.states;
     bool done = false;
     if (plan.ring > 0) {
       a.workspace = static_cast<unsigned char*>(workspace);
@@ -326,6 +328,7 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
       done = kda::launch_prefill_coop_states(a, stream) == hipSuccess;
       if (!done) (void)hipGetLastError();   // not launchable as one resident grid
     }
+    tiles_done = done;
     if (!done) {
       a.workspace = nullptr;
       const int bv = choose_bv(KDA_BF16, static_cast<int32_t>(units), d_k, d_v, cus);
@@ -362,7 +365,9 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
   b.decay = decay;
   b.flags = flags;
   b.scale = scale;
-  if (kda::launch_backward_chain(d_k, b, stream) != hipSuccess) return KDA_ERR_HIP;   // tiles + chain
+  if (tot > 0 && !tiles_done && kda::launch_backward_tiles(d_k, b, stream) != hipSuccess)
+    return KDA_ERR_HIP;
+  if (kda::launch_backward_chain(d_k, b, stream) != hipSuccess) return KDA_ERR_HIP;
   if (tot > 0 && kda::launch_backward_grads(d_k, b, stream) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }

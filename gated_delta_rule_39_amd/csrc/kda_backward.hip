@@ -20,8 +20,9 @@
 // Four launches on one stream:
 //   1. forward sweep (prefill_kernel with STATES): the state at every chunk start,
 //      bf16, into the workspace;
-//   2. bwd_tiles_kernel: one workgroup per (chunk, head) computes the chunk's factors
-//      (Ki, Qg, Kg, X, M, beta, e^{G_n}) once into the workspace; then bwd_chain_kernel:
+//   2. the chunk's factors Ki, Qg, Kg, X diag(beta), M, e^{G_n} once into the workspace:
+//      written by the forward sweep's producers (the producer/consumer kernel), else by
+//      bwd_tiles_kernel (one workgroup per chunk and head); then bwd_chain_kernel:
 //      per (unit, 16 value rows), the chunks in reverse order, streaming those tiles
 //      through two LDS buffers; the chain above only (its value columns are
 //      independent), writing dH' of every chunk (bf16) and dL/dS_0;
@@ -38,6 +39,10 @@
 #include "kda_wy.h"
 
 namespace kda {
+
+static_assert(ChainTiles<64>::kBytes == chain_tile_bytes(64) &&
+                  ChainTiles<128>::kBytes == chain_tile_bytes(128),
+              "host and device chunk-tile sizes agree");
 
 using MB = Mfma<bf16>;
 
@@ -68,39 +73,6 @@ __device__ __forceinline__ bool slot_chunk(const BwdArgs& a, int64_t slot, int& 
   return cc >= 0 && cc * kChunk < eos - bos;
 }
 
-// Per (chunk slot, head), in the workspace, as 16-byte pieces: Ki, Qg, Kg [64][DK] bf16,
-// X, M [64][64] bf16, beta [64] fp32, e^{G_n} [DK] fp32 (rows past a ragged chunk's end
-// are zero; X has identity rows there).  The chain reads them into LDS tiles with the
-// row padding of kda_chunk.h.
-template <int DK>
-struct ChainTiles {
-  static constexpr int PK = kChunk * DK / 8;       // pieces of a [64][DK] tile
-  static constexpr int PC = kChunk * kChunk / 8;   // of a [64][64] tile
-  static constexpr int PB = kChunk * 4 / 16, PE = DK * 4 / 16;
-  static constexpr int kPieces = 3 * PK + 2 * PC + PB + PE;
-  static constexpr size_t kBytes = size_t(kPieces) * 16;
-  static_assert(kBytes == chain_tile_bytes(DK), "host and device tile sizes agree");
-};
-
-// LDS byte offset of piece p, given the byte offsets of the seven tiles (Ki, Qg, Kg, X,
-// M, beta, e^{G_n}) with row strides DK + 8 and 64 + 8 (bf16).
-template <int DK>
-__device__ __forceinline__ uint32_t piece_lds(const uint32_t (&off)[7], int p) {
-  using TL = ChainTiles<DK>;
-  constexpr int RK = DK / 8;
-  if (p < 3 * TL::PK) {
-    const int t = p / TL::PK, q = p % TL::PK;
-    return off[t] + ((q / RK) * (DK + 8) + 8 * (q % RK)) * 2;
-  }
-  p -= 3 * TL::PK;
-  if (p < 2 * TL::PC) {
-    const int t = p / TL::PC, q = p % TL::PC;
-    return off[3 + t] + ((q / 8) * (kChunk + 8) + 8 * (q % 8)) * 2;
-  }
-  p -= 2 * TL::PC;
-  return p < TL::PB ? off[5] + 16 * p : off[6] + 16 * (p - TL::PB);
-}
-
 // One workgroup per (chunk slot, head): the chunk's factors (as the forward computes
 // them), copied to the workspace.
 template <int DK, int DECAY>
@@ -125,11 +97,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_tiles_kernel(BwdArgs a) {
   cp.template factors<DECAY>(n, false, 0, 0);
   cp.products();
   cp.inverse();   // ends with a barrier
-  constexpr uint32_t off[7] = {CL::oKi, CL::oQg, CL::oKg, CL::oTm, CL::oM, CL::oBeta, CL::oEgn};
+  constexpr uint32_t off[6] = {CL::oKi, CL::oQg, CL::oKg, CL::oTm, CL::oM, CL::oEgn};
   u32x4* dst = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.tiles) +
                                         (slot * a.H + h) * TL::kBytes);
-  for (int p = tid; p < TL::kPieces; p += kThreads)
-    dst[p] = *reinterpret_cast<const u32x4*>(smem + piece_lds<DK>(off, p));
+  for (int p = tid; p < TL::kPieces; p += kThreads) {
+    u32x4 x = *reinterpret_cast<const u32x4*>(smem + piece_lds<DK>(off, p));
+    if (p >= 3 * TL::PK && p < 3 * TL::PK + TL::PC) {
+      // this kernel's inverse is X itself: the tile holds X diag(beta)
+      const int s0 = 8 * ((p - 3 * TL::PK) % 8);
+      bf16x8 xb = __builtin_bit_cast(bf16x8, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        xb[e] = static_cast<bf16>(static_cast<float>(xb[e]) * cp.sBeta[s0 + e]);
+      x = __builtin_bit_cast(u32x4, xb);
+    }
+    dst[p] = x;
+  }
 }
 
 // ====================================================================================
@@ -141,9 +124,9 @@ struct ChainLayout {
   static constexpr int LDK = DK + 8, LDC = kChunk + 8;
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
   static constexpr size_t tK = size_t(kChunk) * LDK * 2, tC = size_t(kChunk) * LDC * 2;
-  // one buffer of chunk tiles: Ki, Qg, Kg, X, M, beta, e^{G_n}
+  // one buffer of chunk tiles: Ki, Qg, Kg, X diag(beta), M, e^{G_n}
   static constexpr size_t oKi = 0, oQg = tK, oKg = 2 * tK, oX = 3 * tK, oM = 3 * tK + tC;
-  static constexpr size_t oB = 3 * tK + 2 * tC, oE = oB + kChunk * 4;
+  static constexpr size_t oE = 3 * tK + 2 * tC;
   static constexpr size_t kBuf = al(oE + DK * 4);
   static constexpr size_t oP = 2 * kBuf;                               // [BV][LDK]
   static constexpr size_t oDOT = al(oP + size_t(BV) * LDK * 2);       // [BV][LDC] each
@@ -155,7 +138,7 @@ struct ChainLayout {
 
 // Per (unit, BV value rows), the chunks in reverse order; each chunk's tiles are read
 // from the workspace one chunk ahead into the other of two LDS buffers.
-template <int DK, int BV, int DECAY>
+template <int DK, int BV>
 __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
   using CL = ChainLayout<DK, BV>;
   using TL = ChainTiles<DK>;
@@ -168,7 +151,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
   bf16* sDOT = reinterpret_cast<bf16*>(smem + CL::oDOT);
   bf16* sDET = reinterpret_cast<bf16*>(smem + CL::oDET);
   bf16* sGT = reinterpret_cast<bf16*>(smem + CL::oGT);
-  constexpr uint32_t off[7] = {CL::oKi, CL::oQg, CL::oKg, CL::oX, CL::oM, CL::oB, CL::oE};
+  constexpr uint32_t off[6] = {CL::oKi, CL::oQg, CL::oKg, CL::oX, CL::oM, CL::oE};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -223,9 +206,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
     const bf16* sKi = reinterpret_cast<const bf16*>(buf + CL::oKi);
     const bf16* sQg = reinterpret_cast<const bf16*>(buf + CL::oQg);
     const bf16* sKg = reinterpret_cast<const bf16*>(buf + CL::oKg);
-    const bf16* sX = reinterpret_cast<const bf16*>(buf + CL::oX);
+    const bf16* sTm = reinterpret_cast<const bf16*>(buf + CL::oX);   // X diag(beta)
     const bf16* sM = reinterpret_cast<const bf16*>(buf + CL::oM);
-    const float* sBeta = reinterpret_cast<const float*>(buf + CL::oB);
     const float* sEgn = reinterpret_cast<const float*>(buf + CL::oE);
     const int64_t c0 = bos + int64_t(c) * kChunk;
     const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
@@ -265,17 +247,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
     }
     lds_barrier();
 
-    // G = -beta X^T dE -> G^T
-    {
-      const f32x4 bt = *reinterpret_cast<const f32x4*>(sBeta + 16 * wave + 4 * lq);
+    // G = -diag(beta) X^T dE = -(X diag(beta))^T dE -> G^T
 #pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kk = k0m; kk < kChunk; kk += 32)
-          acc = mma_bf16(frag_tr(sX, LDC, kk, 16 * wave, lane), frow(sDET, LDC, 16 * vb, kk, lane),
-                         acc);
-        store4(sGT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, -(bt * acc));
-      }
+    for (int vb = 0; vb < NVB; ++vb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = k0m; kk < kChunk; kk += 32)
+        acc = mma_bf16(frag_tr(sTm, LDC, kk, 16 * wave, lane), frow(sDET, LDC, 16 * vb, kk, lane),
+                       acc);
+      store4(sGT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, -acc);
     }
     lds_barrier();
 
@@ -797,25 +776,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
 // ====================================================================================
 
 template <int DK, int DECAY>
-static hipError_t launch_chain_k(const BwdArgs& a, hipStream_t stream) {
+static hipError_t launch_tiles_k(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_tiles_kernel<DK, DECAY>), dim3(static_cast<unsigned>(a.slots * a.H)),
-                     dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_chain_kernel<DK, kBwdChainBV, DECAY>), dim3(a.units * a.NV),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_backward_chain(int dk, const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_backward_tiles(int dk, const BwdArgs& a, hipStream_t stream) {
   if (dk == 64) {
-    if (a.decay == 1) return launch_chain_k<64, 1>(a, stream);
-    if (a.decay == 2) return launch_chain_k<64, 2>(a, stream);
-    return launch_chain_k<64, 0>(a, stream);
+    if (a.decay == 1) return launch_tiles_k<64, 1>(a, stream);
+    if (a.decay == 2) return launch_tiles_k<64, 2>(a, stream);
+    return launch_tiles_k<64, 0>(a, stream);
   }
-  if (a.decay == 1) return launch_chain_k<128, 1>(a, stream);
-  if (a.decay == 2) return launch_chain_k<128, 2>(a, stream);
-  return launch_chain_k<128, 0>(a, stream);
+  if (a.decay == 1) return launch_tiles_k<128, 1>(a, stream);
+  if (a.decay == 2) return launch_tiles_k<128, 2>(a, stream);
+  return launch_tiles_k<128, 0>(a, stream);
+}
+
+template <int DK>
+static hipError_t launch_chain_k(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_chain_kernel<DK, kBwdChainBV>), dim3(a.units * a.NV), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_chain(int dk, const BwdArgs& a, hipStream_t stream) {
+  return dk == 64 ? launch_chain_k<64>(a, stream) : launch_chain_k<128>(a, stream);
 }
 
 template <int DK, int DV>

@@ -34,6 +34,7 @@ struct PrefillArgs {
   int32_t flags;              // prologue flags (kda_device.h: kNormK, kBetaLogit, kGateLogit)
   float scale;
   void* chunk_states;         // STATES instantiations: bf16 state at every chunk start
+  void* chunk_tiles;          // STATES producer/consumer kernel: each chunk's factor tiles
 };
 
 // Backward: the forward sweep that writes the chunk-start states (fused kernel, bf16,

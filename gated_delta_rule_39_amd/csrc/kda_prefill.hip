@@ -542,6 +542,25 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   }
 }
 
+// A producer's chunk tiles for the backward's reverse chain (ChainTiles): Ki, Qg, Kg,
+// X diag(beta) and e^{G_n} from its LDS; of M, products<true>() wrote the blocks on and
+// below the diagonal, the blocks above it are zero.
+template <int DK, int DV>
+__device__ __forceinline__ void publish_chain_tiles(const unsigned char* smem, u32x4* dst,
+                                                    int tid) {
+  using TL = ChainTiles<DK>;
+  using PL = WyProducerLayout<DK, DV>;
+  constexpr uint32_t off[6] = {PL::oKi, PL::oQg, PL::oKg, PL::oTm, 0, PL::oEgn};
+  for (int p = tid; p < TL::kPieces; p += kThreads) {
+    const int q = p - (3 * TL::PK + TL::PC);
+    if (q >= 0 && q < TL::PC) {
+      if ((8 * (q % 8)) / 16 > (q / 8) / 16) dst[p] = u32x4{0u, 0u, 0u, 0u};
+    } else {
+      dst[p] = *reinterpret_cast<const u32x4*>(smem + piece_lds<DK>(off, p));
+    }
+  }
+}
+
 template <int DK, int DV>
 struct WyLds {
   static constexpr size_t kCons = WyConsumerLayout<DK, DV>::kBytes > WySplitLayout::kBytes
@@ -645,10 +664,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       lds_barrier();
       if (pFlag[0] == 0) break;
       const uint32_t slot = static_cast<uint32_t>(s) * SL::kBytes;
+      // STATES: this chunk's tiles for the backward's reverse chain
+      [[maybe_unused]] unsigned char* tiles = nullptr;
+      if constexpr (STATES)
+        tiles = static_cast<unsigned char*>(a.chunk_tiles) +
+                ((chunk_slot_base(n_seq, bos) + c) * a.H + h) * ChainTiles<DK>::kBytes;
       // the next chunk's inputs are requested in five slices between the phases
       constexpr int L = PR::kLoads, RPG = PR::RPG;
       if (has_next) pr.template load_slice<DECAY, 0, RPG / 2>(c1, n1);            // g, first half
-      pr.products(rr, slot);
+      if constexpr (STATES)
+        pr.template products<true>(rr, slot, reinterpret_cast<bf16*>(tiles + ChainTiles<DK>::oM));
+      else
+        pr.products(rr, slot);
       if (has_next) pr.template load_slice<DECAY, RPG / 2, RPG>(c1, n1);          // g, second half
       lds_barrier();
       if (has_next) pr.template load_slice<DECAY, RPG, 2 * RPG>(c1, n1);          // k
@@ -663,6 +690,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       pr.inverse_rest();
       if (has_next) pr.template load_slice<DECAY, 3 * RPG, L>(c1, n1);            // v, beta
       pr.publish_wu(rr, slot);
+      if constexpr (STATES) publish_chain_tiles<DK, DV>(smem, reinterpret_cast<u32x4*>(tiles), tid);
       // every slot store of the workgroup acknowledged (device-visible), then publish
       vm_barrier();
       if (tid == 0) __hip_atomic_store(ready + s, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

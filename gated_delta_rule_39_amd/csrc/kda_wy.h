@@ -392,7 +392,11 @@ struct WyProducer {
   // Waves 0, 1: A = strict-lower(diag(beta) Kg Ki^T) into LDS (fp32).
   // Waves 2, 3: M^T = Ki Qg^T (tiles (a, b), a <= b, masked to a row <= column) and
   // its M fragments straight to the ring slot.  No closing barrier.
-  __device__ __forceinline__ void products(__amdgpu_buffer_rsrc_t rr, uint32_t slot) {
+  // TILES: waves 2, 3 also write M itself, row-major bf16 [64][64], to mt (global; the
+  // blocks on and below the diagonal, masked as published).
+  template <bool TILES = false>
+  __device__ __forceinline__ void products(__amdgpu_buffer_rsrc_t rr, uint32_t slot,
+                                           bf16* mt = nullptr) {
     const int lq = lane >> 4, lr = lane & 15;
     f32x4 acc[5];
     if (wave < 2) {
@@ -451,6 +455,27 @@ struct WyProducer {
       // b = 2: fragments (2, 0) = tiles (0, 2), (1, 2); (2, 1) = (2, 2)diag, 0
       st16(rr, base + 2 * SL::kFrag, pack_frag(acc[2], acc[3]));
       st16(rr, base + 4 * SL::kFrag, pack_frag(diag(acc[4]), z));
+    }
+    if constexpr (TILES) {
+      // tile (a, b) holds M[16 b + lr][16 a + 4 lq + i]
+      auto put = [&](int ta, int tb, f32x4 t) {
+        *reinterpret_cast<bf16x4*>(mt + (16 * tb + lr) * kChunk + 16 * ta + 4 * lq) =
+            bf16x4{static_cast<bf16>(t[0]), static_cast<bf16>(t[1]), static_cast<bf16>(t[2]),
+                   static_cast<bf16>(t[3])};
+      };
+      if (wave == 2) {
+        put(0, 0, diag(acc[0]));
+        put(0, 3, acc[1]);
+        put(1, 3, acc[2]);
+        put(2, 3, acc[3]);
+        put(3, 3, diag(acc[4]));
+      } else {
+        put(0, 1, acc[0]);
+        put(1, 1, diag(acc[1]));
+        put(0, 2, acc[2]);
+        put(1, 2, acc[3]);
+        put(2, 2, diag(acc[4]));
+      }
     }
   }
 
