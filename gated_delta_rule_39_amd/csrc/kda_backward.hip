@@ -297,12 +297,14 @@ struct GradLayout {
   static constexpr size_t a2 = kBytes, a2end = kLds;
   static constexpr size_t tV = size_t(VS) * LDK * 2;              // [VS][LDK] bf16
   static constexpr size_t tT = size_t(VS) * LDC * 2;              // [VS][LDC] bf16
+  static constexpr int LDV = VS + 8;                              // [64][LDV] bf16 rows
+  static constexpr size_t tR = size_t(kChunk) * LDV * 2;
   static constexpr size_t tC = size_t(kChunk) * LDC * 2;          // [64][LDC] bf16
   static constexpr size_t tW = size_t(DK) * LDC * 2;              // [DK][LDC] bf16
   // value-slice phase
   static constexpr size_t oH = a1, oDH = a1 + tV, oP = a1 + 2 * tV, oRT = a1 + 3 * tV;
-  static constexpr size_t oET = a2, oDET = a2 + tT, oDOT = a2 + 2 * tT, oVT = a2 + 3 * tT;
-  static_assert(oRT + tT <= a1end && oVT + tT <= a2end, "value-slice tiles overflow");
+  static constexpr size_t oET = a2, oDET = a2 + tT, oDO = a2 + 2 * tT, oV = oDO + tR;
+  static_assert(oRT + tT <= a1end && oV + tR <= a2end, "value-slice tiles overflow");
   // chunk-local phase
   static constexpr size_t oDWT = a1, oDMT = a1 + tW;
   static constexpr size_t oCC1 = a2, oCC2 = a2 + tC, oCC3 = CL::oM;
@@ -310,9 +312,9 @@ struct GradLayout {
   // gradients: raw k, q tiles (then dk, dq) and the reduction scratch
   static constexpr size_t tK = size_t(kChunk) * LDK * 2;
   static constexpr size_t oK = a1, oQ = a1 + tK;
-  static constexpr size_t oRed = a2;                              // fp32 [8 + NPART][DK]
+  static constexpr size_t oRed = a2;                              // fp32 [12][DK]
   static_assert(oQ + tK <= a1end, "k/q tiles overflow");
-  static_assert(oRed + size_t(8 + kThreads / DK) * DK * 4 <= a2end, "reduction overflow");
+  static_assert(oRed + size_t(12) * DK * 4 <= a2end, "reduction overflow");
   static_assert(kBytes <= kLds, "LDS budget exceeded");
 };
 
@@ -391,8 +393,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   bf16* sRT = reinterpret_cast<bf16*>(smem + GL::oRT);
   bf16* sET = reinterpret_cast<bf16*>(smem + GL::oET);
   bf16* sDET = reinterpret_cast<bf16*>(smem + GL::oDET);
-  bf16* sDOT = reinterpret_cast<bf16*>(smem + GL::oDOT);
-  bf16* sVT = reinterpret_cast<bf16*>(smem + GL::oVT);
+  bf16* sDO = reinterpret_cast<bf16*>(smem + GL::oDO);   // dO slice [64][LDV], token rows
+  bf16* sV = reinterpret_cast<bf16*>(smem + GL::oV);     // V slice [64][LDV]
+  constexpr int LDV = GL::LDV;
 
   f32x4 dQg[NKB], dWn[NKB], dKh[NKB], dM[4], dXU[4];
 #pragma unroll
@@ -400,13 +403,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) dM[i] = dXU[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 dbu = f32x4{0.f, 0.f, 0.f, 0.f};   // sum_v d(beta V) V for this lane's rows
-  float ddp = 0.f;                         // partial d e^{G_n}_j from H and dH'
-  constexpr int KPT = DK * VS / kThreads;  // (key, value) pairs per thread for ddp
-  const int dj = tid % DK, dpart = tid / DK;
+  float ddk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // d e^{G_n} of this thread's keys
 
   for (int vs = 0; vs < DV / VS; ++vs) {
     const int v0 = vs * VS;
-    // H, dH' (and P = D dH') slices [VS][DK]; V^T and dO^T slices [VS][64]
+    // H, dH' (and P = D dH') slices [VS][DK]; V and dO slices [64][VS]; d e^{G_n} partial
+    // sums of this thread's eight keys from the same registers
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
       const int idx = tid + i * kThreads;
@@ -415,72 +417,91 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       *reinterpret_cast<bf16x8*>(sDH + r * LDK + c8) = pdh[i];
       bf16x8 p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        p[e] = static_cast<bf16>(static_cast<float>(pdh[i][e]) * cp.sEgn[c8 + e]);
+      for (int e = 0; e < 8; ++e) {
+        const float dh = static_cast<float>(pdh[i][e]);
+        p[e] = static_cast<bf16>(dh * cp.sEgn[c8 + e]);
+        ddk[e] += dh * static_cast<float>(ph[i][e]);
+      }
       *reinterpret_cast<bf16x8*>(sP + r * LDK + c8) = p;
     }
     {
       const int r = tid / (VS / 8), c8 = 8 * (tid % (VS / 8));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sVT[(c8 + e) * LDC + r] = pv[e];
-        sDOT[(c8 + e) * LDC + r] = pdo[e];
-      }
+      *reinterpret_cast<bf16x8*>(sV + r * LDV + c8) = pv;
+      *reinterpret_cast<bf16x8*>(sDO + r * LDV + c8) = pdo;
     }
     if (vs + 1 < DV / VS) fetch_slice(vs + 1);
     lds_barrier();
     f32x4 vreg[VS / 16];   // V in accumulator layout (rows of this wave)
 #pragma unroll
     for (int vb = 0; vb < VS / 16; ++vb)
-      vreg[vb] = widen(*reinterpret_cast<const bf16x4*>(sVT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vreg[vb][i] = static_cast<float>(sV[(16 * wave + 4 * lq + i) * LDV + 16 * vb + lr]);
 
     // R' = beta (V - Kg H) -> R'^T;  dE = Ki P + M^T dO -> dE^T
+    {
+      f32x4 acc[VS / 16], de[VS / 16];
 #pragma unroll
-    for (int vb = 0; vb < VS / 16; ++vb) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, de = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int vb = 0; vb < VS / 16; ++vb) acc[vb] = de[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < DK; kk += 32) {
-        acc = mma_bf16(frow(cp.sKg, LDK, 16 * wave, kk, lane), frow(sH, LDK, 16 * vb, kk, lane), acc);
-        de = mma_bf16(frow(cp.sKi, LDK, 16 * wave, kk, lane), frow(sP, LDK, 16 * vb, kk, lane), de);
+        const bf16x8 aK = frow(cp.sKg, LDK, 16 * wave, kk, lane);
+        const bf16x8 aKi = frow(cp.sKi, LDK, 16 * wave, kk, lane);
+#pragma unroll
+        for (int vb = 0; vb < VS / 16; ++vb) {
+          acc[vb] = mma_bf16(aK, frow(sH, LDK, 16 * vb, kk, lane), acc[vb]);
+          de[vb] = mma_bf16(aKi, frow(sP, LDK, 16 * vb, kk, lane), de[vb]);
+        }
       }
-      for (int kk = k0m; kk < kChunk; kk += 32)
-        de = mma_bf16(frag_tr(cp.sM, LDC, kk, 16 * wave, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
-                      de);
-      store4(sRT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, bt * (vreg[vb] - acc));
-      store4(sDET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, de);
+      for (int kk = k0m; kk < kChunk; kk += 32) {
+        const bf16x8 aM = frag_tr(cp.sM, LDC, kk, 16 * wave, lane);
+#pragma unroll
+        for (int vb = 0; vb < VS / 16; ++vb)
+          de[vb] = mma_bf16(aM, frag_tr(sDO, LDV, kk, 16 * vb, lane), de[vb]);
+      }
+#pragma unroll
+      for (int vb = 0; vb < VS / 16; ++vb) {
+        store4(sRT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, bt * (vreg[vb] - acc[vb]));
+        store4(sDET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, de[vb]);
+      }
     }
     lds_barrier();
 
     // E = X R' -> E^T;  d(beta V) = X^T dE -> dv, and its dot with V
+    {
+      f32x4 e[VS / 16], dbv[VS / 16];
 #pragma unroll
-    for (int vb = 0; vb < VS / 16; ++vb) {
-      f32x4 e = f32x4{0.f, 0.f, 0.f, 0.f}, dbv = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int kk = 0; kk < kend; kk += 32)
-        e = mma_bf16(frow(cp.sTm, LDC, 16 * wave, kk, lane), frow(sRT, LDC, 16 * vb, kk, lane), e);
-      for (int kk = k0m; kk < kChunk; kk += 32)
-        dbv = mma_bf16(frag_tr(cp.sTm, LDC, kk, 16 * wave, lane),
-                       frow(sDET, LDC, 16 * vb, kk, lane), dbv);
-      store4(sET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, e);
-      dbu += dbv * vreg[vb];
+      for (int vb = 0; vb < VS / 16; ++vb) e[vb] = dbv[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < kend; kk += 32) {
+        const bf16x8 aT = frow(cp.sTm, LDC, 16 * wave, kk, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * lq + i;
-        if (r < n)
-          dvout[(c0 + r) * rowV + int64_t(h) * DV + v0 + 16 * vb + lr] =
-              static_cast<bf16>(bt[i] * dbv[i]);
+        for (int vb = 0; vb < VS / 16; ++vb)
+          e[vb] = mma_bf16(aT, frow(sRT, LDC, 16 * vb, kk, lane), e[vb]);
       }
-    }
-    // d e^{G_n}: sum over this slice's values of dH' H, per key
+      for (int kk = k0m; kk < kChunk; kk += 32) {
+        const bf16x8 aTt = frag_tr(cp.sTm, LDC, kk, 16 * wave, lane);
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      const int r = dpart * KPT + e;
-      ddp += static_cast<float>(sDH[r * LDK + dj]) * static_cast<float>(sH[r * LDK + dj]);
+        for (int vb = 0; vb < VS / 16; ++vb)
+          dbv[vb] = mma_bf16(aTt, frow(sDET, LDC, 16 * vb, kk, lane), dbv[vb]);
+      }
+#pragma unroll
+      for (int vb = 0; vb < VS / 16; ++vb) {
+        store4(sET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, e[vb]);
+        dbu += dbv[vb] * vreg[vb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * wave + 4 * lq + i;
+          if (r < n)
+            dvout[(c0 + r) * rowV + int64_t(h) * DV + v0 + 16 * vb + lr] =
+                static_cast<bf16>(bt[i] * dbv[vb][i]);
+        }
+      }
     }
     lds_barrier();
 
     // contractions over this slice's values (K = 32 = one MFMA step)
     {
-      const bf16x8 aDO = frag_tr(sDOT, LDC, 0, 16 * wave, lane);
+      const bf16x8 aDO = frow(sDO, LDV, 16 * wave, 0, lane);
       const bf16x8 aDE = frag_tr(sDET, LDC, 0, 16 * wave, lane);
       const bf16x8 aE = frag_tr(sET, LDC, 0, 16 * wave, lane);
 #pragma unroll
@@ -493,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {
         dM[sb] = mma_bf16(aDO, frag_tr(sET, LDC, 0, 16 * sb, lane), dM[sb]);
-        dXU[sb] = mma_bf16(aDE, frag_tr(sVT, LDC, 0, 16 * sb, lane), dXU[sb]);
+        dXU[sb] = mma_bf16(aDE, frow(sV, LDV, 16 * sb, 0, lane), dXU[sb]);
       }
     }
     lds_barrier();
@@ -613,8 +634,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   // per element: dk, dq, and dL/dG = dKg Kg + dQg Qg - dKi Ki - dKh Kh, summed over the
   // rows at or below it within this wave's token block (suffix); the block totals, the
   // dG_n partials and the d e^{G_n} partials go to LDS
-  float* sRed = reinterpret_cast<float*>(smem + GL::oRed);   // [4][DK] [4][DK] [NPART][DK]
-  constexpr int NPART = kThreads / DK;
+  float* sRed = reinterpret_cast<float*>(smem + GL::oRed);   // [4][DK] [4][DK] [4][DK]
   f32x4 dbk = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 gm[NKB];
   // raw keys: the factors used the unit key bf16(k / n), n = sqrt(|k|^2 + eps) per row;
@@ -678,7 +698,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       sRed[(4 + wave) * DK + j] = gn;
     }
   }
-  sRed[(8 + dpart) * DK + dj] = ddp;
+  // d e^{G_n}: the threads holding the same eight keys (equal tid mod DK / 8) add up,
+  // within the wave by shuffles and across the waves in the dg stage
+  {
+    constexpr int G = DK / 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int m = G; m < 64; m *= 2) ddk[e] += __shfl_xor(ddk[e], m);
+    if (lane < G) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sRed[(8 + wave) * DK + 8 * lane + e] = ddk[e];
+    }
+  }
   if (norm_k) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) kdot[i] = row_sum<16>(kdot[i]);
@@ -732,7 +764,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       const int j = 16 * kb + lr;
       float dd = 0.f;
 #pragma unroll
-      for (int p = 0; p < NPART; ++p) dd += sRed[(8 + p) * DK + j];
+      for (int p = 0; p < 4; ++p) dd += sRed[(8 + p) * DK + j];
       float add = dd * cp.sEgn[j];
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2) {
