@@ -556,12 +556,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
 
   // dX = (dE V^T + dW Kg^T) Diag(beta), strictly lower -> dX^T (sC1)
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
-    f32x4 acc = dXU[sb];
+  for (int kk = 0; kk < DK; kk += 32) {
+    const bf16x8 aW = frag_tr(sDWT, LDC, kk, 16 * wave, lane);
 #pragma unroll
-    for (int kk = 0; kk < DK; kk += 32)
-      acc = mma_bf16(frag_tr(sDWT, LDC, kk, 16 * wave, lane), frow(cp.sKg, LDK, 16 * sb, kk, lane),
-                     acc);
+    for (int sb = 0; sb < 4; ++sb)
+      dXU[sb] = mma_bf16(aW, frow(cp.sKg, LDK, 16 * sb, kk, lane), dXU[sb]);
+  }
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    const f32x4 acc = dXU[sb];
     const float bs = cp.sBeta[16 * sb + lr];
     f32x4 x;
 #pragma unroll
@@ -571,23 +574,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   lds_barrier();
 
   // Y = dX X^T -> Y^T (sC2)
+  {
+    f32x4 acc[4];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kk = 0; kk < kend; kk += 32)
-      acc = mma_bf16(frag_tr(sC1, LDC, kk, 16 * wave, lane), frow(cp.sTm, LDC, 16 * jb, kk, lane),
-                     acc);
-    store4(sC2 + (16 * jb + lr) * LDC + 16 * wave + 4 * lq, acc);
+    for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < kend; kk += 32) {
+      const bf16x8 aX = frag_tr(sC1, LDC, kk, 16 * wave, lane);
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+        acc[jb] = mma_bf16(aX, frow(cp.sTm, LDC, 16 * jb, kk, lane), acc[jb]);
+    }
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) store4(sC2 + (16 * jb + lr) * LDC + 16 * wave + 4 * lq, acc[jb]);
   }
   lds_barrier();
 
   // dA = -strict_lower(X^T Y) -> dA^T (sC1) and (Diag(beta) dA)^T (sC3)
+  f32x4 dAacc[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) dAacc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = k0m; kk < kChunk; kk += 32) {
+    const bf16x8 aXt = frag_tr(cp.sTm, LDC, kk, 16 * wave, lane);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) dAacc[jb] = mma_bf16(aXt, frow(sC2, LDC, 16 * jb, kk, lane), dAacc[jb]);
+  }
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kk = k0m; kk < kChunk; kk += 32)
-      acc = mma_bf16(frag_tr(cp.sTm, LDC, kk, 16 * wave, lane), frow(sC2, LDC, 16 * jb, kk, lane),
-                     acc);
+    const f32x4 acc = dAacc[jb];
     f32x4 x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = 16 * jb + lr < 16 * wave + 4 * lq + i ? -acc[i] : 0.f;
@@ -597,23 +610,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   lds_barrier();
 
   // d(beta Kg) = X^T dW + dA Ki;  dKi = dA^T (beta Kg) + dM^T Qg;  dQg += dM Ki
+  // (the A operands depend on the K step only: loaded once per step for all key blocks)
   f32x4 dBk[NKB], dKi[NKB];
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    f32x4 b = f32x4{0.f, 0.f, 0.f, 0.f}, ki = f32x4{0.f, 0.f, 0.f, 0.f}, qg = dQg[kb];
-    for (int kk = k0m; kk < kChunk; kk += 32) {
-      b = mma_bf16(frag_tr(cp.sTm, LDC, kk, 16 * wave, lane), frow(sDWT, LDC, 16 * kb, kk, lane), b);
-      ki = mma_bf16(frow(sC3, LDC, 16 * wave, kk, lane), frag_tr(cp.sKg, LDK, kk, 16 * kb, lane), ki);
-      ki = mma_bf16(frow(sDMT, LDC, 16 * wave, kk, lane), frag_tr(cp.sQg, LDK, kk, 16 * kb, lane), ki);
+  for (int kb = 0; kb < NKB; ++kb) dBk[kb] = dKi[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = k0m; kk < kChunk; kk += 32) {
+    const bf16x8 aXt = frag_tr(cp.sTm, LDC, kk, 16 * wave, lane);
+    const bf16x8 aAb = frow(sC3, LDC, 16 * wave, kk, lane);
+    const bf16x8 aMt = frow(sDMT, LDC, 16 * wave, kk, lane);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      dBk[kb] = mma_bf16(aXt, frow(sDWT, LDC, 16 * kb, kk, lane), dBk[kb]);
+      dKi[kb] = mma_bf16(aAb, frag_tr(cp.sKg, LDK, kk, 16 * kb, lane), dKi[kb]);
+      dKi[kb] = mma_bf16(aMt, frag_tr(cp.sQg, LDK, kk, 16 * kb, lane), dKi[kb]);
     }
-    for (int kk = 0; kk < kend; kk += 32) {
+  }
+  for (int kk = 0; kk < kend; kk += 32) {
+    const bf16x8 aA = frag_tr(sC1, LDC, kk, 16 * wave, lane);
+    const bf16x8 aM = frag_tr(sDMT, LDC, kk, 16 * wave, lane);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
       const bf16x8 bKi = frag_tr(cp.sKi, LDK, kk, 16 * kb, lane);
-      b = mma_bf16(frag_tr(sC1, LDC, kk, 16 * wave, lane), bKi, b);
-      qg = mma_bf16(frag_tr(sDMT, LDC, kk, 16 * wave, lane), bKi, qg);
+      dBk[kb] = mma_bf16(aA, bKi, dBk[kb]);
+      dQg[kb] = mma_bf16(aM, bKi, dQg[kb]);
     }
-    dBk[kb] = b;
-    dKi[kb] = ki;
-    dQg[kb] = qg;
   }
   lds_barrier();
 
