@@ -211,24 +211,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
     const float* sEgn = reinterpret_cast<const float*>(buf + CL::oE);
     const int64_t c0 = bos + int64_t(c) * kChunk;
     const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
-    if (c > 0) fetch(c - 1);   // the previous chunk in token order (always full)
-    // dL/d(state after chunk c)
-    store_state_bf16<DK, BV>(sacc, dstates, ((slot0 + c) * a.H + h) * a.DV * DK, v0, wave,
-                             lane);
-
-    // P = D dH' (accumulators and snapshot), dO^T tile
-#pragma unroll
-    for (int s = 0; s < ST::NST; ++s) {
-      const int kb = ST::kb(wave, s), vb = ST::vb(s);
-      sacc[s] *= *reinterpret_cast<const f32x4*>(sEgn + 16 * kb + 4 * lq);
-      store4(sP + (16 * vb + lr) * LDK + 16 * kb + 4 * lq, sacc[s]);
-    }
+    // dO^T of this chunk first (its rows were requested a chunk ago), then the requests
+    // for the previous chunk's tiles: a wait for the former never includes the latter
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
       f32x4 x;
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = 16 * wave + 4 * lq + i < n ? dr.f32(vb, i) : 0.f;
       store4(sDOT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, x);
+    }
+    if (c > 0) fetch(c - 1);   // the previous chunk in token order (always full)
+    // dL/d(state after chunk c)
+    store_state_bf16<DK, BV>(sacc, dstates, ((slot0 + c) * a.H + h) * a.DV * DK, v0, wave,
+                             lane);
+
+    // P = D dH' (accumulators and snapshot)
+#pragma unroll
+    for (int s = 0; s < ST::NST; ++s) {
+      const int kb = ST::kb(wave, s), vb = ST::vb(s);
+      sacc[s] *= *reinterpret_cast<const f32x4*>(sEgn + 16 * kb + 4 * lq);
+      store4(sP + (16 * vb + lr) * LDK + 16 * kb + 4 * lq, sacc[s]);
     }
     if (c > 0) dr.load(dout, c0 - kChunk, kChunk, a.H, h, a.DV, v0, wave, lane);
     lds_barrier();
