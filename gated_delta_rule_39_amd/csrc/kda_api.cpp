@@ -237,6 +237,8 @@ int kda_decode_step(int dtype, const void* q, const void* k, const void* v, cons
                             d_v, scale, stream);
 }
 
+}  // extern "C"
+
 namespace {
 // Backward workspace: [producer/consumer ring of the forward sweep, when that kernel
 // applies (d_k = d_v = 128, two consumers) | chunk states | state gradients | chunk
@@ -260,6 +262,8 @@ BwdPlan bwd_plan(int32_t N, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v
   return b;
 }
 }  // namespace
+
+extern "C" {
 
 size_t kda_backward_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_t H, int32_t d_k,
                                     int32_t d_v) {

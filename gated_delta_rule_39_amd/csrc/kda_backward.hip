@@ -132,7 +132,8 @@ struct ChainLayout {
   static constexpr size_t oDOT = al(oP + size_t(BV) * LDK * 2);       // [BV][LDC] each
   static constexpr size_t oDET = al(oDOT + size_t(BV) * LDC * 2);
   static constexpr size_t oGT = al(oDET + size_t(BV) * LDC * 2);
-  static constexpr size_t kBytes = al(oGT + size_t(BV) * LDC * 2);
+  static constexpr size_t oTouch = al(oGT + size_t(BV) * LDC * 2);    // 256 B per wave, never read
+  static constexpr size_t kBytes = oTouch + 4 * 256;
   static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -190,6 +191,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
         *reinterpret_cast<u32x4*>(smem + buf * CL::kBuf + piece_lds<DK>(off, p)) = stage[i];
     }
   };
+  // Chunk c's tiles into L2 two chunks ahead of their use: one 4-byte read per 128-byte
+  // line, issued after the chunk's other reads (no wait for those covers these) and
+  // consumed at the chunk's end, a whole chunk later.
+  constexpr int kLines = static_cast<int>((TL::kBytes + 127) / 128);
+  constexpr int NT = (kLines + 4 * 64 - 1) / (4 * 64);   // reads per lane
+  uint32_t tw[NT], tacc = 0;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) tw[j] = 0;
+  auto touch = [&](int c) {
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(
+        tiles + ((slot0 + c) * a.H + h) * (TL::kBytes / 16));
+#pragma unroll
+    for (int j = 0; j < NT; ++j) tw[j] = base[32 * min(64 * (4 * j + wave) + lane, kLines - 1)];
+  };
   ValueRegs<bf16, NVB> dr;   // dO rows of the chunk, accumulator layout
   if (nch > 0) {
     const int64_t cl = bos + int64_t(nch - 1) * kChunk;
@@ -233,6 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
       store4(sP + (16 * vb + lr) * LDK + 16 * kb + 4 * lq, sacc[s]);
     }
     if (c > 0) dr.load(dout, c0 - kChunk, kChunk, a.H, h, a.DV, v0, wave, lane);
+    if (c > 1) touch(c - 2);
     lds_barrier();
 
     // dE = Ki P + M^T dO for token block `wave` -> dE^T
@@ -276,7 +292,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
     }
     if (c > 0) deposit(cur ^ 1);
     lds_barrier();
+#pragma unroll
+    for (int j = 0; j < NT; ++j) tacc ^= tw[j];
   }
+  // the touched words end in a scratch corner of LDS (volatile: the reads stay)
+  *reinterpret_cast<volatile uint32_t*>(smem + CL::oTouch + 4 * tid) = tacc;
 
   if (a.dinitial_state) store_state<DK, BV>(sacc, a.dinitial_state, st_base, v0, wave, lane);
 }

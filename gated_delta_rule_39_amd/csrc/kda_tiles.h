@@ -103,19 +103,22 @@ struct ChainTiles {
 };
 
 // LDS byte offset of piece p, given the byte offsets of the six tiles (Ki, Qg, Kg,
-// X diag(beta), M, e^{G_n}) with row strides DK + 8 and 64 + 8 (bf16).
+// X diag(beta), M, e^{G_n}) with row strides DK + 8 and 64 + 8 (bf16).  The tile's
+// offset is selected, not indexed: a run-time index into the table would put it in
+// memory and cost a load (and a wait) per piece.
 template <int DK>
 __device__ __forceinline__ uint32_t piece_lds(const uint32_t (&off)[6], int p) {
   using TL = ChainTiles<DK>;
   constexpr int RK = DK / 8;
   if (p < 3 * TL::PK) {
     const int t = p / TL::PK, q = p % TL::PK;
-    return off[t] + ((q / RK) * (DK + 8) + 8 * (q % RK)) * 2;
+    const uint32_t base = t == 0 ? off[0] : (t == 1 ? off[1] : off[2]);
+    return base + ((q / RK) * (DK + 8) + 8 * (q % RK)) * 2;
   }
   p -= 3 * TL::PK;
   if (p < 2 * TL::PC) {
     const int t = p / TL::PC, q = p % TL::PC;
-    return off[3 + t] + ((q / 8) * (kChunk + 8) + 8 * (q % 8)) * 2;
+    return (t == 0 ? off[3] : off[4]) + ((q / 8) * (kChunk + 8) + 8 * (q % 8)) * 2;
   }
   return off[5] + 16 * (p - 2 * TL::PC);
 }
