@@ -543,6 +543,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   }
 
   // ---- chunk-local algebra -------------------------------------------------------------
+  // Every slice read has landed (and the dv stores are acknowledged): saying so lets the
+  // compiler count the reads below exactly instead of waiting for all of them at the
+  // first reuse of a slice register.
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
   // the chunk's raw k and q rows, requested now for the gradients at the end
   constexpr int KPT2 = kChunk * DK / 8 / kThreads;
   bf16x8 pk[KPT2], pq[KPT2];
