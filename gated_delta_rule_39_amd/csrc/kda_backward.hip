@@ -97,18 +97,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_tiles_kernel(BwdArgs a) {
   cp.template factors<DECAY>(n, false, 0, 0);
   cp.products();
   cp.inverse();   // ends with a barrier
-  constexpr uint32_t off[6] = {CL::oKi, CL::oQg, CL::oKg, CL::oTm, CL::oM, CL::oEgn};
+  // -W = -X diag(beta) Kg for token block `wave` into the A area (dead after the
+  // inverse), bf16 rows with the stride of the other tiles
+  constexpr int LDK = CL::LDK, LDC = CL::LDC, NKB = DK / 16;
+  static_assert(LDK == DK + 8 && LDC == kChunk + 8, "tile row strides");
+  static_assert(size_t(kChunk) * LDK * 2 <= CL::oX - CL::oA, "W tile fits the A area");
+  bf16* sW = reinterpret_cast<bf16*>(smem + CL::oA);
+  {
+    const int lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    f32x4 acc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < 16 * (wave + 1); kk += 32) {   // X is lower triangular
+      bf16x8 xa = frow(cp.sTm, LDC, 16 * wave, kk, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        xa[e] = static_cast<bf16>(static_cast<float>(xa[e]) * cp.sBeta[kk + 8 * lq + e]);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        acc[kb] = mma_bf16(xa, frag_tr(cp.sKg, LDK, kk, 16 * kb, lane), acc[kb]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sW[(16 * wave + 4 * lq + i) * LDK + 16 * kb + lr] = static_cast<bf16>(-acc[kb][i]);
+  }
+  lds_barrier();
+  constexpr uint32_t off[5] = {CL::oKi, CL::oQg, CL::oA, CL::oM, CL::oEgn};
   u32x4* dst = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.tiles) +
                                         (slot * a.H + h) * TL::kBytes);
   for (int p = tid; p < TL::kPieces; p += kThreads) {
     u32x4 x = *reinterpret_cast<const u32x4*>(smem + piece_lds<DK>(off, p));
-    if (p >= 3 * TL::PK && p < 3 * TL::PK + TL::PC) {
-      // this kernel's inverse is X itself: the tile holds X diag(beta)
-      const int s0 = 8 * ((p - 3 * TL::PK) % 8);
+    if (p < TL::PK) {
+      // KD = Ki Diag(e^{G_n})
+      const int c8 = 8 * (p % (DK / 8));
       bf16x8 xb = __builtin_bit_cast(bf16x8, x);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        xb[e] = static_cast<bf16>(static_cast<float>(xb[e]) * cp.sBeta[s0 + e]);
+        xb[e] = static_cast<bf16>(static_cast<float>(xb[e]) * cp.sEgn[c8 + e]);
       x = __builtin_bit_cast(u32x4, xb);
     }
     dst[p] = x;
@@ -124,16 +151,14 @@ struct ChainLayout {
   static constexpr int LDK = DK + 8, LDC = kChunk + 8;
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
   static constexpr size_t tK = size_t(kChunk) * LDK * 2, tC = size_t(kChunk) * LDC * 2;
-  // one buffer of chunk tiles: Ki, Qg, Kg, X diag(beta), M, e^{G_n}
-  static constexpr size_t oKi = 0, oQg = tK, oKg = 2 * tK, oX = 3 * tK, oM = 3 * tK + tC;
-  static constexpr size_t oE = 3 * tK + 2 * tC;
+  // one buffer of chunk tiles: KD, Qg, -W, M, e^{G_n}
+  static constexpr size_t oKD = 0, oQg = tK, oW = 2 * tK, oM = 3 * tK, oE = 3 * tK + tC;
   static constexpr size_t kBuf = al(oE + DK * 4);
-  static constexpr size_t oP = 2 * kBuf;                               // [BV][LDK]
+  static constexpr size_t oP = 2 * kBuf;                               // dH'^T [BV][LDK]
   static constexpr size_t oDOT = al(oP + size_t(BV) * LDK * 2);       // [BV][LDC] each
   static constexpr size_t oDET = al(oDOT + size_t(BV) * LDC * 2);
-  static constexpr size_t oGT = al(oDET + size_t(BV) * LDC * 2);
-  static constexpr size_t oTouch = al(oGT + size_t(BV) * LDC * 2);    // 256 B per wave, never read
-  static constexpr size_t kBytes = oTouch + 4 * 256;
+  static constexpr size_t oTouch = al(oDET + size_t(BV) * LDC * 2);   // 4 B per thread, never read
+  static constexpr size_t kBytes = oTouch + size_t(kThreads) * 4;
   static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -151,8 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
   bf16* sP = reinterpret_cast<bf16*>(smem + CL::oP);
   bf16* sDOT = reinterpret_cast<bf16*>(smem + CL::oDOT);
   bf16* sDET = reinterpret_cast<bf16*>(smem + CL::oDET);
-  bf16* sGT = reinterpret_cast<bf16*>(smem + CL::oGT);
-  constexpr uint32_t off[6] = {CL::oKi, CL::oQg, CL::oKg, CL::oX, CL::oM, CL::oE};
+  constexpr uint32_t off[5] = {CL::oKD, CL::oQg, CL::oW, CL::oM, CL::oE};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -218,10 +242,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
   for (int c = nch - 1; c >= 0; --c) {
     const int cur = (nch - 1 - c) & 1;
     const unsigned char* buf = smem + cur * CL::kBuf;
-    const bf16* sKi = reinterpret_cast<const bf16*>(buf + CL::oKi);
+    const bf16* sKD = reinterpret_cast<const bf16*>(buf + CL::oKD);
     const bf16* sQg = reinterpret_cast<const bf16*>(buf + CL::oQg);
-    const bf16* sKg = reinterpret_cast<const bf16*>(buf + CL::oKg);
-    const bf16* sTm = reinterpret_cast<const bf16*>(buf + CL::oX);   // X diag(beta)
+    const bf16* sWn = reinterpret_cast<const bf16*>(buf + CL::oW);   // -W
     const bf16* sM = reinterpret_cast<const bf16*>(buf + CL::oM);
     const float* sEgn = reinterpret_cast<const float*>(buf + CL::oE);
     const int64_t c0 = bos + int64_t(c) * kChunk;
@@ -240,24 +263,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
     store_state_bf16<DK, BV>(sacc, dstates, ((slot0 + c) * a.H + h) * a.DV * DK, v0, wave,
                              lane);
 
-    // P = D dH' (accumulators and snapshot)
+    // dH' (operand of dE), then D dH' in the accumulators
 #pragma unroll
     for (int s = 0; s < ST::NST; ++s) {
       const int kb = ST::kb(wave, s), vb = ST::vb(s);
-      sacc[s] *= *reinterpret_cast<const f32x4*>(sEgn + 16 * kb + 4 * lq);
       store4(sP + (16 * vb + lr) * LDK + 16 * kb + 4 * lq, sacc[s]);
+      sacc[s] *= *reinterpret_cast<const f32x4*>(sEgn + 16 * kb + 4 * lq);
     }
     if (c > 0) dr.load(dout, c0 - kChunk, kChunk, a.H, h, a.DV, v0, wave, lane);
     if (c > 1) touch(c - 2);
     lds_barrier();
 
-    // dE = Ki P + M^T dO for token block `wave` -> dE^T
+    // dE = KD dH' + M^T dO for token block `wave` -> dE^T
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < DK; kk += 32)
-        acc = mma_bf16(frow(sKi, LDK, 16 * wave, kk, lane), frow(sP, LDK, 16 * vb, kk, lane), acc);
+        acc = mma_bf16(frow(sKD, LDK, 16 * wave, kk, lane), frow(sP, LDK, 16 * vb, kk, lane), acc);
       for (int kk = k0m; kk < kChunk; kk += 32)
         acc = mma_bf16(frag_tr(sM, LDC, kk, 16 * wave, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
                        acc);
@@ -265,18 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
     }
     lds_barrier();
 
-    // G = -diag(beta) X^T dE = -(X diag(beta))^T dE -> G^T
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int kk = k0m; kk < kChunk; kk += 32)
-        acc = mma_bf16(frag_tr(sTm, LDC, kk, 16 * wave, lane), frow(sDET, LDC, 16 * vb, kk, lane),
-                       acc);
-      store4(sGT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, -acc);
-    }
-    lds_barrier();
-
-    // dH = P + Qg^T dO + Kg^T G
+    // dH = D dH' + Qg^T dO - W^T dE
 #pragma unroll
     for (int s = 0; s < ST::NST; ++s) {
       const int kb = ST::kb(wave, s), vb = ST::vb(s);
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
       for (int kk = 0; kk < kChunk; kk += 32) {
         acc = mma_bf16(frag_tr(sQg, LDK, kk, 16 * kb, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
                        acc);
-        acc = mma_bf16(frag_tr(sKg, LDK, kk, 16 * kb, lane), frow(sGT, LDC, 16 * vb, kk, lane),
+        acc = mma_bf16(frag_tr(sWn, LDK, kk, 16 * kb, lane), frow(sDET, LDC, 16 * vb, kk, lane),
                        acc);
       }
       sacc[s] = acc;

@@ -41,10 +41,10 @@ constexpr int kBwdChainBV = 16;   // value rows per reverse-chain workgroup
 // Chunk slots of the backward's per-chunk buffers for T_total packed rows and N
 // sequences (slot indexing: chunk_slot_base in kda_tiles.h).
 inline int64_t chunk_slots_host(int64_t T_total, int32_t N) { return T_total / 64 + N + 1; }
-// Bytes of one chunk's reverse-chain tiles (ChainTiles in kda_tiles.h): Ki, Qg, Kg
-// [64][dk] and X diag(beta), M [64][64] bf16, e^{G_n} [dk] fp32.
+// Bytes of one chunk's reverse-chain tiles (ChainTiles in kda_tiles.h): KD, Qg, -W
+// [64][dk] and M [64][64] bf16, e^{G_n} [dk] fp32.
 constexpr size_t chain_tile_bytes(int dk) {
-  return size_t(3 * 64 * dk * 2 + 2 * 64 * 64 * 2 + dk * 4);
+  return size_t(3 * 64 * dk * 2 + 64 * 64 * 2 + dk * 4);
 }
 
 }  // namespace kda

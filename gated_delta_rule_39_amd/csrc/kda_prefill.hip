@@ -550,12 +550,14 @@ __device__ __forceinline__ void publish_chain_tiles(const unsigned char* smem, u
                                                     int tid) {
   using TL = ChainTiles<DK>;
   using PL = WyProducerLayout<DK, DV>;
-  constexpr uint32_t off[6] = {PL::oKi, PL::oQg, PL::oKg, PL::oTm, 0, PL::oEgn};
+  // KD, Qg and e^{G_n} from LDS; -W and the lower blocks of M were written from their
+  // accumulators; the upper blocks of M are zero
+  constexpr uint32_t off[5] = {PL::oKD, PL::oQg, 0, 0, PL::oEgn};
   for (int p = tid; p < TL::kPieces; p += kThreads) {
-    const int q = p - (3 * TL::PK + TL::PC);
+    const int q = p - 3 * TL::PK;
     if (q >= 0 && q < TL::PC) {
       if ((8 * (q % 8)) / 16 > (q / 8) / 16) dst[p] = u32x4{0u, 0u, 0u, 0u};
-    } else {
+    } else if (p < 2 * TL::PK || q >= TL::PC) {
       dst[p] = *reinterpret_cast<const u32x4*>(smem + piece_lds<DK>(off, p));
     }
   }
@@ -689,8 +691,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       lds_barrier();
       pr.inverse_rest();
       if (has_next) pr.template load_slice<DECAY, 3 * RPG, L>(c1, n1);            // v, beta
-      pr.publish_wu(rr, slot);
-      if constexpr (STATES) publish_chain_tiles<DK, DV>(smem, reinterpret_cast<u32x4*>(tiles), tid);
+      if constexpr (STATES) {
+        pr.template publish_wu<true>(rr, slot, reinterpret_cast<bf16*>(tiles + ChainTiles<DK>::oW));
+        publish_chain_tiles<DK, DV>(smem, reinterpret_cast<u32x4*>(tiles), tid);
+      } else {
+        pr.publish_wu(rr, slot);
+      }
       // every slot store of the workgroup acknowledged (device-visible), then publish
       vm_barrier();
       if (tid == 0) __hip_atomic_store(ready + s, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -88,26 +88,28 @@ __host__ __device__ inline int64_t chunk_slot_base(int n_seq, int64_t bos) {
   return bos / kChunk + n_seq;
 }
 
-// Per (chunk slot, head), in the backward's workspace, as 16-byte pieces: Ki, Qg, Kg
-// [64][DK] bf16, X diag(beta) [64][64] bf16, M [64][64] bf16 (row r, column s: Qg_r . Ki_s
-// for s <= r, else 0), e^{G_n} [DK] fp32.  Rows past a ragged chunk's end are zero.  The
-// reverse chain reads them into LDS tiles with the row padding of kda_chunk.h.
+// Per (chunk slot, head), in the backward's workspace, as 16-byte pieces: KD, Qg and -W
+// [64][DK] bf16 (KD_r = k_r e^{G_n - G_r}, W = X diag(beta) Kg), M [64][64] bf16 (row r,
+// column s: Qg_r . Ki_s for s <= r, else 0), e^{G_n} [DK] fp32.  Rows past a ragged
+// chunk's end are zero.  The reverse chain reads them into LDS tiles with the row
+// padding of kda_chunk.h.
 template <int DK>
 struct ChainTiles {
   static constexpr int PK = kChunk * DK / 8;       // pieces of a [64][DK] tile
   static constexpr int PC = kChunk * kChunk / 8;   // of a [64][64] tile
   static constexpr int PE = DK * 4 / 16;
-  static constexpr int kPieces = 3 * PK + 2 * PC + PE;
+  static constexpr int kPieces = 3 * PK + PC + PE;
   static constexpr size_t kBytes = size_t(kPieces) * 16;
-  static constexpr size_t oM = size_t(3 * PK + PC) * 16;   // byte offset of M
+  static constexpr size_t oW = size_t(2 * PK) * 16;   // byte offset of -W
+  static constexpr size_t oM = size_t(3 * PK) * 16;   // byte offset of M
 };
 
-// LDS byte offset of piece p, given the byte offsets of the six tiles (Ki, Qg, Kg,
-// X diag(beta), M, e^{G_n}) with row strides DK + 8 and 64 + 8 (bf16).  The tile's
-// offset is selected, not indexed: a run-time index into the table would put it in
-// memory and cost a load (and a wait) per piece.
+// LDS byte offset of piece p, given the byte offsets of the five tiles (KD, Qg, -W, M,
+// e^{G_n}) with row strides DK + 8 and 64 + 8 (bf16).  The tile's offset is selected,
+// not indexed: a run-time index into the table would put it in memory and cost a load
+// (and a wait) per piece.
 template <int DK>
-__device__ __forceinline__ uint32_t piece_lds(const uint32_t (&off)[6], int p) {
+__device__ __forceinline__ uint32_t piece_lds(const uint32_t (&off)[5], int p) {
   using TL = ChainTiles<DK>;
   constexpr int RK = DK / 8;
   if (p < 3 * TL::PK) {
@@ -116,11 +118,8 @@ __device__ __forceinline__ uint32_t piece_lds(const uint32_t (&off)[6], int p) {
     return base + ((q / RK) * (DK + 8) + 8 * (q % RK)) * 2;
   }
   p -= 3 * TL::PK;
-  if (p < 2 * TL::PC) {
-    const int t = p / TL::PC, q = p % TL::PC;
-    return (t == 0 ? off[3] : off[4]) + ((q / 8) * (kChunk + 8) + 8 * (q % 8)) * 2;
-  }
-  return off[5] + 16 * (p - 2 * TL::PC);
+  if (p < TL::PC) return off[3] + ((p / 8) * (kChunk + 8) + 8 * (p % 8)) * 2;
+  return off[4] + 16 * (p - TL::PC);
 }
 
 // The state tile in accumulators as bf16 [d_v][d_k] rows at dst + base (four

@@ -606,7 +606,10 @@ struct WyProducer {
   // All waves: W^T = -(Kg^T (X diag(beta))^T) as W fragments and U = X diag(beta) V as
   // fp32 tiles, straight to the slot.  Row block tb of X diag(beta) is zero beyond
   // column 16 tb + 15, so tb < 2 needs one K step.
-  __device__ __forceinline__ void publish_wu(__amdgpu_buffer_rsrc_t rr, uint32_t slot) {
+  // TILES: also -W itself, bf16 rows of DK, to wt (global).
+  template <bool TILES = false>
+  __device__ __forceinline__ void publish_wu(__amdgpu_buffer_rsrc_t rr, uint32_t slot,
+                                             bf16* wt = nullptr) {
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
       const int f = wave + 4 * i, tb = f / KS, j = f % KS;
@@ -619,6 +622,17 @@ struct WyProducer {
         hi = mma_bf16(frag_tr(sKg, LDK, 32 * t, 32 * j + 16, lane), xb, hi);
       }
       st16(rr, slot + SL::oW + f * SL::kFrag + 16 * lane, pack_frag(-lo, -hi));
+      if constexpr (TILES) {
+        // lo holds W[16 tb + l % 16][32 j + 4 (l / 16) + e], hi the keys 16 further
+        const int lq = lane >> 4, lr = lane & 15;
+        bf16* wr = wt + (16 * tb + lr) * DK + 32 * j + 4 * lq;
+        *reinterpret_cast<bf16x4*>(wr) =
+            bf16x4{static_cast<bf16>(-lo[0]), static_cast<bf16>(-lo[1]), static_cast<bf16>(-lo[2]),
+                   static_cast<bf16>(-lo[3])};
+        *reinterpret_cast<bf16x4*>(wr + 16) =
+            bf16x4{static_cast<bf16>(-hi[0]), static_cast<bf16>(-hi[1]), static_cast<bf16>(-hi[2]),
+                   static_cast<bf16>(-hi[3])};
+      }
     }
     // U: wave w forms value-block pairs w, w + 4, ... (blocks 2p, 2p + 1)
     for (int pv = wave; pv < SL::NVB / 2; pv += 4) {

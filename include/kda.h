@@ -243,9 +243,9 @@ int kda_backward(int dtype, int decay, int flags,
 
 /* Workspace bytes kda_backward needs, with S = (T_total / 64 + N + 1) * H chunk slots:
  * 2 * S * d_v * d_k * 2 for the chunk states and state gradients (bf16), plus
- * S * (388 d_k + 16384) for each chunk's factor tiles (bf16 Ki, Qg, Kg, X diag(beta), M;
- * fp32 e^{G_n}), plus the producer/consumer ring when that forward sweep applies (0 for
- * unsupported arguments).  Host-only apart from a cached device-attribute query. */
+ * S * (388 d_k + 8192) for each chunk's factor tiles (bf16 KD, Qg, W, M; fp32 e^{G_n}),
+ * plus the producer/consumer ring when that forward sweep applies (0 for unsupported
+ * arguments).  Host-only apart from a cached device-attribute query. */
 size_t kda_backward_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_t H,
                                     int32_t d_k, int32_t d_v);
 

@@ -162,11 +162,10 @@ def test_backward_validation_codes():
     assert backward_status(N=0, B=0) == 0               # nothing to do
     L = kda.lib()
     # two bf16 buffers of (T_total / 64 + N + 1) chunk slots of d_v x d_k per head, and
-    # the factor tiles of every slot (bf16 Ki, Qg, Kg [64][d_k], X diag(beta), M [64][64];
-    # fp32 e^{G_n} [d_k])
+    # the factor tiles of every slot (bf16 KD, Qg, W [64][d_k], M [64][64]; fp32 e^{G_n})
     slots = (1000 // 64 + 4) * 4
-    tiles = 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4
-    assert tiles == 388 * 128 + 16384
+    tiles = 3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4
+    assert tiles == 388 * 128 + 8192
     assert L.kda_backward_workspace_bytes(1, 3, 1000, 4, 128, 64) == \
         slots * (2 * 64 * 128 * 2 + tiles)
     assert L.kda_backward_workspace_bytes(0, 3, 1000, 4, 128, 64) == 0
