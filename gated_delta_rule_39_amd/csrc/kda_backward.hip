@@ -124,22 +124,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_tiles_kernel(BwdArgs a) {
         sW[(16 * wave + 4 * lq + i) * LDK + 16 * kb + lr] = static_cast<bf16>(-acc[kb][i]);
   }
   lds_barrier();
-  constexpr uint32_t off[5] = {CL::oKi, CL::oQg, CL::oA, CL::oM, CL::oEgn};
-  u32x4* dst = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.tiles) +
-                                        (slot * a.H + h) * TL::kBytes);
-  for (int p = tid; p < TL::kPieces; p += kThreads) {
-    u32x4 x = *reinterpret_cast<const u32x4*>(smem + piece_lds<DK>(off, p));
-    if (p < TL::PK) {
-      // KD = Ki Diag(e^{G_n})
-      const int c8 = 8 * (p % (DK / 8));
-      bf16x8 xb = __builtin_bit_cast(bf16x8, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        xb[e] = static_cast<bf16>(static_cast<float>(xb[e]) * cp.sEgn[c8 + e]);
-      x = __builtin_bit_cast(u32x4, xb);
-    }
-    dst[p] = x;
-  }
+  unsigned char* dst = static_cast<unsigned char*>(a.tiles) + (slot * a.H + h) * TL::kBytes;
+  const int lane = tid & 63;
+  store_kd_frags<DK>(dst, cp.sKi, LDK, cp.sEgn, true, wave, lane);   // KD = Ki Diag(e^{G_n})
+  store_tr_frags<DK>(dst + TL::oQT, cp.sQg, LDK, wave, lane);
+  store_tr_frags<DK>(dst + TL::oWT, sW, LDK, wave, lane);
+  for (int q = tid; q < TL::PC; q += kThreads)
+    *reinterpret_cast<bf16x8*>(dst + TL::oM + 16 * size_t(q)) =
+        *reinterpret_cast<const bf16x8*>(cp.sM + (q / 8) * LDC + 8 * (q % 8));
+  store_egn<DK>(dst, cp.sEgn, tid);
 }
 
 // ====================================================================================
@@ -150,11 +143,9 @@ template <int DK, int BV>
 struct ChainLayout {
   static constexpr int LDK = DK + 8, LDC = kChunk + 8;
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
-  static constexpr size_t tK = size_t(kChunk) * LDK * 2, tC = size_t(kChunk) * LDC * 2;
-  // one buffer of chunk tiles: KD, Qg, -W, M, e^{G_n}
-  static constexpr size_t oKD = 0, oQg = tK, oW = 2 * tK, oM = 3 * tK, oE = 3 * tK + tC;
-  static constexpr size_t kBuf = al(oE + DK * 4);
-  static constexpr size_t oP = 2 * kBuf;                               // dH'^T [BV][LDK]
+  static constexpr size_t tC = size_t(kChunk) * LDC * 2;
+  static constexpr size_t oM = 0;                                      // two M tiles [64][LDC]
+  static constexpr size_t oP = 2 * tC;                                 // dH'^T [BV][LDK]
   static constexpr size_t oDOT = al(oP + size_t(BV) * LDK * 2);       // [BV][LDC] each
   static constexpr size_t oDET = al(oDOT + size_t(BV) * LDC * 2);
   static constexpr size_t oTouch = al(oDET + size_t(BV) * LDC * 2);   // 4 B per thread, never read
@@ -162,21 +153,23 @@ struct ChainLayout {
   static_assert(kBytes <= 160 * 1024, "LDS budget exceeded");
 };
 
-// Per (unit, BV value rows), the chunks in reverse order; each chunk's tiles are read
-// from the workspace one chunk ahead into the other of two LDS buffers.
+// Per (unit, BV value rows), the chunks in reverse order.  Each wave loads the operand
+// fragments it uses straight from the chunk's tiles into registers, a chunk ahead: its
+// token block of KD (for dE), its key blocks of Qg^T, -W^T and e^{G_n} (for dH).  M,
+// read transposed, goes through one of two LDS buffers filled a chunk ahead.
 template <int DK, int BV>
 __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
   using CL = ChainLayout<DK, BV>;
   using TL = ChainTiles<DK>;
   using ST = StateTiles<DK, BV>;
-  constexpr int LDK = CL::LDK, LDC = CL::LDC, NVB = BV / 16;
-  constexpr int NPT = (TL::kPieces + kThreads - 1) / kThreads;
+  constexpr int LDK = CL::LDK, LDC = CL::LDC, NVB = BV / 16, NKS = DK / 32;
+  constexpr int MPT = TL::PC / kThreads;   // M pieces per thread
+  static_assert(MPT * kThreads == TL::PC, "M pieces");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[CL::kBytes];
   bf16* sP = reinterpret_cast<bf16*>(smem + CL::oP);
   bf16* sDOT = reinterpret_cast<bf16*>(smem + CL::oDOT);
   bf16* sDET = reinterpret_cast<bf16*>(smem + CL::oDET);
-  constexpr uint32_t off[5] = {CL::oKD, CL::oQg, CL::oW, CL::oM, CL::oE};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -190,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
   const int v0 = vt * BV;
   const bf16* dout = static_cast<const bf16*>(a.dout);
   bf16* dstates = static_cast<bf16*>(a.dstates);
-  const u32x4* tiles = static_cast<const u32x4*>(a.tiles);
+  const unsigned char* tiles = static_cast<const unsigned char*>(a.tiles);
 
   f32x4 sacc[ST::NST];   // dH^T tiles of this value tile (rows = key), fp32
   const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * a.DV * DK;
@@ -198,21 +191,46 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
 
   const int nch = static_cast<int>((eos - bos + kChunk - 1) / kChunk);
   const int64_t slot0 = chunk_slot_base(n_seq, bos);
-  u32x4 stage[NPT];
-  auto fetch = [&](int c) {
-    const u32x4* src = tiles + ((slot0 + c) * a.H + h) * (TL::kBytes / 16);
+  auto tile = [&](int c) { return tiles + ((slot0 + c) * a.H + h) * TL::kBytes; };
+
+  // One chunk's operands in registers, and the next chunk's on their way: a chunk's
+  // reads are issued at the start of the one before it and taken over at its end.
+  struct Ops {
+    bf16x8 kd[NKS];                          // KD row 16 wave + l % 16, keys 32 s + 8 (l / 16) ..
+    bf16x8 qt[ST::NST][2], wt[ST::NST][2];   // Qg^T, -W^T row 16 kb + l % 16, tokens 32 u + 8 (l / 16) ..
+    f32x4 eg[ST::NST];                       // e^{G_n} of keys 16 kb + 4 (l / 16) .. +3
+  };
+  Ops op, nx;
+  u32x4 mp[MPT];                           // M pieces on their way to LDS
+  auto load_ops = [&](Ops& o, int c) {
+    const unsigned char* t = tile(c);
+    const unsigned char* tk = t + TL::oKD + 1024 * size_t(wave * NKS) + 16 * lane;
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int p = tid + i * kThreads;
-      if (p < TL::kPieces) stage[i] = src[p];
+    for (int s = 0; s < NKS; ++s) o.kd[s] = *reinterpret_cast<const bf16x8*>(tk + 1024 * s);
+#pragma unroll
+    for (int s = 0; s < ST::NST; ++s) {
+      const int kb = ST::kb(wave, s);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const size_t q = 1024 * size_t(2 * kb + u) + 16 * lane;
+        o.qt[s][u] = *reinterpret_cast<const bf16x8*>(t + TL::oQT + q);
+        o.wt[s][u] = *reinterpret_cast<const bf16x8*>(t + TL::oWT + q);
+      }
+      o.eg[s] = *reinterpret_cast<const f32x4*>(t + TL::oE + (16 * kb + 4 * lq) * 4);
     }
   };
-  auto deposit = [&](int buf) {
+  auto load_m = [&](int c) {
+    const unsigned char* t = tile(c) + TL::oM;
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int p = tid + i * kThreads;
-      if (p < TL::kPieces)
-        *reinterpret_cast<u32x4*>(smem + buf * CL::kBuf + piece_lds<DK>(off, p)) = stage[i];
+    for (int i = 0; i < MPT; ++i)
+      mp[i] = *reinterpret_cast<const u32x4*>(t + 16 * size_t(tid + i * kThreads));
+  };
+  auto deposit_m = [&](int buf) {
+    bf16* sMb = reinterpret_cast<bf16*>(smem + CL::oM + buf * CL::tC);
+#pragma unroll
+    for (int i = 0; i < MPT; ++i) {
+      const int q = tid + i * kThreads;
+      *reinterpret_cast<u32x4*>(sMb + (q / 8) * LDC + 8 * (q % 8)) = mp[i];
     }
   };
   // Chunk c's tiles into L2 two chunks ahead of their use: one 4-byte read per 128-byte
@@ -221,36 +239,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
   constexpr int kLines = static_cast<int>((TL::kBytes + 127) / 128);
   constexpr int NT = (kLines + 4 * 64 - 1) / (4 * 64);   // reads per lane
   uint32_t tw[NT], tacc = 0;
-#pragma unroll
-  for (int j = 0; j < NT; ++j) tw[j] = 0;
   auto touch = [&](int c) {
-    const uint32_t* base = reinterpret_cast<const uint32_t*>(
-        tiles + ((slot0 + c) * a.H + h) * (TL::kBytes / 16));
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(tile(c));
 #pragma unroll
     for (int j = 0; j < NT; ++j) tw[j] = base[32 * min(64 * (4 * j + wave) + lane, kLines - 1)];
   };
   ValueRegs<bf16, NVB> dr;   // dO rows of the chunk, accumulator layout
   if (nch > 0) {
+    // the loop's own order (M, dO, KD, the dH operands): the compiler's wait at the loop
+    // top for dO then never covers the later reads
     const int64_t cl = bos + int64_t(nch - 1) * kChunk;
-    fetch(nch - 1);
+    load_ops(op, nch - 1);
+    load_m(nch - 1);
     dr.load(dout, cl, static_cast<int>(eos - cl), a.H, h, a.DV, v0, wave, lane);
-    deposit(0);
+    deposit_m(0);
   }
   lds_barrier();
   const int k0m = (16 * wave) & ~31;   // first K step that meets a triangular row block
 
   for (int c = nch - 1; c >= 0; --c) {
     const int cur = (nch - 1 - c) & 1;
-    const unsigned char* buf = smem + cur * CL::kBuf;
-    const bf16* sKD = reinterpret_cast<const bf16*>(buf + CL::oKD);
-    const bf16* sQg = reinterpret_cast<const bf16*>(buf + CL::oQg);
-    const bf16* sWn = reinterpret_cast<const bf16*>(buf + CL::oW);   // -W
-    const bf16* sM = reinterpret_cast<const bf16*>(buf + CL::oM);
-    const float* sEgn = reinterpret_cast<const float*>(buf + CL::oE);
+    const bf16* sM = reinterpret_cast<const bf16*>(smem + CL::oM + cur * CL::tC);
     const int64_t c0 = bos + int64_t(c) * kChunk;
     const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
-    // dO^T of this chunk first (its rows were requested a chunk ago), then the requests
-    // for the previous chunk's tiles: a wait for the former never includes the latter
+    // the chunk whose operands are loaded during this one: the previous chunk in token
+    // order (always full), or the first one again at the end (in bounds, unused)
+    const int cp = c > 0 ? c - 1 : 0;
+    // dO^T of this chunk (its rows were requested a chunk ago)
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
       f32x4 x;
@@ -258,20 +273,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) x[i] = 16 * wave + 4 * lq + i < n ? dr.f32(vb, i) : 0.f;
       store4(sDOT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, x);
     }
-    if (c > 0) fetch(c - 1);   // the previous chunk in token order (always full)
+    load_ops(nx, cp);
+    load_m(cp);
     // dL/d(state after chunk c)
     store_state_bf16<DK, BV>(sacc, dstates, ((slot0 + c) * a.H + h) * a.DV * DK, v0, wave,
                              lane);
-
-    // dH' (operand of dE), then D dH' in the accumulators
+    // dH', the operand of dE
 #pragma unroll
     for (int s = 0; s < ST::NST; ++s) {
       const int kb = ST::kb(wave, s), vb = ST::vb(s);
       store4(sP + (16 * vb + lr) * LDK + 16 * kb + 4 * lq, sacc[s]);
-      sacc[s] *= *reinterpret_cast<const f32x4*>(sEgn + 16 * kb + 4 * lq);
     }
-    if (c > 0) dr.load(dout, c0 - kChunk, kChunk, a.H, h, a.DV, v0, wave, lane);
-    if (c > 1) touch(c - 2);
+    dr.load(dout, bos + int64_t(cp) * kChunk, static_cast<int>(min(eos - bos - int64_t(cp) * kChunk,
+                                                                   static_cast<int64_t>(kChunk))),
+            a.H, h, a.DV, v0, wave, lane);
+    touch(c > 1 ? c - 2 : 0);
     lds_barrier();
 
     // dE = KD dH' + M^T dO for token block `wave` -> dE^T
@@ -279,8 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
     for (int vb = 0; vb < NVB; ++vb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < DK; kk += 32)
-        acc = mma_bf16(frow(sKD, LDK, 16 * wave, kk, lane), frow(sP, LDK, 16 * vb, kk, lane), acc);
+      for (int s = 0; s < NKS; ++s) acc = mma_bf16(op.kd[s], frow(sP, LDK, 16 * vb, 32 * s, lane), acc);
       for (int kk = k0m; kk < kChunk; kk += 32)
         acc = mma_bf16(frag_tr(sM, LDC, kk, 16 * wave, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
                        acc);
@@ -291,25 +306,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
     // dH = D dH' + Qg^T dO - W^T dE
 #pragma unroll
     for (int s = 0; s < ST::NST; ++s) {
-      const int kb = ST::kb(wave, s), vb = ST::vb(s);
-      f32x4 acc = sacc[s];
+      const int vb = ST::vb(s);
+      f32x4 acc = sacc[s] * op.eg[s];
 #pragma unroll
-      for (int kk = 0; kk < kChunk; kk += 32) {
-        acc = mma_bf16(frag_tr(sQg, LDK, kk, 16 * kb, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
-                       acc);
-        acc = mma_bf16(frag_tr(sWn, LDK, kk, 16 * kb, lane), frow(sDET, LDC, 16 * vb, kk, lane),
-                       acc);
+      for (int u = 0; u < 2; ++u) {
+        acc = mma_bf16(op.qt[s][u], frow(sDOT, LDC, 16 * vb, 32 * u, lane), acc);
+        acc = mma_bf16(op.wt[s][u], frow(sDET, LDC, 16 * vb, 32 * u, lane), acc);
       }
       sacc[s] = acc;
     }
-    if (c > 0) deposit(cur ^ 1);
+    deposit_m(cur ^ 1);
+    op = nx;
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < NT; ++j) tacc ^= tw[j];
   }
   // the touched words end in a scratch corner of LDS (volatile: the reads stay)
   *reinterpret_cast<volatile uint32_t*>(smem + CL::oTouch + 4 * tid) = tacc;
-
   if (a.dinitial_state) store_state<DK, BV>(sacc, a.dinitial_state, st_base, v0, wave, lane);
 }
 

@@ -546,21 +546,22 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 // X diag(beta) and e^{G_n} from its LDS; of M, products<true>() wrote the blocks on and
 // below the diagonal, the blocks above it are zero.
 template <int DK, int DV>
-__device__ __forceinline__ void publish_chain_tiles(const unsigned char* smem, u32x4* dst,
-                                                    int tid) {
+__device__ __forceinline__ void publish_chain_tiles(const unsigned char* smem, unsigned char* dst,
+                                                    int tid, int wave, int lane) {
   using TL = ChainTiles<DK>;
   using PL = WyProducerLayout<DK, DV>;
-  // KD, Qg and e^{G_n} from LDS; -W and the lower blocks of M were written from their
-  // accumulators; the upper blocks of M are zero
-  constexpr uint32_t off[5] = {PL::oKD, PL::oQg, 0, 0, PL::oEgn};
-  for (int p = tid; p < TL::kPieces; p += kThreads) {
-    const int q = p - 3 * TL::PK;
-    if (q >= 0 && q < TL::PC) {
-      if ((8 * (q % 8)) / 16 > (q / 8) / 16) dst[p] = u32x4{0u, 0u, 0u, 0u};
-    } else if (p < 2 * TL::PK || q >= TL::PC) {
-      dst[p] = *reinterpret_cast<const u32x4*>(smem + piece_lds<DK>(off, p));
-    }
-  }
+  // KD, Qg^T, -W^T (staged in the A area by publish_wu) and e^{G_n} from LDS; the
+  // lower blocks of M were written from their accumulators, its upper blocks are zero
+  store_kd_frags<DK>(dst, reinterpret_cast<const bf16*>(smem + PL::oKD), PL::LDK, nullptr, false,
+                     wave, lane);
+  store_tr_frags<DK>(dst + TL::oQT, reinterpret_cast<const bf16*>(smem + PL::oQg), PL::LDK, wave,
+                     lane);
+  store_tr_frags<DK>(dst + TL::oWT, reinterpret_cast<const bf16*>(smem + PL::oA), PL::LDK, wave,
+                     lane);
+  for (int q = tid; q < TL::PC; q += kThreads)
+    if ((8 * (q % 8)) / 16 > (q / 8) / 16)
+      *reinterpret_cast<u32x4*>(dst + TL::oM + 16 * size_t(q)) = u32x4{0u, 0u, 0u, 0u};
+  store_egn<DK>(dst, reinterpret_cast<const float*>(smem + PL::oEgn), tid);
 }
 
 template <int DK, int DV>
@@ -692,8 +693,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       pr.inverse_rest();
       if (has_next) pr.template load_slice<DECAY, 3 * RPG, L>(c1, n1);            // v, beta
       if constexpr (STATES) {
-        pr.template publish_wu<true>(rr, slot, reinterpret_cast<bf16*>(tiles + ChainTiles<DK>::oW));
-        publish_chain_tiles<DK, DV>(smem, reinterpret_cast<u32x4*>(tiles), tid);
+        // -W rows staged in the A area (dead after the inverse) for the transposed copy
+        static_assert(size_t(kChunk) * PL::LDK * 2 <= PL::oX - PL::oA, "-W staging fits");
+        pr.template publish_wu<true>(rr, slot, reinterpret_cast<bf16*>(smem + PL::oA));
+        lds_barrier();
+        publish_chain_tiles<DK, DV>(smem, tiles, tid, wave, lane);
       } else {
         pr.publish_wu(rr, slot);
       }

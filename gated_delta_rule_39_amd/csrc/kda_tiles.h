@@ -5,6 +5,7 @@
 
 #include "kda_chunk.h"
 #include "kda_launch.h"
+#include "kda_wy.h"
 
 namespace kda {
 
@@ -88,40 +89,66 @@ __host__ __device__ inline int64_t chunk_slot_base(int n_seq, int64_t bos) {
   return bos / kChunk + n_seq;
 }
 
-// Per (chunk slot, head), in the backward's workspace, as 16-byte pieces: KD, Qg and -W
-// [64][DK] bf16 (KD_r = k_r e^{G_n - G_r}, W = X diag(beta) Kg), M [64][64] bf16 (row r,
-// column s: Qg_r . Ki_s for s <= r, else 0), e^{G_n} [DK] fp32.  Rows past a ragged
-// chunk's end are zero.  The reverse chain reads them into LDS tiles with the row
-// padding of kda_chunk.h.
+// Per (chunk slot, head), in the backward's workspace: KD (KD_r = k_r e^{G_n - G_r}),
+// Qg^T and -W^T (W = X diag(beta) Kg) as bf16 MFMA operand fragments of 1 KiB (64 lanes
+// x 16 bytes, lane-major), M [64][64] bf16 row-major (row r, column s: Qg_r . Ki_s for
+// s <= r, else 0), then e^{G_n} [DK] fp32.  Fragments of KD, block tb * (DK / 32) + s:
+// lane l holds row 16 tb + l % 16, keys 32 s + 8 (l / 16) .. +7.  Qg^T and -W^T, block
+// 2 kb + u: lane l holds key 16 kb + l % 16, tokens 32 u + 8 (l / 16) .. +7.  Rows past a
+// ragged chunk's end are zero.  The reverse chain loads each wave's fragments straight
+// into registers, one contiguous 1 KiB per load.
 template <int DK>
 struct ChainTiles {
-  static constexpr int PK = kChunk * DK / 8;       // pieces of a [64][DK] tile
+  static constexpr int PK = kChunk * DK / 8;       // 16-byte pieces of a 64 x DK tile
   static constexpr int PC = kChunk * kChunk / 8;   // of a [64][64] tile
   static constexpr int PE = DK * 4 / 16;
   static constexpr int kPieces = 3 * PK + PC + PE;
   static constexpr size_t kBytes = size_t(kPieces) * 16;
-  static constexpr size_t oW = size_t(2 * PK) * 16;   // byte offset of -W
-  static constexpr size_t oM = size_t(3 * PK) * 16;   // byte offset of M
+  static constexpr size_t oKD = 0, oQT = size_t(PK) * 16, oWT = size_t(2 * PK) * 16;
+  static constexpr size_t oM = size_t(3 * PK) * 16, oE = size_t(3 * PK + PC) * 16;
 };
 
-// LDS byte offset of piece p, given the byte offsets of the five tiles (KD, Qg, -W, M,
-// e^{G_n}) with row strides DK + 8 and 64 + 8 (bf16).  The tile's offset is selected,
-// not indexed: a run-time index into the table would put it in memory and cost a load
-// (and a wait) per piece.
+// Writers of a chunk's tiles from a workgroup's LDS.  KD fragments from a row-major
+// [64][DK] bf16 tile (each element multiplied by e^{G_n} of its key when scale_egn).
 template <int DK>
-__device__ __forceinline__ uint32_t piece_lds(const uint32_t (&off)[5], int p) {
+__device__ __forceinline__ void store_kd_frags(unsigned char* dst, const bf16* sKD, int ld,
+                                               const float* egn, bool scale_egn, int wave,
+                                               int lane) {
   using TL = ChainTiles<DK>;
-  constexpr int RK = DK / 8;
-  if (p < 3 * TL::PK) {
-    const int t = p / TL::PK, q = p % TL::PK;
-    const uint32_t base = t == 0 ? off[0] : (t == 1 ? off[1] : off[2]);
-    return base + ((q / RK) * (DK + 8) + 8 * (q % RK)) * 2;
+  constexpr int NKS = DK / 32;
+  for (int f = wave; f < 4 * NKS; f += 4) {
+    const int tb = f / NKS, s = f % NKS;
+    bf16x8 x = frag_rows<Mfma<bf16>>(sKD, ld, 16 * tb, 32 * s, lane);
+    if (scale_egn) {
+      const int k0 = 32 * s + 8 * (lane >> 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = static_cast<bf16>(static_cast<float>(x[e]) * egn[k0 + e]);
+    }
+    *reinterpret_cast<bf16x8*>(dst + TL::oKD + 1024 * size_t(f) + 16 * lane) = x;
   }
-  p -= 3 * TL::PK;
-  if (p < TL::PC) return off[3] + ((p / 8) * (kChunk + 8) + 8 * (p % 8)) * 2;
-  return off[4] + 16 * (p - TL::PC);
 }
 
+// The transpose of a row-major [64][DK] bf16 LDS tile as fragments at dst: block
+// 2 kb + u, lane l: column 16 kb + l % 16, rows 32 u + 8 (l / 16) .. +7 (one transposing
+// read per fragment).
+template <int DK>
+__device__ __forceinline__ void store_tr_frags(unsigned char* dst, const bf16* src, int ld,
+                                               int wave, int lane) {
+  for (int f = wave; f < 2 * (DK / 16); f += 4) {
+    const int kb = f >> 1, u = f & 1;
+    *reinterpret_cast<bf16x8*>(dst + 1024 * size_t(f) + 16 * lane) =
+        frag_tr(src, ld, 32 * u, 16 * kb, lane);
+  }
+}
+
+// e^{G_n} of the chunk (fp32 [DK]) at its place in the tiles.
+template <int DK>
+__device__ __forceinline__ void store_egn(unsigned char* dst, const float* egn, int tid) {
+  using TL = ChainTiles<DK>;
+  if (tid < TL::PE)
+    *reinterpret_cast<f32x4*>(dst + TL::oE + 16 * size_t(tid)) =
+        *reinterpret_cast<const f32x4*>(egn + 4 * tid);
+}
 // The state tile in accumulators as bf16 [d_v][d_k] rows at dst + base (four
 // consecutive keys per lane: one 8-byte store per tile).
 template <int DK, int BV, int NST>

@@ -606,7 +606,7 @@ struct WyProducer {
   // All waves: W^T = -(Kg^T (X diag(beta))^T) as W fragments and U = X diag(beta) V as
   // fp32 tiles, straight to the slot.  Row block tb of X diag(beta) is zero beyond
   // column 16 tb + 15, so tb < 2 needs one K step.
-  // TILES: also -W itself, bf16 rows of DK, to wt (global).
+  // TILES: also -W itself, bf16 rows of LDK, to wt (LDS).
   template <bool TILES = false>
   __device__ __forceinline__ void publish_wu(__amdgpu_buffer_rsrc_t rr, uint32_t slot,
                                              bf16* wt = nullptr) {
@@ -625,7 +625,7 @@ struct WyProducer {
       if constexpr (TILES) {
         // lo holds W[16 tb + l % 16][32 j + 4 (l / 16) + e], hi the keys 16 further
         const int lq = lane >> 4, lr = lane & 15;
-        bf16* wr = wt + (16 * tb + lr) * DK + 32 * j + 4 * lq;
+        bf16* wr = wt + (16 * tb + lr) * LDK + 32 * j + 4 * lq;
         *reinterpret_cast<bf16x4*>(wr) =
             bf16x4{static_cast<bf16>(-lo[0]), static_cast<bf16>(-lo[1]), static_cast<bf16>(-lo[2]),
                    static_cast<bf16>(-lo[3])};
