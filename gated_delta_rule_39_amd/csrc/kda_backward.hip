@@ -193,30 +193,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
   const int64_t slot0 = chunk_slot_base(n_seq, bos);
   auto tile = [&](int c) { return tiles + ((slot0 + c) * a.H + h) * TL::kBytes; };
 
-  // One chunk's operands in registers, and the next chunk's on their way: a chunk's
-  // reads are issued at the start of the one before it and taken over at its end.
-  struct Ops {
-    bf16x8 kd[NKS];                          // KD row 16 wave + l % 16, keys 32 s + 8 (l / 16) ..
-    bf16x8 qt[ST::NST][2], wt[ST::NST][2];   // Qg^T, -W^T row 16 kb + l % 16, tokens 32 u + 8 (l / 16) ..
-    f32x4 eg[ST::NST];                       // e^{G_n} of keys 16 kb + 4 (l / 16) .. +3
-  };
-  Ops op, nx;
+  // One chunk's operands in registers.  Each set is requested for the previous chunk
+  // right after its last use in this one, so it has a whole chunk to arrive and the
+  // requests are spread over the chunk.
+  bf16x8 kd[NKS];                          // KD row 16 wave + l % 16, keys 32 s + 8 (l / 16) ..
+  bf16x8 qt[ST::NST][2], wt[ST::NST][2];   // Qg^T, -W^T key 16 kb + l % 16, tokens 32 u + 8 (l / 16) ..
+  f32x4 eg[ST::NST];                       // e^{G_n} of keys 16 kb + 4 (l / 16) .. +3
   u32x4 mp[MPT];                           // M pieces on their way to LDS
-  auto load_ops = [&](Ops& o, int c) {
-    const unsigned char* t = tile(c);
-    const unsigned char* tk = t + TL::oKD + 1024 * size_t(wave * NKS) + 16 * lane;
+  auto load_kd = [&](int c) {
+    const unsigned char* tk = tile(c) + TL::oKD + 1024 * size_t(wave * NKS) + 16 * lane;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) o.kd[s] = *reinterpret_cast<const bf16x8*>(tk + 1024 * s);
+    for (int s = 0; s < NKS; ++s) kd[s] = *reinterpret_cast<const bf16x8*>(tk + 1024 * s);
+  };
+  auto load_dh = [&](int c) {
+    const unsigned char* t = tile(c);
 #pragma unroll
     for (int s = 0; s < ST::NST; ++s) {
       const int kb = ST::kb(wave, s);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const size_t q = 1024 * size_t(2 * kb + u) + 16 * lane;
-        o.qt[s][u] = *reinterpret_cast<const bf16x8*>(t + TL::oQT + q);
-        o.wt[s][u] = *reinterpret_cast<const bf16x8*>(t + TL::oWT + q);
+        qt[s][u] = *reinterpret_cast<const bf16x8*>(t + TL::oQT + q);
+        wt[s][u] = *reinterpret_cast<const bf16x8*>(t + TL::oWT + q);
       }
-      o.eg[s] = *reinterpret_cast<const f32x4*>(t + TL::oE + (16 * kb + 4 * lq) * 4);
+      eg[s] = *reinterpret_cast<const f32x4*>(t + TL::oE + (16 * kb + 4 * lq) * 4);
     }
   };
   auto load_m = [&](int c) {
@@ -249,9 +249,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
     // the loop's own order (M, dO, KD, the dH operands): the compiler's wait at the loop
     // top for dO then never covers the later reads
     const int64_t cl = bos + int64_t(nch - 1) * kChunk;
-    load_ops(op, nch - 1);
     load_m(nch - 1);
     dr.load(dout, cl, static_cast<int>(eos - cl), a.H, h, a.DV, v0, wave, lane);
+    load_kd(nch - 1);
+    load_dh(nch - 1);
     deposit_m(0);
   }
   lds_barrier();
@@ -273,7 +274,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) x[i] = 16 * wave + 4 * lq + i < n ? dr.f32(vb, i) : 0.f;
       store4(sDOT + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, x);
     }
-    load_ops(nx, cp);
     load_m(cp);
     // dL/d(state after chunk c)
     store_state_bf16<DK, BV>(sacc, dstates, ((slot0 + c) * a.H + h) * a.DV * DK, v0, wave,
@@ -295,28 +295,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
     for (int vb = 0; vb < NVB; ++vb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) acc = mma_bf16(op.kd[s], frow(sP, LDK, 16 * vb, 32 * s, lane), acc);
+      for (int s = 0; s < NKS; ++s) acc = mma_bf16(kd[s], frow(sP, LDK, 16 * vb, 32 * s, lane), acc);
       for (int kk = k0m; kk < kChunk; kk += 32)
         acc = mma_bf16(frag_tr(sM, LDC, kk, 16 * wave, lane), frow(sDOT, LDC, 16 * vb, kk, lane),
                        acc);
       store4(sDET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, acc);
     }
+    load_kd(cp);
     lds_barrier();
 
     // dH = D dH' + Qg^T dO - W^T dE
 #pragma unroll
     for (int s = 0; s < ST::NST; ++s) {
       const int vb = ST::vb(s);
-      f32x4 acc = sacc[s] * op.eg[s];
+      f32x4 acc = sacc[s] * eg[s];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        acc = mma_bf16(op.qt[s][u], frow(sDOT, LDC, 16 * vb, 32 * u, lane), acc);
-        acc = mma_bf16(op.wt[s][u], frow(sDET, LDC, 16 * vb, 32 * u, lane), acc);
+        acc = mma_bf16(qt[s][u], frow(sDOT, LDC, 16 * vb, 32 * u, lane), acc);
+        acc = mma_bf16(wt[s][u], frow(sDET, LDC, 16 * vb, 32 * u, lane), acc);
       }
       sacc[s] = acc;
     }
+    load_dh(cp);
     deposit_m(cur ^ 1);
-    op = nx;
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < NT; ++j) tacc ^= tw[j];
