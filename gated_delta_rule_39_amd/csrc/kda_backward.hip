@@ -20,12 +20,13 @@
 // Four launches on one stream:
 //   1. forward sweep (prefill_kernel with STATES): the state at every chunk start,
 //      bf16, into the workspace;
-//   2. the chunk's factors Ki, Qg, Kg, X diag(beta), M, e^{G_n} once into the workspace:
-//      written by the forward sweep's producers (the producer/consumer kernel), else by
-//      bwd_tiles_kernel (one workgroup per chunk and head); then bwd_chain_kernel:
-//      per (unit, 16 value rows), the chunks in reverse order, streaming those tiles
-//      through two LDS buffers; the chain above only (its value columns are
-//      independent), writing dH' of every chunk (bf16) and dL/dS_0;
+//   2. the chunk's factors KD, Qg^T, -W^T (MFMA operand fragments), M and e^{G_n} once
+//      into the workspace: written by the forward sweep's producers (the
+//      producer/consumer kernel), else by bwd_tiles_kernel (one workgroup per chunk and
+//      head); then bwd_chain_kernel: per (unit, 16 value rows), the chunks in reverse
+//      order, each wave loading its fragments of those tiles into registers a chunk
+//      ahead; the chain above only (its value columns are independent), writing dH' of
+//      every chunk (bf16) and dL/dS_0;
 //   3. bwd_grad_kernel: one workgroup per (chunk, head), all chunks at once; reads H
 //      and dH', forms E and dE in 32-wide value slices and accumulates every
 //      d_v-contraction in registers, then the chunk-local algebra and the gradients.

@@ -542,8 +542,8 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   }
 }
 
-// A producer's chunk tiles for the backward's reverse chain (ChainTiles): Ki, Qg, Kg,
-// X diag(beta) and e^{G_n} from its LDS; of M, products<true>() wrote the blocks on and
+// A producer's chunk tiles for the backward's reverse chain (ChainTiles): KD, Qg^T, -W^T
+// fragments and e^{G_n} from its LDS; of M, products<true>() wrote the blocks on and
 // below the diagonal, the blocks above it are zero.
 template <int DK, int DV>
 __device__ __forceinline__ void publish_chain_tiles(const unsigned char* smem, unsigned char* dst,
