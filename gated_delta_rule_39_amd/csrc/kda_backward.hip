@@ -353,7 +353,9 @@ struct GradLayout {
   // value-slice phase
   static constexpr size_t oH = a1, oDH = a1 + tV, oP = a1 + 2 * tV, oRT = a1 + 3 * tV;
   static constexpr size_t oET = a2, oDET = a2 + tT, oDO = a2 + 2 * tT, oV = oDO + tR;
-  static_assert(oRT + tT <= a1end && oV + tR <= a2end, "value-slice tiles overflow");
+  static constexpr size_t oDV = oRT + tT;                         // dv slice [64][VS] bf16
+  static_assert(oDV + size_t(kChunk) * VS * 2 <= a1end && oV + tR <= a2end,
+                "value-slice tiles overflow");
   // chunk-local phase
   static constexpr size_t oDWT = a1, oDMT = a1 + tW;
   static constexpr size_t oCC1 = a2, oCC2 = a2 + tC, oCC3 = CL::oM;
@@ -362,7 +364,9 @@ struct GradLayout {
   static constexpr size_t tK = size_t(kChunk) * LDK * 2;
   static constexpr size_t oK = a1, oQ = a1 + tK;
   static constexpr size_t oRed = a2;                              // fp32 [12][DK]
+  static constexpr int LDG = DK + 8;                              // dg rows (fp32), in area 1
   static_assert(oQ + tK <= a1end, "k/q tiles overflow");
+  static_assert(a1 + size_t(kChunk) * LDG * 4 <= a1end, "dg tile overflow");
   static_assert(oRed + size_t(12) * DK * 4 <= a2end, "reduction overflow");
   static_assert(kBytes <= kLds, "LDS budget exceeded");
 };
@@ -444,6 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   bf16* sDET = reinterpret_cast<bf16*>(smem + GL::oDET);
   bf16* sDO = reinterpret_cast<bf16*>(smem + GL::oDO);   // dO slice [64][LDV], token rows
   bf16* sV = reinterpret_cast<bf16*>(smem + GL::oV);     // V slice [64][LDV]
+  bf16* sDV = reinterpret_cast<bf16*>(smem + GL::oDV);   // dv slice [64][VS]
   constexpr int LDV = GL::LDV;
 
   f32x4 dQg[NKB], dWn[NKB], dKh[NKB], dM[4], dXU[4];
@@ -538,16 +543,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
         store4(sET + (16 * vb + lr) * LDC + 16 * wave + 4 * lq, e[vb]);
         dbu += dbv[vb] * vreg[vb];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * wave + 4 * lq + i;
-          if (r < n)
-            dvout[(c0 + r) * rowV + int64_t(h) * DV + v0 + 16 * vb + lr] =
-                static_cast<bf16>(bt[i] * dbv[vb][i]);
-        }
+        for (int i = 0; i < 4; ++i)
+          sDV[(16 * wave + 4 * lq + i) * VS + 16 * vb + lr] = static_cast<bf16>(bt[i] * dbv[vb][i]);
       }
     }
     lds_barrier();
 
+    // this slice's dv rows leave as 16-byte pieces (one per thread)
+    {
+      const int r = tid / (VS / 8), c8 = 8 * (tid % (VS / 8));
+      if (r < n)
+        *reinterpret_cast<bf16x8*>(dvout + (c0 + r) * rowV + int64_t(h) * DV + v0 + c8) =
+            *reinterpret_cast<const bf16x8*>(sDV + r * VS + c8);
+    }
     // contractions over this slice's values (K = 32 = one MFMA step)
     {
       const bf16x8 aDO = frow(sDO, LDV, 16 * wave, 0, lane);
@@ -828,7 +836,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   }
 
   // dg: G_r = g_1 + ... + g_r and G_n = G_last, so dg_s = sum_{r >= s} dG_r + dG_n with
-  // dG_n = sum_r dKh Kh + d e^{G_n} e^{G_n}
+  // dG_n = sum_r dKh Kh + d e^{G_n} e^{G_n}.  Per key channel the values go through an
+  // LDS tile in area 1 (free once the dq, dk rows have left) and leave as 16-byte pieces.
+  float* sDG = reinterpret_cast<float*>(smem + GL::a1);
+  constexpr int LDG = GL::LDG;
+  if constexpr (DECAY == 0) lds_barrier();
   if constexpr (DECAY != 2) {
     const bool gate_logit = (a.flags & kGateLogit) != 0;
     f32x4 rows = f32x4{0.f, 0.f, 0.f, 0.f};   // one scalar decay: sums over the channels
@@ -848,12 +860,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const float v = gm[kb][i] + add;
         if constexpr (DECAY == 0) {
-          const int r = 16 * wave + 4 * lq + i;
-          if (r < n) {
-            const int64_t o = (c0 + r) * rowK + int64_t(h) * DK + j;
-            // g = log sigmoid(a) from a retention logit a: dg/da = sigmoid(-a)
-            a.dg[o] = gate_logit ? v * __builtin_amdgcn_rcpf(1.f + exp_hw(a.g[o])) : v;
-          }
+          sDG[(16 * wave + 4 * lq + i) * LDG + j] = v;
         } else {
           rows[i] += v;
         }
@@ -870,6 +877,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
             const int64_t o = (c0 + r) * a.H + h;
             a.dg[o] = gate_logit ? rows[i] * __builtin_amdgcn_rcpf(1.f + exp_hw(a.g[o])) : rows[i];
           }
+        }
+      }
+    }
+    if constexpr (DECAY == 0) {
+      lds_barrier();
+      for (int i = tid; i < kChunk * DK / 4; i += kThreads) {
+        const int r = i / (DK / 4), c4 = 4 * (i % (DK / 4));
+        if (r < n) {
+          const int64_t o = (c0 + r) * rowK + int64_t(h) * DK + c4;
+          f32x4 v = *reinterpret_cast<const f32x4*>(sDG + r * LDG + c4);
+          if (gate_logit) {
+            // g = log sigmoid(a) from a retention logit a: dg/da = sigmoid(-a)
+            const f32x4 ga = *reinterpret_cast<const f32x4*>(a.g + o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] *= __builtin_amdgcn_rcpf(1.f + exp_hw(ga[e]));
+          }
+          *reinterpret_cast<f32x4*>(a.dg + o) = v;
         }
       }
     }
