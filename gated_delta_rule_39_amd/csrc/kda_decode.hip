@@ -49,11 +49,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int64_t vbase = static_cast<int64_t>(unit) * DV;
   float* S = state + static_cast<int64_t>(unit) * DV * DK + 4 * c4;
 
-  // Issue every state load first: the whole tile is in flight at once.
+  // Issue every state load first: the whole tile is in flight at once.  Plain loads:
+  // non-temporal ones measured 12 % slower here (189 vs 166 us per step at N=256,
+  // H=32, d=128); the write-back stays non-temporal (plain stores: 205 us).
   f32x4 s[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i)
-    s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (r0 + RPP * i) * DK));
+    s[i] = *reinterpret_cast<const f32x4*>(S + (r0 + RPP * i) * DK);
 
   f32x4 kk = load4(k + kbase);
   if (flags & kNormK) kk *= __builtin_amdgcn_rsqf(row_sum<LPR>(dot4(kk, kk)) + kNormEps);
