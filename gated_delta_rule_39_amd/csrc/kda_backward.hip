@@ -131,8 +131,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_tiles_kernel(BwdArgs a) {
   store_tr_frags<DK>(dst + TL::oQT, cp.sQg, LDK, wave, lane);
   store_tr_frags<DK>(dst + TL::oWT, sW, LDK, wave, lane);
   for (int q = tid; q < TL::PC; q += kThreads)
-    *reinterpret_cast<bf16x8*>(dst + TL::oM + 16 * size_t(q)) =
-        *reinterpret_cast<const bf16x8*>(cp.sM + (q / 8) * LDC + 8 * (q % 8));
+    __builtin_nontemporal_store(*reinterpret_cast<const bf16x8*>(cp.sM + (q / 8) * LDC + 8 * (q % 8)),
+                                reinterpret_cast<bf16x8*>(dst + TL::oM + 16 * size_t(q)));
   store_egn<DK>(dst, cp.sEgn, tid);
 }
 

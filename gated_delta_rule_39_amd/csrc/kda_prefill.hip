@@ -428,10 +428,12 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) {
           const f32x4 x = S[b][vt];
-          *reinterpret_cast<bf16x4*>(cs + int64_t(v0 + 16 * vt + lr) * DK + 32 * wave + 16 * b +
-                                     4 * lq) =
+          // non-temporal, as every checkpoint and tile store: read only by later kernels
+          __builtin_nontemporal_store(
               bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
-                     static_cast<bf16>(x[3])};
+                     static_cast<bf16>(x[3])},
+              reinterpret_cast<bf16x4*>(cs + int64_t(v0 + 16 * vt + lr) * DK + 32 * wave + 16 * b +
+                                        4 * lq));
         }
     }
     // every wave has used chunk c - 1's operands: its slot is free
@@ -560,7 +562,8 @@ __device__ __forceinline__ void publish_chain_tiles(const unsigned char* smem, u
                      lane);
   for (int q = tid; q < TL::PC; q += kThreads)
     if ((8 * (q % 8)) / 16 > (q / 8) / 16)
-      *reinterpret_cast<u32x4*>(dst + TL::oM + 16 * size_t(q)) = u32x4{0u, 0u, 0u, 0u};
+      __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u},
+                                  reinterpret_cast<u32x4*>(dst + TL::oM + 16 * size_t(q)));
   store_egn<DK>(dst, reinterpret_cast<const float*>(smem + PL::oEgn), tid);
 }
 

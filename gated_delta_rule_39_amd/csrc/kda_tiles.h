@@ -108,7 +108,8 @@ struct ChainTiles {
   static constexpr size_t oM = size_t(3 * PK) * 16, oE = size_t(3 * PK + PC) * 16;
 };
 
-// Writers of a chunk's tiles from a workgroup's LDS.  KD fragments from a row-major
+// Writers of a chunk's tiles from a workgroup's LDS (non-temporal stores: the tiles are
+// read only by a later kernel).  KD fragments from a row-major
 // [64][DK] bf16 tile (each element multiplied by e^{G_n} of its key when scale_egn).
 template <int DK>
 __device__ __forceinline__ void store_kd_frags(unsigned char* dst, const bf16* sKD, int ld,
@@ -124,7 +125,8 @@ __device__ __forceinline__ void store_kd_frags(unsigned char* dst, const bf16* s
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = static_cast<bf16>(static_cast<float>(x[e]) * egn[k0 + e]);
     }
-    *reinterpret_cast<bf16x8*>(dst + TL::oKD + 1024 * size_t(f) + 16 * lane) = x;
+    __builtin_nontemporal_store(x, reinterpret_cast<bf16x8*>(dst + TL::oKD + 1024 * size_t(f) +
+                                                             16 * lane));
   }
 }
 
@@ -136,8 +138,8 @@ __device__ __forceinline__ void store_tr_frags(unsigned char* dst, const bf16* s
                                                int wave, int lane) {
   for (int f = wave; f < 2 * (DK / 16); f += 4) {
     const int kb = f >> 1, u = f & 1;
-    *reinterpret_cast<bf16x8*>(dst + 1024 * size_t(f) + 16 * lane) =
-        frag_tr(src, ld, 32 * u, 16 * kb, lane);
+    __builtin_nontemporal_store(frag_tr(src, ld, 32 * u, 16 * kb, lane),
+                                reinterpret_cast<bf16x8*>(dst + 1024 * size_t(f) + 16 * lane));
   }
 }
 
@@ -146,8 +148,8 @@ template <int DK>
 __device__ __forceinline__ void store_egn(unsigned char* dst, const float* egn, int tid) {
   using TL = ChainTiles<DK>;
   if (tid < TL::PE)
-    *reinterpret_cast<f32x4*>(dst + TL::oE + 16 * size_t(tid)) =
-        *reinterpret_cast<const f32x4*>(egn + 4 * tid);
+    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(egn + 4 * tid),
+                                reinterpret_cast<f32x4*>(dst + TL::oE + 16 * size_t(tid)));
 }
 // The state tile in accumulators as bf16 [d_v][d_k] rows at dst + base (four
 // consecutive keys per lane: one 8-byte store per tile).

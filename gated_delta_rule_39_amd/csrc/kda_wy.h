@@ -459,9 +459,10 @@ struct WyProducer {
     if constexpr (TILES) {
       // tile (a, b) holds M[16 b + lr][16 a + 4 lq + i]
       auto put = [&](int ta, int tb, f32x4 t) {
-        *reinterpret_cast<bf16x4*>(mt + (16 * tb + lr) * kChunk + 16 * ta + 4 * lq) =
+        __builtin_nontemporal_store(
             bf16x4{static_cast<bf16>(t[0]), static_cast<bf16>(t[1]), static_cast<bf16>(t[2]),
-                   static_cast<bf16>(t[3])};
+                   static_cast<bf16>(t[3])},
+            reinterpret_cast<bf16x4*>(mt + (16 * tb + lr) * kChunk + 16 * ta + 4 * lq));
       };
       if (wave == 2) {
         put(0, 0, diag(acc[0]));
