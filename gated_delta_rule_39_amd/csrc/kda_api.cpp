@@ -67,9 +67,13 @@ struct CoopPlan {
   int NC = 0, NP = 0, R = 0;
   bool ok() const { return NC > 0; }
 };
-CoopPlan coop_plan(int dtype, int64_t units, int32_t d_v, int cus) {
+CoopPlan coop_plan(int dtype, int64_t units, int32_t H, int32_t d_k, int32_t d_v, int cus) {
   CoopPlan p;
   if (dtype != KDA_BF16 || units <= 0 || env_int("KDA_PREFILL_COOP", 1) == 0) return p;
+  // the producers read a chunk's inputs through buffer resources with 31-bit byte
+  // offsets: 64 rows of g (H d_k fp32) and of v (H d_v bf16) must fit
+  const int64_t row = static_cast<int64_t>(H) * (d_k * 4 > d_v * 2 ? d_k * 4 : d_v * 2);
+  if (64 * row > 0x7fffffff) return p;
   int W = static_cast<int>(cus / units);
   if (W > 16) W = 16;
   if (W < 2) return p;
@@ -111,7 +115,7 @@ size_t kda_prefill_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_
   if (N <= 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
   const int64_t units = static_cast<int64_t>(N) * H;
   if (units > (1 << 24)) return 0;
-  const CoopPlan p = coop_plan(dtype, units, d_v, cu_count());
+  const CoopPlan p = coop_plan(dtype, units, H, d_k, d_v, cu_count());
   if (!p.ok()) return 0;
   return kda::prefill_coop_workspace_bytes(d_k, d_v, static_cast<int>(units), p.R);
 }
@@ -123,7 +127,7 @@ int kda_prefill_coop_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t 
   if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
   const int64_t units = static_cast<int64_t>(N) * H;
   if (units > (1 << 24)) return KDA_ERR_BAD_SHAPE;
-  const CoopPlan p = coop_plan(dtype, units, d_v, cu_count());
+  const CoopPlan p = coop_plan(dtype, units, H, d_k, d_v, cu_count());
   if (consumers) *consumers = p.NC;
   if (producers) *producers = p.NP;
   if (ring_slots) *ring_slots = p.R;
@@ -183,7 +187,7 @@ int kda_prefill_ex(int dtype, int decay, int flags, const void* q, const void* k
   a.decay = decay;
   a.flags = flags;
   const int cus = cu_count();
-  const CoopPlan p = coop_plan(dtype, units, d_v, cus);
+  const CoopPlan p = coop_plan(dtype, units, H, d_k, d_v, cus);
   if (p.ok() && workspace != nullptr &&
       workspace_bytes >= kda::prefill_coop_workspace_bytes(d_k, d_v, static_cast<int>(units), p.R)) {
     a.workspace = static_cast<unsigned char*>(workspace);
@@ -253,7 +257,7 @@ BwdPlan bwd_plan(int32_t N, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v
   const int64_t units = static_cast<int64_t>(N) * H;
   b.states = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H * d_v * d_k * 2);
   b.tiles = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H) * kda::chain_tile_bytes(d_k);
-  const CoopPlan p = coop_plan(KDA_BF16, units, d_v, cu_count());
+  const CoopPlan p = coop_plan(KDA_BF16, units, H, d_k, d_v, cu_count());
   if (p.ok() && d_k == 128 && d_v == 128 && p.NC == 2 && units <= (1 << 24)) {
     b.coop = p;
     b.ring = (kda::prefill_coop_workspace_bytes(d_k, d_v, static_cast<int>(units), p.R) + 255) &

@@ -152,6 +152,8 @@ struct WyProducerLayout {
 // is visible device-wide and a load reads the device-coherent copy, so the hand-off
 // needs no cache write-back or invalidate.
 constexpr int kDeviceScope = 16;
+// Non-temporal (NT) bit of a buffer instruction's cache policy.
+constexpr int kNonTemporal = 2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(unsigned char* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
 }
@@ -256,6 +258,13 @@ struct WyProducer {
   template <int DECAY, int I0, int I1>
   __device__ __forceinline__ void load_slice(int64_t c0, int n) {
     const int64_t rk = (c0 * H + h) * DK;
+    // buffer loads at 32-bit byte offsets from the chunk's first row (fewer address
+    // instructions than 64-bit addresses; the plan keeps 64 rows within 2 GiB)
+    auto rsrc = [](const void* p) {
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7fffffff, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t rsk = rsrc(k + rk), rsq = rsrc(q + rk),
+                                 rsv = rsrc(v + (c0 * H + h) * DV);
 #pragma unroll
     for (int e = I0; e < I1; ++e) {
       if (e < 3 * RPG) {
@@ -265,7 +274,8 @@ struct WyProducer {
           // g per key channel; with one g per (row, head), lane l loads row l's and
           // factors() hands the rows to the threads that use them; no g: zeros
           if constexpr (DECAY == 0) {
-            gr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + rk + off));
+            gr[i] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(g + rk), off * 4, 0, kNonTemporal));
           } else if constexpr (DECAY == 1) {
             if (i == 0) gr[0][0] = g[(c0 + min(lane, n - 1)) * H + h];
           } else {
@@ -273,14 +283,17 @@ struct WyProducer {
           }
         }
         else if (e < 2 * RPG)
-          kr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(k + rk + off));
+          kr[i] = __builtin_bit_cast(bf16x4,
+                                     __builtin_amdgcn_raw_buffer_load_b64(rsk, off * 2, 0, kNonTemporal));
         else
-          qr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(q + rk + off));
+          qr[i] = __builtin_bit_cast(bf16x4,
+                                     __builtin_amdgcn_raw_buffer_load_b64(rsq, off * 2, 0, kNonTemporal));
       } else if (e < 3 * RPG + RPGV) {
         const int i = e - 3 * RPG;
-        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(
-            v + (c0 * H + h) * DV + static_cast<uint32_t>(min(rgv * RPGV + i, n - 1)) * rowV +
-            jv0));
+        vr[i] = __builtin_bit_cast(
+            bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                        rsv, (static_cast<uint32_t>(min(rgv * RPGV + i, n - 1)) * rowV + jv0) * 2, 0,
+                        kNonTemporal));
       } else {
         br = __builtin_nontemporal_load(beta + (c0 + min(lane, n - 1)) * H + h);
       }
