@@ -650,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
     pr.local = pFlag[1] == 1;
     if (p < nch) {
       const int64_t c0 = bos + int64_t(p) * kChunk;
-      pr.template load<DECAY>(c0, static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk))));
+      pr.template load<DECAY, !STATES>(c0, static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk))));
     }
     for (int c = p; c < nch; c += a.NP) {
       const int64_t c0 = bos + int64_t(c) * kChunk;
@@ -677,24 +677,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
                 ((chunk_slot_base(n_seq, bos) + c) * a.H + h) * ChainTiles<DK>::kBytes;
       // the next chunk's inputs are requested in five slices between the phases
       constexpr int L = PR::kLoads, RPG = PR::RPG;
-      if (has_next) pr.template load_slice<DECAY, 0, RPG / 2>(c1, n1);            // g, first half
+      if (has_next) pr.template load_slice<DECAY, 0, RPG / 2, !STATES>(c1, n1);            // g, first half
       if constexpr (STATES)
         pr.template products<true>(rr, slot, reinterpret_cast<bf16*>(tiles + ChainTiles<DK>::oM));
       else
         pr.products(rr, slot);
-      if (has_next) pr.template load_slice<DECAY, RPG / 2, RPG>(c1, n1);          // g, second half
+      if (has_next) pr.template load_slice<DECAY, RPG / 2, RPG, !STATES>(c1, n1);          // g, second half
       lds_barrier();
-      if (has_next) pr.template load_slice<DECAY, RPG, 2 * RPG>(c1, n1);          // k
+      if (has_next) pr.template load_slice<DECAY, RPG, 2 * RPG, !STATES>(c1, n1);          // k
       pr.inverse_blocks();
       lds_barrier();
       if (wave < 2)
         pr.inverse_pairs();
       else
         pr.template publish_qk<2, 2>(rr, slot);
-      if (has_next) pr.template load_slice<DECAY, 2 * RPG, 3 * RPG>(c1, n1);      // q
+      if (has_next) pr.template load_slice<DECAY, 2 * RPG, 3 * RPG, !STATES>(c1, n1);      // q
       lds_barrier();
       pr.inverse_rest();
-      if (has_next) pr.template load_slice<DECAY, 3 * RPG, L>(c1, n1);            // v, beta
+      if (has_next) pr.template load_slice<DECAY, 3 * RPG, L, !STATES>(c1, n1);            // v, beta
       if constexpr (STATES) {
         // -W rows staged in the A area (dead after the inverse) for the transposed copy
         static_assert(size_t(kChunk) * PL::LDK * 2 <= PL::oX - PL::oA, "-W staging fits");

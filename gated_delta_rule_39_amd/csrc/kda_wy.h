@@ -253,13 +253,15 @@ struct WyProducer {
   // (g rows, k rows, q rows, v rows, beta) of which the caller issues slices between the
   // phases of a chunk, so that the per-CU memory pipeline never holds more than one
   // slice of misses; rows past the end re-read the last valid row (masked at use).
-  // Streaming (non-temporal) loads: the inputs are read once.
+  // Streaming (non-temporal) loads: the inputs are read once.  BUF: buffer loads at
+  // 32-bit byte offsets from the chunk's first row (fewer address instructions than
+  // 64-bit flat addresses; the plan keeps 64 rows within 2 GiB).  Measured: 1 % faster
+  // in the forward kernel, 3 % slower in the sweep that also writes states and tiles,
+  // which keeps flat loads.
   static constexpr int kLoads = 3 * RPG + RPGV + 1;
-  template <int DECAY, int I0, int I1>
+  template <int DECAY, int I0, int I1, bool BUF = true>
   __device__ __forceinline__ void load_slice(int64_t c0, int n) {
     const int64_t rk = (c0 * H + h) * DK;
-    // buffer loads at 32-bit byte offsets from the chunk's first row (fewer address
-    // instructions than 64-bit addresses; the plan keeps 64 rows within 2 GiB)
     auto rsrc = [](const void* p) {
       return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7fffffff, 0x00020000);
     };
@@ -274,8 +276,11 @@ struct WyProducer {
           // g per key channel; with one g per (row, head), lane l loads row l's and
           // factors() hands the rows to the threads that use them; no g: zeros
           if constexpr (DECAY == 0) {
-            gr[i] = __builtin_bit_cast(
-                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(g + rk), off * 4, 0, kNonTemporal));
+            if constexpr (BUF)
+              gr[i] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(g + rk), off * 4, 0, kNonTemporal));
+            else
+              gr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + rk + off));
           } else if constexpr (DECAY == 1) {
             if (i == 0) gr[0][0] = g[(c0 + min(lane, n - 1)) * H + h];
           } else {
@@ -283,24 +288,29 @@ struct WyProducer {
           }
         }
         else if (e < 2 * RPG)
-          kr[i] = __builtin_bit_cast(bf16x4,
-                                     __builtin_amdgcn_raw_buffer_load_b64(rsk, off * 2, 0, kNonTemporal));
+          kr[i] = BUF ? __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                       rsk, off * 2, 0, kNonTemporal))
+                      : __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(k + rk + off));
         else
-          qr[i] = __builtin_bit_cast(bf16x4,
-                                     __builtin_amdgcn_raw_buffer_load_b64(rsq, off * 2, 0, kNonTemporal));
+          qr[i] = BUF ? __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                       rsq, off * 2, 0, kNonTemporal))
+                      : __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(q + rk + off));
       } else if (e < 3 * RPG + RPGV) {
         const int i = e - 3 * RPG;
-        vr[i] = __builtin_bit_cast(
-            bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
-                        rsv, (static_cast<uint32_t>(min(rgv * RPGV + i, n - 1)) * rowV + jv0) * 2, 0,
-                        kNonTemporal));
+        const uint32_t ov = static_cast<uint32_t>(min(rgv * RPGV + i, n - 1)) * rowV + jv0;
+        vr[i] = BUF ? __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                     rsv, ov * 2, 0, kNonTemporal))
+                    : __builtin_nontemporal_load(
+                          reinterpret_cast<const bf16x4*>(v + (c0 * H + h) * DV + ov));
       } else {
         br = __builtin_nontemporal_load(beta + (c0 + min(lane, n - 1)) * H + h);
       }
     }
   }
-  template <int DECAY>
-  __device__ __forceinline__ void load(int64_t c0, int n) { load_slice<DECAY, 0, kLoads>(c0, n); }
+  template <int DECAY, bool BUF = true>
+  __device__ __forceinline__ void load(int64_t c0, int n) {
+    load_slice<DECAY, 0, kLoads, BUF>(c0, n);
+  }
 
   // Kg, Qg, Ki, KD, V (row-major), beta and e^{G_n} of the loaded chunk into LDS.  The
   // input registers are free afterwards.  No closing barrier.
