@@ -159,14 +159,29 @@ def _flags(normalize_k: bool, beta_logit: bool, gate_logit: bool) -> int:
             | (KDA_PRO_GATE_LOGIT if gate_logit else 0))
 
 
-def workspace_aborted(ws: torch.Tensor) -> bool:
-    """True if the last producer/consumer call on ``ws`` stopped early (synchronises)."""
-    return int(ws[:4].view(torch.int32).item()) != 0
+def workspace_aborted(ws: torch.Tensor, sticky: bool = False) -> bool:
+    """True if the last producer/consumer call on ``ws`` stopped early (its outputs
+    are invalid); with ``sticky``, if any call did since ``clear_workspace_abort``
+    (synchronises)."""
+    w = ws[:8].view(torch.int32)
+    return int(w[1 if sticky else 0].item()) != 0
+
+
+def clear_workspace_abort(ws: torch.Tensor) -> None:
+    """Zero the sticky abort word of a producer/consumer workspace (enqueued)."""
+    ws[4:8].zero_()
+
+
+def _raise_if_aborted(ws: torch.Tensor, what: str) -> None:
+    """Raise when the producer/consumer call that last used ``ws`` stopped early."""
+    if workspace_aborted(ws):
+        raise KDAError(f"{what}: a producer/consumer hand-off wait timed out and the call "
+                       "stopped early; its outputs are invalid (NaN where not computed)")
 
 
 def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None,
             output_final_state=True, out=None, final_state=None, workspace="auto",
-            normalize_k=False, beta_logit=False, gate_logit=False):
+            normalize_k=False, beta_logit=False, gate_logit=False, check=True):
     """Chunked KDA forward over packed sequences.
 
     q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (all fp32 or all bf16); g (log alpha) fp32:
@@ -179,6 +194,10 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None
     Prologue (fused into the kernels): ``normalize_k`` L2-normalises each raw key row,
     ``beta_logit`` takes beta = sigmoid(beta), ``gate_logit`` takes the retention
     alpha = sigmoid(g) instead of exp(g).
+    ``check``: when the producer/consumer kernel ran, wait for the call and raise
+    ``KDAError`` if its hand-off aborted (outputs invalid).  ``check=False`` returns
+    at once; the caller then reads ``workspace_aborted(ws)`` itself (the sticky word
+    covers many calls: ``workspace_aborted(ws, sticky=True)``).
     Returns (o [B, T, H, d_v], final_state or None).
     """
     dev = q.device
@@ -221,10 +240,10 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None
         if fs.shape != (N, H, d_v, d_k):
             raise ValueError("final_state must be [N, H, d_v, d_k]")
     ws = None
+    nb = workspace_bytes(dt, N, B * T, H, d_k, d_v)
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
-        nb = workspace_bytes(dt, N, B * T, H, d_k, d_v)
         ws = _auto_workspace(dev, nb) if nb > 0 else None
     elif workspace is not None:
         _need(workspace, "workspace", dtype=torch.uint8, device=dev)
@@ -234,6 +253,10 @@ def prefill(q, k, v, g, beta, *, cu_seqlens=None, scale=None, initial_state=None
                                 _ptr(beta), _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
                                 float(scale), _ptr(initial_state), _ptr(fs), _ptr(o), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(dev)))
+    # the library reports a hand-off abort in the workspace only when it ran the
+    # producer/consumer kernel, i.e. when the workspace is large enough for it
+    if check and ws is not None and nb > 0 and ws.numel() >= nb and B * T > 0:
+        _raise_if_aborted(ws, "kda.prefill")
     return o, fs
 
 
@@ -278,9 +301,16 @@ def backward_workspace_bytes(N: int, T_total: int, H: int, d_k: int, d_v: int) -
     return int(lib().kda_backward_workspace_bytes(KDA_BF16, N, T_total, H, d_k, d_v))
 
 
+def _backward_uses_ring(N: int, H: int, d_k: int, d_v: int) -> bool:
+    """Whether kda_backward's forward sweep runs on the producer/consumer kernel (its
+    workspace then starts with the ring and the abort words): d_k = d_v = 128 and a
+    producer/consumer plan with two consumers (include/kda.h, kda_backward)."""
+    return d_k == 128 and d_v == 128 and prefill_coop_plan(torch.bfloat16, N, H, d_k, d_v)[0] == 2
+
+
 def backward(q, k, v, g, beta, do, *, cu_seqlens=None, scale=None, initial_state=None,
              dfinal_state=None, need_dinitial_state=True, workspace="auto",
-             normalize_k=False, beta_logit=False, gate_logit=False):
+             normalize_k=False, beta_logit=False, gate_logit=False, check=True):
     """Gradients of ``prefill`` (bf16 inputs).  The prologue flags must be those of the
     forward call; the gradients are then with respect to the raw k, beta logits and
     retention logits.
@@ -289,6 +319,7 @@ def backward(q, k, v, g, beta, do, *, cu_seqlens=None, scale=None, initial_state
     ``dfinal_state`` [N, H, d_v, d_k] fp32 (or None: zero) is dL/d(final state).
     ``workspace``: "auto" (a cached device buffer) or a uint8 device tensor of at least
     ``backward_workspace_bytes`` bytes.
+    ``check``: as for ``prefill`` (raise if the forward sweep's hand-off aborted).
     Returns (dq, dk, dv [bf16], dg [fp32, g's shape, or None], dbeta [fp32],
     dinitial_state [fp32, or None]).
     """
@@ -342,4 +373,6 @@ def backward(q, k, v, g, beta, do, *, cu_seqlens=None, scale=None, initial_state
                               _ptr(initial_state), _ptr(do), _ptr(dfinal_state), _ptr(dq),
                               _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), _ptr(ws),
                               ws.numel(), _stream(dev)))
+    if check and B * T > 0 and N > 0 and _backward_uses_ring(N, H, d_k, d_v):
+        _raise_if_aborted(ws, "kda.backward")
     return dq, dk, dv, dg, dbeta, ds0

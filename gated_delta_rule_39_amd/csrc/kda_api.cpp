@@ -85,8 +85,10 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t H, int32_t d_k, int32_t d_v
   if (np < 1 || static_cast<int64_t>(units) * (nc + np) > cus) return p;
   p.NC = nc;
   p.NP = np;
+  // the split consumer releases chunk c's slot at the start of chunk c + 1, after it
+  // has waited for chunk c + 2: three slots at least, or that wait never ends
   p.R = env_int("KDA_COOP_R", np + 4);
-  if (p.R < 2) p.R = 2;
+  if (p.R < 3) p.R = 3;
   return p;
 }
 
@@ -147,11 +149,17 @@ int kda_prefill_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
   return KDA_OK;
 }
 
-int kda_prefill_ex(int dtype, int decay, int flags, const void* q, const void* k,
-                   const void* v, const float* g, const float* beta, const int32_t* cu_seqlens,
-                   int32_t N, int32_t B, int64_t T, int32_t H, int32_t d_k, int32_t d_v,
-                   float scale, const float* initial_state, float* final_state, void* o,
-                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace kda {
+// Argument checks of kda_prefill_ex (no HIP call).  KDA_OK with *launch = false when
+// there is nothing to do.
+int prefill_args_status(int dtype, int decay, int flags, const void* q, const void* k,
+                        const void* v, const float* g, const float* beta,
+                        const int32_t* cu_seqlens, int32_t N, int32_t B, int64_t T, int32_t H,
+                        int32_t d_k, int32_t d_v, const float* final_state, const void* o,
+                        bool* launch) {
+  *launch = false;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
   if (decay != KDA_DECAY_CHANNEL && decay != KDA_DECAY_HEAD && decay != KDA_DECAY_NONE)
     return KDA_ERR_UNSUPPORTED;
@@ -168,6 +176,23 @@ int kda_prefill_ex(int dtype, int decay, int flags, const void* q, const void* k
       (!q || !k || !v || (!g && decay != KDA_DECAY_NONE) || !beta || !o))
     return KDA_ERR_NULL_ARG;
   if (static_cast<int64_t>(B) * T == 0 && !final_state) return KDA_OK;
+  *launch = true;
+  return KDA_OK;
+}
+}  // namespace kda
+
+extern "C" {
+
+int kda_prefill_ex(int dtype, int decay, int flags, const void* q, const void* k,
+                   const void* v, const float* g, const float* beta, const int32_t* cu_seqlens,
+                   int32_t N, int32_t B, int64_t T, int32_t H, int32_t d_k, int32_t d_v,
+                   float scale, const float* initial_state, float* final_state, void* o,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool launch = false;
+  const int st = kda::prefill_args_status(dtype, decay, flags, q, k, v, g, beta, cu_seqlens, N, B,
+                                          T, H, d_k, d_v, final_state, o, &launch);
+  if (st != KDA_OK || !launch) return st;
+  const int64_t units = static_cast<int64_t>(N) * H;
   kda::PrefillArgs a{};
   a.q = q;
   a.k = k;

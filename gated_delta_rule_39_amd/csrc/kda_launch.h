@@ -55,5 +55,12 @@ int prefill_max_bv(int dtype, int dk);
 // a.DV / (4 * a.NC) in {16, 32}.
 hipError_t launch_prefill_coop(int dk, const PrefillArgs& a, hipStream_t stream);
 size_t prefill_coop_workspace_bytes(int dk, int dv, int units, int R);
+// The argument checks of kda_prefill_ex (kda_api.cpp), no HIP call: a kda.h status,
+// and *launch = false when there is nothing to do.
+int prefill_args_status(int dtype, int decay, int flags, const void* q, const void* k,
+                        const void* v, const float* g, const float* beta,
+                        const int32_t* cu_seqlens, int32_t N, int32_t B, int64_t T, int32_t H,
+                        int32_t d_k, int32_t d_v, const float* final_state, const void* o,
+                        bool* launch);
 
 }  // namespace kda

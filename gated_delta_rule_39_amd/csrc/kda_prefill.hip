@@ -217,8 +217,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 // Producer / consumer kernel (bf16, WY form; the algebra is in kda_wy.h)
 // ====================================================================================
 
-// Workspace: [0, 256) header (word 0: abort), then per-unit flags ready[R], done[R],
-// arrive, pad (int32), then the ring slots.
+// Workspace: [0, 256) header (word 0: this call aborted; word 1: some call aborted
+// since the caller last cleared it -- the launch's reset kernel clears word 0 and the
+// flags, never word 1), then per-unit flags ready[R], done[R], arrive, pad (int32),
+// then the ring slots.
 constexpr size_t kWsHeader = 256;
 __host__ __device__ inline int coop_flag_words(int R) { return 2 * R + 2; }
 __host__ __device__ inline size_t coop_flags_bytes(int units, int R) {
@@ -235,6 +237,13 @@ __host__ __device__ inline size_t coop_workspace_bytes(int units, int R) {
 
 constexpr uint32_t kSpinLimit = 1u << 22;   // ~ a second of s_sleep polling
 
+// Raise the abort: word 0 (this call; every waiting workgroup then leaves its loop)
+// and the sticky word 1.
+__device__ __forceinline__ void raise_abort(int* abort_word) {
+  __hip_atomic_store(abort_word + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wait (one lane) until *p >= target.  False if the wait ran out or the grid aborted;
 // a wait that runs out raises the abort word.
 __device__ __forceinline__ bool wait_at_least(const int* p, int target, int* abort_word) {
@@ -244,7 +253,7 @@ __device__ __forceinline__ bool wait_at_least(const int* p, int target, int* abo
         __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
       return false;
     if (it >= kSpinLimit) {
-      __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      raise_abort(abort_word);
       return false;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -258,6 +267,38 @@ __device__ __forceinline__ void vm_barrier() {
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// A consumer whose hand-off aborted leaves its outputs invalid.  Make that visible
+// instead of leaving stale values: NaN in every element it owns -- value columns
+// [v0, v0 + ncols) of the unit's o rows, of its final state and (STATES) of its
+// chunk-start states.
+template <int DK, int DV, bool STATES>
+__device__ __forceinline__ void poison_outputs(const PrefillArgs& a, int n_seq, int h, int64_t bos,
+                                            int64_t eos, int nch, int v0, int ncols, int tid) {
+  const int vpr = ncols / 8;   // 16-byte vectors per row
+  const u32x4 nan2 = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+  const u32x4 nan4 = u32x4{0x7fc00000u, 0x7fc00000u, 0x7fc00000u, 0x7fc00000u};
+  if (a.o) {
+    bf16* o = static_cast<bf16*>(a.o);
+    for (int64_t i = tid; i < (eos - bos) * vpr; i += kThreads) {
+      const int64_t r = bos + i / vpr;
+      *reinterpret_cast<u32x4*>(o + (r * a.H + h) * DV + v0 + 8 * (i % vpr)) = nan2;
+    }
+  }
+  const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * DV * DK;
+  if (a.final_state)
+    for (int i = tid; i < ncols * DK / 4; i += kThreads)
+      *reinterpret_cast<u32x4*>(a.final_state + st_base + int64_t(v0) * DK + 4 * i) = nan4;
+  if constexpr (STATES) {
+    bf16* cs = static_cast<bf16*>(a.chunk_states);
+    const int64_t slot0 = chunk_slot_base(n_seq, bos);
+    for (int64_t i = tid; i < int64_t(nch) * ncols * DK / 8; i += kThreads) {
+      const int64_t c = i / (ncols * DK / 8), e = i % (ncols * DK / 8);
+      *reinterpret_cast<u32x4*>(cs + ((slot0 + c) * a.H + h) * DV * DK + int64_t(v0) * DK +
+                                8 * e) = nan2;
+    }
+  }
 }
 
 // Consumer LDS: two staging buffers, two output tiles [64][BV + 8] bf16, flags.
@@ -542,6 +583,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
         *reinterpret_cast<f32x4*>(a.final_state + st_base + int64_t(v0 + 16 * vt + lr) * DK +
                                   32 * wave + 16 * b + 4 * lq) = S[b][vt];
   }
+  if (!ok) poison_outputs<DK, DV, STATES>(a, n_seq, h, bos, eos, nch, v0, 16 * NVT, tid);
 }
 
 // A producer's chunk tiles for the backward's reverse chain (ChainTiles): KD, Qg^T, -W^T
@@ -642,7 +684,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
           break;
         __builtin_amdgcn_s_sleep(2);
       }
-      if (mode < 0) __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (mode < 0) raise_abort(abort_word);
       pFlag[1] = mode;
     }
     lds_barrier();
@@ -964,12 +1006,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
         *reinterpret_cast<f32x4*>(a.final_state + st_base + int64_t(vw0 + 16 * vs + lr) * DK +
                                   16 * kb + 4 * lq) = S[kb][vs];
   }
+  if (!ok) poison_outputs<DK, DV, false>(a, n_seq, h, bos, eos, nch, v0, BV, tid);
 }
 
-// Zero the abort word and the hand-off flags before a producer/consumer launch.
+// Zero the abort word and the hand-off flags before a producer/consumer launch (not
+// the sticky abort word 1).
 __global__ void coop_reset_kernel(int* words, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-    words[i] = 0;
+    if (i != 1) words[i] = 0;
 }
 
 // ====================================================================================

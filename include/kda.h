@@ -117,10 +117,14 @@ const char* kda_status_string(int status);
  *   value-tile workgroups through a ring in the workspace.  Otherwise (NULL, too
  *   small, fp32) the fused kernel runs, in which every value tile recomputes them.
  *   The library owns the workspace's contents during the call (no initialisation
- *   needed); calls that share one workspace must be ordered on one stream.  After
- *   such a call completes, the workspace's first int32 is 0; nonzero means a
- *   cross-workgroup hand-off wait timed out, the call stopped early and its
- *   outputs are invalid.
+ *   needed) except its second int32; calls that share one workspace must be ordered
+ *   on one stream.  Abort report: after such a call completes, the workspace's
+ *   first int32 is 0; nonzero means a cross-workgroup hand-off wait timed out and
+ *   the call stopped early.  Every output element of a (sequence, head) that did
+ *   not complete is then NaN (o rows, final state), so an aborted call never leaves
+ *   stale values that look valid.  The second int32 is sticky: an aborted call sets
+ *   it to 1 and no call clears it, so a caller that zeroes it once can check many
+ *   calls with one read.
  */
 int kda_prefill(int dtype,
                 const void* q, const void* k, const void* v,
@@ -225,8 +229,9 @@ int kda_decode_step_ex(int dtype, int decay, int flags,
  *     With d_k = d_v = 128 and the producer/consumer plan of kda_prefill_coop_plan()
  *     (two consumers), the forward sweep that recomputes the chunk states runs on that
  *     kernel and the workspace starts with its ring: after the call, a nonzero first
- *     int32 means a hand-off wait timed out and the outputs are invalid, as for
- *     kda_prefill.
+ *     int32 means a hand-off wait timed out and the outputs are invalid (the chunk
+ *     states of the units that did not complete are NaN, and so are their
+ *     gradients); the second int32 is the sticky abort word, as for kda_prefill.
  * N = 0 is a no-op returning KDA_OK.  The keys must be unit rows as for the forward.
  */
 int kda_backward(int dtype, int decay, int flags,

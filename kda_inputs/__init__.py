@@ -10,7 +10,11 @@ d_k per (token, head) in fp32 (the caller-side precondition of the delta rule,
 step-by-step page, FAQ "Why does DeltaNet need keys to be normalized?"); then
 q, k, v are rounded to the input dtype (bf16 with round-to-nearest-even).  The
 gate is g = log(alpha) in fp32, either -U(0.001, 0.1) ("uniform") or
--softplus(N(0, 1)) * 0.1 ("softplus"); beta = sigmoid(N(0, 1)) in fp32.  Initial
+-softplus(N(0, 1)) * 0.1 ("softplus"); beta = sigmoid(N(0, 1)) in fp32.  Two
+strong-decay recipes probe the documented range of the per-chunk decay (the sum of
+|g| over 64 tokens, per key channel, below about 80): "moderate", -U(0.25, 0.5)
+(about 24 per chunk), "strong", -U(0.6, 1.1) (about 54) and "edge", -U(0.95, 1.25)
+(about 70).  Initial
 states, where present, are N(0, 0.02^2) fp32 (0.02 read as the standard
 deviation).  The draw order is fixed: sequence lengths (varlen only), q, k, v,
 g, beta, initial state.
@@ -100,6 +104,10 @@ def _gate(gen, shape, kind, device):
         return -(0.001 + 0.099 * u)
     if kind == "softplus":
         return -torch.nn.functional.softplus(_randn(gen, shape, device)) * 0.1
+    if kind in ("moderate", "strong", "edge"):
+        lo, hi = {"moderate": (0.25, 0.5), "strong": (0.6, 1.1), "edge": (0.95, 1.25)}[kind]
+        u = torch.rand(*shape, generator=gen, device=device, dtype=torch.float32)
+        return -(lo + (hi - lo) * u)
     raise ValueError(f"unknown gate recipe {kind!r}")
 
 

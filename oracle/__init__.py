@@ -49,4 +49,4 @@ from .kda_prologue import (  # noqa: F401
     NORM_K,
     prologue,
 )
-from .kda_bwd_ref import backward, recurrence_backward  # noqa: F401
+from .kda_bwd_ref import backward, recurrence_backward, segmented_backward  # noqa: F401

@@ -196,3 +196,51 @@ def backward(q, k, v, g, beta, do, cu_seqlens=None, scale=None, initial_state=No
     if flags:
         dk, dg, dbeta = _prologue_backward(k_raw, g_raw, b_raw, flags, dk, dg, dbeta)
     return (dq.reshape(B, T, H, d_k), dk, dv.reshape(B, T, H, d_v), dg, dbeta, ds0)
+
+
+def segmented_backward(q, k, v, g, beta, do, segment=64, scale=None, initial_state=None,
+                       dfinal_state=None):
+    """:func:`recurrence_backward` over a long sequence, one segment of ``segment``
+    tokens at a time, so that no more than one segment's token states are held.
+
+    The state at a segment's start is all the later tokens depend on ("Kimi Delta
+    Attention Technical Deep Dive", "Systems and implementation tradeoffs" ->
+    "Training": the state at a chunk boundary is the next chunk's initial condition).
+    So one forward pass keeps the state at every segment start; then, from the last
+    segment back to the first, the exact token backward of the segment runs from its
+    stored start state, with the state gradient carried in from the segment after it
+    (the final-state gradient for the last), and hands the gradient of its start
+    state to the segment before.  Same shapes and returns as
+    :func:`recurrence_backward`.
+    """
+    from .kda_ref import recurrence
+    q, k, v, beta, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta, do))
+    g = None if g is None else np.asarray(g, dtype=np.float64)
+    U, T, d_k = k.shape
+    d_v = v.shape[2]
+    starts = list(range(0, T, segment)) or [0]
+    states = []
+    s = (np.zeros((U, d_v, d_k)) if initial_state is None
+         else np.array(initial_state, dtype=np.float64, copy=True))
+    for t0 in starts:
+        states.append(s)
+        sl = slice(t0, t0 + segment)
+        _, s = recurrence(q[:, sl], k[:, sl], v[:, sl], None if g is None else g[:, sl],
+                          beta[:, sl], scale=scale, initial_state=s)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dg = None if g is None else np.zeros_like(g)
+    dbeta = np.zeros_like(beta)
+    ds = None if dfinal_state is None else np.asarray(dfinal_state, dtype=np.float64)
+    for t0, s0 in zip(reversed(starts), reversed(states)):
+        sl = slice(t0, t0 + segment)
+        r = recurrence_backward(q[:, sl], k[:, sl], v[:, sl], None if g is None else g[:, sl],
+                                beta[:, sl], do[:, sl], scale=scale, initial_state=s0,
+                                dfinal_state=ds)
+        dq[:, sl], dk[:, sl], dv[:, sl] = r[0], r[1], r[2]
+        if dg is not None:
+            dg[:, sl] = r[3]
+        dbeta[:, sl] = r[4]
+        ds = r[5]
+    if ds is None:
+        ds = np.zeros((U, d_v, d_k))
+    return dq, dk, dv, dg, dbeta, ds

@@ -45,8 +45,9 @@ def recurrence_parallel(q, k, v, g, beta, scale=None, initial_state=None,
     for i in range(procs):
         sl = slice(bounds[i], bounds[i + 1])
         s0 = None if initial_state is None else np.asarray(initial_state)[sl]
+        gs = None if g is None else np.asarray(g)[sl]   # no decay (DeltaNet): g is None
         jobs.append((np.asarray(q)[sl], np.asarray(k)[sl], np.asarray(v)[sl],
-                     np.asarray(g)[sl], np.asarray(beta)[sl], scale, s0))
+                     gs, np.asarray(beta)[sl], scale, s0))
     if procs == 1:
         outs = [_run(jobs[0])]
     else:

@@ -9,17 +9,21 @@ import pytest
 
 import gated_delta_rule_39_amd as kda
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                      "kda.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "kda.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(kda.LIB_PATH),
                                 reason="libkda.so not built (run __graft_entry__.build())")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+    """Every function declared in include/*.h (kda.h and the headers beside it)."""
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, f)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
@@ -27,7 +31,8 @@ def test_exports_every_declared_symbol():
     assert {"kda_prefill", "kda_decode_step", "kda_abi_version", "kda_status_string",
             "kda_prefill_workspace_bytes", "kda_prefill_plan", "kda_prefill_coop_plan",
             "kda_prefill_ex", "kda_decode_step_ex", "kda_backward",
-            "kda_backward_workspace_bytes"} <= set(names)
+            "kda_backward_workspace_bytes", "kda_probe_hbm_copy", "kda_probe_hbm_read",
+            "kda_probe_mfma_bf16", "kda_probe_read_sink_words"} <= set(names)
     L = kda.lib()
     for name in names:
         assert hasattr(L, name), f"{name} declared in kda.h but not exported"
@@ -169,3 +174,79 @@ def test_backward_validation_codes():
     assert L.kda_backward_workspace_bytes(1, 3, 1000, 4, 128, 64) == \
         slots * (2 * 64 * 128 * 2 + tiles)
     assert L.kda_backward_workspace_bytes(0, 3, 1000, 4, 128, 64) == 0
+
+
+class _FakeLib:
+    """Stands in for libkda.so: every call succeeds and launches nothing; the
+    producer/consumer plan applies with a 1 KiB workspace."""
+
+    def kda_prefill_workspace_bytes(self, *a):
+        return 1024
+
+    def kda_prefill_ex(self, *a):
+        return 0
+
+    def kda_backward_workspace_bytes(self, *a):
+        return 1024
+
+    def kda_backward(self, *a):
+        return 0
+
+    def kda_prefill_coop_plan(self, dtype, N, H, dk, dv, nc, np_, r):
+        nc._obj.value, np_._obj.value, r._obj.value = 2, 5, 9
+        return 0
+
+    def kda_status_string(self, s):
+        return b"KDA fake"
+
+
+@pytest.mark.parametrize("word,raises", [(0, False), (1, True)])
+def test_aborted_hand_off_makes_the_python_call_raise(monkeypatch, word, raises):
+    """A workspace whose abort word is set after the call makes kda.prefill and
+    kda.backward raise instead of returning the outputs (CPU tensors; the library
+    and the device checks are replaced, only the binding's logic runs)."""
+    import torch
+    monkeypatch.setattr(kda, "lib", lambda: _FakeLib())
+    monkeypatch.setattr(kda, "_need", lambda *a, **k: None)
+    monkeypatch.setattr(kda, "_stream", lambda dev: None)
+    B, T, H, d = 1, 64, 2, 128
+    x = torch.zeros(B, T, H, d, dtype=torch.bfloat16)
+    g = torch.zeros(B, T, H, d)
+    beta = torch.zeros(B, T, H)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    ws[:4].view(torch.int32)[0] = word
+    if raises:
+        with pytest.raises(kda.KDAError, match="aborted|timed out"):
+            kda.prefill(x, x, x, g, beta, workspace=ws)
+        with pytest.raises(kda.KDAError, match="timed out"):
+            kda.backward(x, x, x, g, beta, x, workspace=ws)
+    else:
+        o, fs = kda.prefill(x, x, x, g, beta, workspace=ws)
+        assert o.shape == (B, T, H, d) and fs.shape == (1, H, d, d)
+        kda.backward(x, x, x, g, beta, x, workspace=ws)
+    # check=False leaves it to the caller
+    kda.prefill(x, x, x, g, beta, workspace=ws, check=False)
+    assert kda.workspace_aborted(ws) == raises
+
+
+def test_sticky_abort_word():
+    import torch
+    ws = torch.zeros(64, dtype=torch.uint8)
+    assert not kda.workspace_aborted(ws, sticky=True)
+    ws[4:8].view(torch.int32)[0] = 1
+    assert kda.workspace_aborted(ws, sticky=True) and not kda.workspace_aborted(ws)
+    kda.clear_workspace_abort(ws)
+    assert not kda.workspace_aborted(ws, sticky=True)
+
+
+def test_probe_validation_codes():
+    L = kda.lib()
+    L.kda_probe_hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.kda_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    L.kda_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert L.kda_probe_hbm_copy(None, FAKE, 1024, None) == 1
+    assert L.kda_probe_hbm_copy(FAKE, FAKE, 1000, None) == 2      # not a multiple of 16
+    assert L.kda_probe_hbm_read(FAKE, 0, FAKE, None) == 2
+    assert L.kda_probe_mfma_bf16(FAKE, 0, 10, None) == 2
+    assert L.kda_probe_mfma_bf16(None, 4, 10, None) == 1
+    assert L.kda_probe_read_sink_words() > 0

@@ -52,13 +52,18 @@ def run_both(x, do, ds, flags=0):
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
 
 
-def compare(x, got, ref, label):
+def compare(x, got, ref, label, dg_bar=BF16_RMS_REL):
     cu = x["cu_seqlens"]
     for name, a, r in zip(NAMES, got, ref):
         if r is None:
             assert a is None, name
             continue
         a = a.float().cpu().numpy().astype(np.float64)
+        if name == "dg" and dg_bar != BF16_RMS_REL:
+            err = rms_rel(a, r)
+            print(f"  {label} {name}: rms-rel {err:.2e} (bound {dg_bar})", flush=True)
+            assert np.isfinite(a).all() and err <= dg_bar, f"{label} dg: rms-rel {err:.3e}"
+            continue
         err = check("bf16", a, r, f"{label} {name}")
         print(f"  {label} {name}: rms-rel {err:.2e}", flush=True)
         # per (sequence, head): token rows of each sequence, or the state of each unit.
@@ -175,33 +180,64 @@ def test_backward_dv_matches_directional_derivative_of_forward_kernel():
     assert abs(fd - an) <= 2e-2 * max(abs(fd), 1.0), (fd, an)
 
 
-def test_backward_full_size_sampled_window():
+def _segmented_head(args):
+    from oracle import segmented_backward
+    return segmented_backward(*args, segment=64)
+
+
+def test_backward_full_size_every_token():
     """The long-context workload (B=1, H=32, T=65536, d=128, bf16) in the launch
-    configuration bench.py times.  Without a final-state gradient, the gradients of
-    the last W tokens depend only on the state at T - W and on those tokens, so the
-    oracle runs the forward recurrence to T - W (state only) and the exact backward of
-    the last W tokens from there, for two heads."""
-    from oracle import recurrence, recurrence_backward
-    W, heads = 320, [0, 21]
-    print("backward full size, sampled window", flush=True)
+    configuration bench.py times, four heads compared over ALL 65536 tokens: the oracle
+    runs the exact token backward segment by segment (one fp64 forward pass stores the
+    state every 64 tokens; each segment's backward starts from its stored state and
+    the state gradient carried back from the segment after it), one head per process.
+    Every gradient is gated per head and per 64-token window."""
+    import multiprocessing as mp
+    import time
+    from parity import check_unit
+    heads = [0, 9, 21, 31]
+    print("backward full size, every token of four heads", flush=True)
     x = ki.make_prefill_workload(ki.LONG_PREFILL, device=DEV)
     gen = torch.Generator(device=DEV)
     gen.manual_seed(178)
     do = torch.randn(x["v"].shape, generator=gen, device=DEV).to(torch.bfloat16)
     got = kda.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, need_dinitial_state=False)
     torch.cuda.synchronize()
-    T = x["T"]
-    f = lambda t: ki.to_f64(t[0, :, heads].transpose(0, 1))            # [U, T, ...]
-    q, k, v, g, do64 = f(x["q"]), f(x["k"]), f(x["v"]), f(x["g"]), f(do)
-    beta = ki.to_f64(x["beta"][0, :, heads].transpose(0, 1))
-    _, s_mid = recurrence(q[:, :T - W], k[:, :T - W], v[:, :T - W], g[:, :T - W],
-                          beta[:, :T - W])
-    ref = recurrence_backward(q[:, T - W:], k[:, T - W:], v[:, T - W:], g[:, T - W:],
-                              beta[:, T - W:], do64[:, T - W:], initial_state=s_mid)
-    for name, a, r in zip(NAMES[:5], got[:5], ref[:5]):
-        a = ki.to_f64(a[0, T - W:, heads].transpose(0, 1))
-        err = check("bf16", a, r, f"full-size window {name}")
-        print(f"  full-size window {name}: rms-rel {err:.2e}", flush=True)
+    f = lambda t, h: np.ascontiguousarray(ki.to_f64(t[0, :, h]))          # [T, d]
+    jobs = [(f(x["q"], h)[None], f(x["k"], h)[None], f(x["v"], h)[None], f(x["g"], h)[None],
+             ki.to_f64(x["beta"][0, :, h])[None], f(do, h)[None]) for h in heads]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(len(heads)) as pool:
+        refs = pool.map(_segmented_head, jobs)
+    print(f"  segmented oracle: {time.perf_counter() - t0:.1f} s", flush=True)
+    for i, h in enumerate(heads):
+        for name, a, r in zip(NAMES[:5], got[:5], refs[i][:5]):
+            a = ki.to_f64(a[0, :, h])
+            rel, worst, mx = check_unit(a, r[0], f"full-size head {h} {name}")
+            print(f"  head {h} {name}: rms-rel {rel:.2e}, worst window {worst:.2e}, "
+                  f"max|d|/rms {mx:.2e}", flush=True)
+
+
+# The gradient kernel forms dL/dG per element as dKg Kg + dQg Qg - dKi Ki - dKh Kh
+# (products of bf16-operand MFMA results with e^{+-G} factors) and dg by suffix sums
+# over the chunk's rows, in which most of those terms cancel.  The stronger the decay,
+# the larger the terms against what is left, so dg meets the bf16 bar up to a per-chunk
+# decay of about 24 and is bounded at 5e-2 beyond (measured: 2.7e-2 at about 54); the
+# other gradients meet the bar throughout.
+DG_STRONG_BOUND = 5e-2
+
+
+@pytest.mark.parametrize("gate", ["moderate", "strong", "edge"])
+def test_backward_strong_decay(gate):
+    """Gradients with per-chunk sums of |g| of about 24, 54 and 70 (inside the
+    documented range)."""
+    print(f"backward strong decay {gate}", flush=True)
+    x = ki.make_prefill(H=3, d_k=128, d_v=128, dtype="bf16", gate=gate, lengths=[64, 130, 300],
+                        init_state_std=0.02, seed=74, device=DEV)
+    do, ds = grads_in(x, 174)
+    got, ref = run_both(x, do, ds)
+    compare(x, got, ref, f"strong decay {gate}",
+            dg_bar=BF16_RMS_REL if gate == "moderate" else DG_STRONG_BOUND)
 
 
 @pytest.mark.parametrize("decay,flags", [("channel", 7), ("head", 7), ("none", 7),

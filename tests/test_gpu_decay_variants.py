@@ -12,7 +12,7 @@ import gated_delta_rule_39_amd as kda
 import kda_inputs as ki
 from oracle import decode_step as oracle_decode
 from parity import check
-from test_gpu_prefill import DEV, PATHS, _sampled, compare_full, run_gpu, run_oracle
+from test_gpu_prefill import DEV, PATHS, _every_unit, compare_full, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 DECAYS = ["head", "none"]
@@ -97,15 +97,14 @@ def test_deltanet_one_hot_retrieval_exact(path):
 
 
 @pytest.mark.parametrize("decay", DECAYS)
-def test_training_workload_sampled(decay):
-    """B4 H16 T4096 d128 bf16 on the producer/consumer kernel, sampled units."""
-    _sampled(ki.TRAIN_PREFILL, [(0, 0), (1, 7), (3, 11)], f"{decay} B4 H16 T4096", "coop",
-             decay=decay)
+def test_training_workload_every_unit(decay):
+    """B4 H16 T4096 d128 bf16, both kernels, every unit against the oracle."""
+    _every_unit(ki.TRAIN_PREFILL, decay=decay)
 
 
-def test_long_workload_head_decay_sampled():
-    """H32 T65536 d128 bf16 (the long-context shape) with per-head decay."""
-    _sampled(ki.LONG_PREFILL, [(0, 0), (0, 21)], "head H32 T65536", "coop", decay="head")
+def test_long_workload_head_decay_every_unit():
+    """H32 T65536 d128 bf16 (the long-context shape) with per-head decay, every unit."""
+    _every_unit(ki.LONG_PREFILL, decay="head")
 
 
 # ------------------------------------------------------------------ decode

@@ -8,7 +8,7 @@ import torch
 import gated_delta_rule_39_amd as kda
 import kda_inputs as ki
 from oracle import decode_step as oracle_decode
-from parity import check
+from parity import check, check_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -42,16 +42,36 @@ def test_decode_bf16_small(d_k, d_v):
     _run_and_compare("bf16", 5, 3, d_k, d_v, steps=6, seed=22)
 
 
+@pytest.mark.parametrize("gate", ["strong", "edge"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_strong_decay(gate, dtype):
+    """Strong per-channel decay (|g| of 0.6 .. 1.25 per token, the per-chunk sums of
+    the prefill's strong-decay tests) over 70 steps."""
+    print(f"decode strong decay {gate} {dtype}", flush=True)
+    d = ki.make_decode(N=6, H=4, d_k=128, d_v=128, steps=70, dtype=dtype, gate=gate, seed=26,
+                       device=DEV)
+    state = d["state"].clone()
+    ref_state = ki.to_f64(d["state"])
+    for t in range(d["steps"]):
+        o = kda.decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t], state)
+        o_ref, ref_state = oracle_decode(*(ki.to_f64(d[n][t]) for n in ("q", "k", "v", "g", "beta")),
+                                         ref_state)
+        torch.cuda.synchronize()
+        check(dtype, ki.to_f64(o), o_ref, f"strong decode o step {t}")
+    check(dtype, ki.to_f64(state), ref_state, "strong decode final state")
+
+
 def test_decode_full_workload_sampled():
     """Decode at full size (N=256, H=32, d=128, bf16, 1000 in-place steps): every unit
-    for the first two steps, a seeded sample of 64 units at every step and their final
-    states (units are independent, so the sample is exact)."""
+    checked on its own for the first two steps, a seeded sample of 256 units at every
+    step and their final states (units are independent, so the sample is exact)."""
     w = ki.DECODE
     print(f"decode full workload {w.name}", flush=True)
     d = ki.make_decode_workload(w, device=DEV)
     N, H, steps = w.N, w.H, w.steps
     rng = np.random.default_rng(55)
-    flat = rng.choice(N * H, size=64, replace=False)
+    S = 256
+    flat = rng.choice(N * H, size=S, replace=False)
     sn, sh = flat // H, flat % H
     idx_n = torch.tensor(sn, device=DEV)
     idx_h = torch.tensor(sh, device=DEV)
@@ -59,7 +79,7 @@ def test_decode_full_workload_sampled():
     ref_state = ki.to_f64(s0[idx_n, idx_h])[:, None]          # [64, 1, d_v, d_k]
     ref_full = ki.to_f64(s0)
     state = s0.clone()
-    o_samp = torch.empty((steps, 64, w.d_v), dtype=torch.bfloat16, device=DEV)
+    o_samp = torch.empty((steps, S, w.d_v), dtype=torch.bfloat16, device=DEV)
     for t in range(steps):
         o = kda.decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t], state)
         o_samp[t] = o[idx_n, idx_h]
@@ -68,23 +88,25 @@ def test_decode_full_workload_sampled():
             o_ref, ref_full = oracle_decode(*(ki.to_f64(d[x][t]) for x in ("q", "k", "v", "g",
                                                                             "beta")), ref_full)
             o_h = ki.to_f64(o)
-            check("bf16", o_h, o_ref, f"decode full o step {t}",
-                  units=[(f"unit {u}", o_h.reshape(N * H, -1)[u], o_ref.reshape(N * H, -1)[u])
-                         for u in range(0, N * H, 97)])
+            check("bf16", o_h, o_ref, f"decode full o step {t}")
+            check_rows(o_h.reshape(N * H, -1), o_ref.reshape(N * H, -1),
+                       f"decode full o step {t} per unit")
+            check_rows(ki.to_f64(state).reshape(N * H, -1), ref_full.reshape(N * H, -1),
+                       f"decode full state step {t} per unit")
     torch.cuda.synchronize()
     # oracle over the sampled units for all steps
-    o_ref_all = np.empty((steps, 64, w.d_v))
+    o_ref_all = np.empty((steps, S, w.d_v))
     sel = lambda x, t: ki.to_f64(d[x][t][idx_n, idx_h])[:, None]
     for t in range(steps):
         o_ref, ref_state = oracle_decode(sel("q", t), sel("k", t), sel("v", t), sel("g", t),
                                          sel("beta", t), ref_state)
         o_ref_all[t] = o_ref[:, 0]
     got = ki.to_f64(o_samp)
-    check("bf16", got, o_ref_all, "decode sampled o (all steps)",
-          units=[(f"unit {u}", got[:, u], o_ref_all[:, u]) for u in range(64)])
-    check("bf16", ki.to_f64(state[idx_n, idx_h]), ref_state[:, 0], "decode sampled final state",
-          units=[(f"unit {u}", ki.to_f64(state[idx_n[u], idx_h[u]]), ref_state[u, 0])
-                 for u in range(64)])
+    check("bf16", got, o_ref_all, "decode sampled o (all steps)", windows=True,
+          units=[(f"unit {u}", got[:, u], o_ref_all[:, u]) for u in range(S)])
+    fin = ki.to_f64(state[idx_n, idx_h])
+    check("bf16", fin, ref_state[:, 0], "decode sampled final state")
+    check_rows(fin.reshape(S, -1), ref_state[:, 0].reshape(S, -1), "decode sampled final state")
 
 
 def test_decode_deterministic_and_in_place():

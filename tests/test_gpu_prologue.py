@@ -11,7 +11,7 @@ import kda_inputs as ki
 from oracle import BETA_LOGIT, GATE_LOGIT, NORM_K
 from oracle import decode_step as oracle_decode
 from oracle import forward as oracle_forward
-from parity import check
+from parity import check, check_unit
 from test_gpu_prefill import DEV, compare_full, run_gpu, seq_bounds
 
 pytestmark = pytest.mark.gpu
@@ -79,7 +79,7 @@ def test_long_workload_sampled_all_flags():
     og = o.view(-1, H, d_v)
     orf = o_ref.reshape(-1, H, d_v)
     for n, h in units:
-        check("bf16", ki.to_f64(og[:, h]), orf[:, h], f"long o head {h}")
+        check_unit(ki.to_f64(og[:, h]), orf[:, h], f"long o head {h}")
         check("bf16", ki.to_f64(fs[n, h]), s_ref[n, h], f"long state head {h}")
 
 

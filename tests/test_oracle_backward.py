@@ -268,3 +268,35 @@ def test_chunked_backward_equals_recurrence_backward(decay, chunk):
             assert a is None
             continue
         np.testing.assert_allclose(a, r[0], rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+@pytest.mark.parametrize("decay", ["channel", "head", "none"])
+@pytest.mark.parametrize("segment", [1, 7, 64, 200])
+def test_segmented_backward_equals_recurrence_backward(decay, segment):
+    """oracle.segmented_backward (segment by segment from stored start states, the
+    state gradient carried backwards) equals the whole-sequence token backward, with
+    an initial state and a final-state gradient, including a ragged last segment and
+    a segment longer than the sequence."""
+    from oracle import segmented_backward
+    c = small_case(11, U=3, T=150, d_k=5, d_v=4, decay=decay)
+    args = (c["q"], c["k"], c["v"], c["g"], c["beta"], c["do"])
+    kw = dict(scale=0.7, initial_state=c["initial_state"], dfinal_state=c["dfinal_state"])
+    ref = recurrence_backward(*args, **kw)
+    got = segmented_backward(*args, segment=segment, **kw)
+    for name, a, r in zip(NAMES, got, ref):
+        if r is None:
+            assert a is None
+            continue
+        np.testing.assert_allclose(a, r, rtol=0, atol=1e-11, err_msg=name)
+
+
+def test_segmented_backward_carries_the_state_gradient():
+    """A planted mistake -- each segment starting from a zero state gradient instead of
+    the one carried from the segment after it -- changes the earlier segments'
+    gradients, so the comparison above would catch it."""
+    c = small_case(12, U=1, T=20, d_k=3, d_v=2)
+    ref = recurrence_backward(c["q"], c["k"], c["v"], c["g"], c["beta"], c["do"])
+    seg = recurrence_backward(c["q"][:, :10], c["k"][:, :10], c["v"][:, :10], c["g"][:, :10],
+                              c["beta"][:, :10], c["do"][:, :10])
+    # dv depends on the state gradient carried in (dq does not: only on the state)
+    assert np.max(np.abs(seg[2] - ref[2][:, :10])) > 1e-6
