@@ -22,7 +22,7 @@ OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libkda.so")
 
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_backward.hip",
-           "kda_probe.hip"]
+           "kda_probe.hip", "kda_noalloc.hip"]
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_*_f32 generation.  -amdgpu-mfma-vgpr-form: MFMA
 # accumulators in ordinary VGPRs, so loop-carried accumulators (the prefill state)

@@ -3,6 +3,7 @@
 // call, so every status except KDA_ERR_HIP can be produced without a GPU.
 
 #include "kda.h"
+#include "kda_noalloc.h"
 
 #include <atomic>
 #include <cstdlib>
@@ -107,6 +108,10 @@ const char* kda_status_string(int status) {
     case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: dtype must be KDA_F32 (0) or KDA_BF16 (1)";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP kernel launch failed";
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+    case KDA_ERR_SCRATCH:
+      return "KDA_ERR_SCRATCH: the call needs more workspace than the allocation-free entry "
+             "point's fixed scratch (kda_noalloc_scratch_bytes()); pass a workspace to "
+             "kda_prefill_ex instead";
     default: return "KDA: unknown status code";
   }
 }
