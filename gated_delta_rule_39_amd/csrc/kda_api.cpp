@@ -60,7 +60,7 @@ int env_int(const char* name, int dflt) {
 // Producer/consumer geometry: W = CUs / units workgroups per unit (all resident at
 // once, one per CU): NC consumers, each 4 waves owning d_v / (4 NC) value columns
 // (NC = 2 for d_v = 128 when W >= 6, else 1), and NP = min(W - NC, 5) producers
-// (measured: past five producers per unit the consumers set the pace); R = NP + 4
+// (measured: past five producers per unit the consumers set the pace); R = NP + 6
 // ring slots.  Needs bf16 inputs and W >= 2.  KDA_PREFILL_COOP=0 disables it;
 // KDA_COOP_NC / KDA_COOP_NP / KDA_COOP_R override the split and the ring depth
 // (tuning only).
@@ -88,7 +88,7 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t H, int32_t d_k, int32_t d_v
   p.NP = np;
   // the split consumer releases chunk c's slot at the start of chunk c + 1, after it
   // has waited for chunk c + 2: three slots at least, or that wait never ends
-  p.R = env_int("KDA_COOP_R", np + 4);
+  p.R = env_int("KDA_COOP_R", np + 6);
   if (p.R < 3) p.R = 3;
   return p;
 }

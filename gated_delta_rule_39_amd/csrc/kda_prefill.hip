@@ -361,8 +361,15 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   auto offU = [&](int p) {
     return uint32_t(SL::oU + (wave * (SL::NVB / 2) + v0 / 32 + p) * SL::kFrag) + fl;
   };
-  auto offW = [&](int j) { return uint32_t(SL::oW + (wave * KS + j) * SL::kFrag) + fl; };
-  auto offQ = [&](int j) { return uint32_t(SL::oQ + (wave * KS + j) * SL::kFrag) + fl; };
+  // W and Qg fragments are held in wave-rotated K order: register jj is K step
+  // (w + jj) % 4, so jj = 0 is the wave's own key block, whose S^T operand it has in
+  // registers (only the other three come from LDS)
+  auto offW = [&](int jj) {
+    return uint32_t(SL::oW + (wave * KS + ((wave + jj) & (KS - 1))) * SL::kFrag) + fl;
+  };
+  auto offQ = [&](int jj) {
+    return uint32_t(SL::oQ + (wave * KS + ((wave + jj) & (KS - 1))) * SL::kFrag) + fl;
+  };
   // M (w, 0) is block w; (w, 1) is block 2 + w and exists for w >= 2 (else re-read (w, 0))
   auto offM = [&](int t) {
     return uint32_t(SL::oM + (t == 0 || wave < 2 ? wave : 2 + wave) * SL::kFrag) + fl;
@@ -374,8 +381,8 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   unsigned char* sSb = smem + CL::oSb + fl;
   unsigned char* sEb = smem + CL::oEb + fl;
   unsigned char* sO = smem + CL::oO;
-  auto sb_at = [&](int j, int vt) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(sSb + (j * NVT + vt) * 1024);
+  auto sb_at = [&](int jj, int vt) -> bf16x8 {   // K step (w + jj) % 4
+    return *reinterpret_cast<const bf16x8*>(sSb + (((wave + jj) & (KS - 1)) * NVT + vt) * 1024);
   };
   auto eb_at = [&](int t, int vt) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(sEb + (t * NVT + vt) * 1024);
@@ -458,6 +465,17 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   int sp = 0, s0 = 0, s1 = 1 % a.R, s2 = 2 % a.R;
   const int t_own = wave >> 1, h_own = wave & 1;
   const bool write_o = !STATES || a.o != nullptr;
+  // the producers' Qg leaves the query scale out in the forward kernel (kept for the
+  // backward's chain tiles): it is applied to each output tile here
+  const float oscale = STATES ? 1.f : a.scale;
+  // output tile of token block w: O^T accumulators, scaled, as bf16 rows in LDS
+  f32x4 Ot[NVT];
+  auto put_o1 = [&](int vt) {
+    const f32x4 x = Ot[vt] * oscale;
+    *reinterpret_cast<bf16x4*>(sO + ((16 * wave + lr) * CL::LDO + 16 * vt + 4 * lq) * 2) =
+        bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+               static_cast<bf16>(x[3])};
+  };
   [[maybe_unused]] const int64_t slot0 = chunk_slot_base(n_seq, bos);
   for (int c = 0; ok && c < nch; ++c) {
     const int64_t c0 = bos + int64_t(c) * kChunk;
@@ -486,7 +504,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     // they are unused bytes of an idle slot).
     const uint32_t nslot = static_cast<uint32_t>(s1) * SL::kBytes;
 
-    f32x4 E[NVT], Ot[NVT];
+    f32x4 E[NVT];
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt) {
       const bf16x8 u = U[vt / 2];
@@ -495,10 +513,13 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     }
 #pragma unroll
     for (int p = 0; p < NVT / 2; ++p) U[p] = ldf(nslot + offU(p));
-    // E = U - W S^T for token block w; the S^T fragments stay for O
+    // E = U - W S^T for token block w; the S^T fragments stay for O.  The wave's own K
+    // step is its state packed as written to LDS at the end of the last chunk.
     bf16x8 sb[KS][NVT];
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
+    for (int vt = 0; vt < NVT; ++vt) sb[0][vt] = pack_frag(S[0][vt], S[1][vt]);
+#pragma unroll
+    for (int j = 1; j < KS; ++j)
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) sb[j][vt] = sb_at(j, vt);
 #pragma unroll
@@ -552,10 +573,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt) {
       *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = pack_frag(S[0][vt], S[1][vt]);
-      const f32x4 x = Ot[vt];
-      *reinterpret_cast<bf16x4*>(sO + ((16 * wave + lr) * CL::LDO + 16 * vt + 4 * lq) * 2) =
-          bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
-                 static_cast<bf16>(x[3])};
+      put_o1(vt);
     }
 
     if (tid == 0)
@@ -707,7 +725,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       const int need = a.NC * (c / a.R);
       int dv = 0;
       if (tid == 0) dv = __hip_atomic_load(done + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      pr.template factors<DECAY>(n);
+      pr.template factors<DECAY, STATES>(n);
       if (tid == 0) pFlag[0] = (dv >= need || wait_at_least(done + s, need, abort_word)) ? 1 : 0;
       lds_barrier();
       if (pFlag[0] == 0) break;
@@ -717,26 +735,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       if constexpr (STATES)
         tiles = static_cast<unsigned char*>(a.chunk_tiles) +
                 ((chunk_slot_base(n_seq, bos) + c) * a.H + h) * ChainTiles<DK>::kBytes;
-      // the next chunk's inputs are requested in five slices between the phases
+      // the next chunk's inputs are requested in slices between the phases, none of
+      // them in the phase that publishes W and U.  Without a next chunk the slices
+      // re-read this chunk's rows (unused): the loads stay unconditional, so the code
+      // has no branches around them and the compiler can count them exactly.
       constexpr int L = PR::kLoads, RPG = PR::RPG;
-      if (has_next) pr.template load_slice<DECAY, 0, RPG / 2, !STATES>(c1, n1);            // g, first half
+      const int64_t cl = has_next ? c1 : c0;
+      const int nl = has_next ? n1 : n;
+      pr.template load_slice<DECAY, 0, RPG / 2, !STATES>(cl, nl);            // g, first half
+      pr.template load_slice<DECAY, PR::kSB, L, !STATES>(cl, nl);            // beta
       if constexpr (STATES)
         pr.template products<true>(rr, slot, reinterpret_cast<bf16*>(tiles + ChainTiles<DK>::oM));
       else
         pr.products(rr, slot);
-      if (has_next) pr.template load_slice<DECAY, RPG / 2, RPG, !STATES>(c1, n1);          // g, second half
+      pr.template load_slice<DECAY, RPG / 2, RPG, !STATES>(cl, nl);          // g, second half
       lds_barrier();
-      if (has_next) pr.template load_slice<DECAY, RPG, 2 * RPG, !STATES>(c1, n1);          // k
+      pr.template load_slice<DECAY, PR::kSK, PR::kSQ, !STATES>(cl, nl);      // k
+      pr.template load_slice<DECAY, PR::kSV, PR::kSB, !STATES>(cl, nl);      // v
       pr.inverse_blocks();
       lds_barrier();
-      if (wave < 2)
-        pr.inverse_pairs();
-      else
-        pr.template publish_qk<2, 2>(rr, slot);
-      if (has_next) pr.template load_slice<DECAY, 2 * RPG, 3 * RPG, !STATES>(c1, n1);      // q
+      // waves 0, 1 merge the diagonal pairs; the Qg / KD^T fragments are spread over
+      // all four waves
+      if (wave < 2) pr.inverse_pairs();
+      pr.template publish_qk<0, 4>(rr, slot);
+      pr.template load_slice<DECAY, PR::kSQ, PR::kSV, !STATES>(cl, nl);      // q
       lds_barrier();
       pr.inverse_rest();
-      if (has_next) pr.template load_slice<DECAY, 3 * RPG, L, !STATES>(c1, n1);            // v, beta
       if constexpr (STATES) {
         // -W rows staged in the A area (dead after the inverse) for the transposed copy
         static_assert(size_t(kChunk) * PL::LDK * 2 <= PL::oX - PL::oA, "-W staging fits");
@@ -956,7 +980,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
         if constexpr (k < 4 * NVS) {
           // output tile (tb, vs) into LDS: 4 consecutive value columns of token 16 tb + lr
           constexpr int tb = k / NVS, vs = k % NVS;
-          const f32x4 x = Ot[tb][vs];
+          const f32x4 x = Ot[tb][vs] * a.scale;
           *reinterpret_cast<bf16x4*>(Ocur + ((16 * tb + lr) * CL::LDO + VBW * wave + 16 * vs + 4 * lq) * 2) =
               bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
                      static_cast<bf16>(x[3])};

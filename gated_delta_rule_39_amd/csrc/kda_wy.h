@@ -86,6 +86,23 @@ __device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// acc += A B for 16x16 fp32 blocks on the fp32 MFMA, in the permuted K order: step s
+// sums k = 4 (l / 16) + s, so lane l supplies A[l % 16][4 (l / 16) + s] (one 16-byte
+// read of a row-major A) and b[s] = B[4 (l / 16) + s][l % 16] -- exactly the values a
+// 16x16 accumulator holds in lane l.  A product of products then needs no LDS round
+// trip.
+__device__ __forceinline__ f32x4 mm16p(f32x4 acc, const float* A, int lda, f32x4 b, int lane) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(A + (lane & 15) * lda + 4 * (lane >> 4));
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+  return acc;
+}
+// The b operand of mm16p from a row-major fp32 LDS block.
+__device__ __forceinline__ f32x4 acc_layout(const float* B, int ldb, int lane) {
+  const float* p = B + 4 * (lane >> 4) * ldb + (lane & 15);
+  return f32x4{p[0], p[ldb], p[2 * ldb], p[3 * ldb]};
+}
+
 // ---- ring slot ---------------------------------------------------------------------
 // One chunk's published operands.  Every fragment block is the 16 bytes each of 64
 // lanes holds (1 KiB, lane-major), so a block is copied with one 16-byte-per-lane
@@ -180,7 +197,8 @@ struct WyProducer {
   using M = Mfma<bf16>;
   static constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDF = L::LDF;
   static constexpr int CG = DK / 4, RG = kThreads / CG, RPG = kChunk / RG;
-  static constexpr int CGV = DV / 4, RGV = kThreads / CGV, RPGV = kChunk / RGV;
+  // v rows are only copied to LDS: eight channels per thread (16-byte loads)
+  static constexpr int CGV = DV / 8, RGV = kThreads / CGV, RPGV = kChunk / RGV;
   static constexpr int KS = DK / 32;
 
   bf16 *sKg, *sQg, *sKi, *sKD, *sV, *sTm;
@@ -192,7 +210,8 @@ struct WyProducer {
   int tid, lane, wave, rg, j0, rgv, jv0;
   float scale;
   f32x4 gr[RPG];
-  bf16x4 kr[RPG], qr[RPG], vr[RPGV];
+  bf16x4 kr[RPG], qr[RPG];
+  bf16x8 kp[RPG / 2], qp[RPG / 2], vr[RPGV];   // k, q as loaded (pairs of rows), v rows
   float br;
   int32_t flags;   // prologue flags (kNormK, kBetaLogit, kGateLogit)
   // slot stores: plain when the unit's workgroups share one L2, else device-scope
@@ -242,7 +261,7 @@ struct WyProducer {
     rg = tid_ / CG;
     j0 = 4 * (tid_ % CG);
     rgv = tid_ / CGV;
-    jv0 = 4 * (tid_ % CGV);
+    jv0 = 8 * (tid_ % CGV);
     br = 0.f;
     local = false;
     // the strictly upper part of X diag(beta) is never written
@@ -258,7 +277,12 @@ struct WyProducer {
   // 64-bit flat addresses; the plan keeps 64 rows within 2 GiB).  Measured: 1 % faster
   // in the forward kernel, 3 % slower in the sweep that also writes states and tiles,
   // which keeps flat loads.
-  static constexpr int kLoads = 3 * RPG + RPGV + 1;
+  // The list, in order: g rows [0, kSK), k [kSK, kSQ), q [kSQ, kSV), v [kSV, kSB), beta.
+  // k and q take 16-byte loads: the two lanes of a pair (l, l ^ 1) share a row group and
+  // the eight channels j0 & ~7 .. +7; lane l loads rows 2m + (l & 1) of them, and
+  // unpack_pairs() swaps the halves within the pair.
+  static constexpr int kSK = RPG, kSQ = RPG + RPG / 2, kSV = 2 * RPG, kSB = 2 * RPG + RPGV;
+  static constexpr int kLoads = kSB + 1;
   template <int DECAY, int I0, int I1, bool BUF = true>
   __device__ __forceinline__ void load_slice(int64_t c0, int n) {
     const int64_t rk = (c0 * H + h) * DK;
@@ -269,43 +293,69 @@ struct WyProducer {
                                  rsv = rsrc(v + (c0 * H + h) * DV);
 #pragma unroll
     for (int e = I0; e < I1; ++e) {
-      if (e < 3 * RPG) {
-        const int i = e % RPG;
+      if (e < kSK) {
+        const int i = e;
         const uint32_t off = static_cast<uint32_t>(min(rg * RPG + i, n - 1)) * rowK + j0;
-        if (e < RPG) {
-          // g per key channel; with one g per (row, head), lane l loads row l's and
-          // factors() hands the rows to the threads that use them; no g: zeros
-          if constexpr (DECAY == 0) {
-            if constexpr (BUF)
-              gr[i] = __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(g + rk), off * 4, 0, kNonTemporal));
-            else
-              gr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + rk + off));
-          } else if constexpr (DECAY == 1) {
-            if (i == 0) gr[0][0] = g[(c0 + min(lane, n - 1)) * H + h];
-          } else {
-            gr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
+        // g per key channel; with one g per (row, head), lane l loads row l's and
+        // factors() hands the rows to the threads that use them; no g: zeros
+        if constexpr (DECAY == 0) {
+          if constexpr (BUF)
+            gr[i] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(g + rk), off * 4, 0, kNonTemporal));
+          else
+            gr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + rk + off));
+        } else if constexpr (DECAY == 1) {
+          if (i == 0) gr[0][0] = g[(c0 + min(lane, n - 1)) * H + h];
+        } else {
+          gr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        else if (e < 2 * RPG)
-          kr[i] = BUF ? __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
-                                                       rsk, off * 2, 0, kNonTemporal))
-                      : __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(k + rk + off));
+      } else if (e < kSV) {
+        const bool isk = e < kSQ;
+        const int m = isk ? e - kSK : e - kSQ;
+        const uint32_t off =
+            static_cast<uint32_t>(min(rg * RPG + 2 * m + (lane & 1), n - 1)) * rowK + (j0 & ~7);
+        bf16x8 x;
+        if constexpr (BUF)
+          x = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                             isk ? rsk : rsq, off * 2, 0, kNonTemporal));
         else
-          qr[i] = BUF ? __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
-                                                       rsq, off * 2, 0, kNonTemporal))
-                      : __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(q + rk + off));
-      } else if (e < 3 * RPG + RPGV) {
-        const int i = e - 3 * RPG;
+          x = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>((isk ? k : q) + rk + off));
+        if (isk)
+          kp[m] = x;
+        else
+          qp[m] = x;
+      } else if (e < kSB) {
+        const int i = e - kSV;
         const uint32_t ov = static_cast<uint32_t>(min(rgv * RPGV + i, n - 1)) * rowV + jv0;
-        vr[i] = BUF ? __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+        vr[i] = BUF ? __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                                      rsv, ov * 2, 0, kNonTemporal))
                     : __builtin_nontemporal_load(
-                          reinterpret_cast<const bf16x4*>(v + (c0 * H + h) * DV + ov));
+                          reinterpret_cast<const bf16x8*>(v + (c0 * H + h) * DV + ov));
       } else {
         br = __builtin_nontemporal_load(beta + (c0 + min(lane, n - 1)) * H + h);
       }
     }
+  }
+  // k and q rows in the per-thread layout (row rg RPG + i, channels j0 .. j0 + 3) from
+  // the pair loads: a lane keeps its own half of the rows it loaded and takes its half of
+  // its partner's rows with one DPP swap (quad_perm [1, 0, 3, 2]).
+  __device__ __forceinline__ void unpack_pairs() {
+    const bool odd = (lane & 1) != 0;
+    auto swap = [](uint32_t x) {
+      return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0xb1, 0xf, 0xf, false));
+    };
+    auto unpack = [&](const bf16x8(&p)[RPG / 2], bf16x4(&r)[RPG]) {
+#pragma unroll
+      for (int m = 0; m < RPG / 2; ++m) {
+        const u32x4 x = __builtin_bit_cast(u32x4, p[m]);
+        // the partner's channels of the row this lane loaded
+        const uint32_t r0 = swap(odd ? x[0] : x[2]), r1 = swap(odd ? x[1] : x[3]);
+        r[2 * m] = __builtin_bit_cast(bf16x4, u32x2{odd ? r0 : x[0], odd ? r1 : x[1]});
+        r[2 * m + 1] = __builtin_bit_cast(bf16x4, u32x2{odd ? x[2] : r0, odd ? x[3] : r1});
+      }
+    };
+    unpack(kp, kr);
+    unpack(qp, qr);
   }
   template <int DECAY, bool BUF = true>
   __device__ __forceinline__ void load(int64_t c0, int n) {
@@ -333,8 +383,12 @@ struct WyProducer {
     }
   }
 
-  template <int DECAY>
+  // QSCALE: Qg includes the query scale (the backward's chain tiles use it); without it
+  // the consumer applies the scale to each output tile instead (one multiply per output
+  // element rather than one per Qg element).
+  template <int DECAY, bool QSCALE = true>
   __device__ __forceinline__ void factors(int n) {
+    unpack_pairs();
     if (flags & kNormK) normalise_keys();
     if constexpr (DECAY == 1) {
       const float x = gr[0][0];
@@ -349,26 +403,39 @@ struct WyProducer {
 #pragma unroll
       for (int i = 0; i < RPG; ++i) gr[i] = log_sigmoid4(gr[i]);
     }
-    // alpha = e^g in place (1 for rows past the end); per-thread product of its rows
+    // Rows past the end of a partial chunk (they re-read the last row): k, q, v zero and
+    // g zero (alpha = 1).  Only a sequence's last chunk takes this branch, so full
+    // chunks run without per-element masks.
+    if (n < kChunk) {
+      const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+      const bf16x4 zb = bf16x4{static_cast<bf16>(0.f), static_cast<bf16>(0.f),
+                               static_cast<bf16>(0.f), static_cast<bf16>(0.f)};
+#pragma unroll
+      for (int i = 0; i < RPG; ++i)
+        if (rg * RPG + i >= n) {
+          gr[i] = z;
+          kr[i] = zb;
+          qr[i] = zb;
+        }
+#pragma unroll
+      for (int i = 0; i < RPGV; ++i)
+        if (rgv * RPGV + i >= n) vr[i] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+    // alpha = e^g in place; per-thread product of its rows
     f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const f32x4 gg = gr[i];
-      gr[i] = rg * RPG + i < n ? f32x4{exp_hw(gg[0]), exp_hw(gg[1]), exp_hw(gg[2]), exp_hw(gg[3])}
-                               : f32x4{1.f, 1.f, 1.f, 1.f};
+      gr[i] = f32x4{exp_hw(gg[0]), exp_hw(gg[1]), exp_hw(gg[2]), exp_hw(gg[3])};
       tot *= gr[i];
     }
     store4(sScr + rg * DK + j0, tot);
     if (tid < kChunk)
       sBeta[tid] = tid < n ? ((flags & kBetaLogit) ? sigmoid_hw(br) : br) : 0.f;
-    // V rows meanwhile (rows past the end are zero)
+    // V rows meanwhile
 #pragma unroll
-    for (int i = 0; i < RPGV; ++i) {
-      const bool ok = rgv * RPGV + i < n;
-      *reinterpret_cast<bf16x4*>(sV + (rgv * RPGV + i) * LDV + jv0) =
-          ok ? vr[i] : bf16x4{static_cast<bf16>(0.f), static_cast<bf16>(0.f),
-                              static_cast<bf16>(0.f), static_cast<bf16>(0.f)};
-    }
+    for (int i = 0; i < RPGV; ++i)
+      *reinterpret_cast<u32x4*>(sV + (rgv * RPGV + i) * LDV + jv0) = __builtin_bit_cast(u32x4, vr[i]);
     lds_barrier();
     f32x4 tots[RG];
 #pragma unroll
@@ -381,15 +448,16 @@ struct WyProducer {
     }
     const f32x4 egn = cp * tot * cs;   // e^{G_n}
     // forward: e^{G_r} = cp * alpha_first .. alpha_r  ->  Kg, Qg
+    f32x4 kf[RPG];
     {
       f32x4 run = cp;
 #pragma unroll
       for (int i = 0; i < RPG; ++i) {
-        const bool ok = rg * RPG + i < n;
         run *= gr[i];
-        const f32x4 k4 = ok ? widen(kr[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 q4 = ok ? widen(qr[i]) * scale : f32x4{0.f, 0.f, 0.f, 0.f};
-        store4(sKg + (rg * RPG + i) * LDK + j0, k4 * run);
+        kf[i] = widen(kr[i]);
+        f32x4 q4 = widen(qr[i]);
+        if constexpr (QSCALE) q4 *= scale;
+        store4(sKg + (rg * RPG + i) * LDK + j0, kf[i] * run);
         store4(sQg + (rg * RPG + i) * LDK + j0, q4 * run);
       }
     }
@@ -401,15 +469,36 @@ struct WyProducer {
       f32x4 sfx = cs;
 #pragma unroll
       for (int i = RPG - 1; i >= 0; --i) {
-        const bool ok = rg * RPG + i < n;
-        const f32x4 k4 = ok ? widen(kr[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 kd = k4 * sfx;
+        const f32x4 kd = kf[i] * sfx;
         store4(sKD + (rg * RPG + i) * LDK + j0, kd);
         store4(sKi + (rg * RPG + i) * LDK + j0, kd * rn);
         sfx *= gr[i];
       }
     }
     if (rg == 0) store4(sEgn + j0, egn);
+  }
+
+  // M^T tiles (a, B0) for a <= B0 and (a, B1) for a <= B1 (Ki rows a, Qg rows b): every
+  // fragment of the four K steps is read before the products.
+  template <int B0, int B1>
+  __device__ __forceinline__ void mt_blocks(f32x4 (&acc)[5]) const {
+    bf16x8 q0[KS], q1[KS], ki[KS][B1 + 1];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      q0[t] = frag_rows<M>(sQg, LDK, 16 * B0, 32 * t, lane);
+      q1[t] = frag_rows<M>(sQg, LDK, 16 * B1, 32 * t, lane);
+#pragma unroll
+      for (int a = 0; a <= B1; ++a) ki[t][a] = frag_rows<M>(sKi, LDK, 16 * a, 32 * t, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < 5; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+#pragma unroll
+      for (int a = 0; a <= B0; ++a) acc[a] = mma_bf16(ki[t][a], q0[t], acc[a]);
+#pragma unroll
+      for (int a = 0; a <= B1; ++a) acc[B0 + 1 + a] = mma_bf16(ki[t][a], q1[t], acc[B0 + 1 + a]);
+    }
   }
 
   // Waves 0, 1: A = strict-lower(diag(beta) Kg Ki^T) into LDS (fp32).
@@ -434,29 +523,12 @@ struct WyProducer {
       }
       return;
     }
-    // token blocks b of this wave: (0, 3) or (1, 2); tiles (a, b) for a <= b
-    const int b0 = wave == 2 ? 0 : 1, b1 = wave == 2 ? 3 : 2;
+    // token blocks b of this wave: (0, 3) or (1, 2); tiles (a, b) for a <= b:
     // acc[0..b0] = tiles (a, b0), acc[b0+1 .. b0+1+b1] = tiles (a, b1)
-#pragma unroll
-    for (int i = 0; i < 5; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < DK; kk += 32) {
-      const bf16x8 q0 = frag_rows<M>(sQg, LDK, 16 * b0, kk, lane);
-      const bf16x8 q1 = frag_rows<M>(sQg, LDK, 16 * b1, kk, lane);
-      bf16x8 ki[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) ki[a] = frag_rows<M>(sKi, LDK, 16 * a, kk, lane);
-      if (wave == 2) {
-        acc[0] = mma_bf16(ki[0], q0, acc[0]);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) acc[1 + a] = mma_bf16(ki[a], q1, acc[1 + a]);
-      } else {
-#pragma unroll
-        for (int a = 0; a < 2; ++a) acc[a] = mma_bf16(ki[a], q0, acc[a]);
-#pragma unroll
-        for (int a = 0; a < 3; ++a) acc[2 + a] = mma_bf16(ki[a], q1, acc[2 + a]);
-      }
-    }
+    if (wave == 2)
+      mt_blocks<0, 3>(acc);
+    else
+      mt_blocks<1, 2>(acc);
     // causal mask on the diagonal tiles: row (token') 4*lq + i <= column (token) lr
     const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
     auto diag = [&](f32x4 t) {
@@ -547,14 +619,11 @@ struct WyProducer {
   __device__ __forceinline__ void inverse_pairs() {
     const int lr = lane & 15, lq = lane >> 4;
     const int rb = 2 * wave + 1, cb = 2 * wave;
-    float* sY = sScr + wave * 16 * 17;
     const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4 y = mm16(z, sA + 16 * rb * LDF + 16 * cb, LDF, sX + 16 * cb * LDF + 16 * cb, LDF,
-                         lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sY[(4 * lq + i) * 17 + lr] = y[i];
-    wave_lds_sync();
-    const f32x4 x = mm16(z, sX + 16 * rb * LDF + 16 * rb, LDF, sY, 17, lane);
+    // Y = A_10 X_00 lands in accumulator layout, the B operand of X_11 Y as it is
+    const f32x4 y = mm16p(z, sA + 16 * rb * LDF + 16 * cb, LDF,
+                          acc_layout(sX + 16 * cb * LDF + 16 * cb, LDF, lane), lane);
+    const f32x4 x = mm16p(z, sX + 16 * rb * LDF + 16 * rb, LDF, y, lane);
     const float bc = sBeta[16 * cb + lr];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -572,21 +641,20 @@ struct WyProducer {
     float* sY = sScr;
     const int bi = 2 + (wave >> 1), bj = wave & 1;
     {
-      f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        if (kb >= bj) y = mm16(y, sA + (16 * bi) * LDF + 16 * kb, LDF,
-                               sX + (16 * kb) * LDF + 16 * bj, LDF, lane);
+      // both waves of a block row read their operands before either product
+      const f32x4 b1 = acc_layout(sX + 16 * LDF + 16 * bj, LDF, lane);
+      const f32x4 b0 = acc_layout(sX + 16 * bj, LDF, lane);
+      f32x4 y = mm16p(f32x4{0.f, 0.f, 0.f, 0.f}, sA + (16 * bi) * LDF + 16, LDF, b1, lane);
+      if (bj == 0) y = mm16p(y, sA + (16 * bi) * LDF, LDF, b0, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) sY[wave * 16 * 17 + (4 * lq + i) * 17 + lr] = y[i];
     }
     lds_barrier();
     {
-      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 2; kb < 4; ++kb)
-        if (kb <= bi) x = mm16(x, sX + (16 * bi) * LDF + 16 * kb, LDF,
-                               sY + ((kb - 2) * 2 + bj) * 16 * 17, 17, lane);
+      const f32x4 y2 = acc_layout(sY + bj * 16 * 17, 17, lane);
+      const f32x4 y3 = acc_layout(sY + (2 + bj) * 16 * 17, 17, lane);
+      f32x4 x = mm16p(f32x4{0.f, 0.f, 0.f, 0.f}, sX + (16 * bi) * LDF + 32, LDF, y2, lane);
+      if (bi == 3) x = mm16p(x, sX + (16 * bi) * LDF + 48, LDF, y3, lane);
       const float bc = sBeta[16 * bj + lr];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -627,6 +695,52 @@ struct WyProducer {
     if (e >= 0 && e < DK) st4(rr, slot + SL::oEgn + 4 * e, sEgn[e]);
   }
 
+  // publish_wu for d_k = d_v = 128: wave w forms the W fragments (tb, j = w) and the U
+  // tiles of value-block pair w for the four token blocks tb.  Every LDS operand is read
+  // first -- the products of one token block share its X diag(beta) fragments, those of
+  // one K step share the Kg^T and V^T fragments -- then the 24 products run back to back
+  // and the eight fragments leave as 16-byte stores.
+  __device__ __forceinline__ void publish_wu_128(__amdgpu_buffer_rsrc_t rr, uint32_t slot) {
+    static_assert(KS == 4 && SL::NVB / 2 == 4, "one W K step and one U pair per wave");
+    bf16x8 xb[4][2], kt[2][2], vt[2][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int t = 0; t < (tb < 2 ? 1 : 2); ++t) xb[tb][t] = frag_rows<M>(sTm, LDC, 16 * tb, 32 * t, lane);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        kt[t][hb] = frag_tr(sKg, LDK, 32 * t, 32 * wave + 16 * hb, lane);
+        vt[t][hb] = frag_tr(sV, LDV, 32 * t, 16 * (2 * wave + hb), lane);
+      }
+    f32x4 w[4][2], u[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) w[tb][hb] = u[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // W first, its stores while the U products run
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int t = 0; t < (tb < 2 ? 1 : 2); ++t)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) w[tb][hb] = mma_bf16(kt[t][hb], xb[tb][t], w[tb][hb]);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int t = 0; t < (tb < 2 ? 1 : 2); ++t)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) u[tb][hb] = mma_bf16(xb[tb][t], vt[t][hb], u[tb][hb]);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+      st16(rr, slot + SL::oW + (tb * KS + wave) * SL::kFrag + 16 * lane, pack_frag(-w[tb][0], -w[tb][1]));
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+      st16(rr, slot + SL::oU + (tb * (SL::NVB / 2) + wave) * SL::kFrag + 16 * lane,
+           pack_frag(u[tb][0], u[tb][1]));
+  }
+
   // All waves: W^T = -(Kg^T (X diag(beta))^T) as W fragments and U = X diag(beta) V as
   // fp32 tiles, straight to the slot.  Row block tb of X diag(beta) is zero beyond
   // column 16 tb + 15, so tb < 2 needs one K step.
@@ -634,6 +748,10 @@ struct WyProducer {
   template <bool TILES = false>
   __device__ __forceinline__ void publish_wu(__amdgpu_buffer_rsrc_t rr, uint32_t slot,
                                              bf16* wt = nullptr) {
+    if constexpr (DK == 128 && DV == 128 && !TILES) {
+      publish_wu_128(rr, slot);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
       const int f = wave + 4 * i, tb = f / KS, j = f % KS;
