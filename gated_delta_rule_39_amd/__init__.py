@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.kda_prefill_coop_plan.restype = ctypes.c_int
     L.kda_prefill_coop_plan.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.POINTER(i32),
                                         ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.kda_prefill_coop_lanes.restype = ctypes.c_int
+    L.kda_prefill_coop_lanes.argtypes = [ctypes.c_int, i32, i32, i32, i32]
     L.kda_prefill_ex.restype = ctypes.c_int
     L.kda_prefill_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp,
                                  vp, i32, i32, i64, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
@@ -120,6 +122,11 @@ def prefill_coop_plan(dtype: torch.dtype, N: int, H: int, d_k: int, d_v: int):
     _check(lib().kda_prefill_coop_plan(_DTYPE_CODE[dtype], N, H, d_k, d_v, ctypes.byref(a),
                                        ctypes.byref(b), ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+def prefill_coop_lanes(dtype: torch.dtype, N: int, H: int, d_k: int, d_v: int) -> int:
+    """Lanes of the producer/consumer prefill (0: not applicable)."""
+    return int(lib().kda_prefill_coop_lanes(_DTYPE_CODE[dtype], N, H, d_k, d_v))
 
 
 def workspace_bytes(dtype: torch.dtype, N: int, T_total: int, H: int, d_k: int, d_v: int) -> int:

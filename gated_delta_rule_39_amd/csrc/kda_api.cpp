@@ -64,22 +64,49 @@ int env_int(const char* name, int dflt) {
 // ring slots.  Needs bf16 inputs and W >= 2.  KDA_PREFILL_COOP=0 disables it;
 // KDA_COOP_NC / KDA_COOP_NP / KDA_COOP_R override the split and the ring depth
 // (tuning only).
+// Lanes: with d_k = d_v = 128, when the units leave fewer than four workgroups each
+// (measured: a unit per set of four still beats two units one after another on seven),
+// the units are spread over lanes of seven workgroups (two consumers, five producers;
+// as many lanes as the device fits, rounded down to whole XCD groups) by a plan made
+// on the device from cu_seqlens (coop_prep_kernel), longest sequences first, and each
+// lane works through its units one after another.  This keeps every unit on the
+// producer/consumer kernel however many there are, and balances sequences of unequal
+// length.  Up to 256 sequences and 8192 units; KDA_COOP_LANES=0 disables it (tuning
+// only).
+constexpr int kLaneW = 7, kLaneMinW = 4;
+constexpr int kPlanMaxSeqs = 256, kPlanMaxUnits = 8192, kPlanMaxLanes = 64;
 struct CoopPlan {
-  int NC = 0, NP = 0, R = 0;
+  int NC = 0, NP = 0, R = 0, lanes = 0;
+  bool plan = false;   // lanes < units: a device plan spreads the units over the lanes
   bool ok() const { return NC > 0; }
 };
-CoopPlan coop_plan(int dtype, int64_t units, int32_t H, int32_t d_k, int32_t d_v, int cus) {
+CoopPlan coop_plan(int dtype, int64_t units, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                   int cus) {
   CoopPlan p;
   if (dtype != KDA_BF16 || units <= 0 || env_int("KDA_PREFILL_COOP", 1) == 0) return p;
   // the producers read a chunk's inputs through buffer resources with 31-bit byte
   // offsets: 64 rows of g (H d_k fp32) and of v (H d_v bf16) must fit
   const int64_t row = static_cast<int64_t>(H) * (d_k * 4 > d_v * 2 ? d_k * 4 : d_v * 2);
   if (64 * row > 0x7fffffff) return p;
+  const int enp = env_int("KDA_COOP_NP", 0);
+  const int lw = enp > 0 ? 2 + enp : kLaneW;
+  int L = cus / lw < kPlanMaxLanes ? cus / lw : kPlanMaxLanes;
+  L -= L % 8;
+  if (d_k == 128 && d_v == 128 && units > cus / kLaneMinW && units > L && L >= 8 &&
+      N <= kPlanMaxSeqs && units <= kPlanMaxUnits && env_int("KDA_COOP_LANES", 1) != 0) {
+    p.NC = 2;
+    p.NP = lw - 2;
+    p.R = env_int("KDA_COOP_R", p.NP + 6);
+    if (p.R < 3) p.R = 3;
+    p.lanes = L;
+    p.plan = true;
+    return p;
+  }
   int W = static_cast<int>(cus / units);
   if (W > 16) W = 16;
   if (W < 2) return p;
   int nc = (d_v == 128 && W >= 6) ? 2 : 1;
-  const int enc = env_int("KDA_COOP_NC", 0), enp = env_int("KDA_COOP_NP", 0);
+  const int enc = env_int("KDA_COOP_NC", 0);
   if (enc > 0 && d_v % (4 * enc) == 0 && (d_v / (4 * enc) == 16 || d_v / (4 * enc) == 32)) nc = enc;
   int np = W - nc < 5 ? W - nc : 5;
   if (enp > 0) np = enp;
@@ -90,7 +117,25 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t H, int32_t d_k, int32_t d_v
   // has waited for chunk c + 2: three slots at least, or that wait never ends
   p.R = env_int("KDA_COOP_R", np + 6);
   if (p.R < 3) p.R = 3;
+  p.lanes = static_cast<int>(units);
   return p;
+}
+
+size_t coop_ws_bytes(const CoopPlan& p, int32_t d_k, int32_t d_v, int64_t units) {
+  return kda::prefill_coop_workspace_bytes(d_k, d_v, p.lanes, static_cast<int>(units), p.R, p.plan);
+}
+
+// The producer/consumer fields of the kernel arguments; the lane plan lives right after
+// the workspace header.
+void set_coop(kda::PrefillArgs& a, const CoopPlan& p, void* ws) {
+  a.workspace = static_cast<unsigned char*>(ws);
+  a.NC = p.NC;
+  a.NP = p.NP;
+  a.R = p.R;
+  a.lanes = p.lanes;
+  a.xcd_remap = (p.lanes % 8 == 0) ? 1 : 0;
+  a.lane_off = p.plan ? reinterpret_cast<const int32_t*>(a.workspace + 256) : nullptr;
+  a.lane_units = p.plan ? a.lane_off + p.lanes + 1 : nullptr;
 }
 
 }  // namespace
@@ -122,9 +167,9 @@ size_t kda_prefill_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_
   if (N <= 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
   const int64_t units = static_cast<int64_t>(N) * H;
   if (units > (1 << 24)) return 0;
-  const CoopPlan p = coop_plan(dtype, units, H, d_k, d_v, cu_count());
+  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cu_count());
   if (!p.ok()) return 0;
-  return kda::prefill_coop_workspace_bytes(d_k, d_v, static_cast<int>(units), p.R);
+  return coop_ws_bytes(p, d_k, d_v, units);
 }
 
 int kda_prefill_coop_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
@@ -134,11 +179,20 @@ int kda_prefill_coop_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t 
   if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
   const int64_t units = static_cast<int64_t>(N) * H;
   if (units > (1 << 24)) return KDA_ERR_BAD_SHAPE;
-  const CoopPlan p = coop_plan(dtype, units, H, d_k, d_v, cu_count());
+  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cu_count());
   if (consumers) *consumers = p.NC;
   if (producers) *producers = p.NP;
   if (ring_slots) *ring_slots = p.R;
   return KDA_OK;
+}
+
+int kda_prefill_coop_lanes(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v) {
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+  if (N <= 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
+  const int64_t units = static_cast<int64_t>(N) * H;
+  if (units > (1 << 24)) return 0;
+  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cu_count());
+  return p.ok() ? p.lanes : 0;
 }
 
 int kda_prefill_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
@@ -217,15 +271,13 @@ int kda_prefill_ex(int dtype, int decay, int flags, const void* q, const void* k
   a.decay = decay;
   a.flags = flags;
   const int cus = cu_count();
-  const CoopPlan p = coop_plan(dtype, units, H, d_k, d_v, cus);
-  if (p.ok() && workspace != nullptr &&
-      workspace_bytes >= kda::prefill_coop_workspace_bytes(d_k, d_v, static_cast<int>(units), p.R)) {
-    a.workspace = static_cast<unsigned char*>(workspace);
-    a.NC = p.NC;
-    a.NP = p.NP;
-    a.R = p.R;
+  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cus);
+  if (p.ok() && workspace != nullptr && workspace_bytes >= coop_ws_bytes(p, d_k, d_v, units)) {
+    set_coop(a, p, workspace);
     if (kda::launch_prefill_coop(d_k, a, stream) == hipSuccess) return KDA_OK;
     (void)hipGetLastError();   // not launchable as one resident grid: use the fused kernel
+    a.xcd_remap = (units % 8 == 0) ? 1 : 0;
+    a.lane_off = a.lane_units = nullptr;
   }
   const int bv = choose_bv(dtype, static_cast<int32_t>(units), d_k, d_v, cus);
   a.NV = d_v / bv;
@@ -287,11 +339,10 @@ BwdPlan bwd_plan(int32_t N, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v
   const int64_t units = static_cast<int64_t>(N) * H;
   b.states = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H * d_v * d_k * 2);
   b.tiles = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H) * kda::chain_tile_bytes(d_k);
-  const CoopPlan p = coop_plan(KDA_BF16, units, H, d_k, d_v, cu_count());
+  const CoopPlan p = coop_plan(KDA_BF16, units, N, H, d_k, d_v, cu_count());
   if (p.ok() && d_k == 128 && d_v == 128 && p.NC == 2 && units <= (1 << 24)) {
     b.coop = p;
-    b.ring = (kda::prefill_coop_workspace_bytes(d_k, d_v, static_cast<int>(units), p.R) + 255) &
-             ~size_t(255);
+    b.ring = (coop_ws_bytes(p, d_k, d_v, units) + 255) & ~size_t(255);
   }
   return b;
 }
@@ -359,12 +410,13 @@ int kda_backward(int dtype, int decay, int flags, const void* q, const void* k, 
     a.chunk_tiles = dstates + plan.states;
     bool done = false;
     if (plan.ring > 0) {
-      a.workspace = static_cast<unsigned char*>(workspace);
-      a.NC = plan.coop.NC;
-      a.NP = plan.coop.NP;
-      a.R = plan.coop.R;
+      set_coop(a, plan.coop, workspace);
       done = kda::launch_prefill_coop_states(a, stream) == hipSuccess;
-      if (!done) (void)hipGetLastError();   // not launchable as one resident grid
+      if (!done) {
+        (void)hipGetLastError();   // not launchable as one resident grid
+        a.xcd_remap = (units % 8 == 0) ? 1 : 0;
+        a.lane_off = a.lane_units = nullptr;
+      }
     }
     tiles_done = done;
     if (!done) {

@@ -29,6 +29,11 @@ struct PrefillArgs {
   int32_t H, DV, units;
   int32_t NV;                 // fused kernel: value tiles per unit
   int32_t NC, NP, R;          // producer/consumer kernel: consumers, producers, ring slots
+  int32_t lanes;              // producer/consumer kernel: workgroup sets (lanes)
+  // lane l processes units lane_units[lane_off[l] .. lane_off[l + 1]) one after another
+  // (planned on the device, in the workspace); nullptr: lane l is unit l
+  const int32_t* lane_off;
+  const int32_t* lane_units;
   int32_t xcd_remap;          // units % 8 == 0: keep a unit's workgroups on one XCD
   int32_t decay;              // 0: g per key channel, 1: one g per (token, head), 2: none
   int32_t flags;              // prologue flags (kda_device.h: kNormK, kBetaLogit, kGateLogit)
@@ -54,7 +59,9 @@ int prefill_max_bv(int dtype, int dk);
 // Producer/consumer prefill (bf16): a.workspace holds prefill_coop_workspace_bytes bytes;
 // a.DV / (4 * a.NC) in {16, 32}.
 hipError_t launch_prefill_coop(int dk, const PrefillArgs& a, hipStream_t stream);
-size_t prefill_coop_workspace_bytes(int dk, int dv, int units, int R);
+// lanes sets of workgroups; plan: the units are spread over the lanes by a device plan
+// (lanes < units), else lane l is unit l (lanes == units).
+size_t prefill_coop_workspace_bytes(int dk, int dv, int lanes, int units, int R, bool plan);
 // The argument checks of kda_prefill_ex (kda_api.cpp), no HIP call: a kda.h status,
 // and *launch = false when there is nothing to do.
 int prefill_args_status(int dtype, int decay, int flags, const void* q, const void* k,

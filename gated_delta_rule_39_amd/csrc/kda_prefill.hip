@@ -221,18 +221,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 // since the caller last cleared it -- the launch's reset kernel clears word 0 and the
 // flags, never word 1), then per-unit flags ready[R], done[R], arrive, pad (int32),
 // then the ring slots.
+// With a lane plan, the header is followed by it: lane_off[lanes + 1], lane_units[units]
+// (int32), written by coop_prep_kernel.
 constexpr size_t kWsHeader = 256;
 __host__ __device__ inline int coop_flag_words(int R) { return 2 * R + 2; }
-__host__ __device__ inline size_t coop_flags_bytes(int units, int R) {
-  return (size_t(units) * coop_flag_words(R) * 4 + 255) & ~size_t(255);
+__host__ __device__ inline size_t coop_flags_bytes(int lanes, int R) {
+  return (size_t(lanes) * coop_flag_words(R) * 4 + 255) & ~size_t(255);
+}
+__host__ __device__ inline size_t coop_plan_bytes(int lanes, int units, bool plan) {
+  return plan ? (size_t(lanes + 1 + units) * 4 + 255) & ~size_t(255) : 0;
+}
+__device__ __forceinline__ size_t coop_plan_bytes(const PrefillArgs& a) {
+  return coop_plan_bytes(a.lanes, a.units, a.lane_units != nullptr);
 }
 
 // s_getreg operand for the XCC_ID hardware register (id 20, bits 0..15): the XCD the
 // wave runs on.
 constexpr int kHwRegXccId = 20 | (0 << 6) | (15 << 11);
 template <int DK, int DV>
-__host__ __device__ inline size_t coop_workspace_bytes(int units, int R) {
-  return kWsHeader + coop_flags_bytes(units, R) + size_t(units) * R * WySlot<DK, DV>::kBytes;
+__host__ __device__ inline size_t coop_workspace_bytes(int lanes, int units, int R, bool plan) {
+  return kWsHeader + coop_plan_bytes(lanes, units, plan) + coop_flags_bytes(lanes, R) +
+         size_t(lanes) * R * WySlot<DK, DV>::kBytes;
 }
 
 constexpr uint32_t kSpinLimit = 1u << 22;   // ~ a second of s_sleep polling
@@ -324,6 +333,37 @@ struct WySplitLayout {
   static constexpr size_t kBytes = oFlag + 16;
 };
 
+// ---- lanes ---------------------------------------------------------------------------
+// A lane is one set of NC consumer and NP producer workgroups.  It processes a list of
+// units one after another: its chunk stream is the concatenation of their chunks, and the
+// ring slots, flags and producer stripes run over that stream (global chunk index g).
+// Without a lane plan (a.lane_units == nullptr) lane l is unit l.
+struct LaneUnit {
+  int unit, n_seq, h;
+  int64_t bos, eos;
+  int nch, g0;   // chunks of the unit; index of its first chunk in the lane's stream
+};
+__device__ __forceinline__ int lane_count(const PrefillArgs& a, int lid) {
+  return a.lane_units ? a.lane_off[lid + 1] - a.lane_off[lid] : 1;
+}
+__device__ __forceinline__ void lane_unit(const PrefillArgs& a, int lid, int i, int g0,
+                                          LaneUnit& u) {
+  u.unit = a.lane_units ? a.lane_units[a.lane_off[lid] + i] : lid;
+  unit_bounds(a, u.unit, u.n_seq, u.h, u.bos, u.eos);
+  u.nch = static_cast<int>((u.eos - u.bos + kChunk - 1) / kChunk);
+  u.g0 = g0;
+}
+// Chunks in the lane's stream.
+__device__ __forceinline__ int lane_total(const PrefillArgs& a, int lid) {
+  const int nu = lane_count(a, lid);
+  int t = 0;
+  LaneUnit u;
+  for (int i = 0; i < nu; ++i) {
+    lane_unit(a, lid, i, t, u);
+    t += u.nch;
+  }
+  return t;
+}
 // Consumer with the work split by token and key blocks (d_k = 128, 64 value columns):
 // wave w forms the rows of token block w of E = U - W S^T and O = Qg S^T + M E, and
 // owns key blocks 2w, 2w+1 of S^T (keys 32w .. 32w + 31) in fp32 accumulators.  Per
@@ -333,15 +373,16 @@ struct WySplitLayout {
 // published operands it uses (its token block of W, Qg, M, U; its key blocks of KD^T,
 // e^{G_n}) straight from the ring slot into registers, one chunk ahead.  The slot of
 // chunk c is released after chunk c's end-of-chunk barrier, when every wave has used
-// those registers.
+// those registers.  Over a lane's stream of units, the state of a unit is loaded
+// before its first chunk and stored after its last, where the next unit's initial
+// state takes the place of the updated one as the next chunk's S^T operand.
 // STATES: also write the state at every chunk start (bf16, as prefill_kernel's STATES),
 // and write o only when a.o is set.
 template <int DK, int DV, bool STATES = false>
 __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned char* smem,
                                                  __amdgpu_buffer_rsrc_t rr, int* ready,
-                                                 int* done, int* abort_word, int role,
-                                                 int n_seq, int h, int64_t bos, int64_t eos,
-                                                 int nch, int tid, int wave, int lane) {
+                                                 int* done, int* abort_word, int role, int lid,
+                                                 int total, int tid, int wave, int lane) {
   using SL = WySlot<DK, DV>;
   using CL = WySplitLayout;
   constexpr int KS = DK / 32, NVT = CL::NVT;
@@ -387,11 +428,11 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   auto eb_at = [&](int t, int vt) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(sEb + (t * NVT + vt) * 1024);
   };
-  // output rows of this wave (token block w) from the LDS tile to o; rows >= `rows` of
-  // the window starting at token row cs are dropped
-  auto store_rows = [&](int64_t cs, int rows) {
+  // output rows of this wave (token block w) from the LDS tile to o for head hh; rows
+  // >= `rows` of the window starting at token row cs are dropped
+  auto store_rows = [&](int64_t cs, int rows, int hh) {
     const __amdgpu_buffer_rsrc_t win = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<bf16*>(a.o) + (cs * a.H + h) * DV + v0, 0,
+        static_cast<bf16*>(a.o) + (cs * a.H + hh) * DV + v0, 0,
         static_cast<int>(uint32_t(rows) * rowO * 2), 0x00020000);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -403,16 +444,48 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 
   // S^T rows of this wave: S[b][vt] holds S^T[32 w + 16 b + 4 lq + i][v0 + 16 vt + lr]
   f32x4 S[2][NVT];
-  const int64_t st_base = (static_cast<int64_t>(n_seq) * a.H + h) * DV * DK;
+  auto st_off = [&](const LaneUnit& u, int vt, int b) {
+    return (static_cast<int64_t>(u.n_seq) * a.H + u.h) * DV * DK + int64_t(v0 + 16 * vt + lr) * DK +
+           32 * wave + 16 * b + 4 * lq;
+  };
+  auto load_state = [&](const LaneUnit& u) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt)
-      S[b][vt] = a.initial_state
-                     ? *reinterpret_cast<const f32x4*>(a.initial_state + st_base +
-                                                       int64_t(v0 + 16 * vt + lr) * DK +
-                                                       32 * wave + 16 * b + 4 * lq)
-                     : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int vt = 0; vt < NVT; ++vt)
+        S[b][vt] = a.initial_state ? *reinterpret_cast<const f32x4*>(a.initial_state + st_off(u, vt, b))
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto store_final = [&](const LaneUnit& u) {
+    if (a.final_state) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt)
+          *reinterpret_cast<f32x4*>(a.final_state + st_off(u, vt, b)) = S[b][vt];
+    }
+  };
+  // the lane's units: cu is the unit of the current chunk; units without chunks keep
+  // their initial state.  A plan can leave a lane without units (fewer units with
+  // chunks than lanes): it has nothing to do.
+  const int nu = lane_count(a, lid);
+  if (nu == 0) return;
+  LaneUnit cu;
+  int iu = 0;
+  lane_unit(a, lid, 0, 0, cu);
+  auto skip_empty = [&]() {
+    while (cu.nch == 0) {
+      if (a.final_state) {
+        load_state(cu);
+        store_final(cu);
+      }
+      if (iu + 1 >= nu) return false;
+      const int g0 = cu.g0;
+      lane_unit(a, lid, ++iu, g0, cu);
+    }
+    return true;
+  };
+  if (skip_empty()) load_state(cu);
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt)
     *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = pack_frag(S[0][vt], S[1][vt]);
@@ -444,7 +517,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   };
 
   bool ok = true, nok = true;
-  if (nch > 0) {
+  if (total > 0) {
     if (tid == 0) cFlag[0] = wait_at_least(ready, 1, abort_word) ? 1 : 0;
     lds_barrier();
     ok = cFlag[0] != 0;
@@ -456,152 +529,191 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       load_m(0);
       load_kd(0);
     }
-    if (tid == 0) cFlag[1] = nch > 1 ? (wait_at_least(ready + 1 % a.R, 2, abort_word) ? 1 : 0) : 1;
+    if (tid == 0) cFlag[1] = total > 1 ? (wait_at_least(ready + 1 % a.R, 2, abort_word) ? 1 : 0) : 1;
     lds_barrier();
     nok = cFlag[1] != 0;
   }
 
-  // ring slot indices of chunks c - 1, c, c + 1, c + 2
+  // ring slot indices of chunks g - 1, g, g + 1, g + 2
   int sp = 0, s0 = 0, s1 = 1 % a.R, s2 = 2 % a.R;
   const int t_own = wave >> 1, h_own = wave & 1;
   const bool write_o = !STATES || a.o != nullptr;
   // the producers' Qg leaves the query scale out in the forward kernel (kept for the
   // backward's chain tiles): it is applied to each output tile here
   const float oscale = STATES ? 1.f : a.scale;
-  // output tile of token block w: O^T accumulators, scaled, as bf16 rows in LDS
   f32x4 Ot[NVT];
-  auto put_o1 = [&](int vt) {
-    const f32x4 x = Ot[vt] * oscale;
-    *reinterpret_cast<bf16x4*>(sO + ((16 * wave + lr) * CL::LDO + 16 * vt + 4 * lq) * 2) =
-        bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
-               static_cast<bf16>(x[3])};
-  };
-  [[maybe_unused]] const int64_t slot0 = chunk_slot_base(n_seq, bos);
-  for (int c = 0; ok && c < nch; ++c) {
-    const int64_t c0 = bos + int64_t(c) * kChunk;
-    const bool has_next = c + 1 < nch, has2 = c + 2 < nch;
-    if constexpr (STATES) {
-      bf16* cs = static_cast<bf16*>(a.chunk_states) + ((slot0 + c) * a.H + h) * DV * DK;
+  // the o window of the previous chunk (its rows leave during this chunk)
+  int64_t pc0 = 0;
+  int prows = 0, ph = 0, punit = -1;
+  int g = 0;
+  // Outer loop: the lane's units with chunks; inner loop: the chunks of one unit.  The
+  // unit's bounds are fixed over the inner loop, and everything that moves to the next
+  // unit lives outside it, so the per-chunk path carries no lane bookkeeping.
+  while (ok && g < total) {
+    const int uend = cu.g0 + cu.nch;                             // stream index past the unit
+    const int64_t cbase = cu.bos - int64_t(cu.g0) * kChunk;      // chunk g starts at cbase + 64 g
+    const int64_t ueos = cu.eos;
+    const int uh = cu.h;
+    [[maybe_unused]] const int64_t sbase =                       // chunk g's state slot (STATES)
+        STATES ? chunk_slot_base(cu.n_seq, cu.bos) - cu.g0 : 0;
+    for (; ok && g < uend; ++g) {
+      const int64_t c0 = cbase + int64_t(g) * kChunk;
+      const bool has_next = g + 1 < total, has2 = g + 2 < total;
+      if constexpr (STATES) {
+        bf16* cs = static_cast<bf16*>(a.chunk_states) + ((sbase + g) * a.H + uh) * DV * DK;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) {
-          const f32x4 x = S[b][vt];
-          // non-temporal, as every checkpoint and tile store: read only by later kernels
-          __builtin_nontemporal_store(
-              bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
-                     static_cast<bf16>(x[3])},
-              reinterpret_cast<bf16x4*>(cs + int64_t(v0 + 16 * vt + lr) * DK + 32 * wave + 16 * b +
-                                        4 * lq));
-        }
-    }
-    // every wave has used chunk c - 1's operands: its slot is free
-    if (tid == 0 && c > 0) __hip_atomic_fetch_add(done + sp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int fv = 0;
-    if (tid == 0 && has2)
-      fv = __hip_atomic_load(ready + s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // The next chunk's operands are requested unconditionally (past the last chunk
-    // they are unused bytes of an idle slot).
-    const uint32_t nslot = static_cast<uint32_t>(s1) * SL::kBytes;
+          for (int vt = 0; vt < NVT; ++vt) {
+            const f32x4 x = S[b][vt];
+            // non-temporal, as every checkpoint and tile store: read only by later kernels
+            __builtin_nontemporal_store(
+                bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                       static_cast<bf16>(x[3])},
+                reinterpret_cast<bf16x4*>(cs + int64_t(v0 + 16 * vt + lr) * DK + 32 * wave + 16 * b +
+                                          4 * lq));
+          }
+      }
+      // every wave has used chunk g - 1's operands: its slot is free
+      if (tid == 0 && g > 0) __hip_atomic_fetch_add(done + sp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int fv = 0;
+      if (tid == 0 && has2)
+        fv = __hip_atomic_load(ready + s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // The next chunk's operands are requested unconditionally (past the last chunk
+      // they are unused bytes of an idle slot).
+      const uint32_t nslot = static_cast<uint32_t>(s1) * SL::kBytes;
 
-    f32x4 E[NVT];
+      f32x4 E[NVT];
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      const bf16x8 u = U[vt / 2];
-      E[vt] = vt % 2 ? widen(bf16x4{u[4], u[5], u[6], u[7]}) : widen(bf16x4{u[0], u[1], u[2], u[3]});
-      Ot[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int vt = 0; vt < NVT; ++vt) {
+        const bf16x8 u = U[vt / 2];
+        E[vt] = vt % 2 ? widen(bf16x4{u[4], u[5], u[6], u[7]}) : widen(bf16x4{u[0], u[1], u[2], u[3]});
+        Ot[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-    for (int p = 0; p < NVT / 2; ++p) U[p] = ldf(nslot + offU(p));
-    // E = U - W S^T for token block w; the S^T fragments stay for O.  The wave's own K
-    // step is its state packed as written to LDS at the end of the last chunk.
-    bf16x8 sb[KS][NVT];
+      for (int p = 0; p < NVT / 2; ++p) U[p] = ldf(nslot + offU(p));
+      // E = U - W S^T for token block w; the S^T fragments stay for O.  The wave's own K
+      // step is its state packed as written to LDS at the end of the last chunk.
+      bf16x8 sb[KS][NVT];
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) sb[0][vt] = pack_frag(S[0][vt], S[1][vt]);
+      for (int vt = 0; vt < NVT; ++vt) sb[0][vt] = pack_frag(S[0][vt], S[1][vt]);
 #pragma unroll
-    for (int j = 1; j < KS; ++j)
+      for (int j = 1; j < KS; ++j)
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) sb[j][vt] = sb_at(j, vt);
+        for (int vt = 0; vt < NVT; ++vt) sb[j][vt] = sb_at(j, vt);
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
+      for (int j = 0; j < KS; ++j)
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) E[vt] = mma_bf16(Wf[j], sb[j][vt], E[vt]);
-    load_w(nslot);
-    // this wave's E rows into its half of the E operand fragments
+        for (int vt = 0; vt < NVT; ++vt) E[vt] = mma_bf16(Wf[j], sb[j][vt], E[vt]);
+      load_w(nslot);
+      // this wave's E rows into its half of the E operand fragments
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      const f32x4 e = E[vt];
-      *reinterpret_cast<bf16x4*>(sEb + (t_own * NVT + vt) * 1024 + 8 * h_own) =
-          bf16x4{static_cast<bf16>(e[0]), static_cast<bf16>(e[1]), static_cast<bf16>(e[2]),
-                 static_cast<bf16>(e[3])};
-    }
-    // D S^T for this wave's keys, while the other waves finish E
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) S[b][vt] *= eg[b];
-    lds_barrier();
-    bf16x8 eb[2][NVT];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) eb[t][vt] = eb_at(t, vt);
-    // the previous chunk's output rows (a full chunk), from this wave's LDS rows
-    if (c > 0 && write_o) store_rows(c0 - kChunk, kChunk);
-    // O = Qg S^T + M E (token block w reads E blocks <= w: K step 1 only for w >= 2)
-#pragma unroll
-    for (int j = 0; j < KS; ++j)
-#pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) Ot[vt] = mma_bf16(sb[j][vt], Qf[j], Ot[vt]);
-    load_q(nslot);
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) Ot[vt] = mma_bf16(eb[0][vt], Mf[0], Ot[vt]);
-    if (wave >= 2) {
-#pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) Ot[vt] = mma_bf16(eb[1][vt], Mf[1], Ot[vt]);
-    }
-    load_m(nslot);
-    // S^T += KD^T E for this wave's keys
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int vt = 0; vt < NVT; ++vt) {
+        const f32x4 e = E[vt];
+        *reinterpret_cast<bf16x4*>(sEb + (t_own * NVT + vt) * 1024 + 8 * h_own) =
+            bf16x4{static_cast<bf16>(e[0]), static_cast<bf16>(e[1]), static_cast<bf16>(e[2]),
+                   static_cast<bf16>(e[3])};
+      }
+      // D S^T for this wave's keys, while the other waves finish E
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) S[b][vt] = mma_bf16(KDf[b][t], eb[t][vt], S[b][vt]);
-    load_kd(nslot);
-    // the next chunk's S^T operand (K step w) and this chunk's output rows
+        for (int vt = 0; vt < NVT; ++vt) S[b][vt] *= eg[b];
+      lds_barrier();
+      bf16x8 eb[2][NVT];
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) eb[t][vt] = eb_at(t, vt);
+      // the previous chunk's output rows, from this wave's LDS rows
+      if (g > 0 && write_o) store_rows(pc0, prows, ph);
+      // O = Qg S^T + M E (token block w reads E blocks <= w: K step 1 only for w >= 2)
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) Ot[vt] = mma_bf16(sb[j][vt], Qf[j], Ot[vt]);
+      load_q(nslot);
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) Ot[vt] = mma_bf16(eb[0][vt], Mf[0], Ot[vt]);
+      if (wave >= 2) {
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) Ot[vt] = mma_bf16(eb[1][vt], Mf[1], Ot[vt]);
+      }
+      load_m(nslot);
+      // S^T += KD^T E for this wave's keys
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int vt = 0; vt < NVT; ++vt) S[b][vt] = mma_bf16(KDf[b][t], eb[t][vt], S[b][vt]);
+      load_kd(nslot);
+      // this chunk's o window
+      pc0 = c0;
+      prows = static_cast<int>(min(ueos - c0, static_cast<int64_t>(kChunk)));
+      ph = uh;
+      // the next chunk's S^T operand (K step w) and this chunk's output rows
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = pack_frag(S[0][vt], S[1][vt]);
+        const f32x4 x = Ot[vt] * oscale;
+        *reinterpret_cast<bf16x4*>(sO + ((16 * wave + lr) * CL::LDO + 16 * vt + 4 * lq) * 2) =
+            bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                   static_cast<bf16>(x[3])};
+      }
+
+      if (tid == 0)
+        cFlag[g & 1] = !has2 ? 1
+                             : ((fv >= g + 3 || wait_at_least(ready + s2, g + 3, abort_word)) ? 1 : 0);
+      lds_barrier();
+      ok = has_next ? nok : true;
+      nok = cFlag[g & 1] != 0;
+      sp = s0;
+      s0 = s1;
+      s1 = s2;
+      s2 = s2 + 1 == a.R ? 0 : s2 + 1;
+    }
+    punit = cu.unit;
+    if (g < uend) break;   // a hand-off aborted inside the unit
+    // the unit is complete: its final state; then the next unit with chunks, whose
+    // initial state replaces this wave's S^T operand fragments (the end-of-chunk
+    // barrier above has ordered every read of the old ones)
+    store_final(cu);
+    if (g >= total) break;
+    lane_unit(a, lid, ++iu, uend, cu);
+    skip_empty();
+    load_state(cu);
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt)
       *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = pack_frag(S[0][vt], S[1][vt]);
-      put_o1(vt);
-    }
-
-    if (tid == 0)
-      cFlag[c & 1] = !has2 ? 1
-                           : ((fv >= c + 3 || wait_at_least(ready + s2, c + 3, abort_word)) ? 1 : 0);
     lds_barrier();
-    ok = has_next ? nok : true;
-    nok = cFlag[c & 1] != 0;
-    sp = s0;
-    s0 = s1;
-    s1 = s2;
-    s2 = s2 + 1 == a.R ? 0 : s2 + 1;
   }
 
   // the last chunk's output rows (written before the loop's last barrier)
-  if (ok && nch > 0 && write_o) {
-    const int64_t cl = bos + int64_t(nch - 1) * kChunk;
-    store_rows(cl, static_cast<int>(eos - cl));
+  if (ok && total > 0 && write_o) store_rows(pc0, prows, ph);
+  // units after the last one with chunks: empty, they keep their initial state
+  if (ok && total > 0) {
+    while (iu + 1 < nu) {
+      const int g0 = cu.g0 + cu.nch;
+      lane_unit(a, lid, ++iu, g0, cu);
+      if (a.final_state) {
+        load_state(cu);
+        store_final(cu);
+      }
+    }
   }
-  if (ok && a.final_state) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int vt = 0; vt < NVT; ++vt)
-        *reinterpret_cast<f32x4*>(a.final_state + st_base + int64_t(v0 + 16 * vt + lr) * DK +
-                                  32 * wave + 16 * b + 4 * lq) = S[b][vt];
+  if (!ok) {
+    // the rows of the last completed chunk are valid; when they belong to an earlier
+    // unit than the one in progress they are stored (otherwise that unit is poisoned)
+    if (punit >= 0 && punit != cu.unit && write_o) store_rows(pc0, prows, ph);
+    // the unit in progress and every later one did not complete
+    for (;;) {
+      poison_outputs<DK, DV, STATES>(a, cu.n_seq, cu.h, cu.bos, cu.eos, cu.nch, v0, 16 * NVT, tid);
+      if (iu + 1 >= nu) break;
+      const int g0 = cu.g0 + cu.nch;
+      lane_unit(a, lid, ++iu, g0, cu);
+    }
   }
-  if (!ok) poison_outputs<DK, DV, STATES>(a, n_seq, h, bos, eos, nch, v0, 16 * NVT, tid);
 }
 
 // A producer's chunk tiles for the backward's reverse chain (ChainTiles): KD, Qg^T, -W^T
@@ -657,18 +769,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
   const int lr = lane & 15, lq = lane >> 4;
 
   const int W = a.NC + a.NP;
-  int unit, role, n_seq, h;
-  int64_t bos, eos;
-  unit_role(blockIdx.x, W, a.units, a.xcd_remap, unit, role);
-  unit_bounds(a, unit, n_seq, h, bos, eos);
-  const int nch = static_cast<int>((eos - bos + kChunk - 1) / kChunk);
+  int lid, role;
+  unit_role(blockIdx.x, W, a.lanes, a.xcd_remap, lid, role);
+  const int total = lane_total(a, lid);
 
   int* abort_word = reinterpret_cast<int*>(a.workspace);
-  int* ready = reinterpret_cast<int*>(a.workspace + kWsHeader) + size_t(unit) * coop_flag_words(a.R);
+  int* ready = reinterpret_cast<int*>(a.workspace + kWsHeader + coop_plan_bytes(a)) +
+               size_t(lid) * coop_flag_words(a.R);
   int* done = ready + a.R;
   int* arrive = done + a.R;
-  unsigned char* ring = a.workspace + kWsHeader + coop_flags_bytes(a.units, a.R) +
-                        size_t(unit) * a.R * SL::kBytes;
+  unsigned char* ring = a.workspace + kWsHeader + coop_plan_bytes(a) +
+                        coop_flags_bytes(a.lanes, a.R) + size_t(lid) * a.R * SL::kBytes;
   const __amdgpu_buffer_rsrc_t rr = ring_rsrc(ring, static_cast<uint32_t>(a.R * SL::kBytes));
 
   // Co-location.  When every workgroup of the unit runs on the XCD its id was dealt
@@ -687,7 +798,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
     const int p = role - a.NC;
     PR pr;
     pr.init(smem, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-            static_cast<const bf16*>(a.v), a.g, a.beta, a.H, h, a.scale, tid, wave, a.flags);
+            static_cast<const bf16*>(a.v), a.g, a.beta, a.H, 0, a.scale, tid, wave, a.flags);
     int* pFlag = reinterpret_cast<int*>(smem + PL::oFlag);
     if (tid == 0) {
       int mode = -1;
@@ -706,23 +817,46 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       pFlag[1] = mode;
     }
     lds_barrier();
-    if (pFlag[1] < 0) return;
+    if (pFlag[1] < 0 || total == 0) return;
     pr.local = pFlag[1] == 1;
-    if (p < nch) {
-      const int64_t c0 = bos + int64_t(p) * kChunk;
-      pr.template load<DECAY, !STATES>(c0, static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk))));
-    }
-    for (int c = p; c < nch; c += a.NP) {
-      const int64_t c0 = bos + int64_t(c) * kChunk;
-      const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
-      const int cn = c + a.NP;
-      const bool has_next = cn < nch;
-      const int64_t c1 = bos + int64_t(cn) * kChunk;
-      const int n1 = has_next ? static_cast<int>(min(eos - c1, static_cast<int64_t>(kChunk))) : 0;
+    // Producer p takes chunks p, p + NP, ... of the lane's stream.  During chunk g it
+    // loads the inputs of chunk g + NP, whose unit is followed by one cursor (index in
+    // the lane, stream end, row base, end row, head); that unit is the next iteration's
+    // own, so per chunk only the stream end is compared.
+    if (p >= total) return;
+    int ix = 0;
+    LaneUnit ux;
+    lane_unit(a, lid, 0, 0, ux);
+    int xend = ux.g0 + ux.nch, xh = ux.h;
+    int64_t xbase = ux.bos - int64_t(ux.g0) * kChunk, xeos = ux.eos;
+    [[maybe_unused]] int64_t xslot = STATES ? chunk_slot_base(ux.n_seq, ux.bos) - ux.g0 : 0;
+    auto seek = [&](int gg) {
+      while (__builtin_expect(gg >= xend, 0)) {
+        lane_unit(a, lid, ++ix, xend, ux);
+        xend = ux.g0 + ux.nch;
+        xh = ux.h;
+        xbase = ux.bos - int64_t(ux.g0) * kChunk;
+        xeos = ux.eos;
+        if constexpr (STATES) xslot = chunk_slot_base(ux.n_seq, ux.bos) - ux.g0;
+      }
+    };
+    seek(p);
+    // chunk g: first row, rows, head and (STATES) chunk slot
+    int64_t c0 = xbase + int64_t(p) * kChunk;
+    int n = static_cast<int>(min(xeos - c0, static_cast<int64_t>(kChunk)));
+    [[maybe_unused]] int ch = xh;
+    [[maybe_unused]] int64_t cslot = xslot + p;
+    pr.template load<DECAY, !STATES>(c0, n, xh);
+    // ring slot of chunk g and the releases it needs: g mod R, NC * (g div R)
+    int s = p % a.R, need = a.NC * (p / a.R);
+    for (int g = p; g < total; g += a.NP) {
+      const int gn = g + a.NP;
+      const bool has_next = gn < total;
+      if (has_next) seek(gn);
+      const int64_t c1 = xbase + int64_t(gn) * kChunk;
+      const int n1 = static_cast<int>(min(xeos - c1, static_cast<int64_t>(kChunk)));
       // the slot must have been released by every consumer of its previous chunk; its
       // counter is read before the factors, so the check after them rarely waits
-      const int s = c % a.R;
-      const int need = a.NC * (c / a.R);
       int dv = 0;
       if (tid == 0) dv = __hip_atomic_load(done + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       pr.template factors<DECAY, STATES>(n);
@@ -733,8 +867,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       // STATES: this chunk's tiles for the backward's reverse chain
       [[maybe_unused]] unsigned char* tiles = nullptr;
       if constexpr (STATES)
-        tiles = static_cast<unsigned char*>(a.chunk_tiles) +
-                ((chunk_slot_base(n_seq, bos) + c) * a.H + h) * ChainTiles<DK>::kBytes;
+        tiles = static_cast<unsigned char*>(a.chunk_tiles) + (cslot * a.H + ch) * ChainTiles<DK>::kBytes;
       // the next chunk's inputs are requested in slices between the phases, none of
       // them in the phase that publishes W and U.  Without a next chunk the slices
       // re-read this chunk's rows (unused): the loads stay unconditional, so the code
@@ -742,23 +875,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       constexpr int L = PR::kLoads, RPG = PR::RPG;
       const int64_t cl = has_next ? c1 : c0;
       const int nl = has_next ? n1 : n;
-      pr.template load_slice<DECAY, 0, RPG / 2, !STATES>(cl, nl);            // g, first half
-      pr.template load_slice<DECAY, PR::kSB, L, !STATES>(cl, nl);            // beta
+      const int hl = xh;   // chunk g + NP's head, or chunk g's when there is none
+      pr.template load_slice<DECAY, 0, RPG / 2, !STATES>(cl, nl, hl);            // g, first half
+      pr.template load_slice<DECAY, PR::kSB, L, !STATES>(cl, nl, hl);            // beta
       if constexpr (STATES)
         pr.template products<true>(rr, slot, reinterpret_cast<bf16*>(tiles + ChainTiles<DK>::oM));
       else
         pr.products(rr, slot);
-      pr.template load_slice<DECAY, RPG / 2, RPG, !STATES>(cl, nl);          // g, second half
+      pr.template load_slice<DECAY, RPG / 2, RPG, !STATES>(cl, nl, hl);          // g, second half
       lds_barrier();
-      pr.template load_slice<DECAY, PR::kSK, PR::kSQ, !STATES>(cl, nl);      // k
-      pr.template load_slice<DECAY, PR::kSV, PR::kSB, !STATES>(cl, nl);      // v
+      pr.template load_slice<DECAY, PR::kSK, PR::kSQ, !STATES>(cl, nl, hl);      // k
+      pr.template load_slice<DECAY, PR::kSV, PR::kSB, !STATES>(cl, nl, hl);      // v
       pr.inverse_blocks();
       lds_barrier();
       // waves 0, 1 merge the diagonal pairs; the Qg / KD^T fragments are spread over
       // all four waves
       if (wave < 2) pr.inverse_pairs();
       pr.template publish_qk<0, 4>(rr, slot);
-      pr.template load_slice<DECAY, PR::kSQ, PR::kSV, !STATES>(cl, nl);      // q
+      pr.template load_slice<DECAY, PR::kSQ, PR::kSV, !STATES>(cl, nl, hl);      // q
       lds_barrier();
       pr.inverse_rest();
       if constexpr (STATES) {
@@ -772,17 +906,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       }
       // every slot store of the workgroup acknowledged (device-visible), then publish
       vm_barrier();
-      if (tid == 0) __hip_atomic_store(ready + s, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(ready + s, g + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      c0 = c1;
+      n = n1;
+      ch = xh;
+      cslot = xslot + gn;
+      s += a.NP;
+      while (s >= a.R) {
+        s -= a.R;
+        need += a.NC;
+      }
     }
     return;
   }
 
   // ================================== consumer =====================================
   if constexpr (DK == 128 && VBW == 16) {
-    wy_consume_split<DK, DV, STATES>(a, smem, rr, ready, done, abort_word, role, n_seq, h, bos,
-                                     eos, nch, tid, wave, lane);
+    wy_consume_split<DK, DV, STATES>(a, smem, rr, ready, done, abort_word, role, lid, total, tid,
+                                     wave, lane);
     return;
   }
+  // the value-column consumer serves one unit per lane (no lane plan)
+  LaneUnit u0;
+  lane_unit(a, lid, 0, 0, u0);
+  const int n_seq = u0.n_seq, h = u0.h, nch = u0.nch;
+  const int64_t bos = u0.bos, eos = u0.eos;
   const int vw0 = role * 4 * VBW + VBW * wave;     // this wave's first value column
   using CL = WyConsumerLayout<DK, DV>;
   int* cFlag = reinterpret_cast<int*>(smem + CL::oFlag);
@@ -1033,11 +1181,61 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
   if (!ok) poison_outputs<DK, DV, false>(a, n_seq, h, bos, eos, nch, v0, BV, tid);
 }
 
-// Zero the abort word and the hand-off flags before a producer/consumer launch (not
-// the sticky abort word 1).
-__global__ void coop_reset_kernel(int* words, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-    if (i != 1) words[i] = 0;
+// Before a producer/consumer launch (one wave): zero the abort word and the hand-off
+// flags (not the sticky abort word 1).  With a lane plan, spread the units over the
+// lanes: sequences longest first (ties: lower index), each of a sequence's H units to
+// the lane with the fewest chunks so far (ties: the lower lane), so that the lanes'
+// chunk streams come out nearly equal and the longest units start first.
+constexpr int kPlanMaxSeqs = 256, kPlanMaxUnits = 8192, kPlanMaxLanes = 64;
+__global__ __launch_bounds__(64) void coop_prep_kernel(PrefillArgs a, int flag0, int nflag) {
+  int* words = reinterpret_cast<int*>(a.workspace);
+  const int t = threadIdx.x;
+  if (t == 0) words[0] = 0;
+  for (int i = t; i < nflag; i += 64) words[flag0 + i] = 0;
+  if (a.lane_units == nullptr) return;
+  int32_t* off = const_cast<int32_t*>(a.lane_off);
+  int32_t* list = const_cast<int32_t*>(a.lane_units);
+  const int H = a.H, U = a.units, N = U / H, L = a.lanes;
+  __shared__ int nchs[kPlanMaxSeqs], order[kPlanMaxSeqs], soff[kPlanMaxLanes + 1];
+  __shared__ unsigned short lane_of[kPlanMaxUnits], pos_of[kPlanMaxUnits];
+  for (int n = t; n < N; n += 64) {
+    int ns, hh;
+    int64_t bos, eos;
+    unit_bounds(a, n * H, ns, hh, bos, eos);
+    nchs[n] = static_cast<int>((eos - bos + kChunk - 1) / kChunk);
+  }
+  __syncthreads();
+  for (int n = t; n < N; n += 64) {
+    int r = 0;
+    for (int m = 0; m < N; ++m) r += (nchs[m] > nchs[n] || (nchs[m] == nchs[n] && m < n)) ? 1 : 0;
+    order[r] = n;
+  }
+  __syncthreads();
+  int load = 0, cnt = 0;   // lane t's chunks and units so far
+  for (int r = 0; r < N; ++r) {
+    const int n = order[r], c = nchs[n];
+    for (int hh = 0; hh < H; ++hh) {
+      int key = t < L ? (load << 6) | t : 0x7fffffff;
+      for (int o = 32; o > 0; o >>= 1) key = min(key, __shfl_xor(key, o));
+      if (t == (key & 63)) {
+        lane_of[n * H + hh] = static_cast<unsigned short>(t);
+        pos_of[n * H + hh] = static_cast<unsigned short>(cnt);
+        ++cnt;
+        load += c;
+      }
+    }
+  }
+  // lane offsets: exclusive prefix of the unit counts
+  int incl = t < L ? cnt : 0;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (t >= o) incl += y;
+  }
+  if (t < L) soff[t] = incl - cnt;
+  if (t == L - 1) soff[L] = incl;
+  __syncthreads();
+  for (int i = t; i <= L; i += 64) off[i] = soff[i];
+  for (int u = t; u < U; u += 64) list[soff[lane_of[u]] + pos_of[u]] = u;
 }
 
 // ====================================================================================
@@ -1113,24 +1311,27 @@ hipError_t launch_prefill_states(int dk, int bv, const PrefillArgs& a, hipStream
   return launch_states_t<0>(dk, bv, a, stream);
 }
 
-size_t prefill_coop_workspace_bytes(int dk, int dv, int units, int R) {
+size_t prefill_coop_workspace_bytes(int dk, int dv, int lanes, int units, int R, bool plan) {
   if (dk == 64)
-    return dv == 64 ? coop_workspace_bytes<64, 64>(units, R) : coop_workspace_bytes<64, 128>(units, R);
-  return dv == 64 ? coop_workspace_bytes<128, 64>(units, R) : coop_workspace_bytes<128, 128>(units, R);
+    return dv == 64 ? coop_workspace_bytes<64, 64>(lanes, units, R, plan)
+                    : coop_workspace_bytes<64, 128>(lanes, units, R, plan);
+  return dv == 64 ? coop_workspace_bytes<128, 64>(lanes, units, R, plan)
+                  : coop_workspace_bytes<128, 128>(lanes, units, R, plan);
 }
 
 template <int DK, int DV, int VBW, int DECAY, bool STATES = false>
 static hipError_t launch_wy_k(const PrefillArgs& a, hipStream_t stream) {
-  const int nwords = static_cast<int>((kWsHeader + coop_flags_bytes(a.units, a.R)) / 4);
-  hipLaunchKernelGGL(coop_reset_kernel, dim3((nwords + 255) / 256), dim3(256), 0, stream,
-                     reinterpret_cast<int*>(a.workspace), nwords);
+  const bool plan = a.lane_units != nullptr;
+  const int flag0 = static_cast<int>((kWsHeader + coop_plan_bytes(a.lanes, a.units, plan)) / 4);
+  const int nflag = a.lanes * coop_flag_words(a.R);
+  hipLaunchKernelGGL(coop_prep_kernel, dim3(1), dim3(64), 0, stream, a, flag0, nflag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PrefillArgs arg = a;
   void* params[] = {&arg};
   const void* kernel =
       reinterpret_cast<const void*>(&prefill_wy_kernel<DK, DV, VBW, DECAY, STATES>);
-  return hipLaunchCooperativeKernel(kernel, dim3(a.units * (a.NC + a.NP)), dim3(kThreads), params,
+  return hipLaunchCooperativeKernel(kernel, dim3(a.lanes * (a.NC + a.NP)), dim3(kThreads), params,
                                     0, stream);
 }
 

@@ -284,7 +284,7 @@ struct WyProducer {
   static constexpr int kSK = RPG, kSQ = RPG + RPG / 2, kSV = 2 * RPG, kSB = 2 * RPG + RPGV;
   static constexpr int kLoads = kSB + 1;
   template <int DECAY, int I0, int I1, bool BUF = true>
-  __device__ __forceinline__ void load_slice(int64_t c0, int n) {
+  __device__ __forceinline__ void load_slice(int64_t c0, int n, int h) {
     const int64_t rk = (c0 * H + h) * DK;
     auto rsrc = [](const void* p) {
       return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7fffffff, 0x00020000);
@@ -358,8 +358,8 @@ struct WyProducer {
     unpack(qp, qr);
   }
   template <int DECAY, bool BUF = true>
-  __device__ __forceinline__ void load(int64_t c0, int n) {
-    load_slice<DECAY, 0, kLoads, BUF>(c0, n);
+  __device__ __forceinline__ void load(int64_t c0, int n, int h) {
+    load_slice<DECAY, 0, kLoads, BUF>(c0, n, h);
   }
 
   // Kg, Qg, Ki, KD, V (row-major), beta and e^{G_n} of the loaded chunk into LDS.  The

@@ -161,10 +161,22 @@ size_t kda_prefill_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_
                                    int32_t d_k, int32_t d_v);
 
 /* Geometry of the producer/consumer prefill on the current device: value-tile
- * workgroups (consumers), producer workgroups per (sequence, head) and ring slots;
- * all zero when it does not apply.  Output pointers may be NULL. */
+ * workgroups (consumers), producer workgroups per lane and ring slots; all zero when
+ * it does not apply.  Output pointers may be NULL. */
 int kda_prefill_coop_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
                           int32_t* consumers, int32_t* producers, int32_t* ring_slots);
+
+/* Lanes of the producer/consumer prefill (0: it does not apply).  A lane is one set
+ * of consumer and producer workgroups working through a stream of chunks.  With as
+ * many lanes as (sequence, head) units, lane i is unit i.  With d_k = d_v = 128 and
+ * more units than the device has room for lanes of seven workgroups (N <= 256,
+ * N * H <= 8192), a plan made on the device from cu_seqlens at each call spreads the
+ * units over fewer lanes, longest sequences first, each to the lane with the least
+ * work so far; a lane then processes its units one after another, each with its own
+ * boundary state carried from chunk to chunk ("Kimi Delta Attention Technical Deep
+ * Dive", "Systems and implementation tradeoffs" -> "Training").
+ * Host-only apart from a cached device-attribute query. */
+int kda_prefill_coop_lanes(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v);
 
 /*
  * Launch geometry of the fused prefill kernel on the current device: the number of

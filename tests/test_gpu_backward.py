@@ -185,6 +185,20 @@ def _segmented_head(args):
     return segmented_backward(*args, segment=64)
 
 
+def test_backward_lanes_many_units():
+    """More (sequence, head) units than lanes: the forward sweep of the backward runs
+    on the lane plan (units one after another per lane).  All gradients vs the oracle."""
+    lengths = [5, 0, 200, 64, 1, 130, 63, 0, 65, 140, 17, 128, 0, 90, 100, 2, 40, 70, 0, 64]
+    H = 4
+    assert 0 < kda.prefill_coop_lanes(torch.bfloat16, len(lengths), H, 128, 128) < len(lengths) * H
+    print(f"backward lanes N={len(lengths)} H={H}", flush=True)
+    x = ki.make_prefill(H=H, d_k=128, d_v=128, dtype="bf16", lengths=lengths,
+                        init_state_std=0.02, seed=80, device=DEV)
+    do, ds = grads_in(x, 180)
+    got, ref = run_both(x, do, ds)
+    compare(x, got, ref, "lanes")
+
+
 def test_backward_full_size_every_token():
     """The long-context workload (B=1, H=32, T=65536, d=128, bf16) in the launch
     configuration bench.py times, four heads compared over ALL 65536 tokens: the oracle

@@ -284,6 +284,56 @@ def test_packed_equals_separate_calls_and_deterministic(path):
         check("bf16", ki.to_f64(fsn[0]), ki.to_f64(fs[n]), f"separate seq {n} state")
 
 
+# ------------------------------------------------------------------ lanes
+# With more (sequence, head) units than lanes of producer/consumer workgroups, a plan
+# made on the device spreads the units over the lanes and each lane works through its
+# units one after another.
+LANE_LENGTHS = {
+    # every kind of length (empty, sub-chunk, exact, ragged, several chunks), the
+    # longest ones not first
+    "mixed": [5, 0, 200, 64, 1, 130, 63, 0, 65, 300, 17, 128, 0, 90, 257, 2, 40, 191, 0, 64,
+              33, 129, 7, 0, 150, 64, 11, 0, 250, 66, 3, 99, 0, 128, 45, 180, 0, 70, 1, 310],
+    # fewer units with chunks than lanes: some lanes get no unit, the empty ones share
+    "sparse": [0] * 17 + [130, 0, 1, 0, 64] + [0] * 18,
+}
+
+
+@pytest.mark.parametrize("kind", sorted(LANE_LENGTHS))
+def test_lanes_many_units(kind):
+    lengths = LANE_LENGTHS[kind]
+    H = 4
+    lanes = kda.prefill_coop_lanes(torch.bfloat16, len(lengths), H, 128, 128)
+    print(f"prefill lanes {kind}: N={len(lengths)} H={H} lanes={lanes}", flush=True)
+    assert 0 < lanes < len(lengths) * H, "the case must take the lane plan"
+    x = ki.make_prefill(H=H, d_k=128, d_v=128, dtype="bf16", lengths=lengths,
+                        init_state_std=0.02, seed=48, device=DEV)
+    o, fs = run_gpu(x, "coop")
+    o_ref, s_ref = run_oracle(x)
+    compare_full(x, o, fs, o_ref, s_ref, f"lanes {kind}")
+    for n, ln in enumerate(lengths):
+        if ln == 0:   # empty sequences return their initial state untouched
+            assert torch.equal(fs[n], x["initial_state"][n]), f"sequence {n}"
+
+
+def test_lanes_bit_identical_to_one_unit_per_lane(monkeypatch):
+    """The lane plan only changes which workgroups process a unit, not its arithmetic:
+    o and final state equal, bit for bit, those of one unit per lane (the same
+    consumer, forced by KDA_COOP_LANES=0 and KDA_COOP_NC=2)."""
+    lengths = [300, 64, 130, 0, 5, 190]
+    H = 12
+    x = ki.make_prefill(H=H, d_k=128, d_v=128, dtype="bf16", lengths=lengths,
+                        init_state_std=0.02, seed=49, device=DEV)
+    assert 0 < kda.prefill_coop_lanes(torch.bfloat16, len(lengths), H, 128, 128) < len(lengths) * H
+    print("prefill lanes vs one unit per lane", flush=True)
+    o, fs = run_gpu(x, "coop")
+    monkeypatch.setenv("KDA_COOP_LANES", "0")
+    monkeypatch.setenv("KDA_COOP_NC", "2")
+    assert kda.prefill_coop_lanes(torch.bfloat16, len(lengths), H, 128, 128) == len(lengths) * H
+    assert kda.prefill_coop_plan(torch.bfloat16, len(lengths), H, 128, 128)[0] == 2
+    o1, fs1 = run_gpu(x, "coop")
+    assert torch.equal(o, o1) and torch.equal(fs, fs1)
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_decode_steps_match_prefill(path):
     """T decode steps from S_0 give the same outputs and state as one prefill of the

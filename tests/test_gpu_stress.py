@@ -50,14 +50,15 @@ def test_random_varlen(case):
         compare_full(x, o, fs, o_ref, s_ref, f"{name} {path}")
 
 
-def test_coop_not_applicable_falls_back_to_fused():
-    """More units than the grid can hold as co-resident producer/consumer groups:
-    the plan reports none, the workspace size is 0 and the fused kernel runs."""
-    N, H = 16, 16
-    nc, _, _ = kda.prefill_coop_plan(torch.bfloat16, N, H, 128, 128)
-    assert nc == 0
-    assert kda.workspace_bytes(torch.bfloat16, N, N * 70, H, 128, 128) == 0
-    x = ki.make_prefill(B=N, T=70, H=H, d_k=128, d_v=128, dtype="bf16", seed=90, device=DEV)
+@pytest.mark.parametrize("N,H,d", [(16, 16, 64), (300, 1, 128)])
+def test_coop_not_applicable_falls_back_to_fused(N, H, d):
+    """More units than the grid can hold as co-resident producer/consumer groups, and
+    no lane plan (d = 64, or more than 256 sequences): the plan reports none, the
+    workspace size is 0 and the fused kernel runs."""
+    nc, _, _ = kda.prefill_coop_plan(torch.bfloat16, N, H, d, d)
+    assert nc == 0 and kda.prefill_coop_lanes(torch.bfloat16, N, H, d, d) == 0
+    assert kda.workspace_bytes(torch.bfloat16, N, N * 70, H, d, d) == 0
+    x = ki.make_prefill(B=N, T=70, H=H, d_k=d, d_v=d, dtype="bf16", seed=90, device=DEV)
     o, fs = run_gpu(x, "fused")
     o_ref, s_ref = run_oracle(x, {})
     compare_full(x, o, fs, o_ref, s_ref, "fallback")
