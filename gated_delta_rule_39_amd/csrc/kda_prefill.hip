@@ -859,7 +859,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       // counter is read before the factors, so the check after them rarely waits
       int dv = 0;
       if (tid == 0) dv = __hip_atomic_load(done + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      pr.template factors<DECAY, STATES>(n);
+      pr.template factors<DECAY, STATES>(n, g + 1);
       if (tid == 0) pFlag[0] = (dv >= need || wait_at_least(done + s, need, abort_word)) ? 1 : 0;
       lds_barrier();
       if (pFlag[0] == 0) break;
@@ -899,6 +899,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
         // -W rows staged in the A area (dead after the inverse) for the transposed copy
         static_assert(size_t(kChunk) * PL::LDK * 2 <= PL::oX - PL::oA, "-W staging fits");
         pr.template publish_wu<true>(rr, slot, reinterpret_cast<bf16*>(smem + PL::oA));
+        pr.qg_to_chunk_start();
         lds_barrier();
         publish_chain_tiles<DK, DV>(smem, tiles, tid, wave, lane);
       } else {

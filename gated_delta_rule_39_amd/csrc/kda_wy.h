@@ -82,6 +82,29 @@ __device__ __forceinline__ bf16x8 frag_tr_perm(const bf16* base, int ld, int k0,
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// A fragment times per-K factors: s[0..7] for the K order of frag_rows (eight
+// consecutive K), or s[0..3], s[16..19] for frag_perm.
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 f, f32x4 lo, f32x4 hi) {
+  return bf16x8{static_cast<bf16>(static_cast<float>(f[0]) * lo[0]),
+                static_cast<bf16>(static_cast<float>(f[1]) * lo[1]),
+                static_cast<bf16>(static_cast<float>(f[2]) * lo[2]),
+                static_cast<bf16>(static_cast<float>(f[3]) * lo[3]),
+                static_cast<bf16>(static_cast<float>(f[4]) * hi[0]),
+                static_cast<bf16>(static_cast<float>(f[5]) * hi[1]),
+                static_cast<bf16>(static_cast<float>(f[6]) * hi[2]),
+                static_cast<bf16>(static_cast<float>(f[7]) * hi[3])};
+}
+__device__ __forceinline__ bf16x8 scale_rows8(bf16x8 f, const float* s) {
+  return scale_frag(f, *reinterpret_cast<const f32x4*>(s), *reinterpret_cast<const f32x4*>(s + 4));
+}
+__device__ __forceinline__ bf16x8 scale_perm8(bf16x8 f, const float* s) {
+  return scale_frag(f, *reinterpret_cast<const f32x4*>(s), *reinterpret_cast<const f32x4*>(s + 16));
+}
+__device__ __forceinline__ bf16x8 scale_all(bf16x8 f, float x) {
+  const f32x4 v = f32x4{x, x, x, x};
+  return scale_frag(f, v, v);
+}
+
 __device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -161,7 +184,10 @@ struct WyProducerLayout {
   static constexpr size_t oScr = al(oX + size_t(kChunk) * LDF * 4);
   static constexpr size_t oBeta = al(oScr + (scrTot > scrY ? scrTot : scrY));
   static constexpr size_t oEgn = al(oBeta + kChunk * 4);
-  static constexpr size_t oFlag = al(oEgn + DK * 4);
+  // strong-decay chunks: block-pair factors [7][DK] and block-start decays [4][DK]
+  static constexpr size_t oPair = al(oEgn + DK * 4);
+  static constexpr size_t oEc = al(oPair + size_t(7) * DK * 4);
+  static constexpr size_t oFlag = al(oEc + size_t(4) * DK * 4);
   static constexpr size_t kBytes = al(oFlag + 16);
 };
 
@@ -202,7 +228,10 @@ struct WyProducer {
   static constexpr int KS = DK / 32;
 
   bf16 *sKg, *sQg, *sKi, *sKD, *sV, *sTm;
-  float *sA, *sX, *sScr, *sBeta, *sEgn;
+  float *sA, *sX, *sScr, *sBeta, *sEgn, *sPair, *sEc;
+  int* sStrong;
+  // this chunk takes the strong-decay factorization (wave-uniform; set by factors())
+  bool strong;
   const bf16 *q, *k, *v;
   const float *g, *beta;
   int32_t H, h;
@@ -245,6 +274,10 @@ struct WyProducer {
     sScr = reinterpret_cast<float*>(smem + L::oScr);
     sBeta = reinterpret_cast<float*>(smem + L::oBeta);
     sEgn = reinterpret_cast<float*>(smem + L::oEgn);
+    sPair = reinterpret_cast<float*>(smem + L::oPair);
+    sEc = reinterpret_cast<float*>(smem + L::oEc);
+    sStrong = reinterpret_cast<int*>(smem + L::oFlag) + 2;
+    strong = false;
     q = q_;
     k = k_;
     v = v_;
@@ -264,6 +297,8 @@ struct WyProducer {
     jv0 = 8 * (tid_ % CGV);
     br = 0.f;
     local = false;
+    // no chunk tag is negative (a barrier follows before the first chunk)
+    if (tid == 0) *sStrong = -1;
     // the strictly upper part of X diag(beta) is never written
     for (int i = tid; i < kChunk * LDC; i += kThreads) sTm[i] = static_cast<bf16>(0.f);
   }
@@ -383,11 +418,81 @@ struct WyProducer {
     }
   }
 
+  // The strong-decay tiles of factors() (QSCALE as there): Kg, Qg from the start of
+  // the row's 16-row block, Ki to its end, KD to the chunk end; the block-pair factors
+  // [1 / Bd_0 .. 1 / Bd_3, Bd_1, Bd_2, Bd_1 Bd_2] (Bd_a: decay over block a) and the
+  // block-start decays Ec_a = Bd_0 .. Bd_{a-1}.
+  template <bool QSCALE>
+  __device__ __forceinline__ void strong_factors(const f32x4 (&tots)[RG], f32x4 cs, int n) {
+    constexpr int GPB = 16 / RPG;   // row groups per 16-row block
+    const f32x4 one = f32x4{1.f, 1.f, 1.f, 1.f};
+    f32x4 bp = one, bs = one;       // this block's groups before / after this one
+#pragma unroll
+    for (int r2 = 0; r2 < RG; ++r2)
+      if (r2 / GPB == rg / GPB) {
+        if (r2 < rg) bp *= tots[r2];
+        if (r2 > rg) bs *= tots[r2];
+      }
+    f32x4 kf[RPG];
+    f32x4 run = bp;
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      run *= gr[i];
+      kf[i] = widen(kr[i]);
+      f32x4 q4 = widen(qr[i]);
+      if constexpr (QSCALE) q4 *= scale;
+      store4(sKg + (rg * RPG + i) * LDK + j0, kf[i] * run);
+      store4(sQg + (rg * RPG + i) * LDK + j0, q4 * run);
+    }
+    f32x4 sfx = one;
+#pragma unroll
+    for (int i = RPG - 1; i >= 0; --i) {
+      store4(sKD + (rg * RPG + i) * LDK + j0, kf[i] * (cs * sfx));
+      store4(sKi + (rg * RPG + i) * LDK + j0, kf[i] * (bs * sfx));
+      sfx *= gr[i];
+    }
+    f32x4 bd[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      bd[a] = one;
+#pragma unroll
+      for (int r2 = a * GPB; r2 < (a + 1) * GPB; ++r2) bd[a] *= tots[r2];
+    }
+    auto rcp4 = [](f32x4 x) {
+      return f32x4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]),
+                   __builtin_amdgcn_rcpf(x[2]), __builtin_amdgcn_rcpf(x[3])};
+    };
+    if (rg < 7) {
+      f32x4 pv = bd[1] * bd[2];
+      if (rg < 4) pv = rcp4(rg == 0 ? bd[0] : rg == 1 ? bd[1] : rg == 2 ? bd[2] : bd[3]);
+      else if (rg == 4) pv = bd[1];
+      else if (rg == 5) pv = bd[2];
+      store4(sPair + rg * DK + j0, pv);
+    }
+    if (rg < 4) {
+      const f32x4 ec = rg == 0 ? one : rg == 1 ? bd[0] : rg == 2 ? bd[0] * bd[1] : bd[0] * bd[1] * bd[2];
+      store4(sEc + rg * DK + j0, ec);
+    }
+    (void)n;
+  }
+
   // QSCALE: Qg includes the query scale (the backward's chain tiles use it); without it
   // the consumer applies the scale to each output tile instead (one multiply per output
   // element rather than one per Qg element).
+  //
+  // Strong decay.  The factors above are referenced to the chunk start, so Ki carries
+  // e^{-G_r}: past a per-chunk sum of |g| of about 87 it overflows fp32 and A turns
+  // into NaN.  A chunk in which some 8-row group of some channel decays by more than
+  // e^{-10} (so the chunk sum may exceed 80) is factored per 16-row block instead:
+  // Kg and Qg relative to the start of their block, Ki relative to its end, every
+  // stored factor <= 1.  The products then scale the Ki fragment of block pair (a, b)
+  // by e^{G_{16a-1} - G_{16b+15}} (the decay of the blocks between; 1 / the block's own
+  // decay for a = b), and the published Qg and the Kg operand of W get the block-start
+  // decay e^{G_{16a-1}} back.  Values are exact in either form (up to rounding); the
+  // strong form holds while no 16-row block decays by more than about e^{-85} in a
+  // channel.  tag: a number unique to this chunk among this workgroup's chunks.
   template <int DECAY, bool QSCALE = true>
-  __device__ __forceinline__ void factors(int n) {
+  __device__ __forceinline__ void factors(int n, int tag) {
     unpack_pairs();
     if (flags & kNormK) normalise_keys();
     if constexpr (DECAY == 1) {
@@ -430,6 +535,10 @@ struct WyProducer {
       tot *= gr[i];
     }
     store4(sScr + rg * DK + j0, tot);
+    if constexpr (DECAY != 2) {
+      constexpr float kStrongTot = 4.5399930e-05f;   // e^{-10}
+      if (min(min(tot[0], tot[1]), min(tot[2], tot[3])) < kStrongTot) *sStrong = tag;
+    }
     if (tid < kChunk)
       sBeta[tid] = tid < n ? ((flags & kBetaLogit) ? sigmoid_hw(br) : br) : 0.f;
     // V rows meanwhile
@@ -437,6 +546,7 @@ struct WyProducer {
     for (int i = 0; i < RPGV; ++i)
       *reinterpret_cast<u32x4*>(sV + (rgv * RPGV + i) * LDV + jv0) = __builtin_bit_cast(u32x4, vr[i]);
     lds_barrier();
+    strong = __builtin_amdgcn_readfirstlane(*sStrong == tag ? 1 : 0) != 0;
     f32x4 tots[RG];
 #pragma unroll
     for (int r2 = 0; r2 < RG; ++r2) tots[r2] = *reinterpret_cast<const f32x4*>(sScr + r2 * DK + j0);
@@ -447,6 +557,11 @@ struct WyProducer {
       if (r2 > rg) cs *= tots[r2];
     }
     const f32x4 egn = cp * tot * cs;   // e^{G_n}
+    if (strong) {
+      strong_factors<QSCALE>(tots, cs, n);
+      if (rg == 0) store4(sEgn + j0, egn);
+      return;
+    }
     // forward: e^{G_r} = cp * alpha_first .. alpha_r  ->  Kg, Qg
     f32x4 kf[RPG];
     {
@@ -501,6 +616,65 @@ struct WyProducer {
     }
   }
 
+  // Block-pair factor rows of sPair (see strong_factors).
+  static constexpr int kInv0 = 0, kBd1 = 4, kBd2 = 5, kBd12 = 6;
+  // Strong-decay forms of lower_blocks (A, waves 0, 1) and mt_blocks (M^T, waves 2, 3):
+  // the Ki fragment of block b, paired with block a, times the factors of (a, b).
+  // RA = 0: pairs (0,0) (3,0) (3,1) (3,2) (3,3); RA = 1: (1,0) (1,1) (2,0) (2,1) (2,2).
+  template <int RA>
+  __device__ __forceinline__ void scaled_ki(const bf16x8 (&ki)[4], int kk, bf16x8 (&out)[5]) const {
+    const float* pf = sPair + kk + 8 * (lane >> 4);
+    if constexpr (RA == 0) {
+      out[0] = scale_rows8(ki[0], pf + (kInv0 + 0) * DK);
+      out[1] = scale_rows8(ki[0], pf + kBd12 * DK);
+      out[2] = scale_rows8(ki[1], pf + kBd2 * DK);
+      out[3] = ki[2];
+      out[4] = scale_rows8(ki[3], pf + (kInv0 + 3) * DK);
+    } else {
+      out[0] = ki[0];
+      out[1] = scale_rows8(ki[1], pf + (kInv0 + 1) * DK);
+      out[2] = scale_rows8(ki[0], pf + kBd1 * DK);
+      out[3] = ki[1];
+      out[4] = scale_rows8(ki[2], pf + (kInv0 + 2) * DK);
+    }
+  }
+  // A blocks of row blocks (RA, RB) = (0, 3) or (1, 2), as lower_blocks.
+  template <int RA, int RB>
+  __device__ __forceinline__ void lower_blocks_strong(f32x4 (&acc)[5]) const {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < DK; kk += 32) {
+      const bf16x8 a0 = frag_rows<M>(sKg, LDK, 16 * RA, kk, lane);
+      const bf16x8 a1 = frag_rows<M>(sKg, LDK, 16 * RB, kk, lane);
+      bf16x8 ki[4], b[5];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) ki[cb] = frag_rows<M>(sKi, LDK, 16 * cb, kk, lane);
+      scaled_ki<RA>(ki, kk, b);
+#pragma unroll
+      for (int s = 0; s < 5; ++s) acc[s] = mma_bf16(s <= RA ? a0 : a1, b[s], acc[s]);
+    }
+  }
+  // M^T tiles (a, B0), (a, B1) as mt_blocks; (B0, B1) = (0, 3) or (1, 2) pairs with
+  // the same blocks as lower_blocks_strong<B0, B1>.
+  template <int B0, int B1>
+  __device__ __forceinline__ void mt_blocks_strong(f32x4 (&acc)[5]) const {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < DK; kk += 32) {
+      const bf16x8 q0 = frag_rows<M>(sQg, LDK, 16 * B0, kk, lane);
+      const bf16x8 q1 = frag_rows<M>(sQg, LDK, 16 * B1, kk, lane);
+      bf16x8 ki[4], b[5];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) ki[a] = frag_rows<M>(sKi, LDK, 16 * a, kk, lane);
+      scaled_ki<B0>(ki, kk, b);
+      // tile (a, B) = Ki_a Qg_B^T: acc[0..B0] = (a, B0), acc[B0 + 1 + a] = (a, B1)
+#pragma unroll
+      for (int s = 0; s < 5; ++s) acc[s] = mma_bf16(b[s], s <= B0 ? q0 : q1, acc[s]);
+    }
+  }
+
   // Waves 0, 1: A = strict-lower(diag(beta) Kg Ki^T) into LDS (fp32).
   // Waves 2, 3: M^T = Ki Qg^T (tiles (a, b), a <= b, masked to a row <= column) and
   // its M fragments straight to the ring slot.  No closing barrier.
@@ -515,20 +689,33 @@ struct WyProducer {
       const f32x4 bta = *reinterpret_cast<const f32x4*>(sBeta + 16 * (wave ? 1 : 0) + 4 * lq);
       const f32x4 btb = *reinterpret_cast<const f32x4*>(sBeta + 16 * (wave ? 2 : 3) + 4 * lq);
       if (wave == 0) {
-        lower_blocks<M, DK, LDK, 0, 3>(acc, sKg, sKi, lane);
+        if (strong)
+          lower_blocks_strong<0, 3>(acc);
+        else
+          lower_blocks<M, DK, LDK, 0, 3>(acc, sKg, sKi, lane);
         store_lower_blocks<true, bf16, LDF, LDC, 0, 3>(acc, bta, btb, sA, nullptr, lane);
       } else {
-        lower_blocks<M, DK, LDK, 1, 2>(acc, sKg, sKi, lane);
+        if (strong)
+          lower_blocks_strong<1, 2>(acc);
+        else
+          lower_blocks<M, DK, LDK, 1, 2>(acc, sKg, sKi, lane);
         store_lower_blocks<true, bf16, LDF, LDC, 1, 2>(acc, bta, btb, sA, nullptr, lane);
       }
       return;
     }
     // token blocks b of this wave: (0, 3) or (1, 2); tiles (a, b) for a <= b:
     // acc[0..b0] = tiles (a, b0), acc[b0+1 .. b0+1+b1] = tiles (a, b1)
-    if (wave == 2)
-      mt_blocks<0, 3>(acc);
-    else
-      mt_blocks<1, 2>(acc);
+    if (wave == 2) {
+      if (strong)
+        mt_blocks_strong<0, 3>(acc);
+      else
+        mt_blocks<0, 3>(acc);
+    } else {
+      if (strong)
+        mt_blocks_strong<1, 2>(acc);
+      else
+        mt_blocks<1, 2>(acc);
+    }
     // causal mask on the diagonal tiles: row (token') 4*lq + i <= column (token) lr
     const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
     auto diag = [&](f32x4 t) {
@@ -679,6 +866,8 @@ struct WyProducer {
     for (int i = 0; i < TQ; ++i) {
       const int f = min(w1 + NW * i, nQ - 1), tb = f / KS, j = f % KS;
       fq[i] = frag_perm(sQg, LDK, 16 * tb, 32 * j, lane);
+      // strong decay: Qg from its block start back to the chunk start
+      if (strong) fq[i] = scale_perm8(fq[i], sEc + tb * DK + 32 * j + 4 * (lane >> 4));
     }
 #pragma unroll
     for (int i = 0; i < TK; ++i) {
@@ -714,6 +903,15 @@ struct WyProducer {
         kt[t][hb] = frag_tr(sKg, LDK, 32 * t, 32 * wave + 16 * hb, lane);
         vt[t][hb] = frag_tr(sV, LDV, 32 * t, 16 * (2 * wave + hb), lane);
       }
+    if (strong) {
+      // Kg from its block start back to the chunk start: lane l's eight rows lie in
+      // block 2t + l / 32, its column is key 32 w + 16 hb + l % 16
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          kt[t][hb] = scale_all(kt[t][hb], sEc[(2 * t + (lane >> 5)) * DK + 32 * wave + 16 * hb + (lane & 15)]);
+    }
     f32x4 w[4][2], u[4][2];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -741,6 +939,19 @@ struct WyProducer {
            pack_frag(u[tb][0], u[tb][1]));
   }
 
+  // Strong decay: Qg in LDS from block-start to chunk-start reference (for readers
+  // after the products, the backward's chain tiles).  No closing barrier.
+  __device__ __forceinline__ void qg_to_chunk_start() {
+    if (!strong) return;
+    for (int e = tid; e < kChunk * (DK / 4); e += kThreads) {
+      const int r = e / (DK / 4), c = 4 * (e % (DK / 4));
+      bf16x4* p = reinterpret_cast<bf16x4*>(sQg + r * LDK + c);
+      const f32x4 x = widen(*p) * *reinterpret_cast<const f32x4*>(sEc + (r / 16) * DK + c);
+      *p = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                  static_cast<bf16>(x[3])};
+    }
+  }
+
   // All waves: W^T = -(Kg^T (X diag(beta))^T) as W fragments and U = X diag(beta) V as
   // fp32 tiles, straight to the slot.  Row block tb of X diag(beta) is zero beyond
   // column 16 tb + 15, so tb < 2 needs one K step.
@@ -760,8 +971,15 @@ struct WyProducer {
       for (int t = 0; t < 2; ++t) {
         if (t == 1 && tb < 2) break;
         const bf16x8 xb = frag_rows<M>(sTm, LDC, 16 * tb, 32 * t, lane);
-        lo = mma_bf16(frag_tr(sKg, LDK, 32 * t, 32 * j, lane), xb, lo);
-        hi = mma_bf16(frag_tr(sKg, LDK, 32 * t, 32 * j + 16, lane), xb, hi);
+        bf16x8 k0 = frag_tr(sKg, LDK, 32 * t, 32 * j, lane);
+        bf16x8 k1 = frag_tr(sKg, LDK, 32 * t, 32 * j + 16, lane);
+        if (strong) {   // as in publish_wu_128
+          const float* ec = sEc + (2 * t + (lane >> 5)) * DK + 32 * j + (lane & 15);
+          k0 = scale_all(k0, ec[0]);
+          k1 = scale_all(k1, ec[16]);
+        }
+        lo = mma_bf16(k0, xb, lo);
+        hi = mma_bf16(k1, xb, hi);
       }
       st16(rr, slot + SL::oW + f * SL::kFrag + 16 * lane, pack_frag(-lo, -hi));
       if constexpr (TILES) {

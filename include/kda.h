@@ -25,10 +25,15 @@
  *    the host.  A device fault surfaces at the caller's next synchronisation.
  *  - Every argument is validated before any HIP call.  Status codes are below;
  *    nothing throws across the ABI.
- *  - Unchecked device-side preconditions: keys L2-normalised; g <= 0 with the
- *    per-64-token-chunk sum of |g| below about 80 per channel; beta in [0, 2];
- *    cu_seqlens non-decreasing with cu[0] = 0 and cu[N] = B*T.  Outside these the
- *    numerics are defined but not guaranteed; NaN propagates.
+ *  - Unchecked device-side preconditions: keys L2-normalised; g <= 0; beta in
+ *    [0, 2]; cu_seqlens non-decreasing with cu[0] = 0 and cu[N] = B*T; and a bound on
+ *    the decay within a 64-token chunk (chunks start at each sequence's first token),
+ *    as a sum of |g| per key channel: on the bf16 producer/consumer prefill, below
+ *    about 85 over every aligned 16 tokens of a chunk (chunks in which some 8 tokens
+ *    decay by more than e^-10 are factored per 16-token block); on the fused prefill
+ *    kernel (fp32, and bf16 shapes without a producer/consumer plan) and in the
+ *    backward, below about 80 over the whole chunk.  Outside these the numerics are
+ *    defined but not guaranteed; NaN propagates.
  */
 #ifndef KDA_H
 #define KDA_H

@@ -14,7 +14,9 @@ gate is g = log(alpha) in fp32, either -U(0.001, 0.1) ("uniform") or
 strong-decay recipes probe the documented range of the per-chunk decay (the sum of
 |g| over 64 tokens, per key channel, below about 80): "moderate", -U(0.25, 0.5)
 (about 24 per chunk), "strong", -U(0.6, 1.1) (about 54) and "edge", -U(0.95, 1.25)
-(about 70).  Initial
+(about 70).  Past that range: "extreme", -U(2, 4) (about 190 per chunk, 48 per 16
+tokens), and "spiky", the uniform gate plus, with probability 0.01 per token and
+channel, a drop of -U(5, 20) (a near reset of that channel).  Initial
 states, where present, are N(0, 0.02^2) fp32 (0.02 read as the standard
 deviation).  The draw order is fixed: sequence lengths (varlen only), q, k, v,
 g, beta, initial state.
@@ -26,7 +28,8 @@ DeltaNet: one g per token and head, [.., H], same distribution) and "none"
 Raw projections (``raw=True``, for the fused prologue): k ~ N(0, 1) is not
 normalised, beta holds logits ~ N(0, 1) (sigmoid gives the recipe's beta) and g
 holds retention logits a ~ U(2, 7), so that log(sigmoid(a)) spans about the same
-range as the uniform gate, -0.127 .. -0.0009.
+range as the uniform gate, -0.127 .. -0.0009; with gate "extreme", strongly negative
+logits a ~ U(-4, -1) (log(sigmoid(a)) from -4.02 to -1.31).
 """
 
 from __future__ import annotations
@@ -104,10 +107,16 @@ def _gate(gen, shape, kind, device):
         return -(0.001 + 0.099 * u)
     if kind == "softplus":
         return -torch.nn.functional.softplus(_randn(gen, shape, device)) * 0.1
-    if kind in ("moderate", "strong", "edge"):
-        lo, hi = {"moderate": (0.25, 0.5), "strong": (0.6, 1.1), "edge": (0.95, 1.25)}[kind]
+    if kind in ("moderate", "strong", "edge", "extreme"):
+        lo, hi = {"moderate": (0.25, 0.5), "strong": (0.6, 1.1), "edge": (0.95, 1.25),
+                  "extreme": (2.0, 4.0)}[kind]
         u = torch.rand(*shape, generator=gen, device=device, dtype=torch.float32)
         return -(lo + (hi - lo) * u)
+    if kind == "spiky":
+        u = torch.rand(*shape, generator=gen, device=device, dtype=torch.float32)
+        hit = torch.rand(*shape, generator=gen, device=device, dtype=torch.float32) < 0.01
+        drop = torch.rand(*shape, generator=gen, device=device, dtype=torch.float32)
+        return -(0.001 + 0.099 * u) - hit.float() * (5.0 + 15.0 * drop)
     raise ValueError(f"unknown gate recipe {kind!r}")
 
 
@@ -125,7 +134,8 @@ def varlen_lengths(n_seqs: int, lo: int, hi: int, seed: int):
 def _gate_for(gen, lead, d_k, kind, decay, device, raw=False):
     if raw and decay in ("channel", "head"):
         shape = (*lead, d_k) if decay == "channel" else lead
-        return 2.0 + 5.0 * torch.rand(*shape, generator=gen, device=device, dtype=torch.float32)
+        u = torch.rand(*shape, generator=gen, device=device, dtype=torch.float32)
+        return -4.0 + 3.0 * u if kind == "extreme" else 2.0 + 5.0 * u
     if decay == "channel":
         return _gate(gen, (*lead, d_k), kind, device)
     if decay == "head":

@@ -181,6 +181,48 @@ def test_strong_decay_within_documented_range(gate, dtype, path):
     compare_full(x, o, fs, o_ref, s_ref, f"strong decay {gate} {dtype} {path}")
 
 
+# ------------------------------------------------------------------ past the chunk-start range
+def chunk_block_sums(x, rows):
+    """Largest per-channel sum of |g| over an aligned group of ``rows`` tokens of any
+    64-token chunk (chunks start at each sequence's first token)."""
+    g = -ki.to_f64(x["g"])
+    if g.ndim == 3:                      # one g per token and head
+        g = g[..., None]
+    worst = 0.0
+    for _, lo, hi in seq_bounds(x):
+        gs = g.reshape(-1, *g.shape[2:]) if x["cu_seqlens"] is not None else None
+        for c0 in range(lo, hi, 64):
+            for r0 in range(c0, min(c0 + 64, hi), rows):
+                seg = gs[r0:min(r0 + rows, c0 + 64, hi)] if gs is not None else None
+                if seg is not None and seg.size:
+                    worst = max(worst, float(seg.sum(axis=0).max()))
+    return worst
+
+
+@pytest.mark.parametrize("gate,paths", [("spiky", ["fused", "coop"]), ("extreme", ["coop"])])
+def test_strong_decay_block_factored(gate, paths):
+    """Chunks in which some 8 tokens of a channel decay by more than e^-10 take the
+    block-factored form on the producer/consumer kernel.  "spiky": near resets of
+    single channels at a moderate total decay (both kernels); "extreme": about 190
+    per chunk, past the range of chunk-start factors (producer/consumer kernel only;
+    the documented limit of the block form is a 16-token sum of about 85)."""
+    # no single-token sequence: one row's output is one query-key product, whose bf16
+    # relative error is about 2^-8 / |cos(q, k)| once the decay factors are far from 1
+    # (the per-unit bar needs rows to average over)
+    lengths = [45, 64, 130, 300, 17]
+    print(f"prefill strong decay {gate} {paths}", flush=True)
+    x = ki.make_prefill(H=4, d_k=128, d_v=128, dtype="bf16", gate=gate, lengths=lengths,
+                        init_state_std=0.02, seed=51, device=DEV)
+    b8, b16, b64 = chunk_block_sums(x, 8), chunk_block_sums(x, 16), chunk_block_sums(x, 64)
+    print(f"  largest 8-token sum {b8:.1f}, 16-token {b16:.1f}, chunk {b64:.1f}", flush=True)
+    assert b8 > 10.0 and b16 < 80.0
+    assert "fused" not in paths or b64 < 80.0   # the fused kernel's chunk-start range
+    o_ref, s_ref = run_oracle(x)
+    for path in paths:
+        o, fs = run_gpu(x, path)
+        compare_full(x, o, fs, o_ref, s_ref, f"strong decay {gate} {path}")
+
+
 # ------------------------------------------------------------------ method special cases
 @pytest.mark.parametrize("path", PATHS)
 def test_one_hot_retrieval_exact(path):

@@ -46,6 +46,20 @@ def test_varlen_ragged_all_flags(decay, dtype, d_k, d_v, path):
     compare_full(x, o, fs, o_ref, s_ref, f"prologue {decay} {dtype}")
 
 
+@pytest.mark.parametrize("decay", ["channel", "head"])
+def test_strongly_negative_retention_logits(decay):
+    """Retention logits a ~ U(-4, -1): log sigmoid(a) from -4.02 to -1.31 per token,
+    past the range of chunk-start factors; the producer/consumer kernel factors those
+    chunks per 16-row block."""
+    lengths = [45, 64, 130, 200]   # no single-token sequence (see the prefill strong-decay test)
+    print(f"prologue strongly negative logits {decay}", flush=True)
+    x = ki.make_prefill(H=3, d_k=128, d_v=128, dtype="bf16", gate="extreme", lengths=lengths,
+                        init_state_std=0.02, seed=73, device=DEV, decay=decay, raw=True)
+    o, fs = run_gpu(x, "coop", **ALL)
+    o_ref, s_ref = run_oracle(x, ALL)
+    compare_full(x, o, fs, o_ref, s_ref, f"strong logits {decay}")
+
+
 @pytest.mark.parametrize("kw", [dict(normalize_k=True), dict(beta_logit=True),
                                 dict(gate_logit=True)], ids=["norm_k", "beta_logit", "gate_logit"])
 @pytest.mark.parametrize("dtype,path", [("fp32", "fused"), ("bf16", "coop")])
