@@ -38,6 +38,9 @@
 //   they run on one XCD (ids are dealt round-robin to the 8 XCDs) and the ring slots
 //   they share stay in that XCD's L2.
 
+#include <cstdlib>
+#include <cstring>
+
 #include "kda_chunk.h"
 #include "kda_launch.h"
 #include "kda_tiles.h"
@@ -1332,8 +1335,24 @@ static hipError_t launch_wy_k(const PrefillArgs& a, hipStream_t stream) {
   void* params[] = {&arg};
   const void* kernel =
       reinterpret_cast<const void*>(&prefill_wy_kernel<DK, DV, VBW, DECAY, STATES>);
-  return hipLaunchCooperativeKernel(kernel, dim3(a.lanes * (a.NC + a.NP)), dim3(kThreads), params,
-                                    0, stream);
+  const int grid = a.lanes * (a.NC + a.NP);
+  // KDA_COOP_LAUNCH=plain: an ordinary dispatch of the same grid when the device holds
+  // all of it resident at once (for tools that mishandle cooperative dispatches).  The
+  // hand-off waits are bounded either way: a grid that were not resident would abort
+  // (NaN outputs, abort word set), never hang.
+  const char* mode = std::getenv("KDA_COOP_LAUNCH");
+  if (mode != nullptr && std::strcmp(mode, "plain") == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) == hipSuccess &&
+        grid <= cus * per_cu) {
+      hipLaunchKernelGGL((prefill_wy_kernel<DK, DV, VBW, DECAY, STATES>), dim3(grid),
+                         dim3(kThreads), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  return hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(kThreads), params, 0, stream);
 }
 
 template <int DK, int DV, int VBW>
