@@ -40,6 +40,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "kda_chunk.h"
 #include "kda_launch.h"
@@ -1191,6 +1192,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
 // the lane with the fewest chunks so far (ties: the lower lane), so that the lanes'
 // chunk streams come out nearly equal and the longest units start first.
 constexpr int kPlanMaxSeqs = 256, kPlanMaxUnits = 8192, kPlanMaxLanes = 64;
+
+// Minimum of v over the 64 lanes of the wave, returned to every lane: DPP steps within
+// each row of 16 lanes (shift right by 1, 2, 4, 8), then the row minima joined by the
+// row broadcasts of lanes 15 and 31; lane 63 ends with the total.  A lane whose DPP
+// source is out of its row, or whose row or bank is masked off, keeps the identity.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  auto step = [](uint32_t x, auto ctrl, auto row_mask) {
+    const uint32_t y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        static_cast<int>(0xffffffffu), static_cast<int>(x), decltype(ctrl)::value,
+        decltype(row_mask)::value, 0xf, false));
+    return x < y ? x : y;
+  };
+  v = step(v, std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xf>{});   // row_shr:1
+  v = step(v, std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xf>{});   // row_shr:2
+  v = step(v, std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xf>{});   // row_shr:4
+  v = step(v, std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{});   // row_shr:8
+  v = step(v, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{});   // row_bcast:15
+  v = step(v, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{});   // row_bcast:31
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
 __global__ __launch_bounds__(64) void coop_prep_kernel(PrefillArgs a, int flag0, int nflag) {
   int* words = reinterpret_cast<int*>(a.workspace);
   const int t = threadIdx.x;
@@ -1215,19 +1237,52 @@ __global__ __launch_bounds__(64) void coop_prep_kernel(PrefillArgs a, int flag0,
     order[r] = n;
   }
   __syncthreads();
+  __shared__ uint32_t skey[kPlanMaxLanes], sx[2];
   int load = 0, cnt = 0;   // lane t's chunks and units so far
   for (int r = 0; r < N; ++r) {
     const int n = order[r], c = nchs[n];
+    // The sequence's H units weigh the same.  When the H-th smallest lane key is still
+    // below the smallest load plus c (with its lane), the greedy rule gives them one
+    // each to the H least-loaded lanes in key order: head hh to the lane of rank hh.
+    if (H <= L) {
+      const uint32_t key = t < L ? (static_cast<uint32_t>(load) << 6) | t : 0xffffffffu;
+      if (t < L) skey[t] = key;
+      __syncthreads();
+      int rank = 0;
+      for (int j = 0; j < L; ++j) rank += skey[j] < key ? 1 : 0;
+      if (t < L && rank == 0) sx[0] = (static_cast<uint32_t>(load + c) << 6) | t;
+      if (t < L && rank == H - 1) sx[1] = key;
+      __syncthreads();
+      const bool bulk = sx[1] < sx[0];
+      if (bulk && t < L && rank < H) {
+        lane_of[n * H + rank] = static_cast<unsigned short>(t);
+        pos_of[n * H + rank] = static_cast<unsigned short>(cnt);
+        ++cnt;
+        load += c;
+      }
+      __syncthreads();   // skey and sx are rewritten for the next sequence
+      if (bulk) continue;
+    }
     for (int hh = 0; hh < H; ++hh) {
-      int key = t < L ? (load << 6) | t : 0x7fffffff;
-      for (int o = 32; o > 0; o >>= 1) key = min(key, __shfl_xor(key, o));
-      if (t == (key & 63)) {
+      const uint32_t key = wave_min_u32(t < L ? (static_cast<uint32_t>(load) << 6) | t : 0xffffffffu);
+      if (t == static_cast<int>(key & 63)) {
         lane_of[n * H + hh] = static_cast<unsigned short>(t);
         pos_of[n * H + hh] = static_cast<unsigned short>(cnt);
         ++cnt;
         load += c;
       }
     }
+  }
+  // every unit placed exactly once (the lanes' counts sum to U), else a round-robin plan
+  int placed = t < L ? cnt : 0;
+  for (int o = 32; o > 0; o >>= 1) placed += __shfl_xor(placed, o);
+  if (placed != U) {
+    cnt = t < L ? (U - t + L - 1) / L : 0;
+    for (int u = t; u < U; u += 64) {
+      lane_of[u] = static_cast<unsigned short>(u % L);
+      pos_of[u] = static_cast<unsigned short>(u / L);
+    }
+    __syncthreads();
   }
   // lane offsets: exclusive prefix of the unit counts
   int incl = t < L ? cnt : 0;

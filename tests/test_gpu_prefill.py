@@ -357,6 +357,36 @@ def test_lanes_many_units(kind):
             assert torch.equal(fs[n], x["initial_state"][n]), f"sequence {n}"
 
 
+@pytest.mark.parametrize("kind", sorted(LANE_LENGTHS))
+def test_lane_plan_is_longest_first_greedy(kind):
+    """The plan the kernel writes into the workspace (after a 256-byte header:
+    lane_off[lanes + 1], then the lanes' unit lists, int32) is the stated rule:
+    sequences by chunk count, longest first (ties: lower index), each of a sequence's
+    units to the lane with the fewest chunks so far (ties: lower lane).  Recomputed
+    here on the host and compared exactly; so every unit is in exactly one lane."""
+    lengths = LANE_LENGTHS[kind]
+    H, N = 4, len(LANE_LENGTHS[kind])
+    x = ki.make_prefill(H=H, d_k=128, d_v=128, dtype="bf16", lengths=lengths, seed=48, device=DEV)
+    L = kda.prefill_coop_lanes(torch.bfloat16, N, H, 128, 128)
+    U = N * H
+    assert 0 < L < U
+    nb = kda.workspace_bytes(torch.bfloat16, N, sum(lengths), H, 128, 128)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=x["cu_seqlens"], workspace=ws)
+    torch.cuda.synchronize()
+    plan = ws[256:256 + 4 * (L + 1 + U)].view(torch.int32).cpu().numpy()
+    nch = [(n + 63) // 64 for n in lengths]
+    load, lists = [0] * L, [[] for _ in range(L)]
+    for n in sorted(range(N), key=lambda m: (-nch[m], m)):
+        for h in range(H):
+            lane = min(range(L), key=lambda i: (load[i], i))
+            lists[lane].append(n * H + h)
+            load[lane] += nch[n]
+    off = np.cumsum([0] + [len(li) for li in lists])
+    assert np.array_equal(plan[:L + 1], off), "lane offsets"
+    assert np.array_equal(plan[L + 1:], np.concatenate([np.array(li, dtype=np.int64) for li in lists])), "unit lists"
+
+
 def test_lanes_bit_identical_to_one_unit_per_lane(monkeypatch):
     """The lane plan only changes which workgroups process a unit, not its arithmetic:
     o and final state equal, bit for bit, those of one unit per lane (the same
