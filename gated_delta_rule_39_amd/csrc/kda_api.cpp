@@ -71,8 +71,8 @@ int env_int(const char* name, int dflt) {
 // on the device from cu_seqlens (coop_prep_kernel), longest sequences first, and each
 // lane works through its units one after another.  This keeps every unit on the
 // producer/consumer kernel however many there are, and balances sequences of unequal
-// length.  Up to 256 sequences and 8192 units; KDA_COOP_LANES=0 disables it (tuning
-// only).
+// length.  Up to 256 sequences and 8192 units; KDA_COOP_LANES=0 disables it, =2 takes
+// it whenever the units outnumber the lanes (tuning only).
 constexpr int kLaneW = 7, kLaneMinW = 4;
 constexpr int kPlanMaxSeqs = 256, kPlanMaxUnits = 8192, kPlanMaxLanes = 64;
 struct CoopPlan {
@@ -92,8 +92,9 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t N, int32_t H, int32_t d_k, 
   const int lw = enp > 0 ? 2 + enp : kLaneW;
   int L = cus / lw < kPlanMaxLanes ? cus / lw : kPlanMaxLanes;
   L -= L % 8;
-  if (d_k == 128 && d_v == 128 && units > cus / kLaneMinW && units > L && L >= 8 &&
-      N <= kPlanMaxSeqs && units <= kPlanMaxUnits && env_int("KDA_COOP_LANES", 1) != 0) {
+  const int lanes_mode = env_int("KDA_COOP_LANES", 1);   // 0 off, 1 auto, 2 whenever units > L
+  if (d_k == 128 && d_v == 128 && (units > cus / kLaneMinW || lanes_mode == 2) && units > L &&
+      L >= 8 && N <= kPlanMaxSeqs && units <= kPlanMaxUnits && lanes_mode != 0) {
     p.NC = 2;
     p.NP = lw - 2;
     p.R = env_int("KDA_COOP_R", p.NP + 6);
