@@ -17,7 +17,8 @@ from typing import Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "_lib", "libkda.so")
+# KDA_LIB_PATH selects another build of the library (e.g. the host-sanitized copy)
+LIB_PATH = os.environ.get("KDA_LIB_PATH") or os.path.join(_PKG, "_lib", "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}

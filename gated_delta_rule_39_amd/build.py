@@ -1,9 +1,12 @@
 """Build libkda.so (the gfx950 HIP kernels plus the C ABI) in-tree with hipcc.
 
-    python -m gated_delta_rule_39_amd.build
+    python -m gated_delta_rule_39_amd.build [--asan]
 
 writes gated_delta_rule_39_amd/_lib/libkda.so.  Every translation unit is compiled
-for gfx950 only, with packed-fp32 instruction selection disabled.
+for gfx950 only, with packed-fp32 instruction selection disabled.  --asan writes a
+copy to _lib/asan/libkda.so whose host code (the C ABI, argument checks, plans,
+launches) is built with AddressSanitizer; the device code is the same.  It needs the
+sanitizer runtime preloaded into the loading process (tests/test_abi_asan.py).
 """
 
 from __future__ import annotations
@@ -40,9 +43,13 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the KDA library needs the ROCm toolchain to build")
 
 
-def _compile(hipcc: str, src: str, obj: str, verbose: bool):
+# host code only: each -fsanitize= right after -Xarch_host
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(hipcc: str, src: str, obj: str, verbose: bool, extra=()):
     lang = ["-x", "hip"]
-    cmd = [hipcc, *lang, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *lang, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,24 +58,30 @@ def _compile(hipcc: str, src: str, obj: str, verbose: bool):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libkda.so; returns the library path."""
+ASAN_LIB = os.path.join(OUT_DIR, "asan", "libkda.so")
+
+
+def build(verbose: bool = False, asan: bool = False) -> str:
+    """Compile every source and link libkda.so (asan: the host-sanitized copy);
+    returns the library path."""
     hipcc = _hipcc()
-    obj_dir = os.path.join(OUT_DIR, "obj")
+    lib = ASAN_LIB if asan else LIB
+    extra = ASAN_FLAGS if asan else []
+    obj_dir = os.path.join(os.path.dirname(lib), "obj")
     os.makedirs(obj_dir, exist_ok=True)
     objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        list(ex.map(lambda so: _compile(hipcc, so[0], so[1], verbose), zip(SOURCES, objs)))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs]
+        list(ex.map(lambda so: _compile(hipcc, so[0], so[1], verbose, extra), zip(SOURCES, objs)))
+    tmp = lib + ".tmp"
+    cmd = [hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *extra, "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"linking libkda.so failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, asan="--asan" in sys.argv))
