@@ -9,8 +9,8 @@ Sources (pages about the method):
 
 * "Kimi Delta Attention: The Linear Attention Behind Kimi K2 and Qwen3"
   (elsolitario.org), section "How Kimi Delta Attention works step by step": the
-  per-token cycle decay -> predict -> error scaled by beta -> correct -> read, its
-  ``kda_step`` listing and its flowchart.
+  per-token cycle decay -> predict -> error scaled by beta -> correct -> read (its
+  prose and flowchart; the order of the steps).
 * "Kimi Delta Attention Technical Deep Dive" (mohalkarushikesh.github.io),
   section "From attention to recurrent state" (delta rule and its
   forget-plus-write factorisation) and "Systems and implementation tradeoffs"

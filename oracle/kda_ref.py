@@ -1,9 +1,12 @@
 """fp64 token-by-token KDA recurrence (test infrastructure; see the package docstring).
 
-What is computed, per independent unit (one sequence, one head), following the
-per-token cycle of "Kimi Delta Attention: The Linear Attention Behind Kimi K2 and
-Qwen3", section "How Kimi Delta Attention works step by step" (prose, listing and
-flowchart):
+What is computed, per independent unit (one sequence, one head): the delta rule of
+"Kimi Delta Attention Technical Deep Dive", section "From attention to recurrent
+state" (the memory's prediction for the key, the write error against the value, a
+rank-1 correction along the key scaled by the write strength beta), with KDA's
+per-channel gate applied to the memory before the prediction, as the cycle of "Kimi
+Delta Attention: The Linear Attention Behind Kimi K2 and Qwen3", section "How Kimi
+Delta Attention works step by step", orders the steps (its prose and flowchart):
 
     S holds d_v rows and d_k columns and maps keys to values.
     For each token t, with alpha_t = exp(g_t) in (0, 1]^{d_k}:
