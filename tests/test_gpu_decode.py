@@ -42,11 +42,13 @@ def test_decode_bf16_small(d_k, d_v):
     _run_and_compare("bf16", 5, 3, d_k, d_v, steps=6, seed=22)
 
 
-@pytest.mark.parametrize("gate", ["strong", "edge"])
+@pytest.mark.parametrize("gate", ["strong", "edge", "extreme", "spiky"])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_decode_strong_decay(gate, dtype):
-    """Strong per-channel decay (|g| of 0.6 .. 1.25 per token, the per-chunk sums of
-    the prefill's strong-decay tests) over 70 steps."""
+    """Strong per-channel decay over 70 steps: |g| of 0.6 .. 1.25 per token (the
+    per-chunk sums of the prefill's strong-decay tests), 2 .. 4 ("extreme"), and near
+    resets of single channels ("spiky").  Decode multiplies the state by e^g directly,
+    so no decay is out of its range."""
     print(f"decode strong decay {gate} {dtype}", flush=True)
     d = ki.make_decode(N=6, H=4, d_k=128, d_v=128, steps=70, dtype=dtype, gate=gate, seed=26,
                        device=DEV)

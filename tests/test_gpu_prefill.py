@@ -387,6 +387,21 @@ def test_lane_plan_is_longest_first_greedy(kind):
     assert np.array_equal(plan[L + 1:], np.concatenate([np.array(li, dtype=np.int64) for li in lists])), "unit lists"
 
 
+@pytest.mark.parametrize("kind", ["one unit per lane", "lanes"])
+def test_plain_dispatch_equals_cooperative(kind, monkeypatch):
+    """KDA_COOP_LAUNCH=plain (the same grid as an ordinary dispatch, when the device
+    holds all of it resident) gives bit-for-bit the cooperative launch's results."""
+    lengths = [300, 64, 130, 0, 5, 190] if kind == "lanes" else [300, 64, 130]
+    H = 12 if kind == "lanes" else 4
+    x = ki.make_prefill(H=H, d_k=128, d_v=128, dtype="bf16", lengths=lengths,
+                        init_state_std=0.02, seed=52, device=DEV)
+    print(f"prefill plain dispatch, {kind}", flush=True)
+    o, fs = run_gpu(x, "coop")
+    monkeypatch.setenv("KDA_COOP_LAUNCH", "plain")
+    o1, fs1 = run_gpu(x, "coop")
+    assert torch.equal(o, o1) and torch.equal(fs, fs1)
+
+
 def test_lanes_bit_identical_to_one_unit_per_lane(monkeypatch):
     """The lane plan only changes which workgroups process a unit, not its arithmetic:
     o and final state equal, bit for bit, those of one unit per lane (the same
