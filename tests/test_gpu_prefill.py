@@ -357,6 +357,25 @@ def test_lanes_many_units(kind):
             assert torch.equal(fs[n], x["initial_state"][n]), f"sequence {n}"
 
 
+def test_lanes_at_plan_limits():
+    """The largest lane plan: 256 sequences x 32 heads = 8192 units -- 248 short
+    sequences of 0 .. 48 tokens (most units are one partial chunk, so lanes switch
+    units at nearly every chunk) and 8 of 150 .. 300 -- every unit and window against
+    the oracle."""
+    rng = np.random.default_rng(53)
+    lengths = [int(n) for n in rng.integers(0, 49, size=248)] + \
+              [int(n) for n in rng.integers(150, 301, size=8)]
+    lengths = [lengths[i] for i in rng.permutation(len(lengths))]
+    H = 32
+    assert 0 < kda.prefill_coop_lanes(torch.bfloat16, len(lengths), H, 128, 128) < len(lengths) * H
+    print(f"prefill lanes at the plan limits: N=256 H=32, {sum(lengths)} tokens", flush=True)
+    x = ki.make_prefill(H=H, d_k=128, d_v=128, dtype="bf16", lengths=lengths,
+                        init_state_std=0.02, seed=53, device=DEV)
+    o, fs = run_gpu(x, "coop")
+    o_ref, s_ref = run_oracle(x)
+    compare_full(x, o, fs, o_ref, s_ref, "lanes at the plan limits")
+
+
 @pytest.mark.parametrize("kind", sorted(LANE_LENGTHS))
 def test_lane_plan_is_longest_first_greedy(kind):
     """The plan the kernel writes into the workspace (after a 256-byte header:
