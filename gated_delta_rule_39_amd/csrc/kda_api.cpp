@@ -60,10 +60,10 @@ int env_int(const char* name, int dflt) {
 // Producer/consumer geometry: W = CUs / units workgroups per unit (all resident at
 // once, one per CU): NC consumers, each 4 waves owning d_v / (4 NC) value columns
 // (NC = 2 for d_v = 128 when W >= 6, else 1), and NP = min(W - NC, 5) producers
-// (measured: past five producers per unit the consumers set the pace); R = NP + 6
-// ring slots.  Needs bf16 inputs and W >= 2.  KDA_PREFILL_COOP=0 disables it;
-// KDA_COOP_NC / KDA_COOP_NP / KDA_COOP_R override the split and the ring depth
-// (tuning only).
+// (measured: past five producers per unit the consumers set the pace), and
+// ring_slots(NP) ring slots.  Needs bf16 inputs and W >= 2.  KDA_PREFILL_COOP=0
+// disables it; KDA_COOP_NC / KDA_COOP_NP / KDA_COOP_R override the split and the ring
+// depth (tuning only).
 // Lanes: with d_k = d_v = 128, when the units leave fewer than four workgroups each
 // (measured: a unit per set of four still beats two units one after another on seven),
 // the units are spread over lanes of seven workgroups (two consumers, five producers;
@@ -74,6 +74,14 @@ int env_int(const char* name, int dflt) {
 // length.  Up to 256 sequences and 8192 units; KDA_COOP_LANES=0 disables it, =2 takes
 // it whenever the units outnumber the lanes (tuning only).
 constexpr int kLaneW = 7, kLaneMinW = 4;
+// Ring slots per lane.  With five producers, 24 (same-box sweeps at T=65536, H=32, ms
+// per launch: R = 11 1.650, 16 1.600, 20 1.559, 24 1.537, 27 1.536, 32 1.538; B16 H32
+// T4096 1.702 at 11, 1.555 at 24; no decay 1.734 at 11, 1.546 at 20): the deeper
+// ring lets the producers run ahead through the consumers' jitter.  Fewer producers:
+// NP + 6 (B4 H16 T4096 at NP = 3: 9 and 14 slots measure the same).  Every default
+// plan on a 256-CU device stays within 64 MiB of workspace.
+constexpr int kDeepRing = 24;
+int ring_slots(int np) { return np >= 5 ? kDeepRing : np + 6; }
 constexpr int kPlanMaxSeqs = 256, kPlanMaxUnits = 8192, kPlanMaxLanes = 64;
 struct CoopPlan {
   int NC = 0, NP = 0, R = 0, lanes = 0;
@@ -97,7 +105,7 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t N, int32_t H, int32_t d_k, 
       L >= 8 && N <= kPlanMaxSeqs && units <= kPlanMaxUnits && lanes_mode != 0) {
     p.NC = 2;
     p.NP = lw - 2;
-    p.R = env_int("KDA_COOP_R", p.NP + 6);
+    p.R = env_int("KDA_COOP_R", ring_slots(p.NP));
     if (p.R < 3) p.R = 3;
     p.lanes = L;
     p.plan = true;
@@ -116,7 +124,7 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t N, int32_t H, int32_t d_k, 
   p.NP = np;
   // the split consumer releases chunk c's slot at the start of chunk c + 1, after it
   // has waited for chunk c + 2: three slots at least, or that wait never ends
-  p.R = env_int("KDA_COOP_R", np + 6);
+  p.R = env_int("KDA_COOP_R", ring_slots(np));
   if (p.R < 3) p.R = 3;
   p.lanes = static_cast<int>(units);
   return p;
@@ -340,7 +348,10 @@ BwdPlan bwd_plan(int32_t N, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v
   const int64_t units = static_cast<int64_t>(N) * H;
   b.states = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H * d_v * d_k * 2);
   b.tiles = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H) * kda::chain_tile_bytes(d_k);
-  const CoopPlan p = coop_plan(KDA_BF16, units, N, H, d_k, d_v, cu_count());
+  CoopPlan p = coop_plan(KDA_BF16, units, N, H, d_k, d_v, cu_count());
+  // the sweep keeps NP + 6 slots: the deeper forward ring measured no faster here
+  // (8.33-8.39 vs 8.40-8.42 ms per call at T=65536, H=32) and costs 30 MB more
+  if (p.ok()) p.R = env_int("KDA_COOP_R", p.NP + 6);
   if (p.ok() && d_k == 128 && d_v == 128 && p.NC == 2 && units <= (1 << 24)) {
     b.coop = p;
     b.ring = (coop_ws_bytes(p, d_k, d_v, units) + 255) & ~size_t(255);

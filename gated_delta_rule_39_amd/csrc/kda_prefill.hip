@@ -226,14 +226,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 // flags, never word 1), then per-unit flags ready[R], done[R], arrive, pad (int32),
 // then the ring slots.
 // With a lane plan, the header is followed by it: lane_off[lanes + 1], lane_units[units]
-// (int32), written by coop_prep_kernel.
+// and each lane's total chunk count lane_tot[lanes] (int32), written by coop_prep_kernel.
 constexpr size_t kWsHeader = 256;
 __host__ __device__ inline int coop_flag_words(int R) { return 2 * R + 2; }
 __host__ __device__ inline size_t coop_flags_bytes(int lanes, int R) {
   return (size_t(lanes) * coop_flag_words(R) * 4 + 255) & ~size_t(255);
 }
 __host__ __device__ inline size_t coop_plan_bytes(int lanes, int units, bool plan) {
-  return plan ? (size_t(lanes + 1 + units) * 4 + 255) & ~size_t(255) : 0;
+  return plan ? (size_t(2 * lanes + 1 + units) * 4 + 255) & ~size_t(255) : 0;
 }
 __device__ __forceinline__ size_t coop_plan_bytes(const PrefillArgs& a) {
   return coop_plan_bytes(a.lanes, a.units, a.lane_units != nullptr);
@@ -357,8 +357,9 @@ __device__ __forceinline__ void lane_unit(const PrefillArgs& a, int lid, int i, 
   u.nch = static_cast<int>((u.eos - u.bos + kChunk - 1) / kChunk);
   u.g0 = g0;
 }
-// Chunks in the lane's stream.
+// Chunks in the lane's stream (with a plan: the planner's total, after the unit lists).
 __device__ __forceinline__ int lane_total(const PrefillArgs& a, int lid) {
+  if (a.lane_units) return a.lane_units[a.units + lid];
   const int nu = lane_count(a, lid);
   int t = 0;
   LaneUnit u;
@@ -1278,10 +1279,13 @@ __global__ __launch_bounds__(64) void coop_prep_kernel(PrefillArgs a, int flag0,
   for (int o = 32; o > 0; o >>= 1) placed += __shfl_xor(placed, o);
   if (placed != U) {
     cnt = t < L ? (U - t + L - 1) / L : 0;
+    load = 0;
     for (int u = t; u < U; u += 64) {
       lane_of[u] = static_cast<unsigned short>(u % L);
       pos_of[u] = static_cast<unsigned short>(u / L);
     }
+    if (t < L)
+      for (int u = t; u < U; u += L) load += nchs[u / H];
     __syncthreads();
   }
   // lane offsets: exclusive prefix of the unit counts
@@ -1295,6 +1299,7 @@ __global__ __launch_bounds__(64) void coop_prep_kernel(PrefillArgs a, int flag0,
   __syncthreads();
   for (int i = t; i <= L; i += 64) off[i] = soff[i];
   for (int u = t; u < U; u += 64) list[soff[lane_of[u]] + pos_of[u]] = u;
+  if (t < L) list[U + t] = load;   // the lane's total chunks
 }
 
 // ====================================================================================

@@ -28,8 +28,8 @@ enum { KDA_ERR_SCRATCH = 7 };
  * makes no allocation of any kind.  Returns KDA_ERR_SCRATCH, launching nothing, when
  * the call needs more (kda_prefill_workspace_bytes() above the limit).  With the
  * default plans on a 256-CU device every call fits: at d_k = d_v = 128 the units
- * share at most 32 lanes whatever their number (about 25 MiB), and one unit per lane
- * needs at most about 56 MiB (d_k = 128, d_v = 64, 128 units).  When the fused kernel applies (fp32, or no
+ * share at most 32 lanes whatever their number (about 54 MiB), and one unit per lane
+ * needs at most about 63 MiB (d_k = 128, d_v = 64, 42 units).  When the fused kernel applies (fp32, or no
  * producer/consumer plan) it runs without scratch.  Every call on one
  * device shares that device's array: calls that overlap in time on one device (other
  * streams, other threads) race and give undefined results; calls ordered on one

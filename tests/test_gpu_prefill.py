@@ -379,7 +379,8 @@ def test_lanes_at_plan_limits():
 @pytest.mark.parametrize("kind", sorted(LANE_LENGTHS))
 def test_lane_plan_is_longest_first_greedy(kind):
     """The plan the kernel writes into the workspace (after a 256-byte header:
-    lane_off[lanes + 1], then the lanes' unit lists, int32) is the stated rule:
+    lane_off[lanes + 1], the lanes' unit lists, then each lane's chunk total, int32) is
+    the stated rule:
     sequences by chunk count, longest first (ties: lower index), each of a sequence's
     units to the lane with the fewest chunks so far (ties: lower lane).  Recomputed
     here on the host and compared exactly; so every unit is in exactly one lane."""
@@ -393,7 +394,7 @@ def test_lane_plan_is_longest_first_greedy(kind):
     ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
     kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=x["cu_seqlens"], workspace=ws)
     torch.cuda.synchronize()
-    plan = ws[256:256 + 4 * (L + 1 + U)].view(torch.int32).cpu().numpy()
+    plan = ws[256:256 + 4 * (2 * L + 1 + U)].view(torch.int32).cpu().numpy()
     nch = [(n + 63) // 64 for n in lengths]
     load, lists = [0] * L, [[] for _ in range(L)]
     for n in sorted(range(N), key=lambda m: (-nch[m], m)):
@@ -403,7 +404,9 @@ def test_lane_plan_is_longest_first_greedy(kind):
             load[lane] += nch[n]
     off = np.cumsum([0] + [len(li) for li in lists])
     assert np.array_equal(plan[:L + 1], off), "lane offsets"
-    assert np.array_equal(plan[L + 1:], np.concatenate([np.array(li, dtype=np.int64) for li in lists])), "unit lists"
+    assert np.array_equal(plan[L + 1:L + 1 + U],
+                          np.concatenate([np.array(li, dtype=np.int64) for li in lists])), "unit lists"
+    assert np.array_equal(plan[L + 1 + U:], np.array(load)), "lane totals"
 
 
 @pytest.mark.parametrize("kind", ["one unit per lane", "lanes"])
