@@ -88,8 +88,13 @@ struct CoopPlan {
   bool plan = false;   // lanes < units: a device plan spreads the units over the lanes
   bool ok() const { return NC > 0; }
 };
+// flags: the prologue flags of the call.  With any of them on, the producers also
+// normalise keys and turn logits into gates, and a sixth producer pays off where the
+// grid has room (same box, T=65536, H=32, all flags: 1.581 ms with six, 1.679 ms with
+// five; plain inputs: 1.616 against 1.548 ms, so five stay the default).  Neither the
+// workspace size nor the lane count depends on it.
 CoopPlan coop_plan(int dtype, int64_t units, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
-                   int cus) {
+                   int cus, int flags = 0) {
   CoopPlan p;
   if (dtype != KDA_BF16 || units <= 0 || env_int("KDA_PREFILL_COOP", 1) == 0) return p;
   // the producers read a chunk's inputs through buffer resources with 31-bit byte
@@ -105,6 +110,7 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t N, int32_t H, int32_t d_k, 
       L >= 8 && N <= kPlanMaxSeqs && units <= kPlanMaxUnits && lanes_mode != 0) {
     p.NC = 2;
     p.NP = lw - 2;
+    if (enp == 0 && flags != 0 && L * (kLaneW + 1) <= cus) p.NP = kLaneW - 1;
     p.R = env_int("KDA_COOP_R", ring_slots(p.NP));
     if (p.R < 3) p.R = 3;
     p.lanes = L;
@@ -117,7 +123,8 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t N, int32_t H, int32_t d_k, 
   int nc = (d_v == 128 && W >= 6) ? 2 : 1;
   const int enc = env_int("KDA_COOP_NC", 0);
   if (enc > 0 && d_v % (4 * enc) == 0 && (d_v / (4 * enc) == 16 || d_v / (4 * enc) == 32)) nc = enc;
-  int np = W - nc < 5 ? W - nc : 5;
+  const int max_np = flags != 0 ? 6 : 5;
+  int np = W - nc < max_np ? W - nc : max_np;
   if (enp > 0) np = enp;
   if (np < 1 || static_cast<int64_t>(units) * (nc + np) > cus) return p;
   p.NC = nc;
@@ -280,7 +287,7 @@ int kda_prefill_ex(int dtype, int decay, int flags, const void* q, const void* k
   a.decay = decay;
   a.flags = flags;
   const int cus = cu_count();
-  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cus);
+  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cus, flags);
   if (p.ok() && workspace != nullptr && workspace_bytes >= coop_ws_bytes(p, d_k, d_v, units)) {
     set_coop(a, p, workspace);
     if (kda::launch_prefill_coop(d_k, a, stream) == hipSuccess) return KDA_OK;
