@@ -496,15 +496,30 @@ struct WyProducer {
     unpack_pairs();
     if (flags & kNormK) normalise_keys();
     if constexpr (DECAY == 1) {
-      const float x = gr[0][0];
+      // one log-decay per (row, head): lane l holds row l's, turns it into the decay
+      // factor once (rows past the end: 1) and each thread reads the rows of its group
+      // from the lanes that hold them
+      float x = gr[0][0];
+      if (flags & kGateLogit) x = log_sigmoid_hw(x);
+      const int a = __builtin_bit_cast(int, lane < n ? exp_hw(x) : 1.f);
+      constexpr int GW = 64 / CG;   // row groups per wave
+      static_assert(64 % CG == 0, "row groups within a wave");
+      const int r0 = __builtin_amdgcn_readfirstlane(tid >> 6) * GW * RPG;
+      const int sub = lane / CG;
 #pragma unroll
       for (int i = 0; i < RPG; ++i) {
-        const float y = __shfl(x, rg * RPG + i);
-        gr[i] = f32x4{y, y, y, y};
+        int y = __builtin_amdgcn_readlane(a, r0 + i);
+#pragma unroll
+        for (int s = 1; s < GW; ++s) {
+          const int ys = __builtin_amdgcn_readlane(a, r0 + s * RPG + i);
+          y = sub == s ? ys : y;
+        }
+        const float f = __builtin_bit_cast(float, y);
+        gr[i] = f32x4{f, f, f, f};
       }
     }
     // retention logits to log-decays (no decay: alpha = 1 whatever the flag says)
-    if (DECAY != 2 && (flags & kGateLogit)) {
+    if (DECAY == 0 && (flags & kGateLogit)) {
 #pragma unroll
       for (int i = 0; i < RPG; ++i) gr[i] = log_sigmoid4(gr[i]);
     }
@@ -518,7 +533,7 @@ struct WyProducer {
 #pragma unroll
       for (int i = 0; i < RPG; ++i)
         if (rg * RPG + i >= n) {
-          gr[i] = z;
+          if constexpr (DECAY != 1) gr[i] = z;
           kr[i] = zb;
           qr[i] = zb;
         }
@@ -526,12 +541,15 @@ struct WyProducer {
       for (int i = 0; i < RPGV; ++i)
         if (rgv * RPGV + i >= n) vr[i] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
-    // alpha = e^g in place; per-thread product of its rows
+    // alpha = e^g in place (one per row and head: already done); per-thread product
+    // of its rows
     f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
-      const f32x4 gg = gr[i];
-      gr[i] = f32x4{exp_hw(gg[0]), exp_hw(gg[1]), exp_hw(gg[2]), exp_hw(gg[3])};
+      if constexpr (DECAY != 1) {
+        const f32x4 gg = gr[i];
+        gr[i] = f32x4{exp_hw(gg[0]), exp_hw(gg[1]), exp_hw(gg[2]), exp_hw(gg[3])};
+      }
       tot *= gr[i];
     }
     store4(sScr + rg * DK + j0, tot);
