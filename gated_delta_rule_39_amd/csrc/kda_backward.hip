@@ -740,12 +740,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
     const int j = 16 * kb + lr;
     const float egn = cp.sEgn[j];
     float gn = 0.f;
+    // this lane's four rows of column j, one transposing read per tile
+    const bf16x4 k4 = read_tr4(sK, LDK, 16 * wave + 4 * lq + (lr >> 2), 16 * kb + 4 * (lr & 3));
+    const bf16x4 q4 = read_tr4(sQ, LDK, 16 * wave + 4 * lq + (lr >> 2), 16 * kb + 4 * (lr & 3));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * wave + 4 * lq + i;
-      float kf = static_cast<float>(sK[r * LDK + j]);
+      float kf = static_cast<float>(k4[i]);
       if (norm_k) kf = static_cast<float>(static_cast<bf16>(kf * rn[i]));
-      const float qf = static_cast<float>(sQ[r * LDK + j]);
+      const float qf = static_cast<float>(q4[i]);
       const float eg = cp.sEG[r * LDEG + j];
       const float ieg = __builtin_amdgcn_rcpf(eg);
       const float eh = egn * ieg;   // e^{G_n - G_r}
@@ -840,22 +843,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   // LDS tile in area 1 (free once the dq, dk rows have left) and leave as 16-byte pieces.
   float* sDG = reinterpret_cast<float*>(smem + GL::a1);
   constexpr int LDG = GL::LDG;
-  if constexpr (DECAY == 0) lds_barrier();
   if constexpr (DECAY != 2) {
+    // What every row of token block w adds to its own suffix sum, once per key column:
+    // dG_n (the d e^{G_n} and dKh Kh partials of all waves) plus the column totals of
+    // the token blocks after w.  Row w of the reduction scratch takes it (one thread per
+    // column reads and writes only that column).
+    if (tid < DK) {
+      const int j = tid;
+      float base = (sRed[8 * DK + j] + sRed[9 * DK + j] + sRed[10 * DK + j] + sRed[11 * DK + j]) *
+                   cp.sEgn[j];
+      base += sRed[4 * DK + j] + sRed[5 * DK + j] + sRed[6 * DK + j] + sRed[7 * DK + j];
+      const float t1 = sRed[DK + j], t2 = sRed[2 * DK + j], t3 = sRed[3 * DK + j];
+      sRed[3 * DK + j] = base;
+      sRed[2 * DK + j] = base + t3;
+      sRed[DK + j] = base + t3 + t2;
+      sRed[j] = base + t3 + t2 + t1;
+    }
+    lds_barrier();
     const bool gate_logit = (a.flags & kGateLogit) != 0;
     f32x4 rows = f32x4{0.f, 0.f, 0.f, 0.f};   // one scalar decay: sums over the channels
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int j = 16 * kb + lr;
-      float dd = 0.f;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) dd += sRed[(8 + p) * DK + j];
-      float add = dd * cp.sEgn[j];
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        add += sRed[(4 + w2) * DK + j];
-        if (w2 > wave) add += sRed[w2 * DK + j];
-      }
+      const float add = sRed[wave * DK + j];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float v = gm[kb][i] + add;
