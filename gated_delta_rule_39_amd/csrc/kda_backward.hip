@@ -338,8 +338,8 @@ struct GradLayout {
   static constexpr int LDK = CL::LDK, LDC = CL::LDC;
   static constexpr int LDEG = ChunkProducer<bf16, DK, false>::LDEG;
   static constexpr int VS = 32;                                   // value slice
-  static constexpr size_t oEG = CL::kBytes;                       // fp32 e^{G} [64][LDEG]
-  static constexpr size_t kBytes = CL::al(oEG + size_t(kChunk) * LDEG * 4);
+  static constexpr size_t oEG = CL::kBytes;                       // fp32 e^{G} [DK][LDEG]
+  static constexpr size_t kBytes = CL::al(oEG + size_t(DK) * LDEG * 4);
   static constexpr size_t kLds = 160 * 1024;
   // area 1: A and the fp32 inverse (dead after the inverse); area 2: the rest of LDS
   static constexpr size_t a1 = CL::oA, a1end = CL::oScr;
@@ -459,6 +459,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   f32x4 dbu = f32x4{0.f, 0.f, 0.f, 0.f};   // sum_v d(beta V) V for this lane's rows
   float ddk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // d e^{G_n} of this thread's keys
 
+  // e^{G_n} of this thread's eight keys: the same eight in each of its slice pieces
+  static_assert(kThreads % (DK / 8) == 0, "one key octet per thread");
+  float egk[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) egk[e] = cp.sEgn[8 * (tid % (DK / 8)) + e];
+
   for (int vs = 0; vs < DV / VS; ++vs) {
     const int v0 = vs * VS;
     // H, dH' (and P = D dH') slices [VS][DK]; V and dO slices [64][VS]; d e^{G_n} partial
@@ -473,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float dh = static_cast<float>(pdh[i][e]);
-        p[e] = static_cast<bf16>(dh * cp.sEgn[c8 + e]);
+        p[e] = static_cast<bf16>(dh * egk[e]);
         ddk[e] += dh * static_cast<float>(ph[i][e]);
       }
       *reinterpret_cast<bf16x8*>(sP + r * LDK + c8) = p;
@@ -740,16 +746,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
     const int j = 16 * kb + lr;
     const float egn = cp.sEgn[j];
     float gn = 0.f;
-    // this lane's four rows of column j, one transposing read per tile
+    // this lane's four rows of column j: one transposing read per bf16 tile, one read
+    // of the key-major e^{G} tile
     const bf16x4 k4 = read_tr4(sK, LDK, 16 * wave + 4 * lq + (lr >> 2), 16 * kb + 4 * (lr & 3));
     const bf16x4 q4 = read_tr4(sQ, LDK, 16 * wave + 4 * lq + (lr >> 2), 16 * kb + 4 * (lr & 3));
+    const f32x4 eg4 = *reinterpret_cast<const f32x4*>(cp.sEG + CP::eg_at(j, 16 * wave + 4 * lq));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * wave + 4 * lq + i;
       float kf = static_cast<float>(k4[i]);
       if (norm_k) kf = static_cast<float>(static_cast<bf16>(kf * rn[i]));
       const float qf = static_cast<float>(q4[i]);
-      const float eg = cp.sEG[r * LDEG + j];
+      const float eg = eg4[i];
       const float ieg = __builtin_amdgcn_rcpf(eg);
       const float eh = egn * ieg;   // e^{G_n - G_r}
       const float dkg = bt[i] * dBk[kb][i];

@@ -218,13 +218,23 @@ struct ChunkProducer {
   using TC = typename M::TC;
   using raw4 = typename M::raw4;
   using L = ChunkLayout<Tin, DK, KIT>;
-  static constexpr int LDEG = DK + 4;   // row stride of the optional fp32 e^{G} tile
+  // The optional fp32 e^{G} tile is key-major, [DK][LDEG]: a key's 64 rows are
+  // contiguous, in 16 groups of four rows, and group gr of key j sits at position
+  // (gr ^ j ^ (j >> 2)) mod 16.  Four consecutive rows of one key are one 16-byte read.
+  // j ^ (j >> 2) takes 16 distinct values over 16 consecutive keys (the readers: keys
+  // 16b .. 16b + 15) and over keys 4L + c, L = 0 .. 15 (the writers' keys), so neither
+  // side's 16 lanes meet in a bank group.
+  static constexpr int LDEG = kChunk;
+  static_assert(kChunk == 64, "16 row groups per key");
+  __device__ __forceinline__ static int eg_at(int key, int row4) {   // row4: multiple of 4
+    return key * LDEG + ((((row4 >> 2) ^ key ^ (key >> 2)) & 15) << 2);
+  }
   static constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF, LDX = L::LDX;
   static constexpr int CG = L::CG, RG = L::RG, RPG = L::RPG;
 
   TC *sKg, *sQg, *sKi, *sKiT, *sTm, *sM;
   float *sA, *sX, *sScr, *sBeta, *sEgn;
-  float* sEG = nullptr;     // fp32 e^{G_r} tile [64][LDEG] (factors<DECAY, true> only)
+  float* sEG = nullptr;     // fp32 e^{G_r} tile [DK][LDEG] (factors<DECAY, true> only)
   const float* g;
   const Tin* k;
   const Tin* q;
@@ -323,7 +333,7 @@ struct ChunkProducer {
     }
   }
 
-  // KEEP_EG: also write e^{G_r} (fp32) into sEG.
+  // KEEP_EG: also write e^{G_r} (fp32) into sEG, key-major.
   template <int DECAY, bool KEEP_EG = false>
   __device__ __forceinline__ void factors(int n, bool has_next, int64_t c1, int n1) {
     if (flags & kNormK) normalise_keys();
@@ -366,6 +376,7 @@ struct ChunkProducer {
     const f32x4 egn = cp * tot * cs;                              // e^{G_n}
     // forward pass: e^{G_r} = cp * alpha_{first} ... alpha_r  ->  Kg, Qg
     f32x4 run = cp;
+    [[maybe_unused]] f32x4 egr[RPG];
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const bool ok = rg * RPG + i < n;
@@ -374,7 +385,17 @@ struct ChunkProducer {
       const f32x4 q4 = ok ? widen(qr[i]) * scale : f32x4{0.f, 0.f, 0.f, 0.f};
       store4(sKg + (rg * RPG + i) * LDK + j0, k4 * run);
       store4(sQg + (rg * RPG + i) * LDK + j0, q4 * run);
-      if constexpr (KEEP_EG) *reinterpret_cast<f32x4*>(sEG + (rg * RPG + i) * LDEG + j0) = run;
+      if constexpr (KEEP_EG) egr[i] = run;
+    }
+    if constexpr (KEEP_EG) {
+      // this thread's rows of each of its four keys: RPG consecutive floats per key
+      static_assert(RPG % 4 == 0, "whole 16-byte pieces per key");
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < RPG; i += 4)
+          *reinterpret_cast<f32x4*>(sEG + eg_at(j0 + c, rg * RPG + i)) =
+              f32x4{egr[i][c], egr[i + 1][c], egr[i + 2][c], egr[i + 3][c]};
     }
     // backward pass: e^{-G_r} = (alpha_{r+1} ... alpha_n) / e^{G_n}  ->  Ki, Ki^T
     run = cs * f32x4{__builtin_amdgcn_rcpf(egn[0]), __builtin_amdgcn_rcpf(egn[1]),
