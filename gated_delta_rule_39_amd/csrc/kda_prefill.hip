@@ -561,24 +561,32 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     const int uh = cu.h;
     [[maybe_unused]] const int64_t sbase =                       // chunk g's state slot (STATES)
         STATES ? chunk_slot_base(cu.n_seq, cu.bos) - cu.g0 : 0;
+    // STATES: the state at the start of chunk g as bf16 into its slot (non-temporal, as
+    // every checkpoint and tile store: read only by later kernels).  Issued after the
+    // chunk's operand requests: loads complete in issue order, so a store issued before
+    // them would make the next chunk wait for its write to memory as well.  With `keep`
+    // false the buffer range is empty and the stores are dropped, so every chunk issues
+    // the same instructions.
+    [[maybe_unused]] auto store_ckpt = [&](int gg, bool keep) {
+      const __amdgpu_buffer_rsrc_t ck = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<bf16*>(a.chunk_states) + ((sbase + (keep ? gg : cu.g0)) * a.H + uh) * DV * DK, 0,
+          keep ? DV * DK * 2 : 0, 0x00020000);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+          const f32x4 x = S[b][vt];
+          const bf16x4 y = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]),
+                                  static_cast<bf16>(x[2]), static_cast<bf16>(x[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(
+              __builtin_bit_cast(u32x2, y), ck,
+              ((v0 + 16 * vt + lr) * DK + 32 * wave + 16 * b + 4 * lq) * 2, 0, kNonTemporal);
+        }
+    };
+    if constexpr (STATES) store_ckpt(cu.g0, true);   // the unit's initial state
     for (; ok && g < uend; ++g) {
       const int64_t c0 = cbase + int64_t(g) * kChunk;
       const bool has_next = g + 1 < total, has2 = g + 2 < total;
-      if constexpr (STATES) {
-        bf16* cs = static_cast<bf16*>(a.chunk_states) + ((sbase + g) * a.H + uh) * DV * DK;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int vt = 0; vt < NVT; ++vt) {
-            const f32x4 x = S[b][vt];
-            // non-temporal, as every checkpoint and tile store: read only by later kernels
-            __builtin_nontemporal_store(
-                bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
-                       static_cast<bf16>(x[3])},
-                reinterpret_cast<bf16x4*>(cs + int64_t(v0 + 16 * vt + lr) * DK + 32 * wave + 16 * b +
-                                          4 * lq));
-          }
-      }
       // every wave has used chunk g - 1's operands: its slot is free
       if (tid == 0 && g > 0) __hip_atomic_fetch_add(done + sp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       int fv = 0;
@@ -666,6 +674,8 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
             bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
                    static_cast<bf16>(x[3])};
       }
+      // S^T is now the state at the start of chunk g + 1 (none after the unit's last)
+      if constexpr (STATES) store_ckpt(g + 1, g + 1 < uend);
 
       if (tid == 0)
         cFlag[g & 1] = !has2 ? 1
