@@ -638,8 +638,6 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) eb[t][vt] = eb_at(t, vt);
-      // the previous chunk's output rows, from this wave's LDS rows
-      if (g > 0 && write_o) store_rows(pc0, prows, ph);
       // O = Qg S^T + M E (token block w reads E blocks <= w: K step 1 only for w >= 2)
 #pragma unroll
       for (int j = 0; j < KS; ++j)
@@ -661,6 +659,10 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 #pragma unroll
           for (int vt = 0; vt < NVT; ++vt) S[b][vt] = mma_bf16(KDf[b][t], eb[t][vt], S[b][vt]);
       load_kd(nslot);
+      // the previous chunk's output rows, from this wave's LDS rows (after the operand
+      // requests: stores complete in order with the loads, and the next chunk waits
+      // for those)
+      if (g > 0 && write_o) store_rows(pc0, prows, ph);
       // this chunk's o window
       pc0 = c0;
       prows = static_cast<int>(min(ueos - c0, static_cast<int64_t>(kChunk)));
