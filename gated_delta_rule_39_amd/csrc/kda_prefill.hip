@@ -587,8 +587,6 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     for (; ok && g < uend; ++g) {
       const int64_t c0 = cbase + int64_t(g) * kChunk;
       const bool has_next = g + 1 < total, has2 = g + 2 < total;
-      // every wave has used chunk g - 1's operands: its slot is free
-      if (tid == 0 && g > 0) __hip_atomic_fetch_add(done + sp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       int fv = 0;
       if (tid == 0 && has2)
         fv = __hip_atomic_load(ready + s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -663,6 +661,9 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       // requests: stores complete in order with the loads, and the next chunk waits
       // for those)
       if (g > 0 && write_o) store_rows(pc0, prows, ph);
+      // every wave has used chunk g - 1's operands (at the last barrier): its slot is
+      // free.  Released here, after the operand requests, for the same reason.
+      if (tid == 0 && g > 0) __hip_atomic_fetch_add(done + sp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // this chunk's o window
       pc0 = c0;
       prows = static_cast<int>(min(ueos - c0, static_cast<int64_t>(kChunk)));
