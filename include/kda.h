@@ -130,6 +130,12 @@ const char* kda_status_string(int status);
  *   stale values that look valid.  The second int32 is sticky: an aborted call sets
  *   it to 1 and no call clears it, so a caller that zeroes it once can check many
  *   calls with one read.
+ *   Launch: the producer/consumer grid is a cooperative launch, whose workgroups are
+ *   all resident at once.  With the environment variable KDA_COOP_LAUNCH=plain it is
+ *   an ordinary dispatch of the same grid when the device can hold all of it at
+ *   once (about 20 us less per call); the hand-off waits are bounded either way, so
+ *   a grid that were not fully resident (another such grid in flight on another
+ *   stream) aborts as above rather than hanging.
  */
 int kda_prefill(int dtype,
                 const void* q, const void* k, const void* v,
