@@ -1,12 +1,15 @@
 """Build libkda.so (the gfx950 HIP kernels plus the C ABI) in-tree with hipcc.
 
-    python -m gated_delta_rule_39_amd.build [--asan]
+    python -m gated_delta_rule_39_amd.build [--asan | --phases]
 
 writes gated_delta_rule_39_amd/_lib/libkda.so.  Every translation unit is compiled
 for gfx950 only, with packed-fp32 instruction selection disabled.  --asan writes a
 copy to _lib/asan/libkda.so whose host code (the C ABI, argument checks, plans,
 launches) is built with AddressSanitizer; the device code is the same.  It needs the
 sanitizer runtime preloaded into the loading process (tests/test_abi_asan.py).
+--phases writes a timing build to _lib/phase/libkda.so: the same kernels with
+-DKDA_PHASE_STAMPS, whose producer/consumer workgroups record per-phase s_memtime
+sums (read by `bench.py --phases`).  The product library never contains them.
 """
 
 from __future__ import annotations
@@ -59,14 +62,17 @@ def _compile(hipcc: str, src: str, obj: str, verbose: bool, extra=()):
 
 
 ASAN_LIB = os.path.join(OUT_DIR, "asan", "libkda.so")
+PHASE_LIB = os.path.join(OUT_DIR, "phase", "libkda.so")
 
 
-def build(verbose: bool = False, asan: bool = False) -> str:
-    """Compile every source and link libkda.so (asan: the host-sanitized copy);
-    returns the library path."""
+def build(verbose: bool = False, asan: bool = False, phases: bool = False) -> str:
+    """Compile every source and link libkda.so (asan: the host-sanitized copy;
+    phases: the timing build with phase stamps); returns the library path."""
+    if asan and phases:
+        raise ValueError("one variant at a time")
     hipcc = _hipcc()
-    lib = ASAN_LIB if asan else LIB
-    extra = ASAN_FLAGS if asan else []
+    lib = ASAN_LIB if asan else PHASE_LIB if phases else LIB
+    extra = ASAN_FLAGS if asan else ["-DKDA_PHASE_STAMPS"] if phases else []
     obj_dir = os.path.join(os.path.dirname(lib), "obj")
     os.makedirs(obj_dir, exist_ok=True)
     objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
@@ -84,4 +90,5 @@ def build(verbose: bool = False, asan: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, asan="--asan" in sys.argv))
+    print(build(verbose="-v" in sys.argv, asan="--asan" in sys.argv,
+                phases="--phases" in sys.argv))

@@ -257,6 +257,40 @@ __device__ __forceinline__ void raise_abort(int* abort_word) {
   __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- phase clock (only in a build with -DKDA_PHASE_STAMPS) ---------------------------
+// Each producer/consumer workgroup sums s_memtime ticks per phase of its chunk loop (the
+// phases are the stretches between mark(i - 1) and mark(i)) and writes the sums, its
+// chunk count and its role when it leaves; kda_phase_read() copies them out.  The
+// product build compiles none of it (KDA_PHASE expands to nothing).
+#if defined(KDA_PHASE_STAMPS)
+constexpr int kPhaseWgs = 4096, kPhaseWords = 16;
+__device__ unsigned int g_phase[kPhaseWgs * kPhaseWords];
+struct PhaseClock {
+  unsigned long long t[10];
+  unsigned acc[10];
+  int chunks;
+  __device__ __forceinline__ void start() {
+    for (int i = 0; i < 10; ++i) acc[i] = 0;
+    chunks = 0;
+  }
+  __device__ __forceinline__ void mark(int i) { t[i] = __builtin_amdgcn_s_memtime(); }
+  __device__ __forceinline__ void close(int n) {
+    for (int i = 1; i < n; ++i) acc[i] += static_cast<unsigned>(t[i] - t[i - 1]);
+    ++chunks;
+  }
+  __device__ __forceinline__ void write(int tid, int role) const {
+    if (tid != 0 || blockIdx.x >= kPhaseWgs) return;
+    unsigned int* w = g_phase + blockIdx.x * kPhaseWords;
+    for (int i = 0; i < 10; ++i) w[i] = acc[i];
+    w[14] = static_cast<unsigned>(chunks);
+    w[15] = static_cast<unsigned>(role);
+  }
+};
+#define KDA_PHASE(...) __VA_ARGS__
+#else
+#define KDA_PHASE(...)
+#endif
+
 // Wait (one lane) until *p >= target.  False if the wait ran out or the grid aborted;
 // a wait that runs out raises the abort word.
 __device__ __forceinline__ bool wait_at_least(const int* p, int target, int* abort_word) {
@@ -551,6 +585,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   int64_t pc0 = 0;
   int prows = 0, ph = 0, punit = -1;
   int g = 0;
+  KDA_PHASE(PhaseClock phc; phc.start();)
   // Outer loop: the lane's units with chunks; inner loop: the chunks of one unit.  The
   // unit's bounds are fixed over the inner loop, and everything that moves to the next
   // unit lives outside it, so the per-chunk path carries no lane bookkeeping.
@@ -585,6 +620,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     };
     if constexpr (STATES) store_ckpt(cu.g0, true);   // the unit's initial state
     for (; ok && g < uend; ++g) {
+      KDA_PHASE(phc.mark(0);)
       const int64_t c0 = cbase + int64_t(g) * kChunk;
       const bool has_next = g + 1 < total, has2 = g + 2 < total;
       int fv = 0;
@@ -616,6 +652,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       for (int j = 0; j < KS; ++j)
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) E[vt] = mma_bf16(Wf[j], sb[j][vt], E[vt]);
+      KDA_PHASE(phc.mark(1);)
       load_w(nslot);
       // this wave's E rows into its half of the E operand fragments
 #pragma unroll
@@ -631,6 +668,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) S[b][vt] *= eg[b];
       lds_barrier();
+      KDA_PHASE(phc.mark(2);)
       bf16x8 eb[2][NVT];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -649,6 +687,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
         for (int vt = 0; vt < NVT; ++vt) Ot[vt] = mma_bf16(eb[1][vt], Mf[1], Ot[vt]);
       }
       load_m(nslot);
+      KDA_PHASE(phc.mark(3);)
       // S^T += KD^T E for this wave's keys
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -656,6 +695,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int vt = 0; vt < NVT; ++vt) S[b][vt] = mma_bf16(KDf[b][t], eb[t][vt], S[b][vt]);
+      KDA_PHASE(phc.mark(4);)
       load_kd(nslot);
       // the previous chunk's output rows, from this wave's LDS rows (after the operand
       // requests: stores complete in order with the loads, and the next chunk waits
@@ -683,7 +723,9 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       if (tid == 0)
         cFlag[g & 1] = !has2 ? 1
                              : ((fv >= g + 3 || wait_at_least(ready + s2, g + 3, abort_word)) ? 1 : 0);
+      KDA_PHASE(phc.mark(5);)
       lds_barrier();
+      KDA_PHASE(phc.mark(6); phc.close(7);)
       ok = has_next ? nok : true;
       nok = cFlag[g & 1] != 0;
       sp = s0;
@@ -707,6 +749,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     lds_barrier();
   }
 
+  KDA_PHASE(phc.write(tid, role);)
   // the last chunk's output rows (written before the loop's last barrier)
   if (ok && total > 0 && write_o) store_rows(pc0, prows, ph);
   // units after the last one with chunks: empty, they keep their initial state
@@ -867,7 +910,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
     pr.template load<DECAY, !STATES>(c0, n, xh);
     // ring slot of chunk g and the releases it needs: g mod R, NC * (g div R)
     int s = p % a.R, need = a.NC * (p / a.R);
+    KDA_PHASE(PhaseClock phc; phc.start();)
     for (int g = p; g < total; g += a.NP) {
+      KDA_PHASE(phc.mark(0);)
       const int gn = g + a.NP;
       const bool has_next = gn < total;
       if (has_next) seek(gn);
@@ -878,9 +923,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       int dv = 0;
       if (tid == 0) dv = __hip_atomic_load(done + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       pr.template factors<DECAY, STATES>(n, g + 1);
+      KDA_PHASE(phc.mark(1);)
       if (tid == 0) pFlag[0] = (dv >= need || wait_at_least(done + s, need, abort_word)) ? 1 : 0;
       lds_barrier();
       if (pFlag[0] == 0) break;
+      KDA_PHASE(phc.mark(2);)
       const uint32_t slot = static_cast<uint32_t>(s) * SL::kBytes;
       // STATES: this chunk's tiles for the backward's reverse chain
       [[maybe_unused]] unsigned char* tiles = nullptr;
@@ -902,17 +949,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
         pr.products(rr, slot);
       pr.template load_slice<DECAY, RPG / 2, RPG, !STATES>(cl, nl, hl);          // g, second half
       lds_barrier();
+      KDA_PHASE(phc.mark(3);)
       pr.template load_slice<DECAY, PR::kSK, PR::kSQ, !STATES>(cl, nl, hl);      // k
       pr.template load_slice<DECAY, PR::kSV, PR::kSB, !STATES>(cl, nl, hl);      // v
       pr.inverse_blocks();
       lds_barrier();
+      KDA_PHASE(phc.mark(4);)
       // waves 0, 1 merge the diagonal pairs; the Qg / KD^T fragments are spread over
       // all four waves
       if (wave < 2) pr.inverse_pairs();
       pr.template publish_qk<0, 4>(rr, slot);
       pr.template load_slice<DECAY, PR::kSQ, PR::kSV, !STATES>(cl, nl, hl);      // q
       lds_barrier();
+      KDA_PHASE(phc.mark(5);)
       pr.inverse_rest();
+      KDA_PHASE(phc.mark(6);)
       if constexpr (STATES) {
         // -W rows staged in the A area (dead after the inverse) for the transposed copy
         static_assert(size_t(kChunk) * PL::LDK * 2 <= PL::oX - PL::oA, "-W staging fits");
@@ -923,9 +974,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
       } else {
         pr.publish_wu(rr, slot);
       }
+      KDA_PHASE(phc.mark(7);)
       // every slot store of the workgroup acknowledged (device-visible), then publish
       vm_barrier();
       if (tid == 0) __hip_atomic_store(ready + s, g + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      KDA_PHASE(phc.mark(8); phc.close(9);)
       c0 = c1;
       n = n1;
       ch = xh;
@@ -936,6 +989,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wy_kernel(PrefillArgs a) 
         need += a.NC;
       }
     }
+    KDA_PHASE(phc.write(tid, 100 + p);)
     return;
   }
 
@@ -1457,3 +1511,27 @@ hipError_t launch_prefill_coop_states(const PrefillArgs& a, hipStream_t stream) 
 }
 
 }  // namespace kda
+
+#if defined(KDA_PHASE_STAMPS)
+// Phase sums of the producer/consumer launches since the last kda_phase_clear(), one row
+// of kPhaseWords words per workgroup id: words 1..9 ticks per phase, 14 the chunk count,
+// 15 the role (consumer index, or 100 + producer index).  Only in a build with
+// -DKDA_PHASE_STAMPS (a timing build, not the product).
+namespace {
+__global__ void phase_clear_kernel() {
+  for (int i = threadIdx.x; i < kda::kPhaseWgs * kda::kPhaseWords; i += blockDim.x)
+    kda::g_phase[i] = 0;
+}
+}  // namespace
+extern "C" int kda_phase_words(void) { return kda::kPhaseWgs * kda::kPhaseWords; }
+extern "C" int kda_phase_clear(void) {
+  hipLaunchKernelGGL(phase_clear_kernel, dim3(1), dim3(256), 0, 0);
+  return hipDeviceSynchronize() == hipSuccess ? 0 : 1;
+}
+extern "C" int kda_phase_read(unsigned int* host) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(kda::g_phase),
+                             sizeof(unsigned int) * kda::kPhaseWgs * kda::kPhaseWords) == hipSuccess
+             ? 0
+             : 1;
+}
+#endif

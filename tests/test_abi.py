@@ -38,6 +38,24 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, name), f"{name} declared in kda.h but not exported"
 
 
+def test_phase_stamps_only_in_the_timing_build():
+    """The per-phase s_memtime stamps exist only in the timing build
+    (_lib/phase/libkda.so, `python -m gated_delta_rule_39_amd.build --phases`): the
+    product library exports no kda_phase_* function, the timing build (when built)
+    exports all three."""
+    names = ("kda_phase_read", "kda_phase_clear", "kda_phase_words")
+    L = kda.lib()
+    for name in names:
+        assert not hasattr(L, name), f"{name} in the product library"
+    from gated_delta_rule_39_amd import build as kbuild
+    if os.path.exists(kbuild.PHASE_LIB):
+        P = ctypes.CDLL(kbuild.PHASE_LIB)
+        for name in names:
+            assert hasattr(P, name), f"{name} missing from the timing build"
+        P.kda_phase_words.restype = ctypes.c_int
+        assert P.kda_phase_words() == 4096 * 16
+
+
 def test_version_and_status_strings():
     L = kda.lib()
     assert L.kda_abi_version() == 4
