@@ -332,6 +332,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chain_kernel(BwdArgs a) {
 // Chunk-parallel gradients
 // ====================================================================================
 
+#if defined(KDA_PHASE_STAMPS)
+// Timing build only: per (chunk, head) item, the s_memtime ticks of the gradient
+// kernel's phases (words 1..8: loads and factors, A and M, inverse, value slices,
+// chunk-local algebra, k/q deposit, per-element gradients, dq/dk/dg output; words 10..13
+// the value slices' staging, R'/dE, E/dv and d_v contractions summed over slices; word
+// 15 = 1 for a written row), read with kda_grad_phase_read().
+constexpr int kGradPhaseItems = 40000, kGradPhaseWords = 16;
+__device__ unsigned int g_grad_phase[kGradPhaseItems * kGradPhaseWords];
+#endif
+
 template <int DK>
 struct GradLayout {
   using CL = ChunkLayout<bf16, DK, false>;
@@ -392,6 +402,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   const int64_t c0 = bos + int64_t(c) * kChunk;
   const int n = static_cast<int>(min(eos - c0, static_cast<int64_t>(kChunk)));
   const int64_t sbase = ((slot * a.H + h) * a.DV) * DK;
+  KDA_PHASE(unsigned long long gt_[9]; unsigned gs_[4] = {0, 0, 0, 0}; gt_[0] = __builtin_amdgcn_s_memtime();)
   const bf16* states = static_cast<const bf16*>(a.states) + sbase;
   const bf16* dstates = static_cast<const bf16*>(a.dstates) + sbase;
   const bf16* vin = static_cast<const bf16*>(a.v);
@@ -432,8 +443,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   cp.sEG = reinterpret_cast<float*>(smem + GL::oEG);
   cp.template load<DECAY>(c0, n);
   cp.template factors<DECAY, true>(n, false, 0, 0);
+  KDA_PHASE(gt_[1] = __builtin_amdgcn_s_memtime();)
   cp.products();
+  KDA_PHASE(gt_[2] = __builtin_amdgcn_s_memtime();)
   cp.inverse();
+  KDA_PHASE(gt_[3] = __builtin_amdgcn_s_memtime();)
 
   const int k0m = (16 * wave) & ~31;
   const int kend = 16 * (wave + 1);
@@ -467,6 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
 
   for (int vs = 0; vs < DV / VS; ++vs) {
     const int v0 = vs * VS;
+    KDA_PHASE(unsigned long long u0_ = __builtin_amdgcn_s_memtime(), u1_;)
     // H, dH' (and P = D dH') slices [VS][DK]; V and dO slices [64][VS]; d e^{G_n} partial
     // sums of this thread's eight keys from the same registers
 #pragma unroll
@@ -491,6 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
     }
     if (vs + 1 < DV / VS) fetch_slice(vs + 1);
     lds_barrier();
+    KDA_PHASE(u1_ = __builtin_amdgcn_s_memtime(); gs_[0] += unsigned(u1_ - u0_); u0_ = u1_;)
     f32x4 vreg[VS / 16];   // V in accumulator layout (rows of this wave)
 #pragma unroll
     for (int vb = 0; vb < VS / 16; ++vb)
@@ -526,6 +542,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       }
     }
     lds_barrier();
+    KDA_PHASE(u1_ = __builtin_amdgcn_s_memtime(); gs_[1] += unsigned(u1_ - u0_); u0_ = u1_;)
 
     // E = X R' -> E^T;  d(beta V) = X^T dE -> dv, and its dot with V
     {
@@ -554,6 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       }
     }
     lds_barrier();
+    KDA_PHASE(u1_ = __builtin_amdgcn_s_memtime(); gs_[2] += unsigned(u1_ - u0_); u0_ = u1_;)
 
     // this slice's dv rows leave as 16-byte pieces (one per thread)
     {
@@ -581,6 +599,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       }
     }
     lds_barrier();
+    KDA_PHASE(u1_ = __builtin_amdgcn_s_memtime(); gs_[3] += unsigned(u1_ - u0_);)
   }
 
   // ---- chunk-local algebra -------------------------------------------------------------
@@ -588,6 +607,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
   // compiler count the reads below exactly instead of waiting for all of them at the
   // first reuse of a slice register.
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+  KDA_PHASE(gt_[4] = __builtin_amdgcn_s_memtime();)
   // the chunk's raw k and q rows, requested now for the gradients at the end
   constexpr int KPT2 = kChunk * DK / 8 / kThreads;
   bf16x8 pk[KPT2], pq[KPT2];
@@ -703,6 +723,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
     }
   }
   lds_barrier();
+  KDA_PHASE(gt_[5] = __builtin_amdgcn_s_memtime();)
 
   // ---- gradients of k, q, beta, g ----------------------------------------------------
   // the chunk's raw k and q (bf16, exact) into LDS; each element's gradient then
@@ -717,6 +738,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
     *reinterpret_cast<bf16x8*>(sQ + r * LDK + c8) = pq[i];
   }
   lds_barrier();
+  KDA_PHASE(gt_[6] = __builtin_amdgcn_s_memtime();)
 
   // per element: dk, dq, and dL/dG = dKg Kg + dQg Qg - dKi Ki - dKh Kh, summed over the
   // rows at or below it within this wave's token block (suffix); the block totals, the
@@ -831,6 +853,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
     }
   }
   lds_barrier();
+  KDA_PHASE(gt_[7] = __builtin_amdgcn_s_memtime();)
 
   // dq, dk rows
   {
@@ -916,6 +939,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_grad_kernel(BwdArgs a) {
       }
     }
   }
+  KDA_PHASE({
+    gt_[8] = __builtin_amdgcn_s_memtime();
+    if (tid == 0 && blockIdx.x < kGradPhaseItems) {
+      unsigned int* w = g_grad_phase + blockIdx.x * kGradPhaseWords;
+      for (int i = 1; i < 9; ++i) w[i] = static_cast<unsigned>(gt_[i] - gt_[i - 1]);
+      for (int i = 0; i < 4; ++i) w[10 + i] = gs_[i];
+      w[15] = 1;
+    }
+  })
 }
 
 // ====================================================================================
@@ -969,3 +1001,25 @@ hipError_t launch_backward_grads(int dk, const BwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace kda
+
+#if defined(KDA_PHASE_STAMPS)
+// Timing build only: the gradient kernel's per-item phase rows (see g_grad_phase).
+namespace {
+__global__ void grad_phase_clear_kernel() {
+  for (int i = threadIdx.x; i < kda::kGradPhaseItems * kda::kGradPhaseWords; i += blockDim.x)
+    kda::g_grad_phase[i] = 0;
+}
+}  // namespace
+extern "C" int kda_grad_phase_words(void) { return kda::kGradPhaseItems * kda::kGradPhaseWords; }
+extern "C" int kda_grad_phase_clear(void) {
+  hipLaunchKernelGGL(grad_phase_clear_kernel, dim3(1), dim3(256), 0, 0);
+  return hipDeviceSynchronize() == hipSuccess ? 0 : 1;
+}
+extern "C" int kda_grad_phase_read(unsigned int* host) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(kda::g_grad_phase),
+                             sizeof(unsigned int) * kda::kGradPhaseItems * kda::kGradPhaseWords) ==
+                 hipSuccess
+             ? 0
+             : 1;
+}
+#endif

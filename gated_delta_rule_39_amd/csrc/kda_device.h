@@ -9,6 +9,14 @@
 
 #include "kda_launch.h"
 
+// Statements that only a timing build (-DKDA_PHASE_STAMPS) compiles: per-phase
+// s_memtime stamps of the long-running kernels.  Nothing in the product build.
+#if defined(KDA_PHASE_STAMPS)
+#define KDA_PHASE(...) __VA_ARGS__
+#else
+#define KDA_PHASE(...)
+#endif
+
 namespace kda {
 
 typedef __bf16 bf16;

@@ -261,7 +261,7 @@ __device__ __forceinline__ void raise_abort(int* abort_word) {
 // Each producer/consumer workgroup sums s_memtime ticks per phase of its chunk loop (the
 // phases are the stretches between mark(i - 1) and mark(i)) and writes the sums, its
 // chunk count and its role when it leaves; kda_phase_read() copies them out.  The
-// product build compiles none of it (KDA_PHASE expands to nothing).
+// product build compiles none of it (KDA_PHASE, kda_device.h, expands to nothing).
 #if defined(KDA_PHASE_STAMPS)
 constexpr int kPhaseWgs = 4096, kPhaseWords = 16;
 __device__ unsigned int g_phase[kPhaseWgs * kPhaseWords];
@@ -286,9 +286,6 @@ struct PhaseClock {
     w[15] = static_cast<unsigned>(role);
   }
 };
-#define KDA_PHASE(...) __VA_ARGS__
-#else
-#define KDA_PHASE(...)
 #endif
 
 // Wait (one lane) until *p >= target.  False if the wait ran out or the grid aborted;

@@ -43,7 +43,8 @@ def test_phase_stamps_only_in_the_timing_build():
     (_lib/phase/libkda.so, `python -m gated_delta_rule_39_amd.build --phases`): the
     product library exports no kda_phase_* function, the timing build (when built)
     exports all three."""
-    names = ("kda_phase_read", "kda_phase_clear", "kda_phase_words")
+    names = ("kda_phase_read", "kda_phase_clear", "kda_phase_words", "kda_grad_phase_read",
+             "kda_grad_phase_clear", "kda_grad_phase_words")
     L = kda.lib()
     for name in names:
         assert not hasattr(L, name), f"{name} in the product library"
