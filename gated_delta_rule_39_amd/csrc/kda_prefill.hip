@@ -522,13 +522,19 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     return true;
   };
   if (skip_empty()) load_state(cu);
+  // this wave's K step of the S^T operand, packed once per chunk: written to LDS for
+  // the other waves and kept in registers for its own products of the next chunk
+  bf16x8 sown[NVT];
 #pragma unroll
-  for (int vt = 0; vt < NVT; ++vt)
-    *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = pack_frag(S[0][vt], S[1][vt]);
+  for (int vt = 0; vt < NVT; ++vt) {
+    sown[vt] = pack_frag(S[0][vt], S[1][vt]);
+    *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = sown[vt];
+  }
 
   // this chunk's operands; each is reloaded from the next chunk's slot right after its
   // last use here, so a request has about one chunk of time to arrive
   bf16x8 U[NVT / 2];
+  f32x4 Uw[NVT];   // U widened to fp32: the E accumulators' initial values
   f32x4 eg[2];
   bf16x8 Wf[KS], Qf[KS], Mf[2], KDf[2][2];
   auto load_w = [&](uint32_t slot) {
@@ -560,6 +566,10 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     if (ok) {
 #pragma unroll
       for (int p = 0; p < NVT / 2; ++p) U[p] = ldf(offU(p));
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt)
+        Uw[vt] = vt % 2 ? widen(bf16x4{U[vt / 2][4], U[vt / 2][5], U[vt / 2][6], U[vt / 2][7]})
+                        : widen(bf16x4{U[vt / 2][0], U[vt / 2][1], U[vt / 2][2], U[vt / 2][3]});
       load_w(0);
       load_q(0);
       load_m(0);
@@ -630,8 +640,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       f32x4 E[NVT];
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) {
-        const bf16x8 u = U[vt / 2];
-        E[vt] = vt % 2 ? widen(bf16x4{u[4], u[5], u[6], u[7]}) : widen(bf16x4{u[0], u[1], u[2], u[3]});
+        E[vt] = Uw[vt];
         Ot[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
@@ -640,7 +649,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       // step is its state packed as written to LDS at the end of the last chunk.
       bf16x8 sb[KS][NVT];
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) sb[0][vt] = pack_frag(S[0][vt], S[1][vt]);
+      for (int vt = 0; vt < NVT; ++vt) sb[0][vt] = sown[vt];
 #pragma unroll
       for (int j = 1; j < KS; ++j)
 #pragma unroll
@@ -659,11 +668,16 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
             bf16x4{static_cast<bf16>(e[0]), static_cast<bf16>(e[1]), static_cast<bf16>(e[2]),
                    static_cast<bf16>(e[3])};
       }
-      // D S^T for this wave's keys, while the other waves finish E
+      // D S^T for this wave's keys, while the E products run: the empty asm keeps the
+      // multiplies ahead of the barrier (the compiler would otherwise sink them to the
+      // state update, where they delay its products)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) S[b][vt] *= eg[b];
+        for (int vt = 0; vt < NVT; ++vt) {
+          S[b][vt] *= eg[b];
+          asm volatile("" : "+v"(S[b][vt]));
+        }
       lds_barrier();
       KDA_PHASE(phc.mark(2);)
       bf16x8 eb[2][NVT];
@@ -693,6 +707,12 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 #pragma unroll
           for (int vt = 0; vt < NVT; ++vt) S[b][vt] = mma_bf16(KDf[b][t], eb[t][vt], S[b][vt]);
       KDA_PHASE(phc.mark(4);)
+      // the next chunk's U (requested at this chunk's start) widened while the state
+      // products run
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt)
+        Uw[vt] = vt % 2 ? widen(bf16x4{U[vt / 2][4], U[vt / 2][5], U[vt / 2][6], U[vt / 2][7]})
+                        : widen(bf16x4{U[vt / 2][0], U[vt / 2][1], U[vt / 2][2], U[vt / 2][3]});
       load_kd(nslot);
       // the previous chunk's output rows, from this wave's LDS rows (after the operand
       // requests: stores complete in order with the loads, and the next chunk waits
@@ -708,7 +728,8 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       // the next chunk's S^T operand (K step w) and this chunk's output rows
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) {
-        *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = pack_frag(S[0][vt], S[1][vt]);
+        sown[vt] = pack_frag(S[0][vt], S[1][vt]);
+        *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = sown[vt];
         const f32x4 x = Ot[vt] * oscale;
         *reinterpret_cast<bf16x4*>(sO + ((16 * wave + lr) * CL::LDO + 16 * vt + 4 * lq) * 2) =
             bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
@@ -741,8 +762,10 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     skip_empty();
     load_state(cu);
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt)
-      *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = pack_frag(S[0][vt], S[1][vt]);
+    for (int vt = 0; vt < NVT; ++vt) {
+      sown[vt] = pack_frag(S[0][vt], S[1][vt]);
+      *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = sown[vt];
+    }
     lds_barrier();
   }
 
