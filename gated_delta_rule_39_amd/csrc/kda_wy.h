@@ -542,20 +542,30 @@ struct WyProducer {
         if (rgv * RPGV + i >= n) vr[i] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
     // alpha = e^g in place (one per row and head: already done); per-thread product
-    // of its rows
-    f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
+    // of its rows.  With one decay per (row, head) every channel of a row carries the
+    // same factor, so its running products are kept as scalars (the same products in
+    // the same order as the per-channel form, so the tiles are bit for bit those of a
+    // per-channel g broadcast over the channels); with no decay every factor is 1 and
+    // the tiles are the inputs themselves.
+    [[maybe_unused]] f32x4 tot = f32x4{1.f, 1.f, 1.f, 1.f};
+    [[maybe_unused]] float tot1 = 1.f;
+    if constexpr (DECAY == 0) {
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      if constexpr (DECAY != 1) {
+      for (int i = 0; i < RPG; ++i) {
         const f32x4 gg = gr[i];
         gr[i] = f32x4{exp_hw(gg[0]), exp_hw(gg[1]), exp_hw(gg[2]), exp_hw(gg[3])};
+        tot *= gr[i];
       }
-      tot *= gr[i];
+      store4(sScr + rg * DK + j0, tot);
+    } else if constexpr (DECAY == 1) {
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) tot1 *= gr[i][0];
+      if (j0 == 0) sScr[rg * DK] = tot1;
     }
-    store4(sScr + rg * DK + j0, tot);
     if constexpr (DECAY != 2) {
       constexpr float kStrongTot = 4.5399930e-05f;   // e^{-10}
-      if (min(min(tot[0], tot[1]), min(tot[2], tot[3])) < kStrongTot) *sStrong = tag;
+      const float tmin = DECAY == 1 ? tot1 : min(min(tot[0], tot[1]), min(tot[2], tot[3]));
+      if (tmin < kStrongTot) *sStrong = tag;
     }
     if (tid < kChunk)
       sBeta[tid] = tid < n ? ((flags & kBetaLogit) ? sigmoid_hw(br) : br) : 0.f;
@@ -564,6 +574,66 @@ struct WyProducer {
     for (int i = 0; i < RPGV; ++i)
       *reinterpret_cast<u32x4*>(sV + (rgv * RPGV + i) * LDV + jv0) = __builtin_bit_cast(u32x4, vr[i]);
     lds_barrier();
+    if constexpr (DECAY == 2) {
+      // Kg = Ki = KD = k and Qg = q (times the scale with QSCALE): the input rows as
+      // loaded; e^{G_n} = 1
+      strong = false;
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const int r = (rg * RPG + i) * LDK + j0;
+        *reinterpret_cast<bf16x4*>(sKg + r) = kr[i];
+        *reinterpret_cast<bf16x4*>(sKD + r) = kr[i];
+        *reinterpret_cast<bf16x4*>(sKi + r) = kr[i];
+        if constexpr (QSCALE)
+          store4(sQg + r, widen(qr[i]) * scale);
+        else
+          *reinterpret_cast<bf16x4*>(sQg + r) = qr[i];
+      }
+      if (rg == 0) store4(sEgn + j0, f32x4{1.f, 1.f, 1.f, 1.f});
+      return;
+    } else if constexpr (DECAY == 1) {
+      strong = __builtin_amdgcn_readfirstlane(*sStrong == tag ? 1 : 0) != 0;
+      float tt[RG];
+#pragma unroll
+      for (int r2 = 0; r2 < RG; ++r2) tt[r2] = sScr[r2 * DK];
+      float cp = 1.f, cs = 1.f;
+#pragma unroll
+      for (int r2 = 0; r2 < RG; ++r2) {
+        if (r2 < rg) cp *= tt[r2];
+        if (r2 > rg) cs *= tt[r2];
+      }
+      const float egn = cp * tot1 * cs;   // e^{G_n}
+      if (strong) {
+        f32x4 tots[RG];
+#pragma unroll
+        for (int r2 = 0; r2 < RG; ++r2) tots[r2] = f32x4{tt[r2], tt[r2], tt[r2], tt[r2]};
+        strong_factors<QSCALE>(tots, f32x4{cs, cs, cs, cs}, n);
+        if (rg == 0) store4(sEgn + j0, f32x4{egn, egn, egn, egn});
+        return;
+      }
+      f32x4 kf[RPG];
+      float run = cp;
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        run *= gr[i][0];
+        kf[i] = widen(kr[i]);
+        f32x4 q4 = widen(qr[i]);
+        if constexpr (QSCALE) q4 *= scale;
+        store4(sKg + (rg * RPG + i) * LDK + j0, kf[i] * run);
+        store4(sQg + (rg * RPG + i) * LDK + j0, q4 * run);
+      }
+      const float rn = __builtin_amdgcn_rcpf(egn);
+      float sfx = cs;
+#pragma unroll
+      for (int i = RPG - 1; i >= 0; --i) {
+        const f32x4 kd = kf[i] * sfx;
+        store4(sKD + (rg * RPG + i) * LDK + j0, kd);
+        store4(sKi + (rg * RPG + i) * LDK + j0, kd * rn);
+        sfx *= gr[i][0];
+      }
+      if (rg == 0) store4(sEgn + j0, f32x4{egn, egn, egn, egn});
+      return;
+    }
     strong = __builtin_amdgcn_readfirstlane(*sStrong == tag ? 1 : 0) != 0;
     f32x4 tots[RG];
 #pragma unroll
