@@ -72,8 +72,9 @@ enum { KDA_DECAY_CHANNEL = 0, KDA_DECAY_HEAD = 1, KDA_DECAY_NONE = 2 };
  * normalized?"), a sigmoid-like retention and a positive write strength ("Kimi
  * Delta Attention Technical Deep Dive", "From attention to recurrent state").
  *   KDA_PRO_NORM_K      k is raw: each (token, head) row is replaced by
- *                       k / sqrt(sum_j k_j^2 + 1e-6) before use (bf16 keys are
- *                       rounded to bf16 again after the division)
+ *                       k / sqrt(sum_j k_j^2 + 1e-6) before use (the prefill
+ *                       rounds the unit key of bf16 inputs to bf16 again, its
+ *                       MFMA operand type; the decode step keeps it in fp32)
  *   KDA_PRO_BETA_LOGIT  beta holds logits: beta <- 1 / (1 + exp(-beta))
  *   KDA_PRO_GATE_LOGIT  g holds retention logits a: alpha = 1 / (1 + exp(-a))
  *                       (instead of alpha = exp(g)); ignored with KDA_DECAY_NONE
