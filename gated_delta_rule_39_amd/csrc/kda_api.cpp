@@ -88,13 +88,18 @@ struct CoopPlan {
   bool plan = false;   // lanes < units: a device plan spreads the units over the lanes
   bool ok() const { return NC > 0; }
 };
-// flags: the prologue flags of the call.  With any of them on, the producers also
-// normalise keys and turn logits into gates, and a sixth producer pays off where the
-// grid has room (same box, T=65536, H=32, all flags: 1.581 ms with six, 1.679 ms with
-// five; plain inputs: 1.616 against 1.548 ms, so five stay the default).  Neither the
-// workspace size nor the lane count depends on it.
+// Producers per lane for a prefill call.  Six where the producers set the pace — any
+// decay, or the prologue flags (then they also normalise keys and turn logits into
+// gates) — and five without decay, whose consumers set it (same box, T=65536, H=32:
+// per-channel decay 1.435 ms with six against 1.517 with five, per-head decay 1.360 vs
+// 1.501, the prologue flags 1.432 vs 1.638, no decay 1.445 vs 1.344; B=16, H=32,
+// T=4096 1.477 vs 1.533; the varlen workload 0.662 vs 0.663).  The backward's sweep,
+// measured no faster with six, keeps five.
+int max_producers(int decay, int flags) { return (flags != 0 || decay != KDA_DECAY_NONE) ? 6 : 5; }
+// max_np: producers per lane where the grid has room for them (max_producers below).
+// Neither the workspace size nor the lane count depends on it.
 CoopPlan coop_plan(int dtype, int64_t units, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
-                   int cus, int flags = 0) {
+                   int cus, int max_np) {
   CoopPlan p;
   if (dtype != KDA_BF16 || units <= 0 || env_int("KDA_PREFILL_COOP", 1) == 0) return p;
   // the producers read a chunk's inputs through buffer resources with 31-bit byte
@@ -110,7 +115,7 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t N, int32_t H, int32_t d_k, 
       L >= 8 && N <= kPlanMaxSeqs && units <= kPlanMaxUnits && lanes_mode != 0) {
     p.NC = 2;
     p.NP = lw - 2;
-    if (enp == 0 && flags != 0 && L * (kLaneW + 1) <= cus) p.NP = kLaneW - 1;
+    if (enp == 0 && max_np > kLaneW - 2 && L * (kLaneW + 1) <= cus) p.NP = kLaneW - 1;
     p.R = env_int("KDA_COOP_R", ring_slots(p.NP));
     if (p.R < 3) p.R = 3;
     p.lanes = L;
@@ -123,7 +128,6 @@ CoopPlan coop_plan(int dtype, int64_t units, int32_t N, int32_t H, int32_t d_k, 
   int nc = (d_v == 128 && W >= 6) ? 2 : 1;
   const int enc = env_int("KDA_COOP_NC", 0);
   if (enc > 0 && d_v % (4 * enc) == 0 && (d_v / (4 * enc) == 16 || d_v / (4 * enc) == 32)) nc = enc;
-  const int max_np = flags != 0 ? 6 : 5;
   int np = W - nc < max_np ? W - nc : max_np;
   if (enp > 0) np = enp;
   if (np < 1 || static_cast<int64_t>(units) * (nc + np) > cus) return p;
@@ -183,7 +187,8 @@ size_t kda_prefill_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_
   if (N <= 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
   const int64_t units = static_cast<int64_t>(N) * H;
   if (units > (1 << 24)) return 0;
-  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cu_count());
+  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cu_count(),
+                               max_producers(KDA_DECAY_CHANNEL, 0));
   if (!p.ok()) return 0;
   return coop_ws_bytes(p, d_k, d_v, units);
 }
@@ -195,7 +200,8 @@ int kda_prefill_coop_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t 
   if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
   const int64_t units = static_cast<int64_t>(N) * H;
   if (units > (1 << 24)) return KDA_ERR_BAD_SHAPE;
-  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cu_count());
+  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cu_count(),
+                               max_producers(KDA_DECAY_CHANNEL, 0));
   if (consumers) *consumers = p.NC;
   if (producers) *producers = p.NP;
   if (ring_slots) *ring_slots = p.R;
@@ -207,7 +213,8 @@ int kda_prefill_coop_lanes(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t
   if (N <= 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
   const int64_t units = static_cast<int64_t>(N) * H;
   if (units > (1 << 24)) return 0;
-  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cu_count());
+  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cu_count(),
+                               max_producers(KDA_DECAY_CHANNEL, 0));
   return p.ok() ? p.lanes : 0;
 }
 
@@ -287,7 +294,7 @@ int kda_prefill_ex(int dtype, int decay, int flags, const void* q, const void* k
   a.decay = decay;
   a.flags = flags;
   const int cus = cu_count();
-  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cus, flags);
+  const CoopPlan p = coop_plan(dtype, units, N, H, d_k, d_v, cus, max_producers(decay, flags));
   if (p.ok() && workspace != nullptr && workspace_bytes >= coop_ws_bytes(p, d_k, d_v, units)) {
     set_coop(a, p, workspace);
     if (kda::launch_prefill_coop(d_k, a, stream) == hipSuccess) return KDA_OK;
@@ -355,7 +362,7 @@ BwdPlan bwd_plan(int32_t N, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v
   const int64_t units = static_cast<int64_t>(N) * H;
   b.states = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H * d_v * d_k * 2);
   b.tiles = static_cast<size_t>(kda::chunk_slots_host(T_total, N) * H) * kda::chain_tile_bytes(d_k);
-  CoopPlan p = coop_plan(KDA_BF16, units, N, H, d_k, d_v, cu_count());
+  CoopPlan p = coop_plan(KDA_BF16, units, N, H, d_k, d_v, cu_count(), 5);
   // the sweep keeps NP + 6 slots: the deeper forward ring measured no faster here
   // (8.33-8.39 vs 8.40-8.42 ms per call at T=65536, H=32) and costs 30 MB more
   if (p.ok()) p.R = env_int("KDA_COOP_R", p.NP + 6);

@@ -551,11 +551,13 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   };
   auto load_kd = [&](uint32_t slot) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int t = 0; t < 2; ++t) KDf[b][t] = ldf(slot + offKD(b, t));
-      eg[b] = ldv(slot + offEg(b));
-    }
+  };
+  auto load_eg = [&](uint32_t slot) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) eg[b] = ldv(slot + offEg(b));
   };
 
   bool ok = true, nok = true;
@@ -570,7 +572,10 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       for (int vt = 0; vt < NVT; ++vt)
         Uw[vt] = vt % 2 ? widen(bf16x4{U[vt / 2][4], U[vt / 2][5], U[vt / 2][6], U[vt / 2][7]})
                         : widen(bf16x4{U[vt / 2][0], U[vt / 2][1], U[vt / 2][2], U[vt / 2][3]});
+      // the order of the loop's own requests (U, W, e^{G_n}, Qg, M, KD^T), so the
+      // compiler's count of loads in flight agrees on both paths into the loop
       load_w(0);
+      load_eg(0);
       load_q(0);
       load_m(0);
       load_kd(0);
@@ -678,6 +683,10 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
           S[b][vt] *= eg[b];
           asm volatile("" : "+v"(S[b][vt]));
         }
+      // the next chunk's e^{G_n}, right after its last use: requested here rather than
+      // with KD^T at the chunk's end, its wait in the next chunk's E phase does not
+      // also wait for the operand requests that follow it
+      load_eg(nslot);
       lds_barrier();
       KDA_PHASE(phc.mark(2);)
       bf16x8 eb[2][NVT];
@@ -710,9 +719,11 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       // the next chunk's U (requested at this chunk's start) widened while the state
       // products run
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt)
+      for (int vt = 0; vt < NVT; ++vt) {
         Uw[vt] = vt % 2 ? widen(bf16x4{U[vt / 2][4], U[vt / 2][5], U[vt / 2][6], U[vt / 2][7]})
                         : widen(bf16x4{U[vt / 2][0], U[vt / 2][1], U[vt / 2][2], U[vt / 2][3]});
+        asm volatile("" : "+v"(Uw[vt]));   // here, not after the end-of-chunk barrier
+      }
       load_kd(nslot);
       // the previous chunk's output rows, from this wave's LDS rows (after the operand
       // requests: stores complete in order with the loads, and the next chunk waits

@@ -174,9 +174,9 @@ size_t kda_prefill_workspace_bytes(int dtype, int32_t N, int64_t T_total, int32_
 
 /* Geometry of the producer/consumer prefill on the current device: value-tile
  * workgroups (consumers), producer workgroups per lane and ring slots; all zero when
- * it does not apply.  For a call without prologue flags; with flags one more producer
- * runs where the grid has room (the workspace size is the same).  Output pointers may
- * be NULL. */
+ * it does not apply.  For a call with per-channel decay (kda_prefill); a call without
+ * decay and without prologue flags runs one producer fewer where six would fit (the
+ * workspace size is the same).  Output pointers may be NULL. */
 int kda_prefill_coop_plan(int dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
                           int32_t* consumers, int32_t* producers, int32_t* ring_slots);
 
