@@ -74,13 +74,14 @@ int env_int(const char* name, int dflt) {
 // length.  Up to 256 sequences and 8192 units; KDA_COOP_LANES=0 disables it, =2 takes
 // it whenever the units outnumber the lanes (tuning only).
 constexpr int kLaneW = 7, kLaneMinW = 4;
-// Ring slots per lane.  With five producers, 24 (same-box sweeps at T=65536, H=32, ms
-// per launch: R = 11 1.650, 16 1.600, 20 1.559, 24 1.537, 27 1.536, 32 1.538; B16 H32
-// T4096 1.702 at 11, 1.555 at 24; no decay 1.734 at 11, 1.546 at 20): the deeper
-// ring lets the producers run ahead through the consumers' jitter.  Fewer producers:
-// NP + 6 (B4 H16 T4096 at NP = 3: 9 and 14 slots measure the same).  Every default
-// plan on a 256-CU device stays within 64 MiB of workspace.
-constexpr int kDeepRing = 24;
+// Ring slots per lane.  With five or six producers, 32 (same-box sweeps at T=65536,
+// H=32, ms per launch, six producers: R = 12 1.525, 16 1.495, 20 1.456, 24 1.449-1.451,
+// 32 1.417, 40 1.411, 48 1.410; B16 H32 T4096 1.441 at 24, 1.403 at 32; varlen 0.658 at
+// 24, 0.629 at 32; earlier, five producers: 11 1.650, 24 1.537): the deeper ring lets
+// the producers run ahead through the consumers' jitter.  Fewer producers: NP + 6 (B4
+// H16 T4096 at NP = 3: 9 and 14 slots measure the same).  Every default plan on a
+// 256-CU device stays within 85 MiB of workspace (d_k = 128, d_v = 64, 42 units).
+constexpr int kDeepRing = 32;
 int ring_slots(int np) { return np >= 5 ? kDeepRing : np + 6; }
 constexpr int kPlanMaxSeqs = 256, kPlanMaxUnits = 8192, kPlanMaxLanes = 64;
 struct CoopPlan {

@@ -17,19 +17,19 @@ extern "C" {
 enum { KDA_ERR_SCRATCH = 7 };
 
 /* Bytes of the per-device scratch array behind kda_prefill_noalloc. */
-#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define KDA_NOALLOC_SCRATCH_BYTES (96u << 20)
 
 /*
  * kda_prefill_noalloc -- kda_prefill_ex for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments without a workspace; the producer/consumer kernel's
- * workspace is a library-owned device array of KDA_NOALLOC_SCRATCH_BYTES (64 MiB) per
+ * workspace is a library-owned device array of KDA_NOALLOC_SCRATCH_BYTES (96 MiB) per
  * device, held from the first call on that device until the process ends.  The call
  * makes no allocation of any kind.  Returns KDA_ERR_SCRATCH, launching nothing, when
  * the call needs more (kda_prefill_workspace_bytes() above the limit).  With the
  * default plans on a 256-CU device every call fits: at d_k = d_v = 128 the units
- * share at most 32 lanes whatever their number (about 54 MiB), and one unit per lane
- * needs at most about 63 MiB (d_k = 128, d_v = 64, 42 units).  When the fused kernel applies (fp32, or no
+ * share at most 32 lanes whatever their number (about 72 MiB), and one unit per lane
+ * needs at most about 84 MiB (d_k = 128, d_v = 64, 42 units).  When the fused kernel applies (fp32, or no
  * producer/consumer plan) it runs without scratch.  Every call on one
  * device shares that device's array: calls that overlap in time on one device (other
  * streams, other threads) race and give undefined results; calls ordered on one
