@@ -357,14 +357,16 @@ struct WyConsumerLayout {
 };
 
 // Split consumer LDS: the bf16 S^T operand fragments [KS][4] (1 KiB each), the bf16 E
-// operand fragments [2][4], one output tile [64][64 + 8] bf16, flags.
+// operand fragments [2][4], two output tiles [64][64 + 8] bf16 (chunk g's in tile g % 2),
+// flags.
 struct WySplitLayout {
   static constexpr int NVT = 4;                 // 64 value columns per consumer
   static constexpr int LDO = 16 * NVT + 8;
   static constexpr size_t oSb = 0;
   static constexpr size_t oEb = oSb + size_t(4) * NVT * 1024;
   static constexpr size_t oO = oEb + size_t(2) * NVT * 1024;
-  static constexpr size_t oFlag = oO + size_t(kChunk) * LDO * 2;
+  static constexpr size_t kOBytes = size_t(kChunk) * LDO * 2;
+  static constexpr size_t oFlag = oO + 2 * kOBytes;
   static constexpr size_t kBytes = oFlag + 16;
 };
 
@@ -464,16 +466,24 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   auto eb_at = [&](int t, int vt) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(sEb + (t * NVT + vt) * 1024);
   };
-  // output rows of this wave (token block w) from the LDS tile to o for head hh; rows
-  // >= `rows` of the window starting at token row cs are dropped
-  auto store_rows = [&](int64_t cs, int rows, int hh) {
+  // output rows of this wave (token block w) of chunk gg from its LDS tile to o for head
+  // hh; rows >= `rows` of the window starting at token row cs are dropped
+  auto store_rows = [&](int64_t cs, int rows, int hh, int gg) {
+    const unsigned char* ob = sO + (gg & 1) * CL::kOBytes;
+    // the window is the same for every lane: made wave-uniform, the buffer stores need
+    // no loop over distinct descriptors
+    cs = static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(
+             __builtin_amdgcn_readfirstlane(static_cast<int>(cs >> 32)))) << 32) |
+                              static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(cs))));
+    rows = __builtin_amdgcn_readfirstlane(rows);
+    hh = __builtin_amdgcn_readfirstlane(hh);
     const __amdgpu_buffer_rsrc_t win = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<bf16*>(a.o) + (cs * a.H + hh) * DV + v0, 0,
         static_cast<int>(uint32_t(rows) * rowO * 2), 0x00020000);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 16 * wave + 8 * i + lane / 8, col = 8 * (lane % 8);
-      const u32x4 x = *reinterpret_cast<const u32x4*>(sO + (r * CL::LDO + col) * 2);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(ob + (r * CL::LDO + col) * 2);
       __builtin_amdgcn_raw_buffer_store_b128(x, win, (r * rowO + col) * 2, 0, 0);
     }
   };
@@ -716,6 +726,16 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 #pragma unroll
           for (int vt = 0; vt < NVT; ++vt) S[b][vt] = mma_bf16(KDf[b][t], eb[t][vt], S[b][vt]);
       KDA_PHASE(phc.mark(4);)
+      // this chunk's output rows into its LDS tile while the state products run (the
+      // other tile holds the previous chunk's rows until they are stored below)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        const f32x4 x = Ot[vt] * oscale;
+        *reinterpret_cast<bf16x4*>(sO + (g & 1) * CL::kOBytes +
+                                   ((16 * wave + lr) * CL::LDO + 16 * vt + 4 * lq) * 2) =
+            bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                   static_cast<bf16>(x[3])};
+      }
       // the next chunk's U (requested at this chunk's start) widened while the state
       // products run
 #pragma unroll
@@ -728,7 +748,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       // the previous chunk's output rows, from this wave's LDS rows (after the operand
       // requests: stores complete in order with the loads, and the next chunk waits
       // for those)
-      if (g > 0 && write_o) store_rows(pc0, prows, ph);
+      if (g > 0 && write_o) store_rows(pc0, prows, ph, g - 1);
       // every wave has used chunk g - 1's operands (at the last barrier): its slot is
       // free.  Released here, after the operand requests, for the same reason.
       if (tid == 0 && g > 0) __hip_atomic_fetch_add(done + sp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -736,15 +756,11 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
       pc0 = c0;
       prows = static_cast<int>(min(ueos - c0, static_cast<int64_t>(kChunk)));
       ph = uh;
-      // the next chunk's S^T operand (K step w) and this chunk's output rows
+      // the next chunk's S^T operand (K step w)
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) {
         sown[vt] = pack_frag(S[0][vt], S[1][vt]);
         *reinterpret_cast<bf16x8*>(sSb + (wave * NVT + vt) * 1024) = sown[vt];
-        const f32x4 x = Ot[vt] * oscale;
-        *reinterpret_cast<bf16x4*>(sO + ((16 * wave + lr) * CL::LDO + 16 * vt + 4 * lq) * 2) =
-            bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
-                   static_cast<bf16>(x[3])};
       }
       // S^T is now the state at the start of chunk g + 1 (none after the unit's last)
       if constexpr (STATES) store_ckpt(g + 1, g + 1 < uend);
@@ -782,7 +798,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
 
   KDA_PHASE(phc.write(tid, role);)
   // the last chunk's output rows (written before the loop's last barrier)
-  if (ok && total > 0 && write_o) store_rows(pc0, prows, ph);
+  if (ok && total > 0 && write_o) store_rows(pc0, prows, ph, g - 1);
   // units after the last one with chunks: empty, they keep their initial state
   if (ok && total > 0) {
     while (iu + 1 < nu) {
@@ -797,7 +813,7 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
   if (!ok) {
     // the rows of the last completed chunk are valid; when they belong to an earlier
     // unit than the one in progress they are stored (otherwise that unit is poisoned)
-    if (punit >= 0 && punit != cu.unit && write_o) store_rows(pc0, prows, ph);
+    if (punit >= 0 && punit != cu.unit && write_o) store_rows(pc0, prows, ph, g - 1);
     // the unit in progress and every later one did not complete
     for (;;) {
       poison_outputs<DK, DV, STATES>(a, cu.n_seq, cu.h, cu.bos, cu.eos, cu.nch, v0, 16 * NVT, tid);
