@@ -480,12 +480,13 @@ __device__ __forceinline__ void wy_consume_split(const PrefillArgs& a, unsigned 
     const __amdgpu_buffer_rsrc_t win = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<bf16*>(a.o) + (cs * a.H + hh) * DV + v0, 0,
         static_cast<int>(uint32_t(rows) * rowO * 2), 0x00020000);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 16 * wave + 8 * i + lane / 8, col = 8 * (lane % 8);
-      const u32x4 x = *reinterpret_cast<const u32x4*>(ob + (r * CL::LDO + col) * 2);
-      __builtin_amdgcn_raw_buffer_store_b128(x, win, (r * rowO + col) * 2, 0, 0);
-    }
+    // both LDS reads before either store (the compiler keeps LDS reads behind a buffer
+    // store, which would serialise two read round trips)
+    const int r0 = 16 * wave + lane / 8, col = 8 * (lane % 8);
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(ob + (r0 * CL::LDO + col) * 2);
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(ob + ((r0 + 8) * CL::LDO + col) * 2);
+    __builtin_amdgcn_raw_buffer_store_b128(x0, win, (r0 * rowO + col) * 2, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(x1, win, ((r0 + 8) * rowO + col) * 2, 0, 0);
   };
 
   // S^T rows of this wave: S[b][vt] holds S^T[32 w + 16 b + 4 lq + i][v0 + 16 vt + lr]
