@@ -59,15 +59,16 @@ int env_int(const char* name, int dflt) {
 
 // Producer/consumer geometry: W = CUs / units workgroups per unit (all resident at
 // once, one per CU): NC consumers, each 4 waves owning d_v / (4 NC) value columns
-// (NC = 2 for d_v = 128 when W >= 6, else 1), and NP = min(W - NC, 5) producers
-// (measured: past five producers per unit the consumers set the pace), and
-// ring_slots(NP) ring slots.  Needs bf16 inputs and W >= 2.  KDA_PREFILL_COOP=0
+// (NC = 2 for d_v = 128 when W >= 6, else 1), and NP = min(W - NC, max_np) producers
+// (max_producers: six, or five for a call without decay, whose consumers set the pace
+// sooner), and ring_slots(NP) ring slots.  Needs bf16 inputs and W >= 2.  KDA_PREFILL_COOP=0
 // disables it; KDA_COOP_NC / KDA_COOP_NP / KDA_COOP_R override the split and the ring
 // depth (tuning only).
 // Lanes: with d_k = d_v = 128, when the units leave fewer than four workgroups each
 // (measured: a unit per set of four still beats two units one after another on seven),
 // the units are spread over lanes of seven workgroups (two consumers, five producers;
-// as many lanes as the device fits, rounded down to whole XCD groups) by a plan made
+// as many lanes as the device fits, rounded down to whole XCD groups; a sixth producer
+// per lane where the grid has room, as max_producers says) by a plan made
 // on the device from cu_seqlens (coop_prep_kernel), longest sequences first, and each
 // lane works through its units one after another.  This keeps every unit on the
 // producer/consumer kernel however many there are, and balances sequences of unequal
